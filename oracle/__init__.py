@@ -1,0 +1,258 @@
+"""CPU oracle for the MLA Prolog (numpy/ctypes front end of ``mlap_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It shares no code
+with the HIP path (``mla_prolog_amd``) and never imports it; the only module
+both sides use is the seeded input generator ``synth``.
+
+Every function documents the passage of the pages it follows; the arithmetic
+itself lives in ``mlap_oracle.c``. Pins: ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mlap_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-std=c11", "-Wall", "-Wno-unknown-pragmas"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (plain C, OpenMP over token rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cfg(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("hidden", "q_lora", "kv_lora", "rope_dim", "nope_dim",
+                                          "v_dim", "n_heads", "max_pos")] + \
+               [("eps", C.c_float), ("w8a8", C.c_int32)]
+
+
+class _Inputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("x", "positions", "w_qa", "w_qb", "w_kva", "w_kvb",
+                                          "ws_qa", "ws_qb", "ws_kva", "ws_kvb", "gamma_q",
+                                          "gamma_kv", "cos", "sin")]
+
+
+_OUT_FIELDS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_i8",
+               "q_scale", "kv_i8", "kv_scale")
+
+
+class _Outputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _OUT_FIELDS]
+
+
+def load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = C.CDLL(_LIB_PATH)
+            lib.orc_bf16.restype = C.c_uint16
+            lib.orc_bf16.argtypes = [C.c_float]
+            lib.orc_bf16_array.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+            lib.orc_gemm_bf16.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                          C.c_void_p]
+            lib.orc_gemm_i8.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                        C.c_void_p]
+            lib.orc_gemm_i8.restype = C.c_int
+            lib.orc_rmsnorm_row.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_float,
+                                            C.c_void_p]
+            lib.orc_rope_row.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+            lib.orc_quant_row.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+            lib.orc_prolog.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p, C.c_int32,
+                                       C.POINTER(_Outputs)]
+            lib.orc_prolog.restype = C.c_int
+            lib.orc_num_threads.restype = C.c_int
+            _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _np(t, dtype=None):
+    """torch tensor or numpy array -> contiguous numpy array (bf16 -> uint16 bits)."""
+    if t is None:
+        return None
+    if hasattr(t, "detach"):
+        import torch
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        t = t.numpy()
+    a = np.ascontiguousarray(t)
+    if dtype is not None:
+        a = a.astype(dtype, copy=False)
+    return a
+
+
+def num_threads() -> int:
+    return int(load().orc_num_threads())
+
+
+# ----------------------------------------------------------------- pieces ----
+
+def bf16(v):
+    """fp32 -> bf16 bits, round to nearest even (definition-based; see mlap_oracle.c)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    load().orc_bf16_array(_p(v), _p(out), v.size)
+    return out
+
+
+def f32(b):
+    """bf16 bits -> fp32 (exact widening)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def gemm_bf16(X, W):
+    """Y = bf16(fp32(sum_k X W^T)) with an fp64 sum; X [M,K], W [N,K] as bf16 bits.
+
+    AT-10 card (matmul with BF16 out, weight [N,K], b_trans) -- "PyPTO-Gym 算子设计模式
+    AT-10", sections 二 and 五."""
+    X, W = _np(X, np.uint16), _np(W, np.uint16)
+    M, K = X.shape
+    N, K2 = W.shape
+    assert K == K2
+    Y = np.empty((M, N), np.uint16)
+    load().orc_gemm_bf16(_p(X), _p(W), M, N, K, _p(Y))
+    return Y
+
+
+def gemm_i8(A, B):
+    """Exact int32 C = A B^T for int8 A [M,K], B [N,K] (AT-09 INT8 W8A8 matmul, section 四)."""
+    A, B = _np(A, np.int8), _np(B, np.int8)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2
+    Cm = np.empty((M, N), np.int32)
+    rc = load().orc_gemm_i8(_p(A), _p(B), M, N, K, _p(Cm))
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow")
+    return Cm
+
+
+def rmsnorm_row(v, gamma, eps):
+    """RMSNorm variant B (sqrt then divide) in fp32, times fp32(gamma), cast to bf16.
+
+    AT-10 card, section 三 (variant B) and section 五 (gamma in fp32, then BF16)."""
+    v = _np(v, np.uint16).reshape(-1)
+    g = None if gamma is None else _np(gamma, np.uint16).reshape(-1)
+    out = np.empty_like(v)
+    load().orc_rmsnorm_row(_p(v), _p(g), v.size, C.c_float(eps), _p(out))
+    return out
+
+
+def rope_row(u, c, s):
+    """Rotate-half RoPE of one slice: x*cos + rotate_half(x)*sin, fp32, back to bf16.
+
+    "PyPTO Operator 深度解析", section 3.3 (QuantRope, RotateHalf)."""
+    u = _np(u, np.uint16).reshape(-1)
+    c = np.ascontiguousarray(c, np.float32).reshape(-1)
+    s = np.ascontiguousarray(s, np.float32).reshape(-1)
+    out = np.empty_like(u)
+    load().orc_rope_row(_p(u), _p(c), _p(s), u.size, _p(out))
+    return out
+
+
+def quant_row(z):
+    """Per-row dynamic symmetric INT8: m = 127/amax, rint(z*m) saturated, scale = amax/127.
+
+    "PyPTO Operator 深度解析", section 3.1 (PrologQuant); grouped_matmul_swiglu_quant
+    article, section 实现特点 5."""
+    z = _np(z, np.uint16).reshape(-1)
+    codes = np.empty(z.size, np.int8)
+    sc = np.zeros(1, np.float32)
+    load().orc_quant_row(_p(z), z.size, _p(codes), _p(sc))
+    return codes, float(sc[0])
+
+
+def quant_rows(Z):
+    """quant_row over each row of a 2-D bf16 array."""
+    Z = _np(Z, np.uint16)
+    Z2 = Z.reshape(Z.shape[0], -1)
+    codes = np.empty(Z2.shape, np.int8)
+    scales = np.empty(Z2.shape[0], np.float32)
+    for i in range(Z2.shape[0]):
+        codes[i], scales[i] = quant_row(Z2[i])
+    return codes.reshape(Z.shape), scales
+
+
+# ----------------------------------------------------------------- prolog ----
+
+def prolog(cfg, inputs, rows=None):
+    """Run the whole MLA Prolog for token ``rows`` (default: all) of ``inputs``.
+
+    ``cfg`` is a ``synth.Config`` (or anything with its attributes); ``inputs``
+    the dict from ``synth.make_inputs``. Returns a dict of numpy arrays, one row
+    per entry of ``rows``: bf16 outputs as uint16 bits, codes int8, scales fp32.
+    The chain is the V3 MLA Prolog of the AT-10 card, section 五 (q_a -> RMSNorm
+    -> *gamma -> bf16 -> q_b; kv_a -> RMSNorm -> *gamma -> bf16), with the kv_b
+    stage of the V2-Lite KV Prolog ("DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南",
+    section 背景) when ``v_dim > 0``, rotate-half RoPE on the rope slices and the
+    per-token INT8 quant of q (after RoPE) and of kv_norm.
+    """
+    T = int(inputs["x"].shape[0])
+    rows = np.arange(T, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+    n = int(rows.size)
+    H, Dn, R, Dv = cfg.n_heads, cfg.nope_dim, cfg.rope_dim, cfg.v_dim
+    Lq, Lkv = cfg.q_lora, cfg.kv_lora
+    w8 = bool(cfg.w8a8)
+    wdt = np.int8 if w8 else np.uint16
+
+    arrs = {
+        "x": _np(inputs["x"], np.uint16),
+        "positions": _np(inputs["positions"], np.int32),
+        "gamma_kv": _np(inputs["gamma_kv"], np.uint16),
+        "w_kva": _np(inputs["w_kva"], wdt),
+        "cos": _np(inputs["cos"], np.float32),
+        "sin": _np(inputs["sin"], np.float32),
+    }
+    for k in ("w_qa", "w_qb", "w_kvb"):
+        if k in inputs:
+            arrs[k] = _np(inputs[k], wdt)
+    if "gamma_q" in inputs:
+        arrs["gamma_q"] = _np(inputs["gamma_q"], np.uint16)
+    if w8:
+        for k in ("w_qa", "w_qb", "w_kva", "w_kvb"):
+            if k + "_scale" in inputs:
+                arrs["ws" + k[1:]] = _np(inputs[k + "_scale"], np.float32)
+
+    outs = {
+        "kv_norm": np.empty((n, Lkv), np.uint16),
+        "k_pe": np.empty((n, R), np.uint16),
+        "kv_i8": np.empty((n, Lkv), np.int8),
+        "kv_scale": np.empty((n,), np.float32),
+    }
+    if Lq > 0:
+        outs.update(q_nope=np.empty((n, H, Dn), np.uint16), q_pe=np.empty((n, H, R), np.uint16),
+                    q_norm=np.empty((n, Lq), np.uint16), q_i8=np.empty((n, H, Dn + R), np.int8),
+                    q_scale=np.empty((n,), np.float32))
+    if Dv > 0:
+        outs.update(k_nope=np.empty((n, H, Dn), np.uint16), value=np.empty((n, H, Dv), np.uint16))
+
+    c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8))
+    i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
+    o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
+    rc = load().orc_prolog(C.byref(c), C.byref(i), _p(rows), n, C.byref(o))
+    if rc != 0:
+        raise ValueError("oracle rejected the inputs (rc=%d)" % rc)
+    return outs

@@ -1,0 +1,359 @@
+/*
+ * mlap_oracle.c -- plain CPU oracle for the MLA Prolog.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. It shares no code with the HIP path.
+ *
+ * It computes, one token row at a time, exactly what the method defines, in the
+ * order the pages give and with the casts at the points they give:
+ *
+ *   GEMM  : Y = bf16(fp32(sum_k X[k] * W[n,k]))      products and sum in fp64
+ *           ("PyPTO-Gym 算子设计模式 AT-10 ... MLAProlog 实战", section 二 and
+ *            section 五: matmul with BF16 output dtype, weight laid out [N,K]).
+ *   RMSNorm (variant B, sqrt then divide), fp32:
+ *           x^2 -> *(1/D) -> row sum -> +eps -> sqrt -> 1/std -> x*rstd,
+ *           then *fp32(gamma) and cast to bf16
+ *           (same page, section 三 variant B; section 五 gamma applied by the caller
+ *            in fp32, then cast to BF16).
+ *   RoPE  : rotate-half, out = x*cos + rotate_half(x)*sin, rotate_half(x1,x2) = (-x2,x1),
+ *           fp32 math, cast back to bf16
+ *           ("PyPTO Operator 深度解析 (DeepSeek-V3.2-Exp)", section 3.3 QuantRope;
+ *            "DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南", section 精度验证).
+ *   Quant : per row, fp32: amax = max|z|, m = 127/amax, code = rint(z*m) (half to even),
+ *           saturated to [-127,127]; stored scale = amax/127
+ *           ("PyPTO Operator 深度解析", section 3.1 PrologQuant;
+ *            "PyPTO Gym 中的 grouped_matmul_swiglu_quant", sections 算子语义与数学公式
+ *            and 实现特点 5).
+ *   W8A8  : per-token activation quant (as above) -> int8 x int8 -> exact int32 ->
+ *           dequant bf16(fp32(acc) * (x_scale[t] * w_scale[n]))
+ *           ("PyPTO-Gym 算子设计模式 AT-10", section 四, INT8 W8A8 mode).
+ *
+ * Readings where the pages leave a step open are listed in the design notes; the
+ * ones that shape the arithmetic here: head-major q_b/kv_b output with
+ * [nope | rope] (q) or [nope | v] (kv_b) inside a head; kv_a output ordered
+ * [c_kv | k_pe]; one q scale per token over all heads, taken after RoPE; an
+ * all-zero row quantises to codes 0 and scale 0.
+ *
+ * Parity pins: every function here is pinned by the not-gpu tests against
+ * closed forms, invariants, library routines or brute force; see tests/.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_API __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------- bf16 ---- */
+
+/* Exact widening: a bf16 value is the top 16 bits of an IEEE fp32. */
+static float orc_f32(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t orc_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/*
+ * fp32 -> bf16, round to nearest, ties to even, from the definition: take the
+ * two bf16 neighbours of v (truncation and one unit up, in magnitude), compare
+ * the distances exactly in fp64 and keep the nearer; on a tie keep the one whose
+ * last mantissa bit is 0. Overflow past the largest finite bf16 rounds to inf
+ * under the same rule. NaN stays NaN (quiet).
+ */
+ORC_API uint16_t orc_bf16(float v) {
+    uint32_t u = orc_bits(v);
+    if (isnan(v)) return (uint16_t)((u >> 16) | 0x0040u);
+    if (isinf(v)) return (uint16_t)(u >> 16);
+    uint16_t lo = (uint16_t)(u >> 16);              /* |lo| <= |v| (truncation) */
+    if ((u & 0xffffu) == 0) return lo;              /* exactly representable */
+    uint16_t hi = (uint16_t)(lo + 1);               /* next magnitude up, same sign */
+    double dv = (double)v;
+    double dl = fabs(dv - (double)orc_f32(lo));
+    double dh;
+    if ((hi & 0x7f80u) == 0x7f80u) {
+        /* hi is inf: measure against the value one ulp above the max finite */
+        double maxf = (double)orc_f32((uint16_t)(lo | 0x7f7fu));
+        double ulp = ldexp(1.0, 127 - 7);
+        dh = fabs(fabs(dv) - (fabs(maxf) + ulp));
+    } else {
+        dh = fabs(dv - (double)orc_f32(hi));
+    }
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
+ORC_API void orc_bf16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16(in[i]);
+}
+
+/* ---------------------------------------------------------------- GEMM ---- */
+
+/* One output: bf16(fp32(sum_k fp64(x_k) * fp64(w_k))). bf16 x bf16 products are
+ * exact in fp64 (16 significant bits), so the fp64 sum is the exact sum up to
+ * fp64 rounding; it is rounded once to fp32 (the accumulator type), then to bf16. */
+static float orc_dot_bf16(const uint16_t* x, const uint16_t* w, int64_t K) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += (double)orc_f32(x[k]) * (double)orc_f32(w[k]);
+    return (float)acc;
+}
+
+/* Y[m,n] = bf16(X[m,:] . W[n,:]); X [M,K], W [N,K], Y [M,N], all row-major. */
+ORC_API void orc_gemm_bf16(const uint16_t* X, const uint16_t* W, int64_t M, int64_t N,
+                           int64_t K, uint16_t* Y) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            Y[m * N + n] = orc_bf16(orc_dot_bf16(X + m * K, W + n * K, K));
+}
+
+/* C[m,n] = sum_k A[m,k] * B[n,k] exactly (int64 sum, checked to fit int32). */
+ORC_API int orc_gemm_i8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K,
+                        int32_t* C) {
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)A[m * K + k] * (int64_t)B[n * K + k];
+            if (acc > INT32_MAX || acc < INT32_MIN) bad = 1;
+            C[m * N + n] = (int32_t)acc;
+        }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------- RMSNorm ---- */
+
+/* Variant B in fp32, step by step: sq_k = (y_k*y_k)*(1/D) each rounded to fp32,
+ * mean_sq = their sum (fp64, rounded once to fp32), std = sqrt(mean_sq + eps),
+ * rstd = 1/std, out_k = bf16((y_k*rstd)*f32(gamma_k)). gamma may be NULL (no gamma). */
+ORC_API void orc_rmsnorm_row(const uint16_t* v, const uint16_t* gamma, int64_t D, float eps,
+                             uint16_t* out) {
+    const float invD = 1.0f / (float)D;
+    double s = 0.0;
+    for (int64_t k = 0; k < D; ++k) {
+        float y = orc_f32(v[k]);
+        float sq = y * y;
+        float sqd = sq * invD;
+        s += (double)sqd;
+    }
+    float mean_sq = (float)s;
+    float var = mean_sq + eps;
+    float stdv = sqrtf(var);
+    float rstd = 1.0f / stdv;
+    for (int64_t k = 0; k < D; ++k) {
+        float y = orc_f32(v[k]) * rstd;
+        if (gamma) y = y * orc_f32(gamma[k]);
+        out[k] = orc_bf16(y);
+    }
+}
+
+/* ---------------------------------------------------------------- RoPE ---- */
+
+/* Rotate-half RoPE of one R-wide slice u (bf16) with the token's cos/sin rows:
+ * out_i     = u_i * c_i       + (-u_{i+h}) * s_i        (i < h = R/2)
+ * out_{i+h} = u_{i+h} * c_{i+h} + u_i * s_{i+h}
+ * each product rounded to fp32, then the fp32 sum, then bf16. */
+ORC_API void orc_rope_row(const uint16_t* u, const float* c, const float* s, int64_t R,
+                          uint16_t* out) {
+    int64_t h = R / 2;
+    for (int64_t i = 0; i < h; ++i) {
+        float x1 = orc_f32(u[i]), x2 = orc_f32(u[i + h]);
+        float a = x1 * c[i];
+        float b = (-x2) * s[i];
+        float lo = a + b;
+        float d = x2 * c[i + h];
+        float e = x1 * s[i + h];
+        float hi = d + e;
+        out[i] = orc_bf16(lo);
+        out[i + h] = orc_bf16(hi);
+    }
+}
+
+/* --------------------------------------------------------------- Quant ---- */
+
+/* Per-row symmetric dynamic INT8 quant of n bf16 values z (fp32 math). */
+ORC_API void orc_quant_row(const uint16_t* z, int64_t n, int8_t* codes, float* scale) {
+    float amax = 0.0f;
+    for (int64_t k = 0; k < n; ++k) {
+        float a = fabsf(orc_f32(z[k]));
+        if (a > amax) amax = a;
+    }
+    if (!(amax > 0.0f)) {
+        for (int64_t k = 0; k < n; ++k) codes[k] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    float m = 127.0f / amax;
+    for (int64_t k = 0; k < n; ++k) {
+        float p = orc_f32(z[k]) * m;
+        float r = rintf(p); /* default rounding mode: nearest, ties to even */
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        codes[k] = (int8_t)r;
+    }
+    *scale = amax / 127.0f;
+}
+
+/* Dequant of one int32 accumulator: bf16(fp32(acc) * (xs * ws)). */
+static uint16_t orc_dequant(int32_t acc, float xs, float ws) {
+    float sc = xs * ws;
+    float y = (float)acc * sc;
+    return orc_bf16(y);
+}
+
+/* --------------------------------------------------------------- Prolog --- */
+
+typedef struct {
+    int32_t hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads, max_pos;
+    float eps;
+    int32_t w8a8;
+} orc_cfg;
+
+typedef struct {
+    const uint16_t* x;        /* [T, hidden] bf16 */
+    const int32_t* positions; /* [T] */
+    const void* w_qa;         /* [q_lora, hidden]: bf16, or int8 when w8a8 */
+    const void* w_qb;         /* [H*(nope+rope), q_lora] */
+    const void* w_kva;        /* [kv_lora+rope, hidden] */
+    const void* w_kvb;        /* [H*(nope+v), kv_lora] */
+    const float* ws_qa;       /* W8A8 per-output-channel scales [N] */
+    const float* ws_qb;
+    const float* ws_kva;
+    const float* ws_kvb;
+    const uint16_t* gamma_q;  /* [q_lora] bf16 */
+    const uint16_t* gamma_kv; /* [kv_lora] bf16 */
+    const float* cos;         /* [max_pos, rope] fp32 */
+    const float* sin;
+} orc_inputs;
+
+typedef struct { /* every array is [nrows, ...] in the order of rows[] */
+    uint16_t* q_nope;   /* [nrows, H, nope] */
+    uint16_t* q_pe;     /* [nrows, H, rope] */
+    uint16_t* kv_norm;  /* [nrows, kv_lora] */
+    uint16_t* k_pe;     /* [nrows, rope] */
+    uint16_t* k_nope;   /* [nrows, H, nope] (kv_b) */
+    uint16_t* value;    /* [nrows, H, v] (kv_b) */
+    uint16_t* q_norm;   /* [nrows, q_lora] */
+    int8_t* q_i8;       /* [nrows, H, nope+rope] */
+    float* q_scale;     /* [nrows] */
+    int8_t* kv_i8;      /* [nrows, kv_lora] */
+    float* kv_scale;    /* [nrows] */
+} orc_outputs;
+
+/* One projection of one bf16 row v (length K) through W [N,K]: bf16 or W8A8. */
+static void orc_project(const orc_cfg* cfg, const uint16_t* v, int64_t K, const void* W,
+                        const float* ws, int64_t N, uint16_t* out, int8_t* tmp_codes) {
+    if (!cfg->w8a8) {
+        const uint16_t* Wb = (const uint16_t*)W;
+        for (int64_t n = 0; n < N; ++n) out[n] = orc_bf16(orc_dot_bf16(v, Wb + n * K, K));
+        return;
+    }
+    const int8_t* Wq = (const int8_t*)W;
+    float xs;
+    orc_quant_row(v, K, tmp_codes, &xs);
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k) acc += (int64_t)tmp_codes[k] * (int64_t)Wq[n * K + k];
+        out[n] = orc_dequant((int32_t)acc, xs, ws[n]);
+    }
+}
+
+/* Full prolog for the token rows listed in rows[0..nrows). NULL outputs are skipped.
+ * Returns 0, or -1 on an argument the oracle does not accept. */
+ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
+                       int32_t nrows, const orc_outputs* out) {
+    const int64_t Hd = cfg->hidden, Lq = cfg->q_lora, Lkv = cfg->kv_lora, R = cfg->rope_dim;
+    const int64_t Dn = cfg->nope_dim, Dv = cfg->v_dim, H = cfg->n_heads;
+    const int64_t QH = Dn + R, KH = Dn + Dv;
+    if (R <= 0 || (R & 1) || Lkv <= 0 || Hd <= 0) return -1;
+    for (int32_t i = 0; i < nrows; ++i) {
+        int32_t p = in->positions[rows[i]];
+        if (p < 0 || p >= cfg->max_pos) return -1;
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t i = 0; i < nrows; ++i) {
+        const int64_t t = rows[i];
+        const uint16_t* x = in->x + t * Hd;
+        const int64_t p = in->positions[t];
+        const float* c = in->cos + p * R;
+        const float* s = in->sin + p * R;
+        int64_t maxK = Hd > Lq ? Hd : Lq;
+        if (Lkv > maxK) maxK = Lkv;
+        int64_t maxN = H * (QH > KH ? QH : KH);
+        if (Lq > maxN) maxN = Lq;
+        if (Lkv + R > maxN) maxN = Lkv + R;
+        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)maxN);
+        uint16_t* qn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(Lq > 0 ? Lq : 1));
+        uint16_t* kvn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Lkv);
+        uint16_t* qrow = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(H * QH));
+        int8_t* codes = (int8_t*)malloc((size_t)(maxK > H * QH ? maxK : H * QH));
+        if (!a || !qn || !kvn || !qrow || !codes) {
+            bad = 1;
+            free(a); free(qn); free(kvn); free(qrow); free(codes);
+            continue;
+        }
+
+        /* kv branch: kv_a projection -> [c_kv | k_pe] */
+        orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, Lkv + R, a, codes);
+        orc_rmsnorm_row(a, in->gamma_kv, Lkv, cfg->eps, kvn);
+        if (out->kv_norm) memcpy(out->kv_norm + i * Lkv, kvn, sizeof(uint16_t) * (size_t)Lkv);
+        if (out->k_pe) orc_rope_row(a + Lkv, c, s, R, out->k_pe + i * R);
+        if (out->kv_i8 || out->kv_scale) {
+            float sc;
+            orc_quant_row(kvn, Lkv, codes, &sc);
+            if (out->kv_i8) memcpy(out->kv_i8 + i * Lkv, codes, (size_t)Lkv);
+            if (out->kv_scale) out->kv_scale[i] = sc;
+        }
+        if (Dv > 0) { /* kv_b projection of the normalised compressed KV */
+            orc_project(cfg, kvn, Lkv, in->w_kvb, in->ws_kvb, H * KH, a, codes);
+            for (int64_t h = 0; h < H; ++h) {
+                if (out->k_nope)
+                    memcpy(out->k_nope + (i * H + h) * Dn, a + h * KH, sizeof(uint16_t) * (size_t)Dn);
+                if (out->value)
+                    memcpy(out->value + (i * H + h) * Dv, a + h * KH + Dn, sizeof(uint16_t) * (size_t)Dv);
+            }
+        }
+
+        /* q branch: q_a projection -> RMSNorm*gamma -> q_b projection -> split, RoPE */
+        if (Lq > 0) {
+            orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, Lq, a, codes);
+            orc_rmsnorm_row(a, in->gamma_q, Lq, cfg->eps, qn);
+            if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
+            orc_project(cfg, qn, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
+            for (int64_t h = 0; h < H; ++h) {
+                const uint16_t* head = a + h * QH;
+                uint16_t* qh = qrow + h * QH;
+                memcpy(qh, head, sizeof(uint16_t) * (size_t)Dn);
+                orc_rope_row(head + Dn, c, s, R, qh + Dn);
+                if (out->q_nope) memcpy(out->q_nope + (i * H + h) * Dn, qh, sizeof(uint16_t) * (size_t)Dn);
+                if (out->q_pe) memcpy(out->q_pe + (i * H + h) * R, qh + Dn, sizeof(uint16_t) * (size_t)R);
+            }
+            if (out->q_i8 || out->q_scale) {
+                float sc;
+                orc_quant_row(qrow, H * QH, codes, &sc);
+                if (out->q_i8) memcpy(out->q_i8 + i * H * QH, codes, (size_t)(H * QH));
+                if (out->q_scale) out->q_scale[i] = sc;
+            }
+        }
+        free(a); free(qn); free(kvn); free(qrow); free(codes);
+    }
+    return bad ? -1 : 0;
+}
+
+ORC_API int orc_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
