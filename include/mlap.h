@@ -1,0 +1,187 @@
+/*
+ * mlap.h -- C ABI of the MI355X (gfx950) MLA Prolog library, libmlap.so.
+ *
+ * The MLA Prolog is the per-token stage in front of DeepSeek's multi-head latent
+ * attention. For every token row it computes
+ *
+ *   A      = x . [W_qa ; W_kva]^T                 bf16 out, fp32 accumulate
+ *   q_norm = bf16(RMSNorm(A[:, :q_lora]) * gamma_q)
+ *   kv_norm= bf16(RMSNorm(A[:, q_lora:q_lora+kv_lora]) * gamma_kv)
+ *   k_pe   = RoPE(A[:, q_lora+kv_lora:])
+ *   Q      = q_norm . W_qb^T  -> per head [q_nope | q_pe_raw], q_pe = RoPE(q_pe_raw)
+ *   KVB    = kv_norm . W_kvb^T -> per head [k_nope | value]      (KV-Prolog mode)
+ *   q_i8, q_scale  = per-token INT8 quant of all heads' [q_nope | q_pe]
+ *   kv_i8, kv_scale= per-token INT8 quant of kv_norm
+ *
+ * Passages this follows (page title, section):
+ *   - the q_a -> RMSNorm -> *gamma -> bf16 -> q_b chain and the parallel kv branch:
+ *     "PyPTO-Gym 算子设计模式 AT-10：RMSNorm + Linear 融合（V→C 排布）的原理与 MLAProlog
+ *     实战", section 五 (MLAProlog, DeepSeek-V4 source walk-through) and section 二
+ *     (norm in FP32, cast to BF16, matmul with BF16 out, weight [N, K]);
+ *   - RMSNorm variant B (sqrt, then divide): same page, section 三;
+ *   - the KV Prolog flow kv_a -> split -> RMSNorm -> kv_b -> reshape/split -> RoPE:
+ *     "DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南", sections 背景 and 源码级原理;
+ *   - rotate-half RoPE with one cos/sin row per token: "PyPTO Operator 深度解析
+ *     (DeepSeek-V3.2-Exp)", section 3.3 QuantRope;
+ *   - per-token symmetric INT8 quant (127/amax multiplier, round half to even,
+ *     scale = amax/127): same page, section 3.1 PrologQuant; and "PyPTO Gym 中的
+ *     grouped_matmul_swiglu_quant", sections 算子语义与数学公式 and 实现特点 5;
+ *   - the INT8 W8A8 linear (per-token activation quant, int8 x int8 -> int32,
+ *     dequant with x_scale * w_scale): AT-10 page, section 四.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major. Weights are [N, K] (output channel major, K contiguous).
+ *   - bf16 tensors are passed as raw 16-bit patterns (void pointers).
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them past the call. They must be 16-byte
+ *     aligned and must not overlap (inputs may alias other inputs).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     on it; no call synchronises the host except where stated.
+ *   - Errors are returned as status codes (mlap_status); nothing aborts and no
+ *     C++ exception crosses the ABI. A kernel launch failure is reported as
+ *     MLAP_ERR_HIP; a device fault surfaces at the caller's next synchronisation.
+ */
+#ifndef MLAP_H
+#define MLAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef MLAP_API
+#define MLAP_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    MLAP_OK = 0,
+    MLAP_ERR_INVALID_ARG = 1, /* NULL required pointer, T out of [0, t_max], bad handle */
+    MLAP_ERR_UNSUPPORTED = 2, /* dimensions the kernels do not support */
+    MLAP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than mlap_workspace_size */
+    MLAP_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} mlap_status;
+
+/* Configuration flags. */
+#define MLAP_W8A8 0x1u /* int8 weights + per-output-channel fp32 scales; W8A8 GEMMs */
+
+typedef struct {
+    int32_t t_max;    /* largest token count a run may pass (sizes nothing on device) */
+    int32_t hidden;   /* model width (K of the down projection); multiple of 64 (128 with W8A8) */
+    int32_t q_lora;   /* q low-rank width; 0 = no q branch (KV-Prolog mode); multiple of 64 (128) */
+    int32_t kv_lora;  /* compressed-KV width; multiple of 8 (64, or 128 with W8A8, if v_dim > 0) */
+    int32_t rope_dim; /* RoPE slice width of q and k; multiple of 16 */
+    int32_t nope_dim; /* per-head non-rotary width of q (and of k_nope); multiple of 8 */
+    int32_t v_dim;    /* per-head value width of kv_b; 0 = no kv_b projection; multiple of 8 */
+    int32_t n_heads;  /* attention heads */
+    int32_t max_pos;  /* rows of the cos/sin tables */
+    float eps;        /* RMSNorm epsilon (added to the mean square) */
+    uint32_t flags;   /* MLAP_W8A8 */
+} mlap_config;
+
+/*
+ * Inputs of one run (device pointers). Shapes use T = tokens of this run,
+ * Hd = hidden, Lq = q_lora, Lkv = kv_lora, R = rope_dim, Dn = nope_dim,
+ * Dv = v_dim, H = n_heads.
+ */
+typedef struct {
+    int32_t T;                 /* tokens in this run, 0 <= T <= t_max */
+    const void* x;             /* [T, Hd] bf16 token activations */
+    const int32_t* positions;  /* [T] position of each token in [0, max_pos); values outside
+                                  are clamped into range (a violated precondition) */
+    const void* w_qa;          /* [Lq, Hd]          bf16 (int8 with W8A8); unused if Lq == 0 */
+    const void* w_qb;          /* [H*(Dn+R), Lq]    bf16 (int8); per head [nope | rope] rows */
+    const void* w_kva;         /* [Lkv+R, Hd]       bf16 (int8); rows [c_kv | k_pe] */
+    const void* w_kvb;         /* [H*(Dn+Dv), Lkv]  bf16 (int8); per head [nope | v]; if Dv > 0 */
+    const float* ws_qa;        /* W8A8 only: per-output-channel weight scales, [Lq] */
+    const float* ws_qb;        /* W8A8 only: [H*(Dn+R)] */
+    const float* ws_kva;       /* W8A8 only: [Lkv+R] */
+    const float* ws_kvb;       /* W8A8 only: [H*(Dn+Dv)] */
+    const void* gamma_q;       /* [Lq] bf16 RMSNorm weight of the q branch */
+    const void* gamma_kv;      /* [Lkv] bf16 RMSNorm weight of the kv branch */
+    const float* cos;          /* [max_pos, R] fp32, the rotate-half table (both halves) */
+    const float* sin;          /* [max_pos, R] fp32 */
+} mlap_inputs;
+
+/*
+ * Outputs of one run (device pointers, caller-allocated). A NULL output is not
+ * produced. Token-major layouts; per-head tensors are [T, H, d].
+ */
+typedef struct {
+    void* q_nope;     /* [T, H, Dn] bf16                      (needs Lq > 0) */
+    void* q_pe;       /* [T, H, R]  bf16, after RoPE          (needs Lq > 0) */
+    void* kv_norm;    /* [T, Lkv]   bf16 */
+    void* k_pe;       /* [T, R]     bf16, after RoPE */
+    void* k_nope;     /* [T, H, Dn] bf16                      (needs Dv > 0) */
+    void* value;      /* [T, H, Dv] bf16                      (needs Dv > 0) */
+    void* q_norm;     /* [T, Lq]    bf16, the normalised q_a projection (optional) */
+    int8_t* q_i8;     /* [T, H, Dn+R] int8 codes of [q_nope | q_pe] per head */
+    float* q_scale;   /* [T] fp32, amax/127 over the token's H*(Dn+R) values */
+    int8_t* kv_i8;    /* [T, Lkv] int8 codes of kv_norm */
+    float* kv_scale;  /* [T] fp32 */
+} mlap_outputs;
+
+typedef struct mlap_prolog* mlap_handle;
+
+/* Validate `cfg` and create a host-side handle (no device allocation, no sync).
+ * Returns MLAP_ERR_UNSUPPORTED for dimensions the kernels do not handle. */
+MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out);
+
+/* Bytes of device workspace a run with T tokens needs (GEMM intermediates, the
+ * per-tile partial amax of q, the W8A8 int8 activations). The caller allocates it. */
+MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes);
+
+/* Enqueue the whole prolog for in->T tokens on `stream`. `ws` must hold at least
+ * mlap_workspace_size(h, in->T) bytes, 256-byte aligned. T == 0 is a no-op.
+ * Runs on one handle must not overlap in time unless they use distinct workspaces. */
+MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
+             void* ws, size_t ws_bytes);
+
+/* Free the handle (host memory and any timing events). NULL is allowed. */
+MLAP_API void mlap_destroy(mlap_handle h);
+
+/* Static description of a status code. */
+MLAP_API const char* mlap_status_str(int status);
+
+/*
+ * Test export of the W8A8 matmul core (AT-10 page, section 四: int8 x int8 ->
+ * int32): C[m, n] = sum_k A[m, k] * B[n, k], exact int32, with the same MFMA
+ * kernel the W8A8 prolog uses. A [M, K] int8, B [N, K] int8, C [M, N] int32,
+ * device pointers; K must be a multiple of 128. Enqueued on `stream`.
+ */
+MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, int32_t* C, int32_t M,
+                     int32_t N, int32_t K);
+
+/*
+ * Test export of the bf16 matmul core (AT-10 page, sections 二 and 五: matmul with
+ * BF16 output, weight [N, K]): C = bf16(A . B^T) with fp32 accumulation. A [M, K],
+ * B [N, K], C [M, N] bf16, device pointers; K must be a multiple of 64.
+ */
+MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C, int32_t M, int32_t N,
+                   int32_t K);
+
+/*
+ * Per-kernel timing (measurement support). Kernel ids: see mlap_kernel_name.
+ * mlap_timing_begin arms HIP events around every launch of kernel `kernel_id`
+ * in the next `max_launches` runs of `h` (events are created here). The events
+ * are recorded on the run's stream, so they time exactly that kernel.
+ * mlap_timing_end waits for the recorded events (host sync), writes up to `cap`
+ * per-launch durations in milliseconds to `ms`, stores the count in *n and
+ * disarms timing.
+ */
+MLAP_API int mlap_timing_begin(mlap_handle h, int32_t kernel_id, int32_t max_launches);
+MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n);
+
+/* Name of kernel `kernel_id` ("gemm_down", "norm_rope", "gemm_up_q", ...), or NULL
+ * past the last one. */
+MLAP_API const char* mlap_kernel_name(int32_t kernel_id);
+
+/* Library version string. */
+MLAP_API const char* mlap_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLAP_H */

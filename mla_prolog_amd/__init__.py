@@ -1,0 +1,260 @@
+"""mla_prolog_amd -- Python binding of libmlap.so, the gfx950 MLA Prolog.
+
+Argument marshalling only: every step of the prolog runs in the HIP kernels of
+``libmlap.so`` (C ABI in ``include/mlap.h``). PyTorch is used for device memory
+and for the current HIP stream. There is no CPU fallback: if the library is not
+built, importing this package raises.
+
+    >>> p = Prolog(t_max=256, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
+    ...            nope_dim=128, v_dim=0, n_heads=128, max_pos=8192)
+    >>> out = p.run(x, positions, weights, cos, sin)      # dict of cuda tensors
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # noqa: F401  -- must precede the library: libmlap binds to torch's HIP runtime
+
+__all__ = ["Prolog", "MlapError", "gemm_i8_i32", "gemm_bf16", "KERNELS", "lib_path", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libmlap.so")
+
+MLAP_OK, MLAP_ERR_INVALID_ARG, MLAP_ERR_UNSUPPORTED, MLAP_ERR_WORKSPACE, MLAP_ERR_HIP = range(5)
+MLAP_W8A8 = 0x1
+
+EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
+           "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_timing_begin", "mlap_timing_end",
+           "mlap_kernel_name", "mlap_version")
+
+
+class MlapError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, _lib.mlap_status_str(status).decode(), status))
+
+
+class _Config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("t_max", "hidden", "q_lora", "kv_lora", "rope_dim",
+                                          "nope_dim", "v_dim", "n_heads", "max_pos")] + \
+               [("eps", C.c_float), ("flags", C.c_uint32)]
+
+
+class _Inputs(C.Structure):
+    _fields_ = [("T", C.c_int32)] + [(n, C.c_void_p) for n in (
+        "x", "positions", "w_qa", "w_qb", "w_kva", "w_kvb", "ws_qa", "ws_qb", "ws_kva", "ws_kvb",
+        "gamma_q", "gamma_kv", "cos", "sin")]
+
+
+OUTPUTS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_i8", "q_scale",
+           "kv_i8", "kv_scale")
+
+
+class _Outputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in OUTPUTS]
+
+
+def _load():
+    if not os.path.exists(_LIB):
+        raise ImportError("libmlap.so is not built (run `python mla_prolog_amd/build.py`); "
+                          "there is no fallback path")
+    lib = C.CDLL(_LIB)
+    for name in EXPORTS:
+        getattr(lib, name)  # raises AttributeError if an ABI symbol is missing
+    lib.mlap_create.argtypes = [C.POINTER(_Config), C.POINTER(C.c_void_p)]
+    lib.mlap_workspace_size.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]
+    lib.mlap_run.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(_Inputs), C.POINTER(_Outputs),
+                             C.c_void_p, C.c_size_t]
+    lib.mlap_destroy.argtypes = [C.c_void_p]
+    lib.mlap_destroy.restype = None
+    lib.mlap_status_str.argtypes = [C.c_int]
+    lib.mlap_status_str.restype = C.c_char_p
+    lib.mlap_gemm_i8_i32.argtypes = [C.c_void_p] * 4 + [C.c_int32] * 3
+    lib.mlap_gemm_bf16.argtypes = [C.c_void_p] * 4 + [C.c_int32] * 3
+    lib.mlap_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
+    lib.mlap_timing_end.argtypes = [C.c_void_p, C.POINTER(C.c_float), C.c_int32,
+                                    C.POINTER(C.c_int32)]
+    lib.mlap_kernel_name.argtypes = [C.c_int32]
+    lib.mlap_kernel_name.restype = C.c_char_p
+    lib.mlap_version.restype = C.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def version() -> str:
+    return _lib.mlap_version().decode()
+
+
+def _kernels():
+    names, i = [], 0
+    while True:
+        n = _lib.mlap_kernel_name(i)
+        if n is None:
+            return tuple(names)
+        names.append(n.decode())
+        i += 1
+
+
+KERNELS = _kernels()
+
+
+def _check(status, what):
+    if status != MLAP_OK:
+        raise MlapError(status, what)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+class Prolog:
+    """One MLA Prolog configuration (a host-side handle; holds no device memory)."""
+
+    def __init__(self, t_max, hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads,
+                 max_pos, eps=1e-6, w8a8=False):
+        self.cfg = dict(t_max=t_max, hidden=hidden, q_lora=q_lora, kv_lora=kv_lora,
+                        rope_dim=rope_dim, nope_dim=nope_dim, v_dim=v_dim, n_heads=n_heads,
+                        max_pos=max_pos, eps=eps, w8a8=bool(w8a8))
+        c = _Config(int(t_max), int(hidden), int(q_lora), int(kv_lora), int(rope_dim),
+                    int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps),
+                    MLAP_W8A8 if w8a8 else 0)
+        h = C.c_void_p()
+        _check(_lib.mlap_create(C.byref(c), C.byref(h)), "mlap_create")
+        self._h = h
+        self._ws = None
+
+    @classmethod
+    def from_config(cls, cfg, t_max=None):
+        """Build from any object with the fields of ``synth.Config``."""
+        return cls(t_max or cfg.T, cfg.hidden, cfg.q_lora, cfg.kv_lora, cfg.rope_dim,
+                   cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.mlap_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, T) -> int:
+        n = C.c_size_t()
+        _check(_lib.mlap_workspace_size(self._h, int(T), C.byref(n)), "mlap_workspace_size")
+        return int(n.value)
+
+    def workspace(self, T, device=None):
+        """A workspace tensor for T tokens (cached and grown on demand)."""
+        n = self.workspace_size(T)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+        return self._ws
+
+    def alloc_outputs(self, T, device="cuda", want=None):
+        """Allocate output tensors; ``want`` selects names (default: all this config makes)."""
+        c = self.cfg
+        H, Dn, R, Dv, Lq, Lkv = (c["n_heads"], c["nope_dim"], c["rope_dim"], c["v_dim"],
+                                 c["q_lora"], c["kv_lora"])
+        bf, i8, f = torch.bfloat16, torch.int8, torch.float32
+        shapes = {"kv_norm": ((T, Lkv), bf), "k_pe": ((T, R), bf), "kv_i8": ((T, Lkv), i8),
+                  "kv_scale": ((T,), f)}
+        if Lq > 0:
+            shapes.update(q_nope=((T, H, Dn), bf), q_pe=((T, H, R), bf), q_i8=((T, H, Dn + R), i8),
+                          q_scale=((T,), f), q_norm=((T, Lq), bf))
+        if Dv > 0:
+            shapes.update(k_nope=((T, H, Dn), bf), value=((T, H, Dv), bf))
+        if want is None:
+            want = [k for k in shapes if k != "q_norm"]
+        return {k: torch.empty(shapes[k][0], dtype=shapes[k][1], device=device) for k in want}
+
+    def run(self, inputs, outputs=None, workspace=None, stream=None):
+        """Enqueue one prolog run. ``inputs``: dict with x, positions, w_kva, gamma_kv,
+        cos, sin and (as configured) w_qa, w_qb, gamma_q, w_kvb, and ``*_scale`` for
+        W8A8. ``outputs``: dict of preallocated tensors (default: alloc_outputs).
+        Returns the outputs dict."""
+        x = inputs["x"]
+        T = int(x.shape[0])
+        w8 = self.cfg["w8a8"]
+        wdt = torch.int8 if w8 else torch.bfloat16
+        if outputs is None:
+            outputs = self.alloc_outputs(T, device=x.device)
+        g = inputs.get
+        i = _Inputs(T=T, x=_ptr(x, torch.bfloat16, "x"),
+                    positions=_ptr(inputs["positions"], torch.int32, "positions"),
+                    w_qa=_ptr(g("w_qa"), wdt, "w_qa"), w_qb=_ptr(g("w_qb"), wdt, "w_qb"),
+                    w_kva=_ptr(inputs["w_kva"], wdt, "w_kva"), w_kvb=_ptr(g("w_kvb"), wdt, "w_kvb"),
+                    ws_qa=_ptr(g("w_qa_scale"), torch.float32, "w_qa_scale"),
+                    ws_qb=_ptr(g("w_qb_scale"), torch.float32, "w_qb_scale"),
+                    ws_kva=_ptr(g("w_kva_scale"), torch.float32, "w_kva_scale"),
+                    ws_kvb=_ptr(g("w_kvb_scale"), torch.float32, "w_kvb_scale"),
+                    gamma_q=_ptr(g("gamma_q"), torch.bfloat16, "gamma_q"),
+                    gamma_kv=_ptr(inputs["gamma_kv"], torch.bfloat16, "gamma_kv"),
+                    cos=_ptr(inputs["cos"], torch.float32, "cos"),
+                    sin=_ptr(inputs["sin"], torch.float32, "sin"))
+        dts = {"q_i8": torch.int8, "kv_i8": torch.int8, "q_scale": torch.float32,
+               "kv_scale": torch.float32}
+        o = _Outputs(**{k: _ptr(outputs.get(k), dts.get(k, torch.bfloat16), k) for k in OUTPUTS})
+        ws = self.workspace(T, device=x.device) if workspace is None else workspace
+        _check(_lib.mlap_run(self._h, _stream(stream), C.byref(i), C.byref(o),
+                             C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel() * ws.element_size())),
+               "mlap_run")
+        return outputs
+
+    # -- per-kernel timing ---------------------------------------------------
+    def timing_begin(self, kernel, max_launches):
+        kid = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+        _check(_lib.mlap_timing_begin(self._h, kid, int(max_launches)), "mlap_timing_begin")
+
+    def timing_end(self, cap=100000):
+        buf = (C.c_float * cap)()
+        n = C.c_int32()
+        _check(_lib.mlap_timing_end(self._h, buf, cap, C.byref(n)), "mlap_timing_end")
+        return [float(buf[k]) for k in range(n.value)]
+
+
+def gemm_i8_i32(A, B, out=None, stream=None):
+    """Exact int32 C = A . B^T on the W8A8 MFMA core (test export)."""
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.int32, device=A.device)
+    _check(_lib.mlap_gemm_i8_i32(_stream(stream), C.c_void_p(_ptr(A, torch.int8, "A")),
+                                 C.c_void_p(_ptr(B, torch.int8, "B")),
+                                 C.c_void_p(_ptr(out, torch.int32, "C")), M, N, K),
+           "mlap_gemm_i8_i32")
+    return out
+
+
+def gemm_bf16(A, B, out=None, stream=None):
+    """bf16(A . B^T) with fp32 accumulation on the bf16 MFMA core (test export)."""
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    _check(_lib.mlap_gemm_bf16(_stream(stream), C.c_void_p(_ptr(A, torch.bfloat16, "A")),
+                               C.c_void_p(_ptr(B, torch.bfloat16, "B")),
+                               C.c_void_p(_ptr(out, torch.bfloat16, "C")), M, N, K),
+           "mlap_gemm_bf16")
+    return out

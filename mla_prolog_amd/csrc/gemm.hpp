@@ -1,0 +1,369 @@
+// gemm.hpp -- LDS-staged MFMA GEMM for gfx950, C = A . B^T with A [M,K], B [N,K].
+//
+// Both operands are K-contiguous (activations [T, K], weights [N, K] as the
+// AT-10 card's b_trans layout), so every lane fetches 16-byte runs along K for
+// both MFMA operands and no transpose is needed anywhere.
+//
+// One K-tile is 128 bytes of every row: 64 bf16 or 128 int8. The tile is read
+// from HBM into registers (16-byte loads, 8 lanes per 128-byte row segment),
+// written to LDS with a 16-byte row pad (rows 144 bytes apart, so the 128-bit
+// LDS reads of consecutive rows hit distinct banks), and consumed by
+// v_mfma_f32_32x32x16_bf16 or v_mfma_i32_32x32x32_i8: each instruction eats 32
+// bytes of K per row, so a K-tile is four MFMA k-steps for either type. The
+// next K-tile is fetched into registers while the current one is multiplied.
+//
+// Accumulator layout of a 32x32 MFMA block (lane l, register r in 0..15):
+// column l % 32, row 8*(r/4) + 4*(l/32) + r%4.
+//
+// Epilogues: bf16 store, fp32 split-K partial store, int32 store (test export),
+// and the per-head epilogue of the up projection (split into two segments per
+// head, rotate-half RoPE of the second, per-tile partial row amax for the
+// per-token INT8 quant). The bf16 cast happens once, when accumulators are
+// staged to LDS, which is exactly the GEMM's bf16 output cast point.
+#pragma once
+
+#include "common.hpp"
+
+namespace mlap {
+
+enum class Epi : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreI32 = 2, kHeads = 3 };
+
+struct GemmArgs {
+    int M, N, K;
+    // A [M, lda] and B rows: row n < b_split comes from B0 + n*ldb, else B1 + (n-b_split)*ldb.
+    const void* A;
+    int lda;
+    const void* B0;
+    const void* B1;
+    int b_split;
+    int ldb;
+    int k_splits;  // grid.z; each split covers K/k_splits (kStoreF32 only)
+    // W8A8 dequant: y = f32(acc) * (a_scale[m] * b_scale[n]); b_scale split like B.
+    const float* a_scale;
+    const float* b_scale0;
+    const float* b_scale1;
+    // plain stores: out [M, ldo] (kStoreF32: [k_splits][M][ldo])
+    void* out;
+    int ldo;
+    // per-head epilogue
+    int head_w, d0, d1, rope, n_heads;
+    void* out0;  // [M, n_heads, d0] bf16
+    void* out1;  // [M, n_heads, d1] bf16
+    const int* positions;
+    const float* cos;
+    const float* sin;
+    int max_pos;
+    float* part_amax;  // [M, n_tiles] or null
+    int n_tiles;
+};
+
+template <typename Tin>
+struct MfmaOp;
+
+template <>
+struct MfmaOp<uint16_t> {  // bf16
+    typedef f32x16 acc_t;
+    static __device__ __forceinline__ acc_t zero() {
+        acc_t z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+        return z;
+    }
+    static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) {
+        bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct MfmaOp<int8_t> {  // int8
+    typedef i32x16 acc_t;
+    static __device__ __forceinline__ acc_t zero() {
+        acc_t z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0;
+        return z;
+    }
+    static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) {
+        i32x4 av = __builtin_bit_cast(i32x4, a);
+        i32x4 bv = __builtin_bit_cast(i32x4, b);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
+    }
+};
+
+constexpr int kTileKBytes = 128;
+constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
+
+template <int BM, int BN, int WM, int WN>
+struct TileShape {
+    static constexpr int NT = kWave * WM * WN;
+    static constexpr int TM = BM / WM;
+    static constexpr int TN = BN / WN;
+    static constexpr int FM = TM / 32;
+    static constexpr int FN = TN / 32;
+    static constexpr int A_PER = BM * 8 / NT;  // 16-byte chunks per thread per K-tile
+    static constexpr int B_PER = BN * 8 / NT;
+    static constexpr int MAIN_LDS = (BM + BN) * kLdsRow;
+    static constexpr int EPI_ROWS = TM;                      // rows staged per epilogue pass
+    static constexpr int EPI_PITCH = BN + 8;                 // bf16 elements per staged row
+    static constexpr int EPI_LDS = EPI_ROWS * EPI_PITCH * 2 + EPI_ROWS * 4;
+    static constexpr int LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32-aligned");
+    static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile rows must split over threads");
+    static_assert(LDS <= 65536, "LDS budget");
+};
+
+// Per-head epilogue on one staged pass of rows [r0, r0+rows) of the tile.
+// The staged tile holds the GEMM output already rounded to bf16.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void heads_epilogue(const GemmArgs& g, const uint16_t* cs,
+                                               uint32_t* row_amax, int m_base, int n0,
+                                               int rows, int tid) {
+    using S = TileShape<BM, BN, WM, WN>;
+    const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
+    const int heads_in_tile = BN / HW;
+    const int h0 = n0 / HW;
+    const int c0 = d0 >> 3;
+    const int half = d1 >> 1;
+    const int c1 = g.rope ? (half >> 3) : (d1 >> 3);
+    const int per_head = c0 + c1;
+    const int items = rows * heads_in_tile * per_head;
+    uint16_t* out0 = static_cast<uint16_t*>(g.out0);
+    uint16_t* out1 = static_cast<uint16_t*>(g.out1);
+    for (int it = tid; it < items; it += S::NT) {
+        const int lr = it / (heads_in_tile * per_head);
+        const int rem = it - lr * heads_in_tile * per_head;
+        const int hh = rem / per_head;
+        const int j = rem - hh * per_head;
+        const int m = m_base + lr;
+        const int h = h0 + hh;
+        if (m >= g.M || h >= g.n_heads) continue;
+        const uint16_t* src = cs + lr * S::EPI_PITCH + hh * HW;
+        float amax;
+        if (j < c0) {
+            uint4 v = *reinterpret_cast<const uint4*>(src + j * 8);
+            if (out0)
+                *reinterpret_cast<uint4*>(out0 + (static_cast<size_t>(m) * g.n_heads + h) * d0 +
+                                          j * 8) = v;
+            amax = absmax8(v);
+        } else if (g.rope) {
+            const int i0 = (j - c0) * 8;
+            const int p = clamp_pos(g.positions[m], g.max_pos);
+            const float* cr = g.cos + static_cast<size_t>(p) * d1;
+            const float* sr = g.sin + static_cast<size_t>(p) * d1;
+            float x1[8], x2[8], lo[8], hi[8];
+            unpack8(*reinterpret_cast<const uint4*>(src + d0 + i0), x1);
+            unpack8(*reinterpret_cast<const uint4*>(src + d0 + half + i0), x2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // rotate_half(x) = (-x2, x1): out = x*cos + rotate_half(x)*sin
+                float a = x1[e] * cr[i0 + e];
+                float b = (-x2[e]) * sr[i0 + e];
+                lo[e] = a + b;
+                float c = x2[e] * cr[half + i0 + e];
+                float d = x1[e] * sr[half + i0 + e];
+                hi[e] = c + d;
+            }
+            uint4 vlo = pack8(lo), vhi = pack8(hi);
+            if (out1) {
+                uint16_t* dst = out1 + (static_cast<size_t>(m) * g.n_heads + h) * d1;
+                *reinterpret_cast<uint4*>(dst + i0) = vlo;
+                *reinterpret_cast<uint4*>(dst + half + i0) = vhi;
+            }
+            amax = fmaxf(absmax8(vlo), absmax8(vhi));
+        } else {
+            const int i0 = (j - c0) * 8;
+            uint4 v = *reinterpret_cast<const uint4*>(src + d0 + i0);
+            if (out1)
+                *reinterpret_cast<uint4*>(out1 + (static_cast<size_t>(m) * g.n_heads + h) * d1 +
+                                          i0) = v;
+            amax = absmax8(v);
+        }
+        if (g.part_amax) atomicMax(row_amax + lr, __float_as_uint(amax));
+    }
+}
+
+template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI>
+__global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
+    using S = TileShape<BM, BN, WM, WN>;
+    using Op = MfmaOp<Tin>;
+    __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int n_tile = blockIdx.x;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = n_tile * BN;
+
+    const int kbytes_total = g.K * static_cast<int>(sizeof(Tin));
+    const int kbytes_split = kbytes_total / g.k_splits;
+    const int kb0 = blockIdx.z * kbytes_split;
+    const int n_ktiles = kbytes_split / kTileKBytes;
+
+    const size_t lda_b = static_cast<size_t>(g.lda) * sizeof(Tin);
+    const size_t ldb_b = static_cast<size_t>(g.ldb) * sizeof(Tin);
+
+    // Per-thread source rows for the global->LDS copy (nullptr = outside the matrix).
+    const char* a_src[S::A_PER];
+    const char* b_src[S::B_PER];
+    int a_lds[S::A_PER], b_lds[S::B_PER];
+#pragma unroll
+    for (int i = 0; i < S::A_PER; ++i) {
+        const int c = tid + i * S::NT;
+        const int r = c >> 3, cc = c & 7;
+        const int m = m0 + r;
+        a_src[i] = (m < g.M) ? static_cast<const char*>(g.A) + m * lda_b + kb0 + cc * 16 : nullptr;
+        a_lds[i] = r * kLdsRow + cc * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < S::B_PER; ++i) {
+        const int c = tid + i * S::NT;
+        const int r = c >> 3, cc = c & 7;
+        const int n = n0 + r;
+        const char* base = nullptr;
+        if (n < g.N)
+            base = (n < g.b_split)
+                       ? static_cast<const char*>(g.B0) + n * ldb_b
+                       : static_cast<const char*>(g.B1) + (n - g.b_split) * ldb_b;
+        b_src[i] = base ? base + kb0 + cc * 16 : nullptr;
+        b_lds[i] = BM * kLdsRow + r * kLdsRow + cc * 16;
+    }
+
+    uint4 ra[S::A_PER], rb[S::B_PER];
+    auto fetch = [&](int kt) {
+        const int off = kt * kTileKBytes;
+#pragma unroll
+        for (int i = 0; i < S::A_PER; ++i)
+            ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < S::B_PER; ++i)
+            rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + off) : make_uint4(0, 0, 0, 0);
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < S::A_PER; ++i) *reinterpret_cast<uint4*>(smem + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < S::B_PER; ++i) *reinterpret_cast<uint4*>(smem + b_lds[i]) = rb[i];
+    };
+
+    typename Op::acc_t acc[S::FM][S::FN];
+#pragma unroll
+    for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::FN; ++j) acc[i][j] = Op::zero();
+
+    // LDS read offsets of this lane's MFMA operands (row l%32, 16-byte half l/32).
+    const int a_rd = (wm * S::TM + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+    const int b_rd = BM * kLdsRow + (wn * S::TN + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+
+    fetch(0);
+    stash();
+    __syncthreads();
+    for (int kt = 0; kt < n_ktiles; ++kt) {
+        if (kt + 1 < n_ktiles) fetch(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 af[S::FM], bfr[S::FN];
+#pragma unroll
+            for (int i = 0; i < S::FM; ++i)
+                af[i] = *reinterpret_cast<const uint4*>(smem + a_rd + i * 32 * kLdsRow + ks * 32);
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j)
+                bfr[j] = *reinterpret_cast<const uint4*>(smem + b_rd + j * 32 * kLdsRow + ks * 32);
+#pragma unroll
+            for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::FN; ++j) Op::mma(acc[i][j], af[i], bfr[j]);
+        }
+        __syncthreads();
+        if (kt + 1 < n_ktiles) {
+            stash();
+            __syncthreads();
+        }
+    }
+
+    // ------------------------------------------------------------- epilogues --
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+
+    if constexpr (EPI == Epi::kStoreI32 || EPI == Epi::kStoreF32) {
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * S::TM + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                    const int n = n0 + wn * S::TN + j * 32 + col_l;
+                    if (m < g.M && n < g.N) {
+                        if constexpr (EPI == Epi::kStoreI32) {
+                            static_cast<int32_t*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = acc[i][j][r];
+                        } else {
+                            static_cast<float*>(g.out)[(static_cast<size_t>(blockIdx.z) * g.M + m) * g.ldo + n] =
+                                acc[i][j][r];
+                        }
+                    }
+                }
+        return;
+    } else {
+        uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
+        uint32_t* row_amax = reinterpret_cast<uint32_t*>(smem + S::EPI_ROWS * S::EPI_PITCH * 2);
+        for (int pass = 0; pass < WM; ++pass) {
+            // stage rows [pass*TM, pass*TM + TM) of the tile as bf16
+            if (wm == pass) {
+#pragma unroll
+                for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int lr = i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                            const int lc = wn * S::TN + j * 32 + col_l;
+                            float v;
+                            if constexpr (sizeof(Tin) == 1) {
+                                const int m = m0 + pass * S::TM + lr;
+                                const int n = n0 + lc;
+                                const float as = (m < g.M) ? g.a_scale[m] : 0.f;
+                                const float bs = (n < g.N) ? ((n < g.b_split) ? g.b_scale0[n]
+                                                                              : g.b_scale1[n - g.b_split])
+                                                           : 0.f;
+                                const float sc = as * bs;
+                                v = static_cast<float>(acc[i][j][r]) * sc;
+                            } else {
+                                v = acc[i][j][r];
+                            }
+                            cs[lr * S::EPI_PITCH + lc] = f2bf(v);
+                        }
+            }
+            if (tid < S::EPI_ROWS) row_amax[tid] = 0u;
+            __syncthreads();
+            const int m_base = m0 + pass * S::TM;
+            if constexpr (EPI == Epi::kStoreBf16) {
+                constexpr int CPR = BN / 8;  // 16-byte chunks per row
+                uint16_t* out = static_cast<uint16_t*>(g.out);
+                for (int c = tid; c < S::EPI_ROWS * CPR; c += S::NT) {
+                    const int lr = c / CPR, cc = c % CPR;
+                    const int m = m_base + lr, n = n0 + cc * 8;
+                    if (m < g.M && n < g.N)  // N is a multiple of 8
+                        *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) =
+                            *reinterpret_cast<const uint4*>(cs + lr * S::EPI_PITCH + cc * 8);
+                }
+            } else {
+                heads_epilogue<BM, BN, WM, WN>(g, cs, row_amax, m_base, n0, S::EPI_ROWS, tid);
+                if (g.part_amax) {
+                    __syncthreads();
+                    if (tid < S::EPI_ROWS && m_base + tid < g.M)
+                        g.part_amax[static_cast<size_t>(m_base + tid) * g.n_tiles + n_tile] =
+                            __uint_as_float(row_amax[tid]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace mlap

@@ -1,0 +1,59 @@
+// launch.hpp -- host-side launch interface of the gfx950 MLA Prolog kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.hpp"
+
+namespace mlap {
+
+enum class InType : int { kBf16 = 0, kInt8 = 1 };
+
+// Launch C = A . B^T with the given tile shape and epilogue. Returns hipErrorInvalidValue for
+// a (type, BM, BN, epilogue) combination that has no instantiation.
+hipError_t launch_gemm(const GemmArgs& g, InType t, int BM, int BN, Epi epi, hipStream_t s);
+
+// Per-token row stage after the down projection: RMSNorm*gamma -> bf16 for the q and kv
+// segments, rotate-half RoPE of the k_pe segment, per-token INT8 quant of kv_norm and (W8A8)
+// of q_norm. One workgroup per token.
+struct NormArgs {
+    int T, Lq, Lkv, R, N1, k_splits;
+    const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output (k_splits == 1)
+    const float* a_f32;      // [k_splits, T, N1] fp32 split-K partial sums (k_splits > 1)
+    const uint16_t* gamma_q;
+    const uint16_t* gamma_kv;
+    float eps;
+    const int* positions;
+    const float* cos;
+    const float* sin;
+    int max_pos;
+    uint16_t* q_norm;    // [T, Lq] or null
+    uint16_t* kv_norm;   // [T, Lkv] or null
+    uint16_t* k_pe;      // [T, R] or null
+    int8_t* kv_i8;       // [T, Lkv] or null
+    float* kv_scale;     // [T] or null
+    int8_t* kv_i8_b;     // second destination of the kv codes (W8A8 kv_b input) or null
+    float* kv_scale_b;
+    int8_t* qn_i8;       // [T, Lq] W8A8 activation codes of q_norm, or null
+    float* qn_scale;     // [T]
+};
+hipError_t launch_norm(const NormArgs& a, hipStream_t s);
+
+// Per-token dynamic INT8 quant of a bf16 matrix [T, K] (W8A8 activation quant of x).
+hipError_t launch_act_quant(const uint16_t* x, int T, int K, int8_t* codes, float* scale,
+                            hipStream_t s);
+
+// Per-token INT8 quant of q = [q_nope | q_pe] per head, from the per-tile partial amax the
+// up-projection epilogue wrote.
+struct QuantQArgs {
+    int T, H, Dn, R, n_tiles;
+    const float* part_amax;   // [T, n_tiles]
+    const uint16_t* q_nope;   // [T, H, Dn]
+    const uint16_t* q_pe;     // [T, H, R]
+    int8_t* q_i8;             // [T, H, Dn+R] or null
+    float* q_scale;           // [T] or null
+};
+hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s);
+
+}  // namespace mlap

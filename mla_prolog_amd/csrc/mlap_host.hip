@@ -1,0 +1,465 @@
+// mlap_host.hip -- the C ABI of libmlap.so: validation, per-run plan and launches.
+//
+// The run is a fixed chain of kernels on the caller's stream (no host sync):
+//   [W8A8: act_quant(x)] -> gemm_down (x . [W_qa; W_kva]^T, bf16 out)
+//   -> norm_rope (RMSNorm*gamma -> bf16 for q_a and c_kv, RoPE of k_pe, kv quant)
+//   -> gemm_up_q (q_norm . W_qb^T; per head: q_nope, RoPE'd q_pe, partial amax)
+//   -> gemm_up_kv (kv_norm . W_kvb^T; per head: k_nope, value)   [KV-Prolog mode]
+//   -> quant_q (per-token INT8 codes and scale of all heads' q)
+// The chain follows the MLAProlog walk-through of the AT-10 card ("PyPTO-Gym 算子设计
+// 模式 AT-10 ... MLAProlog 实战", section 五) and the KV Prolog flow of the V2-Lite
+// migration guide ("DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南", section 背景).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/mlap.h"
+#include "launch.hpp"
+
+using namespace mlap;
+
+namespace {
+
+enum KernelId : int32_t {
+    kKActQuant = 0,
+    kKGemmDown = 1,
+    kKNormRope = 2,
+    kKGemmUpQ = 3,
+    kKGemmUpKv = 4,
+    kKQuantQ = 5,
+    kKCount = 6
+};
+const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope",
+                                           "gemm_up_q", "gemm_up_kv", "quant_q"};
+
+constexpr int kBM = 128;
+constexpr int kBNDown = 128;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Widest supported up-projection tile that holds whole heads.
+int heads_tile(int head_w) {
+    static const int cand[] = {256, 192, 128, 64};
+    for (int bn : cand)
+        if (bn % head_w == 0) return bn;
+    return 0;
+}
+
+struct Timer {
+    int32_t kernel = -1;
+    int32_t cap = 0;
+    int32_t used = 0;
+    std::vector<hipEvent_t> ev;  // 2 per launch
+};
+
+// Workspace carve-up for T tokens.
+struct WsLayout {
+    size_t a1 = 0, qn = 0, kvn = 0, qpart = 0, xq = 0, xs = 0, qnq = 0, qns = 0, kvq = 0, kvs = 0;
+    size_t total = 0;
+};
+
+}  // namespace
+
+struct mlap_prolog {
+    mlap_config cfg;
+    bool w8a8;
+    int N1;       // down-projection width
+    int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
+    int bn_q, bn_kv;
+    int nt_q;     // up-projection N tiles of q (partial amax entries per token)
+    Timer timer;
+
+    WsLayout layout(int T) const {
+        WsLayout L;
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = off;
+            off += align_up(bytes);
+            return o;
+        };
+        const size_t t = static_cast<size_t>(T);
+        L.a1 = take(t * N1 * 2);
+        if (cfg.q_lora > 0) L.qn = take(t * cfg.q_lora * 2);
+        if (cfg.v_dim > 0) L.kvn = take(t * cfg.kv_lora * 2);
+        if (cfg.q_lora > 0) L.qpart = take(t * nt_q * 4);
+        if (w8a8) {
+            L.xq = take(t * cfg.hidden);
+            L.xs = take(t * 4);
+            if (cfg.q_lora > 0) {
+                L.qnq = take(t * cfg.q_lora);
+                L.qns = take(t * 4);
+            }
+            if (cfg.v_dim > 0) {
+                L.kvq = take(t * cfg.kv_lora);
+                L.kvs = take(t * 4);
+            }
+        }
+        L.total = std::max<size_t>(off, kAlign);
+        return L;
+    }
+
+    void tick(int32_t k, hipStream_t s, bool begin) {
+        Timer& tm = timer;
+        if (tm.kernel != k || tm.used >= tm.cap) return;
+        (void)hipEventRecord(tm.ev[2 * tm.used + (begin ? 0 : 1)], s);
+        if (!begin) ++tm.used;
+    }
+};
+
+namespace {
+
+int validate(const mlap_config* c) {
+    const bool w8 = (c->flags & MLAP_W8A8) != 0;
+    if (c->flags & ~MLAP_W8A8) return MLAP_ERR_INVALID_ARG;
+    if (c->t_max < 1 || c->hidden < 1 || c->kv_lora < 1 || c->rope_dim < 1 || c->n_heads < 1 ||
+        c->max_pos < 1 || c->q_lora < 0 || c->v_dim < 0 || c->nope_dim < 0 || !(c->eps >= 0.f))
+        return MLAP_ERR_INVALID_ARG;
+    const int kmul = w8 ? 128 : 64;  // K of every GEMM: whole 128-byte K-tiles
+    if (c->hidden % kmul) return MLAP_ERR_UNSUPPORTED;
+    if (c->q_lora % kmul) return MLAP_ERR_UNSUPPORTED;
+    if (c->kv_lora % 8 || (c->v_dim > 0 && c->kv_lora % kmul)) return MLAP_ERR_UNSUPPORTED;
+    if (c->rope_dim % 16) return MLAP_ERR_UNSUPPORTED;
+    if (c->nope_dim % 8 || c->v_dim % 8) return MLAP_ERR_UNSUPPORTED;
+    if (c->q_lora > 8192 || c->kv_lora > 8192) return MLAP_ERR_UNSUPPORTED;  // row kernel
+    if (c->q_lora > 0 && heads_tile(c->nope_dim + c->rope_dim) == 0) return MLAP_ERR_UNSUPPORTED;
+    if (c->v_dim > 0 && heads_tile(c->nope_dim + c->v_dim) == 0) return MLAP_ERR_UNSUPPORTED;
+    // GEMM sizes and grid dimensions are 32-bit in the kernels
+    if (c->t_max > (1 << 24) || c->hidden > (1 << 20) || c->n_heads > 4096 || c->max_pos > (1 << 26))
+        return MLAP_ERR_UNSUPPORTED;
+    return MLAP_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+MLAP_API const char* mlap_version(void) { return "mlap 0.1 gfx950"; }
+
+MLAP_API const char* mlap_status_str(int status) {
+    switch (status) {
+        case MLAP_OK: return "ok";
+        case MLAP_ERR_INVALID_ARG: return "invalid argument";
+        case MLAP_ERR_UNSUPPORTED: return "unsupported dimensions";
+        case MLAP_ERR_WORKSPACE: return "workspace missing or too small";
+        case MLAP_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+MLAP_API const char* mlap_kernel_name(int32_t kernel_id) {
+    return (kernel_id >= 0 && kernel_id < kKCount) ? kKernelNames[kernel_id] : nullptr;
+}
+
+MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
+    if (!cfg || !out) return MLAP_ERR_INVALID_ARG;
+    *out = nullptr;
+    const int v = validate(cfg);
+    if (v != MLAP_OK) return v;
+    mlap_prolog* h = new (std::nothrow) mlap_prolog();
+    if (!h) return MLAP_ERR_INVALID_ARG;
+    h->cfg = *cfg;
+    h->w8a8 = (cfg->flags & MLAP_W8A8) != 0;
+    h->N1 = cfg->q_lora + cfg->kv_lora + cfg->rope_dim;
+    h->QH = cfg->nope_dim + cfg->rope_dim;
+    h->KH = cfg->nope_dim + cfg->v_dim;
+    h->bn_q = cfg->q_lora > 0 ? heads_tile(h->QH) : 0;
+    h->bn_kv = cfg->v_dim > 0 ? heads_tile(h->KH) : 0;
+    h->nt_q = cfg->q_lora > 0 ? (cfg->n_heads * h->QH + h->bn_q - 1) / h->bn_q : 0;
+    *out = h;
+    return MLAP_OK;
+}
+
+MLAP_API void mlap_destroy(mlap_handle h) {
+    if (!h) return;
+    for (hipEvent_t e : h->timer.ev) (void)hipEventDestroy(e);
+    delete h;
+}
+
+MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes) {
+    if (!h || !bytes || T < 0 || T > h->cfg.t_max) return MLAP_ERR_INVALID_ARG;
+    *bytes = h->layout(T).total;
+    return MLAP_OK;
+}
+
+MLAP_API int mlap_timing_begin(mlap_handle h, int32_t kernel_id, int32_t max_launches) {
+    if (!h || kernel_id < 0 || kernel_id >= kKCount || max_launches < 1 || max_launches > 100000)
+        return MLAP_ERR_INVALID_ARG;
+    Timer& tm = h->timer;
+    while (static_cast<int32_t>(tm.ev.size()) < 2 * max_launches) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return MLAP_ERR_HIP;
+        tm.ev.push_back(e);
+    }
+    tm.kernel = kernel_id;
+    tm.cap = max_launches;
+    tm.used = 0;
+    return MLAP_OK;
+}
+
+MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n) {
+    if (!h || !n || (cap > 0 && !ms)) return MLAP_ERR_INVALID_ARG;
+    Timer& tm = h->timer;
+    int rc = MLAP_OK;
+    int32_t k = 0;
+    for (int32_t i = 0; i < tm.used; ++i) {
+        if (hipEventSynchronize(tm.ev[2 * i + 1]) != hipSuccess) {
+            rc = MLAP_ERR_HIP;
+            break;
+        }
+        float v = 0.f;
+        if (hipEventElapsedTime(&v, tm.ev[2 * i], tm.ev[2 * i + 1]) != hipSuccess) {
+            rc = MLAP_ERR_HIP;
+            break;
+        }
+        if (k < cap) ms[k++] = v;
+    }
+    *n = k;
+    tm.kernel = -1;
+    tm.cap = tm.used = 0;
+    return rc;
+}
+
+MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
+             void* ws, size_t ws_bytes) {
+    if (!h || !in || !out) return MLAP_ERR_INVALID_ARG;
+    const mlap_config& c = h->cfg;
+    const int T = in->T;
+    if (T < 0 || T > c.t_max) return MLAP_ERR_INVALID_ARG;
+    if (T == 0) return MLAP_OK;
+    const bool has_q = c.q_lora > 0, has_kvb = c.v_dim > 0, w8 = h->w8a8;
+    // required inputs
+    if (!in->x || !in->positions || !in->w_kva || !in->gamma_kv || !in->cos || !in->sin)
+        return MLAP_ERR_INVALID_ARG;
+    if (has_q && (!in->w_qa || !in->w_qb || !in->gamma_q)) return MLAP_ERR_INVALID_ARG;
+    if (has_kvb && !in->w_kvb) return MLAP_ERR_INVALID_ARG;
+    if (w8 && (!in->ws_kva || (has_q && (!in->ws_qa || !in->ws_qb)) || (has_kvb && !in->ws_kvb)))
+        return MLAP_ERR_INVALID_ARG;
+    // outputs that need a branch this configuration lacks
+    if (!has_q && (out->q_nope || out->q_pe || out->q_norm || out->q_i8 || out->q_scale))
+        return MLAP_ERR_INVALID_ARG;
+    if (!has_kvb && (out->k_nope || out->value)) return MLAP_ERR_INVALID_ARG;
+    // the q quant reads the q tensors back
+    const bool quant_q = out->q_i8 || out->q_scale;
+    if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
+    const WsLayout L = h->layout(T);
+    if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign))
+        return MLAP_ERR_WORKSPACE;
+
+    char* wsb = static_cast<char*>(ws);
+    hipStream_t s = as_stream(stream);
+    const int Lq = c.q_lora, Lkv = c.kv_lora, R = c.rope_dim, H = c.n_heads;
+    uint16_t* a1 = reinterpret_cast<uint16_t*>(wsb + L.a1);
+    uint16_t* qn = has_q ? (out->q_norm ? static_cast<uint16_t*>(out->q_norm)
+                                        : reinterpret_cast<uint16_t*>(wsb + L.qn))
+                         : nullptr;
+    // kv_norm is the kv_b input in KV-Prolog mode: write it to the output when the caller
+    // wants it, else to the workspace.
+    uint16_t* kvn = out->kv_norm ? static_cast<uint16_t*>(out->kv_norm)
+                                 : (has_kvb ? reinterpret_cast<uint16_t*>(wsb + L.kvn) : nullptr);
+    hipError_t e = hipSuccess;
+#define MLAP_LAUNCH(kid, call)       \
+    do {                             \
+        h->tick(kid, s, true);       \
+        e = (call);                  \
+        h->tick(kid, s, false);      \
+        if (e != hipSuccess) return MLAP_ERR_HIP; \
+    } while (0)
+
+    // 1. down projection x . [W_qa ; W_kva]^T -> a1 [T, N1] bf16
+    GemmArgs g{};
+    g.M = T;
+    g.N = h->N1;
+    g.K = c.hidden;
+    g.lda = c.hidden;
+    g.ldb = c.hidden;
+    g.B0 = has_q ? in->w_qa : in->w_kva;
+    g.B1 = in->w_kva;
+    g.b_split = Lq;
+    g.k_splits = 1;
+    g.out = a1;
+    g.ldo = h->N1;
+    if (w8) {
+        int8_t* xq = reinterpret_cast<int8_t*>(wsb + L.xq);
+        float* xs = reinterpret_cast<float*>(wsb + L.xs);
+        MLAP_LAUNCH(kKActQuant, launch_act_quant(static_cast<const uint16_t*>(in->x), T, c.hidden,
+                                                 xq, xs, s));
+        g.A = xq;
+        g.a_scale = xs;
+        g.b_scale0 = has_q ? in->ws_qa : in->ws_kva;
+        g.b_scale1 = in->ws_kva;
+        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kInt8, kBM, kBNDown, Epi::kStoreBf16, s));
+    } else {
+        g.A = in->x;
+        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kBf16, kBM, kBNDown, Epi::kStoreBf16, s));
+    }
+
+    // 2. row stage
+    NormArgs na{};
+    na.T = T;
+    na.Lq = Lq;
+    na.Lkv = Lkv;
+    na.R = R;
+    na.N1 = h->N1;
+    na.k_splits = 1;
+    na.a_bf16 = a1;
+    na.gamma_q = static_cast<const uint16_t*>(in->gamma_q);
+    na.gamma_kv = static_cast<const uint16_t*>(in->gamma_kv);
+    na.eps = c.eps;
+    na.positions = in->positions;
+    na.cos = in->cos;
+    na.sin = in->sin;
+    na.max_pos = c.max_pos;
+    na.q_norm = qn;
+    na.kv_norm = static_cast<uint16_t*>(out->kv_norm);
+    na.k_pe = static_cast<uint16_t*>(out->k_pe);
+    na.kv_i8 = out->kv_i8;
+    na.kv_scale = out->kv_scale;
+    const bool need_q = has_q && (out->q_nope || out->q_pe || quant_q);
+    const bool need_kvb = has_kvb && (out->k_nope || out->value);
+    if (need_kvb && !w8) na.kv_norm = kvn;  // the bf16 kv_b reads it
+    if (w8 && need_q) {
+        na.qn_i8 = reinterpret_cast<int8_t*>(wsb + L.qnq);
+        na.qn_scale = reinterpret_cast<float*>(wsb + L.qns);
+    }
+    if (w8 && need_kvb) {
+        na.kv_i8_b = reinterpret_cast<int8_t*>(wsb + L.kvq);
+        na.kv_scale_b = reinterpret_cast<float*>(wsb + L.kvs);
+    }
+    MLAP_LAUNCH(kKNormRope, launch_norm(na, s));
+
+    // 3. q up projection with split / RoPE / partial amax epilogue
+    if (need_q) {
+        GemmArgs u{};
+        u.M = T;
+        u.N = H * h->QH;
+        u.K = Lq;
+        u.lda = Lq;
+        u.ldb = Lq;
+        u.B0 = u.B1 = in->w_qb;
+        u.b_split = u.N;
+        u.k_splits = 1;
+        u.head_w = h->QH;
+        u.d0 = c.nope_dim;
+        u.d1 = R;
+        u.rope = 1;
+        u.n_heads = H;
+        u.out0 = out->q_nope;
+        u.out1 = out->q_pe;
+        u.positions = in->positions;
+        u.cos = in->cos;
+        u.sin = in->sin;
+        u.max_pos = c.max_pos;
+        u.part_amax = quant_q ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+        u.n_tiles = h->nt_q;
+        if (w8) {
+            u.A = na.qn_i8;
+            u.a_scale = na.qn_scale;
+            u.b_scale0 = u.b_scale1 = in->ws_qb;
+            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kInt8, kBM, h->bn_q, Epi::kHeads, s));
+        } else {
+            u.A = qn;
+            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kBf16, kBM, h->bn_q, Epi::kHeads, s));
+        }
+    }
+
+    // 4. kv_b up projection (KV-Prolog mode): per head [k_nope | value]
+    if (need_kvb) {
+        GemmArgs u{};
+        u.M = T;
+        u.N = H * h->KH;
+        u.K = Lkv;
+        u.lda = Lkv;
+        u.ldb = Lkv;
+        u.B0 = u.B1 = in->w_kvb;
+        u.b_split = u.N;
+        u.k_splits = 1;
+        u.head_w = h->KH;
+        u.d0 = c.nope_dim;
+        u.d1 = c.v_dim;
+        u.rope = 0;
+        u.n_heads = H;
+        u.out0 = out->k_nope;
+        u.out1 = out->value;
+        if (w8) {
+            u.A = na.kv_i8_b;
+            u.a_scale = na.kv_scale_b;
+            u.b_scale0 = u.b_scale1 = in->ws_kvb;
+            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kInt8, kBM, h->bn_kv, Epi::kHeads, s));
+        } else {
+            u.A = kvn;
+            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kBf16, kBM, h->bn_kv, Epi::kHeads, s));
+        }
+    }
+
+    // 5. per-token INT8 quant of q (after RoPE), one scale over all heads
+    if (has_q && quant_q) {
+        QuantQArgs qa{};
+        qa.T = T;
+        qa.H = H;
+        qa.Dn = c.nope_dim;
+        qa.R = R;
+        qa.n_tiles = h->nt_q;
+        qa.part_amax = reinterpret_cast<const float*>(wsb + L.qpart);
+        qa.q_nope = static_cast<const uint16_t*>(out->q_nope);
+        qa.q_pe = static_cast<const uint16_t*>(out->q_pe);
+        qa.q_i8 = out->q_i8;
+        qa.q_scale = out->q_scale;
+        MLAP_LAUNCH(kKQuantQ, launch_quant_q(qa, s));
+    }
+#undef MLAP_LAUNCH
+    return MLAP_OK;
+}
+
+MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, int32_t* C, int32_t M,
+                     int32_t N, int32_t K) {
+    if (M < 0 || N < 0 || K <= 0) return MLAP_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MLAP_OK;
+    if (!A || !B || !C) return MLAP_ERR_INVALID_ARG;
+    if (K % 128) return MLAP_ERR_UNSUPPORTED;
+    GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.lda = K;
+    g.B0 = g.B1 = B;
+    g.b_split = N;
+    g.ldb = K;
+    g.k_splits = 1;
+    g.out = C;
+    g.ldo = N;
+    return launch_gemm(g, InType::kInt8, kBM, 128, Epi::kStoreI32, as_stream(stream)) == hipSuccess
+               ? MLAP_OK
+               : MLAP_ERR_HIP;
+}
+
+MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C, int32_t M, int32_t N,
+                   int32_t K) {
+    if (M < 0 || N < 0 || K <= 0) return MLAP_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MLAP_OK;
+    if (!A || !B || !C) return MLAP_ERR_INVALID_ARG;
+    if (K % 64 || N % 8) return MLAP_ERR_UNSUPPORTED;
+    GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.lda = K;
+    g.B0 = g.B1 = B;
+    g.b_split = N;
+    g.ldb = K;
+    g.k_splits = 1;
+    g.out = C;
+    g.ldo = N;
+    return launch_gemm(g, InType::kBf16, kBM, 128, Epi::kStoreBf16, as_stream(stream)) == hipSuccess
+               ? MLAP_OK
+               : MLAP_ERR_HIP;
+}
+
+}  // extern "C"

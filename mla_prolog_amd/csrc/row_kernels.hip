@@ -1,0 +1,251 @@
+// row_kernels.hip -- per-token row stages of the MLA Prolog on gfx950.
+//
+// These stages are tiny next to the GEMMs (a few hundred bytes per token) and
+// are latency work: one 256-thread workgroup owns one token row, keeps it in
+// registers, and reduces across the row with wave-wide butterfly shuffles plus
+// a 4-entry LDS exchange in a fixed order (so results do not depend on timing).
+//
+// RMSNorm follows variant B of the AT-10 card ("PyPTO-Gym 算子设计模式 AT-10 ...
+// MLAProlog 实战", section 三): fp32 x^2, times 1/D, row sum, +eps, sqrt, 1/std
+// by an IEEE divide, x*rstd; then *fp32(gamma) and the bf16 cast (section 五).
+// RoPE is rotate-half with one cos/sin row per token ("PyPTO Operator 深度解析",
+// section 3.3). The INT8 quant is the per-row PrologQuant of the same page,
+// section 3.1: multiplier 127/amax, round half to even, saturate, scale amax/127.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mlap {
+
+constexpr int kRowThreads = 256;
+constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kMaxChunks = 4;  // 8-element chunks per thread and segment: widths <= 8192
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) t += sh[w];
+    return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) t = fmaxf(t, sh[w]);
+    return t;
+}
+
+// 8 consecutive down-projection outputs of token t starting at column col, as the fp32
+// values of their bf16 rounding (the GEMM's bf16 output cast point).
+__device__ __forceinline__ void load_a8(const NormArgs& a, int t, int col, float* f) {
+    if (a.k_splits == 1) {
+        unpack8(*reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col), f);
+        return;
+    }
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < a.k_splits; ++sp) {
+        const float4* p = reinterpret_cast<const float4*>(
+            a.a_f32 + (static_cast<size_t>(sp) * a.T + t) * a.N1 + col);
+        const float4 x0 = p[0], x1 = p[1];
+        s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
+        s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+}
+
+__global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
+    __shared__ float red[kRowWaves];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
+
+    float qv[kMaxChunks][8], kv[kMaxChunks][8];
+    float sq = 0.f, skv = 0.f;
+    const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
+    const float invkv = 1.0f / static_cast<float>(a.Lkv);
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = tid + i * kRowThreads;
+        if (c < nq) {
+            load_a8(a, t, c * 8, qv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = qv[i][e] * qv[i][e];
+                sq += p * invq;
+            }
+        }
+        if (c < nkv) {
+            load_a8(a, t, a.Lq + c * 8, kv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = kv[i][e] * kv[i][e];
+                skv += p * invkv;
+            }
+        }
+    }
+    const float msq = (a.Lq > 0) ? block_sum(sq, red) : 0.f;
+    const float mskv = block_sum(skv, red);
+    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
+    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+
+    float qmax = 0.f, kvmax = 0.f;
+    uint4 qo[kMaxChunks], kvo[kMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+        const int c = tid + i * kRowThreads;
+        if (c < nq) {
+            float g[8], o[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.gamma_q + c * 8), g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = qv[i][e] * rstd_q;
+                o[e] = y * g[e];
+            }
+            qo[i] = pack8(o);
+            if (a.q_norm)
+                *reinterpret_cast<uint4*>(a.q_norm + static_cast<size_t>(t) * a.Lq + c * 8) = qo[i];
+            qmax = fmaxf(qmax, absmax8(qo[i]));
+        }
+        if (c < nkv) {
+            float g[8], o[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.gamma_kv + c * 8), g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = kv[i][e] * rstd_kv;
+                o[e] = y * g[e];
+            }
+            kvo[i] = pack8(o);
+            if (a.kv_norm)
+                *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
+            kvmax = fmaxf(kvmax, absmax8(kvo[i]));
+        }
+    }
+
+    // rotate-half RoPE of the k_pe slice (pairs i, i + R/2), one cos/sin row per token
+    const int half = a.R >> 1;
+    if (a.k_pe && tid < (half >> 3)) {
+        const int i0 = tid * 8;
+        const int p = clamp_pos(a.positions[t], a.max_pos);
+        const float* cr = a.cos + static_cast<size_t>(p) * a.R;
+        const float* sr = a.sin + static_cast<size_t>(p) * a.R;
+        float x1[8], x2[8], lo[8], hi[8];
+        load_a8(a, t, a.Lq + a.Lkv + i0, x1);
+        load_a8(a, t, a.Lq + a.Lkv + half + i0, x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float p1 = x1[e] * cr[i0 + e];
+            float p2 = (-x2[e]) * sr[i0 + e];
+            lo[e] = p1 + p2;
+            float p3 = x2[e] * cr[half + i0 + e];
+            float p4 = x1[e] * sr[half + i0 + e];
+            hi[e] = p3 + p4;
+        }
+        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
+        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
+        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+    }
+
+    // per-token INT8 quant of kv_norm
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+        const float amax = block_max(kvmax, red);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxChunks; ++i) {
+            const int c = tid + i * kRowThreads;
+            if (c < nkv) {
+                const uint2 codes = quant8(kvo[i], mult);
+                const size_t off = static_cast<size_t>(t) * a.Lkv + c * 8;
+                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+            }
+        }
+        if (tid == 0) {
+            const float sc = amax / 127.0f;
+            if (a.kv_scale) a.kv_scale[t] = sc;
+            if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+        }
+    }
+    // W8A8: per-token activation quant of q_norm for the int8 up projection
+    if (a.qn_i8) {
+        const float amax = block_max(qmax, red);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxChunks; ++i) {
+            const int c = tid + i * kRowThreads;
+            if (c < nq)
+                *reinterpret_cast<uint2*>(a.qn_i8 + static_cast<size_t>(t) * a.Lq + c * 8) =
+                    quant8(qo[i], mult);
+        }
+        if (tid == 0) a.qn_scale[t] = amax / 127.0f;
+    }
+}
+
+__global__ __launch_bounds__(kRowThreads) void act_quant_kernel(const uint16_t* x, int K,
+                                                                int8_t* codes, float* scale) {
+    __shared__ float red[kRowWaves];
+    const int t = blockIdx.x;
+    const uint16_t* row = x + static_cast<size_t>(t) * K;
+    const int nc = K >> 3;
+    float m = 0.f;
+    for (int c = threadIdx.x; c < nc; c += kRowThreads)
+        m = fmaxf(m, absmax8(*reinterpret_cast<const uint4*>(row + c * 8)));
+    const float amax = block_max(m, red);
+    const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+    for (int c = threadIdx.x; c < nc; c += kRowThreads)
+        *reinterpret_cast<uint2*>(codes + static_cast<size_t>(t) * K + c * 8) =
+            quant8(*reinterpret_cast<const uint4*>(row + c * 8), mult);
+    if (threadIdx.x == 0) scale[t] = amax / 127.0f;
+}
+
+__global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
+    __shared__ float red[kRowWaves];
+    const int t = blockIdx.x;
+    float m = 0.f;
+    for (int i = threadIdx.x; i < a.n_tiles; i += kRowThreads)
+        m = fmaxf(m, a.part_amax[static_cast<size_t>(t) * a.n_tiles + i]);
+    const float amax = block_max(m, red);
+    if (threadIdx.x == 0 && a.q_scale) a.q_scale[t] = amax / 127.0f;
+    if (!a.q_i8) return;
+    const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+    const int QH = a.Dn + a.R;
+    const int cph = QH >> 3, cn = a.Dn >> 3;
+    const int total = a.H * cph;
+    for (int c = threadIdx.x; c < total; c += kRowThreads) {
+        const int h = c / cph, j = c - h * cph;
+        const size_t th = static_cast<size_t>(t) * a.H + h;
+        const uint4 v = (j < cn) ? *reinterpret_cast<const uint4*>(a.q_nope + th * a.Dn + j * 8)
+                                 : *reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
+        *reinterpret_cast<uint2*>(a.q_i8 + th * QH + j * 8) = quant8(v, mult);
+    }
+}
+
+hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(norm_rope_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int T, int K, int8_t* codes, float* scale,
+                            hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(act_quant_kernel, dim3(T), dim3(kRowThreads), 0, s, x, K, codes, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_q_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace mlap

@@ -78,6 +78,9 @@ def load():
             lib.orc_prolog.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p, C.c_int32,
                                        C.POINTER(_Outputs)]
             lib.orc_prolog.restype = C.c_int
+            lib.orc_prolog_from.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p,
+                                            C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(_Outputs)]
+            lib.orc_prolog_from.restype = C.c_int
             lib.orc_num_threads.restype = C.c_int
             _lib = lib
     return _lib
@@ -198,12 +201,14 @@ def quant_rows(Z):
 
 # ----------------------------------------------------------------- prolog ----
 
-def prolog(cfg, inputs, rows=None):
+def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
     """Run the whole MLA Prolog for token ``rows`` (default: all) of ``inputs``.
 
     ``cfg`` is a ``synth.Config`` (or anything with its attributes); ``inputs``
     the dict from ``synth.make_inputs``. Returns a dict of numpy arrays, one row
     per entry of ``rows``: bf16 outputs as uint16 bits, codes int8, scales fp32.
+    ``q_norm`` / ``kv_norm`` (optional, [len(rows), width] bf16): start the q_b / kv_b
+    projections from these rows instead of the oracle's own normalised rows.
     The chain is the V3 MLA Prolog of the AT-10 card, section 五 (q_a -> RMSNorm
     -> *gamma -> bf16 -> q_b; kv_a -> RMSNorm -> *gamma -> bf16), with the kv_b
     stage of the V2-Lite KV Prolog ("DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南",
@@ -252,7 +257,9 @@ def prolog(cfg, inputs, rows=None):
     c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8))
     i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
     o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
-    rc = load().orc_prolog(C.byref(c), C.byref(i), _p(rows), n, C.byref(o))
+    qn = None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq)
+    kvn = None if kv_norm is None else _np(kv_norm, np.uint16).reshape(n, Lkv)
+    rc = load().orc_prolog_from(C.byref(c), C.byref(i), _p(rows), n, _p(qn), _p(kvn), C.byref(o))
     if rc != 0:
         raise ValueError("oracle rejected the inputs (rc=%d)" % rc)
     return outs

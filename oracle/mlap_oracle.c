@@ -267,9 +267,14 @@ static void orc_project(const orc_cfg* cfg, const uint16_t* v, int64_t K, const 
 }
 
 /* Full prolog for the token rows listed in rows[0..nrows). NULL outputs are skipped.
+ * qn_given [nrows, q_lora] / kvn_given [nrows, kv_lora] (bf16, optional): when given,
+ * the up projections start from these normalised rows instead of the ones this
+ * function computes (the rest of the chain is unchanged); this lets a caller check
+ * the second stage on exactly the inputs another implementation fed it.
  * Returns 0, or -1 on an argument the oracle does not accept. */
-ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
-                       int32_t nrows, const orc_outputs* out) {
+ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
+                            int32_t nrows, const uint16_t* qn_given, const uint16_t* kvn_given,
+                            const orc_outputs* out) {
     const int64_t Hd = cfg->hidden, Lq = cfg->q_lora, Lkv = cfg->kv_lora, R = cfg->rope_dim;
     const int64_t Dn = cfg->nope_dim, Dv = cfg->v_dim, H = cfg->n_heads;
     const int64_t QH = Dn + R, KH = Dn + Dv;
@@ -314,7 +319,8 @@ ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* 
             if (out->kv_scale) out->kv_scale[i] = sc;
         }
         if (Dv > 0) { /* kv_b projection of the normalised compressed KV */
-            orc_project(cfg, kvn, Lkv, in->w_kvb, in->ws_kvb, H * KH, a, codes);
+            const uint16_t* kv_src = kvn_given ? kvn_given + i * Lkv : kvn;
+            orc_project(cfg, kv_src, Lkv, in->w_kvb, in->ws_kvb, H * KH, a, codes);
             for (int64_t h = 0; h < H; ++h) {
                 if (out->k_nope)
                     memcpy(out->k_nope + (i * H + h) * Dn, a + h * KH, sizeof(uint16_t) * (size_t)Dn);
@@ -328,7 +334,8 @@ ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* 
             orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, Lq, a, codes);
             orc_rmsnorm_row(a, in->gamma_q, Lq, cfg->eps, qn);
             if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
-            orc_project(cfg, qn, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
+            const uint16_t* q_src = qn_given ? qn_given + i * Lq : qn;
+            orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
             for (int64_t h = 0; h < H; ++h) {
                 const uint16_t* head = a + h * QH;
                 uint16_t* qh = qrow + h * QH;
@@ -347,6 +354,11 @@ ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* 
         free(a); free(qn); free(kvn); free(qrow); free(codes);
     }
     return bad ? -1 : 0;
+}
+
+ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
+                       int32_t nrows, const orc_outputs* out) {
+    return orc_prolog_from(cfg, in, rows, nrows, NULL, NULL, out);
 }
 
 ORC_API int orc_num_threads(void) {

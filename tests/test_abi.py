@@ -1,0 +1,165 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host-side validation returns the documented status codes
+before touching the GPU (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_prolog_amd as mlap
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlap.h")
+lib = mlap._lib
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"MLAP_API\s+[\w\s\*]+?\b(mlap_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    syms = declared_symbols()
+    assert set(syms) == set(mlap.EXPORTS), syms
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", mlap.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mlap_\w+)", out))
+    missing = set(declared_symbols()) - exported
+    assert not missing, missing
+    # internal kernels and helpers stay hidden
+    assert all(s.startswith("mlap_") for s in re.findall(r"\bT (\w+)", out) if "mlap" in s)
+
+
+def test_status_strings_and_kernel_names():
+    for s in range(5):
+        assert lib.mlap_status_str(s)
+    assert lib.mlap_status_str(99) == b"unknown status"
+    assert mlap.KERNELS == ("act_quant", "gemm_down", "norm_rope", "gemm_up_q", "gemm_up_kv",
+                            "quant_q")
+    assert mlap.version().startswith("mlap")
+
+
+def cfg_struct(**kw):
+    base = dict(t_max=256, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64, nope_dim=128,
+                v_dim=0, n_heads=128, max_pos=8192, eps=1e-6, flags=0)
+    base.update(kw)
+    return mlap._Config(*(base[k] for k in ("t_max", "hidden", "q_lora", "kv_lora", "rope_dim",
+                                            "nope_dim", "v_dim", "n_heads", "max_pos")),
+                        C.c_float(base["eps"]), base["flags"])
+
+
+def create(**kw):
+    h = C.c_void_p()
+    rc = lib.mlap_create(C.byref(cfg_struct(**kw)), C.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), mlap.MLAP_OK),
+    (dict(q_lora=0, v_dim=128, n_heads=16, hidden=2048), mlap.MLAP_OK),
+    (dict(flags=mlap.MLAP_W8A8), mlap.MLAP_OK),
+    (dict(t_max=0), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(eps=-1.0), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=0x80), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(hidden=7000), mlap.MLAP_ERR_UNSUPPORTED),          # not whole 128-byte K tiles
+    (dict(hidden=7168 + 64, flags=mlap.MLAP_W8A8), mlap.MLAP_ERR_UNSUPPORTED),
+    (dict(rope_dim=24), mlap.MLAP_ERR_UNSUPPORTED),          # RoPE pairs in 8-wide chunks
+    (dict(nope_dim=100), mlap.MLAP_ERR_UNSUPPORTED),
+    (dict(nope_dim=120, rope_dim=64), mlap.MLAP_ERR_UNSUPPORTED),  # head 184 fits no tile
+    (dict(q_lora=16384), mlap.MLAP_ERR_UNSUPPORTED),
+])
+def test_create_validation(kw, status):
+    rc, h = create(**kw)
+    assert rc == status
+    if rc == mlap.MLAP_OK:
+        lib.mlap_destroy(h)
+    else:
+        assert not h.value
+
+
+def test_create_null_args_and_destroy_null():
+    h = C.c_void_p()
+    assert lib.mlap_create(None, C.byref(h)) == mlap.MLAP_ERR_INVALID_ARG
+    assert lib.mlap_create(C.byref(cfg_struct()), None) == mlap.MLAP_ERR_INVALID_ARG
+    lib.mlap_destroy(None)
+
+
+def test_workspace_size_grows_with_T_and_is_aligned():
+    p = mlap.Prolog.from_config(synth.get_config("v3_prefill"))
+    sizes = [p.workspace_size(T) for T in (0, 1, 256, 8192)]
+    assert sizes == sorted(sizes) and all(s % 256 == 0 for s in sizes)
+    # down-projection output + q_norm + partial amax (128 tiles of one 192-wide head)
+    T = 8192
+    assert sizes[-1] >= T * 2112 * 2 + T * 1536 * 2 + T * 128 * 4
+    with pytest.raises(mlap.MlapError):
+        p.workspace_size(8193)
+    w8 = mlap.Prolog.from_config(synth.get_config("v3_w8a8"))
+    assert w8.workspace_size(16) > mlap.Prolog.from_config(
+        synth.get_config("v3_decode")).workspace_size(16)
+
+
+def _run_raw(h, inp, out, ws, ws_bytes):
+    return lib.mlap_run(h, None, C.byref(inp), C.byref(out), C.c_void_p(ws), C.c_size_t(ws_bytes))
+
+
+def test_run_argument_errors_return_before_any_launch():
+    rc, h = create(t_max=64)
+    assert rc == 0
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    full = dict(T=8, x=fake, positions=fake, w_qa=fake, w_qb=fake, w_kva=fake, gamma_q=fake,
+                gamma_kv=fake, cos=fake, sin=fake)
+    ws_need = C.c_size_t()
+    assert lib.mlap_workspace_size(h, 8, C.byref(ws_need)) == 0
+    out = mlap._Outputs(q_nope=fake, q_pe=fake, q_i8=fake, q_scale=fake)
+    # workspace missing / too small / misaligned
+    assert _run_raw(h, mlap._Inputs(**full), out, None, 0) == mlap.MLAP_ERR_WORKSPACE
+    assert _run_raw(h, mlap._Inputs(**full), out, 0x100000, ws_need.value - 1) == \
+        mlap.MLAP_ERR_WORKSPACE
+    assert _run_raw(h, mlap._Inputs(**full), out, 0x100010, ws_need.value) == \
+        mlap.MLAP_ERR_WORKSPACE
+    # T outside [0, t_max]
+    assert _run_raw(h, mlap._Inputs(**dict(full, T=65)), out, 0x100000, 1 << 30) == \
+        mlap.MLAP_ERR_INVALID_ARG
+    assert _run_raw(h, mlap._Inputs(**dict(full, T=-1)), out, 0x100000, 1 << 30) == \
+        mlap.MLAP_ERR_INVALID_ARG
+    # T == 0 is a no-op that succeeds without touching anything
+    assert _run_raw(h, mlap._Inputs(**dict(full, T=0)), out, None, 0) == mlap.MLAP_OK
+    # missing required inputs
+    for k in ("x", "positions", "w_kva", "gamma_kv", "cos", "sin", "w_qa", "w_qb", "gamma_q"):
+        assert _run_raw(h, mlap._Inputs(**dict(full, **{k: None})), out, 0x100000, 1 << 30) == \
+            mlap.MLAP_ERR_INVALID_ARG, k
+    # outputs of a branch the configuration lacks (no kv_b here)
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(k_nope=fake), 0x100000, 1 << 30) == \
+        mlap.MLAP_ERR_INVALID_ARG
+    # q codes need the q tensors they are computed from
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(q_i8=fake, q_pe=fake), 0x100000,
+                    1 << 30) == mlap.MLAP_ERR_INVALID_ARG
+    assert lib.mlap_run(None, None, C.byref(mlap._Inputs(**full)), C.byref(out), None, 0) == \
+        mlap.MLAP_ERR_INVALID_ARG
+    lib.mlap_destroy(h)
+
+
+def test_w8a8_run_needs_weight_scales():
+    rc, h = create(t_max=64, flags=mlap.MLAP_W8A8)
+    assert rc == 0
+    fake = 0x10000
+    full = dict(T=8, x=fake, positions=fake, w_qa=fake, w_qb=fake, w_kva=fake, gamma_q=fake,
+                gamma_kv=fake, cos=fake, sin=fake, ws_qa=fake, ws_qb=fake)
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(), 0x100000, 1 << 30) == \
+        mlap.MLAP_ERR_INVALID_ARG  # ws_kva missing
+    lib.mlap_destroy(h)
+
+
+def test_export_gemm_argument_errors():
+    assert lib.mlap_gemm_i8_i32(None, None, None, None, 4, 4, 100) == mlap.MLAP_ERR_INVALID_ARG
+    assert lib.mlap_gemm_i8_i32(None, 1, 1, 1, 4, 4, 100) == mlap.MLAP_ERR_UNSUPPORTED
+    assert lib.mlap_gemm_i8_i32(None, None, None, None, 0, 4, 128) == mlap.MLAP_OK
+    assert lib.mlap_gemm_bf16(None, 1, 1, 1, 4, 4, 96) == mlap.MLAP_ERR_UNSUPPORTED
+    assert lib.mlap_gemm_bf16(None, 1, 1, 1, 4, 12, 64) == mlap.MLAP_ERR_UNSUPPORTED
+    assert lib.mlap_gemm_bf16(None, None, None, None, 4, 4, -1) == mlap.MLAP_ERR_INVALID_ARG
