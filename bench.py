@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MLA Prolog (one GPU).
+
+One step = one whole prolog (every kernel of mlap_run) over one batch of
+synthetic tokens already resident in HBM. The headline workload is the
+DeepSeek-V3-shape prolog in prefill (T=8192 tokens, hidden 7168, q_lora 1536,
+kv_lora 512, rope 64, nope 128, 128 heads, bf16, 1% outlier channels x20); the
+same line carries the V3 decode batch (T=256) as a second measurement, timed
+with four rotating weight/input sets (423 MB) so the 256 MB last-level cache
+cannot hold the weights between steps.
+
+Prints ONE JSON line. ``roofline`` is for the dominant kernel (the q up
+projection, gemm_up_q): algorithmic FLOPs (or bytes) per launch divided by the
+kernel's average duration, measured with HIP events recorded around that
+kernel on the stream it runs on. ``cpu_baseline`` times the CPU oracle on a
+bounded sample of token rows of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DOMINANT = "gemm_up_q"
+KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "gemm_kernels.hip"]
+
+
+def up_q_work(cfg, T):
+    """Algorithmic FLOPs and bytes of one gemm_up_q launch over T tokens.
+
+    FLOPs: 2*T*N*K with N = H*(nope+rope), K = q_lora. Bytes: the q_b weight once,
+    q_norm in, q_nope and q_pe out (bf16), and each token's cos/sin row."""
+    N = cfg.n_heads * cfg.q_head
+    wbytes = N * cfg.q_lora * (1 if cfg.w8a8 else 2)
+    flops = 2.0 * T * N * cfg.q_lora
+    byts = wbytes + T * cfg.q_lora * 2 + T * N * 2 + T * cfg.rope_dim * 8
+    return flops, byts
+
+
+def path_work(cfg, T):
+    """Algorithmic FLOPs and HBM bytes of the whole prolog (weights, x and outputs once)."""
+    H, Dn, R, Lq, Lkv, Hd = cfg.n_heads, cfg.nope_dim, cfg.rope_dim, cfg.q_lora, cfg.kv_lora, cfg.hidden
+    wb = 1 if cfg.w8a8 else 2
+    N1 = Lq + Lkv + R
+    flops = 2.0 * T * (N1 * Hd + H * (Dn + R) * Lq)
+    weights = (N1 * Hd + H * (Dn + R) * Lq) * wb + (Lq + Lkv) * 2
+    per_tok = (Hd * 2 + 4 + R * 8 + H * Dn * 2 + H * R * 2 + Lkv * 2 + R * 2 +
+               H * (Dn + R) + 4 + Lkv + 4)
+    return flops, weights + T * per_tok
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_prolog_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "gemm_up_q_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT):
+    import torch
+
+    import mla_prolog_amd as mlap
+    import synth
+
+    cfg = synth.get_config(name)
+    T = cfg.T
+    sets = []
+    for r in range(rotate):
+        seed = None if r == 0 else synth.seed_for(cfg) + 100 * r
+        inp = synth.make_inputs(cfg, seed=seed)
+        sets.append({k: v.cuda() for k, v in inp.items()})
+        del inp
+    p = mlap.Prolog.from_config(cfg)
+    outs = p.alloc_outputs(T)
+    ws = p.workspace(T)
+    for i in range(warmup):
+        p.run(sets[i % rotate], outputs=outs, workspace=ws)
+    torch.cuda.synchronize()
+    p.timing_begin(dominant, steps)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        p.run(sets[i % rotate], outputs=outs, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    kms = p.timing_end()
+    k_avg = sum(kms) / len(kms)
+    del sets
+    return cfg, ms_step, k_avg, len(kms)
+
+
+def roofline_for(cfg, T, k_ms, workload):
+    flops, byts = up_q_work(cfg, T)
+    intensity = flops / byts
+    peak_c = PEAK_I8_TOPS if cfg.w8a8 else PEAK_BF16_TFLOPS
+    ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(workload)
+    if intensity >= ridge:
+        ach = flops / (k_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_c,
+                "unit": "TOP/s" if cfg.w8a8 else "TFLOP/s", "frac": round(ach / peak_c, 4),
+                "traffic": traffic, "kernel": DOMINANT, "kernel_ms": round(k_ms, 5),
+                "algorithmic_flops": flops, "algorithmic_bytes": byts}
+    ach = byts / (k_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": DOMINANT,
+            "kernel_ms": round(k_ms, 5), "algorithmic_flops": flops, "algorithmic_bytes": byts}
+
+
+def cpu_baseline(name, seconds=12.0):
+    """The CPU oracle, as it stands, on the first token rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    cfg = synth.get_config(name)
+    inp = synth.make_inputs(cfg)
+    n = 8
+    t0 = time.time()
+    oracle.prolog(cfg, inp, rows=np.arange(n, dtype=np.int32))
+    dt = time.time() - t0
+    n = int(min(cfg.T, max(n, seconds / max(dt / n, 1e-6))))
+    t0 = time.time()
+    oracle.prolog(cfg, inp, rows=np.arange(n, dtype=np.int32))
+    dt = time.time() - t0
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d of the %d token rows of %s (whole prolog per row, fp64 sums, "
+                      "OpenMP over rows), %.1f s" % (n, cfg.T, name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--decode-workload", default="v3_decode")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg, ms, k_ms, nk = bench_workload(a.workload, a.steps, a.warmup, rotate=1)
+    T = cfg.T
+    pf, pb = path_work(cfg, T)
+    line = {
+        "metric": "MLA Prolog tokens/s at V3 dims (T=256, T=8192); % MFMA / HBM roofline",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if cfg.w8a8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: DeepSeek-V3 MLA Prolog, T=%d, hidden %d, q_lora %d, kv_lora %d, "
+                               "rope %d, nope %d, heads %d" % (cfg.name, T, cfg.hidden, cfg.q_lora,
+                                                               cfg.kv_lora, cfg.rope_dim,
+                                                               cfg.nope_dim, cfg.n_heads),
+                   "tokens": T, "parallelism": "none (1 GPU)"},
+        "roofline": roofline_for(cfg, T, k_ms, cfg.name),
+        "path": {"tflops": round(pf / (ms * 1e-3) / 1e12, 2),
+                 "frac_bf16_peak": round(pf / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+    }
+    if a.decode_workload:
+        dcfg, dms, dk_ms, _ = bench_workload(a.decode_workload, a.decode_steps, a.warmup, rotate=4)
+        dpf, dpb = path_work(dcfg, dcfg.T)
+        line["decode"] = {
+            "workload": "%s: DeepSeek-V3 MLA Prolog decode batch, T=%d, 4 rotating weight sets"
+                        % (dcfg.name, dcfg.T),
+            "value": round(dcfg.T / (dms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(dms, 5), "steps": a.decode_steps,
+            "roofline": roofline_for(dcfg, dcfg.T, dk_ms, dcfg.name),
+            "path": {"hbm_gbs": round(dpb / (dms * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(dpb / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": dpb},
+        }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace mlap {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,6 +15,17 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1. Every index seen
+// by the body is a constant, so register arrays it touches are never demoted to memory.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // bf16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf2f(uint16_t b) {

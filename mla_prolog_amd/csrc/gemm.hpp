@@ -37,7 +37,8 @@ struct GemmArgs {
     const void* B1;
     int b_split;
     int ldb;
-    int k_splits;  // grid.z; each split covers K/k_splits (kStoreF32 only)
+    int k_splits;  // each split covers K/k_splits (kStoreF32 only)
+    int group_m;   // M-tiles per group in the workgroup -> tile order
     // W8A8 dequant: y = f32(acc) * (a_scale[m] * b_scale[n]); b_scale split like B.
     const float* a_scale;
     const float* b_scale0;
@@ -69,7 +70,7 @@ struct MfmaOp<uint16_t> {  // bf16
         for (int i = 0; i < 16; ++i) z[i] = 0.f;
         return z;
     }
-    static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) {
+    static __device__ __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x4& b) {
         bf16x8 av = __builtin_bit_cast(bf16x8, a);
         bf16x8 bv = __builtin_bit_cast(bf16x8, b);
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
@@ -85,17 +86,18 @@ struct MfmaOp<int8_t> {  // int8
         for (int i = 0; i < 16; ++i) z[i] = 0;
         return z;
     }
-    static __device__ __forceinline__ void mma(acc_t& c, const uint4& a, const uint4& b) {
-        i32x4 av = __builtin_bit_cast(i32x4, a);
-        i32x4 bv = __builtin_bit_cast(i32x4, b);
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
+    static __device__ __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x4& b) {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
     }
 };
 
 constexpr int kTileKBytes = 128;
 constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 
-template <int BM, int BN, int WM, int WN>
+// Tile geometry. BM x BN output tile per workgroup of WM x WN waves; each wave owns a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA fragments. P K-tiles are kept in flight in
+// registers ahead of the one being multiplied; LDS holds two K-tiles.
+template <int BM, int BN, int WM, int WN, int P>
 struct TileShape {
     static constexpr int NT = kWave * WM * WN;
     static constexpr int TM = BM / WM;
@@ -104,23 +106,48 @@ struct TileShape {
     static constexpr int FN = TN / 32;
     static constexpr int A_PER = BM * 8 / NT;  // 16-byte chunks per thread per K-tile
     static constexpr int B_PER = BN * 8 / NT;
-    static constexpr int MAIN_LDS = (BM + BN) * kLdsRow;
+    static constexpr int CH = A_PER + B_PER;
+    static constexpr int STAGE_LDS = (BM + BN) * kLdsRow;
+    static constexpr int MAIN_LDS = 2 * STAGE_LDS;
     static constexpr int EPI_ROWS = TM;                      // rows staged per epilogue pass
     static constexpr int EPI_PITCH = BN + 8;                 // bf16 elements per staged row
     static constexpr int EPI_LDS = EPI_ROWS * EPI_PITCH * 2 + EPI_ROWS * 4;
     static constexpr int LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
     static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32-aligned");
     static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile rows must split over threads");
-    static_assert(LDS <= 65536, "LDS budget");
+    static_assert(P >= 1 && P <= 4, "prefetch depth");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// Workgroup -> tile order. The hardware hands workgroup i to XCD i % 8; this makes
+// each XCD own one contiguous range of the (split, tile) space, walked in groups of
+// `group_m` M-tiles, so the workgroups that run together on an XCD share A and B
+// rows in that XCD's L2.
+__device__ __forceinline__ void tile_of(int lin, int tiles_m, int tiles_n, int splits, int group_m,
+                                        int& m_tile, int& n_tile, int& split) {
+    const int total = tiles_m * tiles_n * splits;
+    const int x = lin & 7, j = lin >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int t2 = x * q + (x < r ? x : r) + j;
+    const int tiles = tiles_m * tiles_n;
+    split = t2 / tiles;
+    const int t = t2 - split * tiles;
+    const int gsz_full = group_m * tiles_n;
+    const int grp = t / gsz_full;
+    const int first_m = grp * group_m;
+    const int gsz = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int within = t - grp * gsz_full;
+    m_tile = first_m + within % gsz;
+    n_tile = within / gsz;
+}
 
 // Per-head epilogue on one staged pass of rows [r0, r0+rows) of the tile.
 // The staged tile holds the GEMM output already rounded to bf16.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int P>
 __device__ __forceinline__ void heads_epilogue(const GemmArgs& g, const uint16_t* cs,
                                                uint32_t* row_amax, int m_base, int n0,
                                                int rows, int tid) {
-    using S = TileShape<BM, BN, WM, WN>;
+    using S = TileShape<BM, BN, WM, WN, P>;
     const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
     const int heads_in_tile = BN / HW;
     const int h0 = n0 / HW;
@@ -184,9 +211,9 @@ __device__ __forceinline__ void heads_epilogue(const GemmArgs& g, const uint16_t
     }
 }
 
-template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI>
+template <typename Tin, int BM, int BN, int WM, int WN, int P, Epi EPI>
 __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
-    using S = TileShape<BM, BN, WM, WN>;
+    using S = TileShape<BM, BN, WM, WN, P>;
     using Op = MfmaOp<Tin>;
     __shared__ __attribute__((aligned(16))) char smem[S::LDS];
 
@@ -195,95 +222,120 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
     const int wave = tid >> 6;
     const int wm = wave / WN;
     const int wn = wave % WN;
-    const int n_tile = blockIdx.x;
-    const int m0 = blockIdx.y * BM;
+    const int tiles_m = (g.M + BM - 1) / BM;
+    const int tiles_n = (g.N + BN - 1) / BN;
+    int m_tile, n_tile, split;
+    tile_of(blockIdx.x, tiles_m, tiles_n, g.k_splits, g.group_m, m_tile, n_tile, split);
+    const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
 
-    const int kbytes_total = g.K * static_cast<int>(sizeof(Tin));
-    const int kbytes_split = kbytes_total / g.k_splits;
-    const int kb0 = blockIdx.z * kbytes_split;
+    const int kbytes_split = g.K * static_cast<int>(sizeof(Tin)) / g.k_splits;
     const int n_ktiles = kbytes_split / kTileKBytes;
-
     const size_t lda_b = static_cast<size_t>(g.lda) * sizeof(Tin);
     const size_t ldb_b = static_cast<size_t>(g.ldb) * sizeof(Tin);
 
-    // Per-thread source rows for the global->LDS copy (nullptr = outside the matrix).
-    const char* a_src[S::A_PER];
-    const char* b_src[S::B_PER];
-    int a_lds[S::A_PER], b_lds[S::B_PER];
-#pragma unroll
-    for (int i = 0; i < S::A_PER; ++i) {
-        const int c = tid + i * S::NT;
-        const int r = c >> 3, cc = c & 7;
-        const int m = m0 + r;
-        a_src[i] = (m < g.M) ? static_cast<const char*>(g.A) + m * lda_b + kb0 + cc * 16 : nullptr;
-        a_lds[i] = r * kLdsRow + cc * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < S::B_PER; ++i) {
-        const int c = tid + i * S::NT;
-        const int r = c >> 3, cc = c & 7;
-        const int n = n0 + r;
-        const char* base = nullptr;
-        if (n < g.N)
-            base = (n < g.b_split)
-                       ? static_cast<const char*>(g.B0) + n * ldb_b
-                       : static_cast<const char*>(g.B1) + (n - g.b_split) * ldb_b;
-        b_src[i] = base ? base + kb0 + cc * 16 : nullptr;
-        b_lds[i] = BM * kLdsRow + r * kLdsRow + cc * 16;
-    }
+    // Workgroup-uniform row bases (the host keeps every B tile inside one segment) and
+    // per-thread row/chunk coordinates. Thread t copies 16-byte chunk (t % 8) of rows
+    // t/8 + i*NT/8. Rows past the matrix edge re-read its last row: their results land
+    // in tile rows/columns that are never stored.
+    const char* a_base = static_cast<const char*>(g.A) + static_cast<size_t>(m0) * lda_b +
+                         static_cast<size_t>(split) * kbytes_split;
+    const bool seg0 = n0 < g.b_split;
+    const char* b_base = (seg0 ? static_cast<const char*>(g.B0) + static_cast<size_t>(n0) * ldb_b
+                               : static_cast<const char*>(g.B1) +
+                                     static_cast<size_t>(n0 - g.b_split) * ldb_b) +
+                         static_cast<size_t>(split) * kbytes_split;
+    const int a_last = g.M - 1 - m0;
+    const int b_last = g.N - 1 - n0;
+    const int row0 = tid >> 3;
+    const int cc16 = (tid & 7) * 16;
+    constexpr int R8 = S::NT / 8;  // rows covered by one pass of the workgroup
+    const uint32_t lda32 = static_cast<uint32_t>(lda_b), ldb32 = static_cast<uint32_t>(ldb_b);
 
-    uint4 ra[S::A_PER], rb[S::B_PER];
-    auto fetch = [&](int kt) {
-        const int off = kt * kTileKBytes;
-#pragma unroll
-        for (int i = 0; i < S::A_PER; ++i)
-            ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + off) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < S::B_PER; ++i)
-            rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + off) : make_uint4(0, 0, 0, 0);
+    i32x4 pre[P][S::CH];
+    auto fetch = [&](int kt, auto slot_c) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        const char* ap = a_base + kt * kTileKBytes;
+        const char* bp = b_base + kt * kTileKBytes;
+        static_for<S::CH>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            if constexpr (i < S::A_PER) {
+                const int r = row0 + i * R8;
+                const uint32_t off = static_cast<uint32_t>(r < a_last ? r : a_last) * lda32 + cc16;
+                pre[slot][i] = *reinterpret_cast<const i32x4*>(ap + off);
+            } else {
+                const int r = row0 + (i - S::A_PER) * R8;
+                const uint32_t off = static_cast<uint32_t>(r < b_last ? r : b_last) * ldb32 + cc16;
+                pre[slot][i] = *reinterpret_cast<const i32x4*>(bp + off);
+            }
+        });
     };
-    auto stash = [&]() {
-#pragma unroll
-        for (int i = 0; i < S::A_PER; ++i) *reinterpret_cast<uint4*>(smem + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < S::B_PER; ++i) *reinterpret_cast<uint4*>(smem + b_lds[i]) = rb[i];
+    const int lds_w = row0 * kLdsRow + cc16;
+    auto stash = [&](auto slot_c, int buf) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        char* base = smem + buf * S::STAGE_LDS + lds_w;
+        static_for<S::CH>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int off = (i < S::A_PER) ? i * R8 * kLdsRow
+                                               : (BM + (i - S::A_PER) * R8) * kLdsRow;
+            *reinterpret_cast<i32x4*>(base + off) = pre[slot][i];
+        });
     };
 
     typename Op::acc_t acc[S::FM][S::FN];
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::FN; ++j) acc[i][j] = Op::zero();
+    static_for<S::FM>([&](auto i_c) __attribute__((always_inline)) {
+        static_for<S::FN>([&](auto j_c) __attribute__((always_inline)) {
+            acc[decltype(i_c)::value][decltype(j_c)::value] = Op::zero();
+        });
+    });
 
     // LDS read offsets of this lane's MFMA operands (row l%32, 16-byte half l/32).
     const int a_rd = (wm * S::TM + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
     const int b_rd = BM * kLdsRow + (wn * S::TN + (lane & 31)) * kLdsRow + (lane >> 5) * 16;
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const char* base = smem + buf * S::STAGE_LDS;
+        static_for<4>([&](auto ks_c) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_c)::value;
+            i32x4 af[S::FM], bfr[S::FN];
+            static_for<S::FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                af[i] = *reinterpret_cast<const i32x4*>(base + a_rd + i * 32 * kLdsRow + ks * 32);
+            });
+            static_for<S::FN>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                bfr[j] = *reinterpret_cast<const i32x4*>(base + b_rd + j * 32 * kLdsRow + ks * 32);
+            });
+            static_for<S::FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                static_for<S::FN>([&](auto j_c) __attribute__((always_inline)) {
+                    constexpr int j = decltype(j_c)::value;
+                    Op::mma(acc[i][j], af[i], bfr[j]);
+                });
+            });
+        });
+    };
 
-    fetch(0);
-    stash();
+    // K-tile j travels HBM -> registers (slot j % P) -> LDS buffer j % 2 -> MFMA.
+    // (prologue loads are clamped to the last K-tile: always valid, never used past the end)
+    static_for<P>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value;
+        fetch(s < n_ktiles ? s : n_ktiles - 1, s_c);
+    });
+    stash(std::integral_constant<int, 0>{}, 0);
+    fetch(P < n_ktiles ? P : n_ktiles - 1, std::integral_constant<int, 0>{});
     __syncthreads();
-    for (int kt = 0; kt < n_ktiles; ++kt) {
-        if (kt + 1 < n_ktiles) fetch(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint4 af[S::FM], bfr[S::FN];
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(smem + a_rd + i * 32 * kLdsRow + ks * 32);
-#pragma unroll
-            for (int j = 0; j < S::FN; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(smem + b_rd + j * 32 * kLdsRow + ks * 32);
-#pragma unroll
-            for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < S::FN; ++j) Op::mma(acc[i][j], af[i], bfr[j]);
-        }
-        __syncthreads();
-        if (kt + 1 < n_ktiles) {
-            stash();
-            __syncthreads();
-        }
+    for (int kt0 = 0; kt0 < n_ktiles; kt0 += P) {
+        static_for<P>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int nslot = (s + 1) % P;
+            const int kt = kt0 + s;
+            if (kt < n_ktiles) {
+                compute(kt & 1);
+                if (kt + 1 < n_ktiles) stash(std::integral_constant<int, nslot>{}, (kt + 1) & 1);
+                if (kt + 1 + P < n_ktiles) fetch(kt + 1 + P, std::integral_constant<int, nslot>{});
+                __syncthreads();
+            }
+        });
     }
 
     // ------------------------------------------------------------- epilogues --
@@ -303,7 +355,7 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
                         if constexpr (EPI == Epi::kStoreI32) {
                             static_cast<int32_t*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = acc[i][j][r];
                         } else {
-                            static_cast<float*>(g.out)[(static_cast<size_t>(blockIdx.z) * g.M + m) * g.ldo + n] =
+                            static_cast<float*>(g.out)[(static_cast<size_t>(split) * g.M + m) * g.ldo + n] =
                                 acc[i][j][r];
                         }
                     }
@@ -353,7 +405,7 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
                             *reinterpret_cast<const uint4*>(cs + lr * S::EPI_PITCH + cc * 8);
                 }
             } else {
-                heads_epilogue<BM, BN, WM, WN>(g, cs, row_amax, m_base, n0, S::EPI_ROWS, tid);
+                heads_epilogue<BM, BN, WM, WN, P>(g, cs, row_amax, m_base, n0, S::EPI_ROWS, tid);
                 if (g.part_amax) {
                     __syncthreads();
                     if (tid < S::EPI_ROWS && m_base + tid < g.M)

@@ -1,4 +1,12 @@
 // gemm_kernels.hip -- instantiations of the gfx950 MFMA GEMM and their launcher.
+//
+// Tile shapes (rows x columns of the output tile, K-tiles of prefetch in flight):
+//   256 x {64..256}, 1 ahead  -- large batches (prefill): 128x128 (or 64x64) per wave,
+//                                enough MFMA work per LDS byte to stay MFMA-bound;
+//   128 x {64..256}, 3 ahead  -- small batches (decode): weight streaming, where the
+//                                bytes in flight per workgroup set the bandwidth;
+//   256 x 64, 3 ahead         -- the split-K down projection of small batches;
+//   128 x 128, 1 ahead        -- the GEMM-core test exports.
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -6,34 +14,44 @@ namespace mlap {
 
 namespace {
 
-template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI>
+template <typename Tin, int BM, int BN, int WM, int WN, int P, Epi EPI>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-    const dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.k_splits);
-    hipLaunchKernelGGL((gemm_nt_kernel<Tin, BM, BN, WM, WN, EPI>), grid, dim3(kWave * WM * WN), 0, s,
-                       g);
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.k_splits;
+    hipLaunchKernelGGL((gemm_nt_kernel<Tin, BM, BN, WM, WN, P, EPI>), dim3(tiles),
+                       dim3(kWave * WM * WN), 0, s, g);
     return hipGetLastError();
 }
 
 template <typename Tin>
-hipError_t dispatch(const GemmArgs& g, int BM, int BN, Epi epi, hipStream_t s) {
-    if (BM != 128) return hipErrorInvalidValue;
+hipError_t dispatch(const GemmArgs& g, const GemmTile& t, Epi epi, hipStream_t s) {
+    const int BM = t.bm, BN = t.bn, P = t.prefetch;
     switch (epi) {
         case Epi::kStoreBf16:
-            if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, Epi::kStoreBf16>(g, s);
+            if (BM == 128 && BN == 128 && P == 1) return launch_one<Tin, 128, 128, 2, 2, 1, Epi::kStoreBf16>(g, s);
+            if (BM == 256 && BN == 192 && P == 1) return launch_one<Tin, 256, 192, 2, 2, 1, Epi::kStoreBf16>(g, s);
+            if (BM == 256 && BN == 64 && P == 1) return launch_one<Tin, 256, 64, 4, 1, 1, Epi::kStoreBf16>(g, s);
             break;
         case Epi::kStoreF32:
             if constexpr (sizeof(Tin) == 2)
-                if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, Epi::kStoreF32>(g, s);
+                if (BM == 256 && BN == 64 && P == 3) return launch_one<Tin, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
             break;
         case Epi::kStoreI32:
             if constexpr (sizeof(Tin) == 1)
-                if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, Epi::kStoreI32>(g, s);
+                if (BM == 128 && BN == 128 && P == 1) return launch_one<Tin, 128, 128, 2, 2, 1, Epi::kStoreI32>(g, s);
             break;
         case Epi::kHeads:
-            if (BN == 64) return launch_one<Tin, 128, 64, 2, 2, Epi::kHeads>(g, s);
-            if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, Epi::kHeads>(g, s);
-            if (BN == 192) return launch_one<Tin, 128, 192, 2, 2, Epi::kHeads>(g, s);
-            if (BN == 256) return launch_one<Tin, 128, 256, 2, 2, Epi::kHeads>(g, s);
+            if (BM == 128 && P == 3) {
+                if (BN == 64) return launch_one<Tin, 128, 64, 2, 2, 3, Epi::kHeads>(g, s);
+                if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, 3, Epi::kHeads>(g, s);
+                if (BN == 192) return launch_one<Tin, 128, 192, 2, 2, 3, Epi::kHeads>(g, s);
+                if (BN == 256) return launch_one<Tin, 128, 256, 2, 2, 3, Epi::kHeads>(g, s);
+            }
+            if (BM == 256 && P == 1) {
+                if (BN == 64) return launch_one<Tin, 256, 64, 4, 1, 1, Epi::kHeads>(g, s);
+                if (BN == 128) return launch_one<Tin, 256, 128, 2, 2, 1, Epi::kHeads>(g, s);
+                if (BN == 192) return launch_one<Tin, 256, 192, 2, 2, 1, Epi::kHeads>(g, s);
+                if (BN == 256) return launch_one<Tin, 256, 256, 2, 2, 1, Epi::kHeads>(g, s);
+            }
             break;
     }
     return hipErrorInvalidValue;
@@ -41,10 +59,9 @@ hipError_t dispatch(const GemmArgs& g, int BM, int BN, Epi epi, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, InType t, int BM, int BN, Epi epi, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& g, InType type, const GemmTile& t, Epi epi, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    return t == InType::kBf16 ? dispatch<uint16_t>(g, BM, BN, epi, s)
-                              : dispatch<int8_t>(g, BM, BN, epi, s);
+    return type == InType::kBf16 ? dispatch<uint16_t>(g, t, epi, s) : dispatch<int8_t>(g, t, epi, s);
 }
 
 }  // namespace mlap

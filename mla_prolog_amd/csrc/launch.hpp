@@ -10,17 +10,24 @@ namespace mlap {
 
 enum class InType : int { kBf16 = 0, kInt8 = 1 };
 
-// Launch C = A . B^T with the given tile shape and epilogue. Returns hipErrorInvalidValue for
-// a (type, BM, BN, epilogue) combination that has no instantiation.
-hipError_t launch_gemm(const GemmArgs& g, InType t, int BM, int BN, Epi epi, hipStream_t s);
+// Output tile rows x columns and K-tiles of register prefetch.
+struct GemmTile {
+    int bm, bn, prefetch;
+};
+
+// Launch C = A . B^T with the given tile shape and epilogue on a 1-D grid of
+// tiles x k_splits workgroups. The B operand's segment split (b_split) must be a
+// multiple of the tile width or >= N. Returns hipErrorInvalidValue for a
+// (type, tile, epilogue) combination that has no instantiation.
+hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi epi, hipStream_t s);
 
 // Per-token row stage after the down projection: RMSNorm*gamma -> bf16 for the q and kv
 // segments, rotate-half RoPE of the k_pe segment, per-token INT8 quant of kv_norm and (W8A8)
 // of q_norm. One workgroup per token.
 struct NormArgs {
     int T, Lq, Lkv, R, N1, k_splits;
-    const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output (k_splits == 1)
-    const float* a_f32;      // [k_splits, T, N1] fp32 split-K partial sums (k_splits > 1)
+    const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output, or
+    const float* a_f32;      // [k_splits, T, N1] fp32 split-K partial sums (used when set)
     const uint16_t* gamma_q;
     const uint16_t* gamma_kv;
     float eps;

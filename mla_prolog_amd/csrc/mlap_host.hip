@@ -35,9 +35,9 @@ enum KernelId : int32_t {
 const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope",
                                            "gemm_up_q", "gemm_up_kv", "quant_q"};
 
-constexpr int kBM = 128;
-constexpr int kBNDown = 128;
 constexpr size_t kAlign = 256;
+constexpr int kSmallBatch = 512;  // token counts up to this use the weight-streaming tiles
+constexpr int kGroupM = 4;        // M-tiles per group in the XCD-aware tile order
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -48,6 +48,17 @@ int heads_tile(int head_w) {
         if (bn % head_w == 0) return bn;
     return 0;
 }
+
+// Kernel shapes for one run of T tokens: the counterpart of a tile table bucketed by token
+// count. Small batches stream the weights (the projection is bound by HBM bandwidth):
+// 128-row tiles with 3 K-tiles in flight, and a split-K down projection whose fp32 partial
+// sums the row kernel adds up. Large batches are bound by MFMA throughput: 256-row tiles.
+struct Plan {
+    GemmTile down;
+    Epi down_epi;
+    int down_splits;
+    GemmTile up_q, up_kv;
+};
 
 struct Timer {
     int32_t kernel = -1;
@@ -73,8 +84,35 @@ struct mlap_prolog {
     int nt_q;     // up-projection N tiles of q (partial amax entries per token)
     Timer timer;
 
+    Plan plan(int T) const {
+        Plan p{};
+        const bool small = T <= kSmallBatch;
+        const int kb = w8a8 ? 128 : 64;  // elements per 128-byte K-tile
+        const int nk = cfg.hidden / kb;
+        if (!w8a8 && small) {
+            p.down = {256, 64, 3};
+            p.down_epi = Epi::kStoreF32;
+            const int tiles = ((T + 255) / 256) * ((N1 + 63) / 64);
+            int s = 1;
+            for (int c = 1; c <= 16; ++c) {
+                if (nk % c) continue;
+                s = c;
+                if (tiles * c >= 256) break;
+            }
+            p.down_splits = s;
+        } else {
+            p.down = (cfg.q_lora % 192 == 0 && !small) ? GemmTile{256, 192, 1} : GemmTile{256, 64, 1};
+            p.down_epi = Epi::kStoreBf16;
+            p.down_splits = 1;
+        }
+        p.up_q = {small ? 128 : 256, bn_q, small ? 3 : 1};
+        p.up_kv = {small ? 128 : 256, bn_kv, small ? 3 : 1};
+        return p;
+    }
+
     WsLayout layout(int T) const {
         WsLayout L;
+        const Plan p = plan(T);
         size_t off = 0;
         auto take = [&](size_t bytes) {
             size_t o = off;
@@ -82,7 +120,7 @@ struct mlap_prolog {
             return o;
         };
         const size_t t = static_cast<size_t>(T);
-        L.a1 = take(t * N1 * 2);
+        L.a1 = take(p.down_epi == Epi::kStoreF32 ? t * N1 * 4 * p.down_splits : t * N1 * 2);
         if (cfg.q_lora > 0) L.qn = take(t * cfg.q_lora * 2);
         if (cfg.v_dim > 0) L.kvn = take(t * cfg.kv_lora * 2);
         if (cfg.q_lora > 0) L.qpart = take(t * nt_q * 4);
@@ -281,7 +319,9 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     g.B0 = has_q ? in->w_qa : in->w_kva;
     g.B1 = in->w_kva;
     g.b_split = Lq;
-    g.k_splits = 1;
+    const Plan plan = h->plan(T);
+    g.k_splits = plan.down_splits;
+    g.group_m = kGroupM;
     g.out = a1;
     g.ldo = h->N1;
     if (w8) {
@@ -293,10 +333,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         g.a_scale = xs;
         g.b_scale0 = has_q ? in->ws_qa : in->ws_kva;
         g.b_scale1 = in->ws_kva;
-        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kInt8, kBM, kBNDown, Epi::kStoreBf16, s));
+        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
     } else {
         g.A = in->x;
-        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kBf16, kBM, kBNDown, Epi::kStoreBf16, s));
+        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
     }
 
     // 2. row stage
@@ -306,8 +346,11 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     na.Lkv = Lkv;
     na.R = R;
     na.N1 = h->N1;
-    na.k_splits = 1;
-    na.a_bf16 = a1;
+    na.k_splits = plan.down_splits;
+    if (plan.down_epi == Epi::kStoreF32)
+        na.a_f32 = reinterpret_cast<const float*>(a1);
+    else
+        na.a_bf16 = a1;
     na.gamma_q = static_cast<const uint16_t*>(in->gamma_q);
     na.gamma_kv = static_cast<const uint16_t*>(in->gamma_kv);
     na.eps = c.eps;
@@ -344,6 +387,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.B0 = u.B1 = in->w_qb;
         u.b_split = u.N;
         u.k_splits = 1;
+        u.group_m = kGroupM;
         u.head_w = h->QH;
         u.d0 = c.nope_dim;
         u.d1 = R;
@@ -361,10 +405,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
             u.A = na.qn_i8;
             u.a_scale = na.qn_scale;
             u.b_scale0 = u.b_scale1 = in->ws_qb;
-            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kInt8, kBM, h->bn_q, Epi::kHeads, s));
+            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kInt8, plan.up_q, Epi::kHeads, s));
         } else {
             u.A = qn;
-            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kBf16, kBM, h->bn_q, Epi::kHeads, s));
+            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kBf16, plan.up_q, Epi::kHeads, s));
         }
     }
 
@@ -379,6 +423,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.B0 = u.B1 = in->w_kvb;
         u.b_split = u.N;
         u.k_splits = 1;
+        u.group_m = kGroupM;
         u.head_w = h->KH;
         u.d0 = c.nope_dim;
         u.d1 = c.v_dim;
@@ -390,10 +435,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
             u.A = na.kv_i8_b;
             u.a_scale = na.kv_scale_b;
             u.b_scale0 = u.b_scale1 = in->ws_kvb;
-            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kInt8, kBM, h->bn_kv, Epi::kHeads, s));
+            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kInt8, plan.up_kv, Epi::kHeads, s));
         } else {
             u.A = kvn;
-            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kBf16, kBM, h->bn_kv, Epi::kHeads, s));
+            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kBf16, plan.up_kv, Epi::kHeads, s));
         }
     }
 
@@ -432,9 +477,10 @@ MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, in
     g.b_split = N;
     g.ldb = K;
     g.k_splits = 1;
+    g.group_m = kGroupM;
     g.out = C;
     g.ldo = N;
-    return launch_gemm(g, InType::kInt8, kBM, 128, Epi::kStoreI32, as_stream(stream)) == hipSuccess
+    return launch_gemm(g, InType::kInt8, GemmTile{128, 128, 1}, Epi::kStoreI32, as_stream(stream)) == hipSuccess
                ? MLAP_OK
                : MLAP_ERR_HIP;
 }
@@ -455,9 +501,10 @@ MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C,
     g.b_split = N;
     g.ldb = K;
     g.k_splits = 1;
+    g.group_m = kGroupM;
     g.out = C;
     g.ldo = N;
-    return launch_gemm(g, InType::kBf16, kBM, 128, Epi::kStoreBf16, as_stream(stream)) == hipSuccess
+    return launch_gemm(g, InType::kBf16, GemmTile{128, 128, 1}, Epi::kStoreBf16, as_stream(stream)) == hipSuccess
                ? MLAP_OK
                : MLAP_ERR_HIP;
 }

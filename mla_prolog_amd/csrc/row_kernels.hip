@@ -47,7 +47,7 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 // 8 consecutive down-projection outputs of token t starting at column col, as the fp32
 // values of their bf16 rounding (the GEMM's bf16 output cast point).
 __device__ __forceinline__ void load_a8(const NormArgs& a, int t, int col, float* f) {
-    if (a.k_splits == 1) {
+    if (!a.a_f32) {
         unpack8(*reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col), f);
         return;
     }

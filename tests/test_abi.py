@@ -99,9 +99,14 @@ def test_workspace_size_grows_with_T_and_is_aligned():
     assert sizes[-1] >= T * 2112 * 2 + T * 1536 * 2 + T * 128 * 4
     with pytest.raises(mlap.MlapError):
         p.workspace_size(8193)
+    # W8A8 adds the int8 copies of x and q_norm (plus their per-token scales)
     w8 = mlap.Prolog.from_config(synth.get_config("v3_w8a8"))
-    assert w8.workspace_size(16) > mlap.Prolog.from_config(
-        synth.get_config("v3_decode")).workspace_size(16)
+    bf = mlap.Prolog.from_config(synth.get_config("v3_prefill"), t_max=16384)
+    T = 8192
+    assert w8.workspace_size(T) - bf.workspace_size(T) >= T * (7168 + 1536)
+    # small batches split the down projection over K: fp32 partial sums per split
+    dec = mlap.Prolog.from_config(synth.get_config("v3_decode"))
+    assert dec.workspace_size(256) >= 2 * 256 * 2112 * 4
 
 
 def _run_raw(h, inp, out, ws, ws_bytes):
