@@ -166,7 +166,12 @@ def main():
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="weight/input sets the headline workload cycles through")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (the reference "
+                         "kernel whose HBM counters scale the profiled traffic)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -176,7 +181,15 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    cfg, ms, k_ms, nk = bench_workload(a.workload, a.steps, a.warmup, rotate=1)
+    if a.copy_calibrate:
+        n = a.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cfg, ms, k_ms, nk = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate)
     T = cfg.T
     pf, pb = path_work(cfg, T)
     line = {

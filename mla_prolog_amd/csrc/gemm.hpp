@@ -324,7 +324,21 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
     stash(std::integral_constant<int, 0>{}, 0);
     fetch(P < n_ktiles ? P : n_ktiles - 1, std::integral_constant<int, 0>{});
     __syncthreads();
-    for (int kt0 = 0; kt0 < n_ktiles; kt0 += P) {
+    // Steady state without guards (every sub-step stashes and refills), so the compiler's
+    // wait counts stay exact and P K-tiles really are in flight; then a guarded tail.
+    int kt0 = 0;
+    for (; kt0 + 2 * P < n_ktiles; kt0 += P) {
+        static_for<P>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int nslot = (s + 1) % P;
+            const int kt = kt0 + s;
+            compute(kt & 1);
+            stash(std::integral_constant<int, nslot>{}, (kt + 1) & 1);
+            fetch(kt + 1 + P, std::integral_constant<int, nslot>{});
+            __syncthreads();
+        });
+    }
+    for (; kt0 < n_ktiles; kt0 += P) {
         static_for<P>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int nslot = (s + 1) % P;
