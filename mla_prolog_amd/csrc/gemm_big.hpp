@@ -1,0 +1,382 @@
+// gemm_big.hpp -- MFMA-bound GEMM for large token batches on gfx950: C = A . B^T.
+//
+// A [M, K] holds token activations, B [N, K] the weights (the AT-10 card's b_trans
+// layout), both K-contiguous. One workgroup of four 64-wide waves (2 x 2) computes a
+// BM x BN output tile; each wave owns a (BM/2) x (BN/2) block held in accumulator
+// registers (128 x 128 fp32 = 256 registers per lane at BM = BN = 256), so the
+// workgroup runs alone on its CU with one wave per SIMD.
+//
+// Operand staging. A K-stage is 64 bytes of every tile row (32 bf16 or 64 int8):
+// (BM + BN) rows x 64 B = 32 KB at 256 x 256. S stages form a ring in LDS. Every stage
+// is copied HBM -> LDS directly by the buffer unit (global_load_lds_dwordx4: each
+// lane moves 16 bytes and a wave writes 1 KB of consecutive LDS), so no register holds
+// operands in flight and S - 1 stages are in the air while one is multiplied. A lane
+// fetches the global chunk that lands on its fixed LDS slot: 16-byte chunk c of tile
+// row r lives at chunk c ^ swz(r), which spreads the 128-bit operand reads of the 16
+// lanes the LDS serves per cycle over distinct banks.
+//
+// Per stage a wave runs two k-steps of v_mfma_f32_32x32x16_bf16 (or
+// v_mfma_i32_32x32x32_i8). The weight fragment is the MFMA's first operand and the
+// activation fragment its second, so the accumulator is the transposed tile: lane l,
+// register 4g + q holds token (l % 32) and output column 8g + 4(l / 32) + q. Every lane
+// therefore owns runs of four consecutive output columns of its tokens, and the
+// epilogue works in registers: one 8-byte store per run, rotate-half pairs (i, i + 32)
+// in the same lane one fragment apart, and a token's row amax as a lane-local max plus
+// one exchange with lane l ^ 32.
+//
+// Synchronisation per stage: wait until this wave's copies of the stage have landed
+// (vmcnt), one workgroup barrier (all waves' copies visible, and every wave is done
+// reading the slot the next copy overwrites), issue the copy S - 1 stages ahead,
+// multiply.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace mlap {
+namespace big {
+
+// Chunk swizzle of a tile row of KB bytes (KB / 16 chunks of 16 bytes), chosen by
+// measurement on gfx950 (rocprofv3 SQ_LDS_BANK_CONFLICT over this kernel's fragment read
+// pattern): with 64-byte rows (r >> 2) & 3 reads conflict-free where the unswizzled layout
+// is 4-way; with 128-byte rows (r >> 1) & 7 is conflict-free where unswizzled is 8-way.
+// Both are invariant under r -> r + 32, so every 32-row fragment shares the lane's swizzle.
+template <int KB>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (KB == 64)
+        return (r >> 2) & 3;
+    else
+        return (r >> 1) & 7;
+}
+
+template <int BM, int BN, int WM, int WN, int KB, int S>
+struct Shape {
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;  // per-wave block
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int KS = KB / 32;                // MFMA k-steps per stage (32 bytes each)
+    static constexpr int LPR = KB / 16;               // copy lanes per tile row
+    static constexpr int ROWS = BM + BN;
+    static constexpr int RROWS = NT / LPR;            // rows one workgroup-wide copy round fills
+    static constexpr int ROUNDS = ROWS / RROWS;
+    static constexpr int STAGE = ROWS * KB;
+    static constexpr int MAIN = S * STAGE;
+    static constexpr int LDS = MAIN > BM * BN * 2 ? MAIN : BM * BN * 2;
+    static_assert(KB == 64 || KB == 128, "stage row bytes");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave block must be whole 32x32 fragments");
+    static_assert(BM % RROWS == 0 && BN % RROWS == 0, "tile rows must fill whole copy rounds");
+    static_assert(S >= 2 && LDS <= 160 * 1024, "LDS budget");
+    static_assert((S - 2) * ROUNDS < 64, "vmcnt range");
+};
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS traffic without waiting for outstanding global
+// loads (a __syncthreads() fence would drain the copy ring).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4); `lds` must be
+// wave-uniform: lane l writes lds + 16 l. A device function rather than a lambda body:
+// lambdas are host-device in HIP, and a device builtin inside one suppresses the
+// kernel's host-side launch stub.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(lds), 16, 0, 0);
+}
+
+// An empty statement that needs `v` in VGPRs (an allocation hint, no instruction).
+__device__ __forceinline__ void pin_vgpr(i32x4& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32, RNE
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+}  // namespace big
+
+template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
+    using SH = big::Shape<BM, BN, WM, WN, KB, S>;
+    using Op = MfmaOp<Tin>;
+    constexpr int TM = SH::TM, TN = SH::TN, FM = SH::FM, FN = SH::FN, KS = SH::KS;
+    constexpr int ROUNDS = SH::ROUNDS, LPR = SH::LPR;
+    __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int tiles_m = (g.M + BM - 1) / BM;
+    const int tiles_n = (g.N + BN - 1) / BN;
+    int m_tile, n_tile, split;
+    tile_of(blockIdx.x, tiles_m, tiles_n, 1, g.group_m, m_tile, n_tile, split);
+    const int m0 = m_tile * BM;
+    const int n0 = n_tile * BN;
+    const int nk = g.K * static_cast<int>(sizeof(Tin)) / KB;
+
+    // Copy sources: round i moves tile row i*RROWS + tid/LPR, physical chunk tid%LPR.
+    // Rows past the matrix edge re-read its last row; their results are never stored.
+    const char* src[ROUNDS];
+    {
+        const size_t lda_b = static_cast<size_t>(g.lda) * sizeof(Tin);
+        const size_t ldb_b = static_cast<size_t>(g.ldb) * sizeof(Tin);
+        static_for<ROUNDS>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            const int r = i * SH::RROWS + tid / LPR;
+            const int c = (tid % LPR) ^ big::swz<KB>(r);
+            if constexpr (i * SH::RROWS < BM) {
+                const int m = min(m0 + r, g.M - 1);
+                src[i] = static_cast<const char*>(g.A) + static_cast<size_t>(m) * lda_b + c * 16;
+            } else {
+                const int n = min(n0 + r - BM, g.N - 1);
+                const char* row = n < g.b_split
+                                      ? static_cast<const char*>(g.B0) + static_cast<size_t>(n) * ldb_b
+                                      : static_cast<const char*>(g.B1) +
+                                            static_cast<size_t>(n - g.b_split) * ldb_b;
+                src[i] = row + c * 16;
+            }
+        });
+    }
+    // Copy rounds [R0, R1) of stage kt into `slot`.
+    auto issue_part = [&](int kt, int slot, auto r0_c, auto r1_c) __attribute__((always_inline)) {
+        constexpr int R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
+        char* dst = smem + slot * SH::STAGE + wave * 1024;
+        const int koff = kt * KB;
+        static_for<R1 - R0>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = R0 + decltype(i_c)::value;
+            big::copy16_to_lds(src[i] + koff, dst + i * SH::RROWS * KB);
+        });
+    };
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+        issue_part(kt, slot, std::integral_constant<int, 0>{}, std::integral_constant<int, ROUNDS>{});
+    };
+
+    // LDS read offsets of this lane's operands: row (l % 32) of each 32-row fragment,
+    // logical 16-byte chunk 2*ks + l/32.
+    const int lr = lane & 31, lh = lane >> 5;
+    int a_rd[KS], b_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int chunk = ((2 * ks + lh) ^ big::swz<KB>(lr)) * 16;
+        a_rd[ks] = (wm * TM + lr) * KB + chunk;
+        b_rd[ks] = (BM + wn * TN + lr) * KB + chunk;
+    }
+
+    typename Op::acc_t acc[FN][FM];
+    static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            acc[decltype(j_c)::value][decltype(i_c)::value] = Op::zero();
+        });
+    });
+
+    // One k-step's operands: FN weight and FM activation fragments.
+    struct Frags {
+        i32x4 w[FN], x[FM];
+    };
+    auto read = [&](const char* base, auto ks_c, Frags& f) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ks_c)::value;
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            f.w[j] = *reinterpret_cast<const i32x4*>(base + b_rd[ks] + j * 32 * KB);
+        });
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            f.x[i] = *reinterpret_cast<const i32x4*>(base + a_rd[ks] + i * 32 * KB);
+        });
+    };
+    auto multiply = [&](Frags& f) __attribute__((always_inline)) {
+        // Pin the operand fragments to VGPRs: left to itself the register allocator may
+        // park them in AGPRs, which the accumulators fill completely.
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            big::pin_vgpr(f.w[decltype(j_c)::value]);
+        });
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            big::pin_vgpr(f.x[decltype(i_c)::value]);
+        });
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                Op::mma(acc[j][i], f.w[j], f.x[i]);
+            });
+        });
+    };
+
+    // Stage j goes to slot j % S and is copied S - 1 stages ahead. The barrier at the top
+    // of iteration kt certifies that stage kt has landed for every wave and that every wave
+    // is done with slot (kt - 1) % S, which the copy of stage kt + S - 1 then reuses.
+    // Inside a stage, the fragments of k-step ks + 1 are read while k-step ks multiplies.
+    static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value;
+        if (s < nk) issue(s, s);
+    });
+    int slot = 0;  // kt % S
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + S - 2 < nk)
+            big::wait_vmcnt<(S - 2) * ROUNDS>();
+        else
+            big::wait_vmcnt<0>();
+        big::lds_barrier();
+        // The next copy is spread over the k-steps so that a busy memory pipeline never
+        // holds up all MFMA issue at once.
+        const bool copy = kt + S - 1 < nk;
+        const int cslot = slot == 0 ? S - 1 : slot - 1;
+        const char* base = smem + slot * SH::STAGE;
+        Frags f[2];
+        read(base, std::integral_constant<int, 0>{}, f[0]);
+        static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_c)::value;
+            constexpr int r0 = ROUNDS * ks / KS, r1 = ROUNDS * (ks + 1) / KS;
+            if (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
+            if constexpr (ks + 1 < KS) read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
+            multiply(f[ks & 1]);
+        });
+        slot = slot + 1 == S ? 0 : slot + 1;
+    }
+
+    // ------------------------------------------------------------- epilogues --
+    // Lane view of the transposed accumulator: token m = mb + 32 i + lr, columns
+    // nb + 32 j + 8 g + 4 lh + q for register 4 g + q.
+    const int mb = m0 + wm * TM + lr;
+    const int nb = n0 + wn * TN + 4 * lh;
+
+    // Fragment (j, i) as eight packed bf16 pairs (the GEMM's bf16 output cast), with the
+    // W8A8 dequantisation f32(acc) * (a_scale[m] * b_scale[n]) applied first.
+    auto frag_bf16 = [&](int j, int i, uint32_t* w) __attribute__((always_inline)) {
+        const int m = mb + 32 * i;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            float v[4];
+            if constexpr (sizeof(Tin) == 1) {
+                const int n = nb + 32 * j + 8 * gq;
+                const float as = m < g.M ? g.a_scale[min(m, g.M - 1)] : 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nn = min(n + q, g.N - 1);
+                    const float bs = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
+                    const float sc = as * bs;
+                    v[q] = static_cast<float>(acc[j][i][4 * gq + q]) * sc;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = acc[j][i][4 * gq + q];
+            }
+            w[2 * gq] = big::pack_bf16x2(v[0], v[1]);
+            w[2 * gq + 1] = big::pack_bf16x2(v[2], v[3]);
+        }
+    };
+
+    // The bf16 tile is transposed through LDS (the stage buffers are free now) so that
+    // stores leave as whole 16-byte chunks, a row's chunks on consecutive lanes: row r's
+    // 16-byte chunk c sits at chunk c ^ (r % CPR) of its BN*2-byte LDS row.
+    constexpr int CPR = BN / 8;            // 16-byte chunks per tile row
+    constexpr int RPP = SH::NT / CPR;      // rows per read-back pass
+    static_assert(CPR <= 64 && SH::NT % CPR == 0 && BM % RPP == 0, "read-back geometry");
+    static_assert(BM * BN * 2 <= SH::LDS, "LDS holds the bf16 tile");
+    big::lds_barrier();  // every wave is done reading the last stage
+    static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            uint32_t w[8];
+            frag_bf16(j, i, w);
+            const int row = wm * TM + 32 * i + lr;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int chunk = (wn * TN + 32 * j + 8 * gq) >> 3;
+                *reinterpret_cast<uint2*>(smem + row * (BN * 2) + ((chunk ^ (row % CPR)) << 4) + 8 * lh) =
+                    make_uint2(w[2 * gq], w[2 * gq + 1]);
+            }
+        });
+    });
+    big::lds_barrier();
+
+    const int c = tid % CPR;          // this thread's chunk of each row
+    const int n = n0 + 8 * c;         // its first output column
+    auto tile_chunk = [&](int row, int ch) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(smem + row * (BN * 2) + ((ch ^ (row % CPR)) << 4));
+    };
+    if constexpr (EPI == Epi::kStoreBf16) {
+        uint16_t* out = static_cast<uint16_t*>(g.out);
+        for (int row = tid / CPR; row < BM; row += RPP) {
+            const int m = m0 + row;
+            if (m < g.M && n < g.N)  // N is a multiple of 8
+                *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) = tile_chunk(row, c);
+        }
+    } else if constexpr (EPI == Epi::kHeads) {
+        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the 64-wide
+        // rotate-half slice. Head width and d0 are multiples of 64 and tiles start on
+        // multiples of 64, so a chunk lies in one segment and the rotate-half partner of
+        // chunk c (32 columns away) is chunk c ^ 4 of the same tile row.
+        const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
+        uint16_t* out0 = static_cast<uint16_t*>(g.out0);
+        uint16_t* out1 = static_cast<uint16_t*>(g.out1);
+        const bool nok = n < g.N;
+        const int h = nok ? n / HW : 0;
+        const int d = n - h * HW;
+        const bool seg0 = d < d0;
+        const int dr = d - d0;  // column within seg1
+        for (int row = tid / CPR; row < BM; row += RPP) {
+            const int m = m0 + row;
+            const bool ok = nok && m < g.M;
+            const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
+            const uint4 v = tile_chunk(row, c);
+            uint4 o = v;
+            if (!seg0 && g.rope) {
+                // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
+                // cos/sin at this chunk's own columns; the partner is the other half.
+                const uint4 pv = tile_chunk(row, c ^ 4);
+                const int p = clamp_pos(g.positions[min(m, g.M - 1)], g.max_pos);
+                const float* cr = g.cos + static_cast<size_t>(p) * d1 + dr;
+                const float* sr = g.sin + static_cast<size_t>(p) * d1 + dr;
+                float own[8], oth[8], res[8];
+                unpack8(v, own);
+                unpack8(pv, oth);
+                const float4 c0 = *reinterpret_cast<const float4*>(cr);
+                const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
+                const float4 s0 = *reinterpret_cast<const float4*>(sr);
+                const float4 s1 = *reinterpret_cast<const float4*>(sr + 4);
+                const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                const bool low = dr < (d1 >> 1);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float t1 = own[e] * cs[e];
+                    const float t2 = (low ? -oth[e] : oth[e]) * sn[e];
+                    res[e] = t1 + t2;
+                }
+                o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
+                               big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
+            }
+            if (ok) {
+                if (seg0) {
+                    if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
+                } else if (out1) {
+                    *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
+                }
+            }
+            if (g.part_amax) {
+                // the token's amax over this tile's columns: max over the CPR lanes of the row
+                float amax = ok ? absmax8(o) : 0.f;
+#pragma unroll
+                for (int o2 = CPR / 2; o2 > 0; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2, kWave));
+                if (c == 0 && m < g.M) g.part_amax[static_cast<size_t>(m) * g.n_tiles + n_tile] = amax;
+            }
+        }
+    }
+}
+
+}  // namespace mlap

@@ -7,7 +7,10 @@
 //                                bytes in flight per workgroup set the bandwidth;
 //   256 x 64, 3 ahead         -- the split-K down projection of small batches;
 //   128 x 128, 1 ahead        -- the GEMM-core test exports.
+// and the large-batch kernel of gemm_big.hpp: 256 x 256 tiles, eight waves, operands
+// copied HBM -> LDS directly in 128-byte row stages, two stages in LDS.
 #include "gemm.hpp"
+#include "gemm_big.hpp"
 #include "launch.hpp"
 
 namespace mlap {
@@ -57,7 +60,37 @@ hipError_t dispatch(const GemmArgs& g, const GemmTile& t, Epi epi, hipStream_t s
     return hipErrorInvalidValue;
 }
 
+template <typename Tin, Epi EPI>
+hipError_t launch_big_one(const GemmArgs& g, hipStream_t s) {
+    constexpr int BM = kBigTile, BN = kBigTile, WM = 4, WN = 2, KB = 128, S = 2;
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, KB, S, EPI>), dim3(tiles),
+                       dim3(64 * WM * WN), 0, s, g);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi) {
+    const int kbytes = g.K * (t == InType::kInt8 ? 1 : 2);
+    if (g.K <= 0 || kbytes % 128) return false;  // whole 128-byte stages
+    if (epi == Epi::kStoreBf16) return g.N % 8 == 0 && g.ldo % 8 == 0;
+    if (epi == Epi::kHeads) {
+        if (g.head_w % 64 || g.d0 % 64) return false;
+        return g.rope ? g.d1 == 64 : g.d1 % 8 == 0;
+    }
+    return false;
+}
+
+hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (!gemm_big_fits(g, t, epi)) return hipErrorInvalidValue;
+    if (t == InType::kBf16)
+        return epi == Epi::kStoreBf16 ? launch_big_one<uint16_t, Epi::kStoreBf16>(g, s)
+                                      : launch_big_one<uint16_t, Epi::kHeads>(g, s);
+    return epi == Epi::kStoreBf16 ? launch_big_one<int8_t, Epi::kStoreBf16>(g, s)
+                                  : launch_big_one<int8_t, Epi::kHeads>(g, s);
+}
 
 hipError_t launch_gemm(const GemmArgs& g, InType type, const GemmTile& t, Epi epi, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;

@@ -21,6 +21,15 @@ struct GemmTile {
 // (type, tile, epilogue) combination that has no instantiation.
 hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi epi, hipStream_t s);
 
+// Large-batch GEMM (gemm_big.hpp): kBigTile x kBigTile output tiles. Epilogues kStoreBf16
+// and kHeads; with kHeads, g.n_tiles must be ceil(N / kBigTile) (one partial amax per
+// token and tile). gemm_big_fits says whether the shapes suit it (K a whole number of
+// 128-byte stages; N a multiple of 8; for heads, head width and d0 multiples of 64 and
+// a 64-wide rope slice).
+constexpr int kBigTile = 256;
+bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi);
+hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s);
+
 // Per-token row stage after the down projection: RMSNorm*gamma -> bf16 for the q and kv
 // segments, rotate-half RoPE of the k_pe segment, per-token INT8 quant of kv_norm and (W8A8)
 // of q_norm. One workgroup per token.

@@ -58,6 +58,8 @@ struct Plan {
     Epi down_epi;
     int down_splits;
     GemmTile up_q, up_kv;
+    bool big_down = false, big_q = false, big_kv = false;  // large-batch kernel (gemm_big.hpp)
+    int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
 };
 
 struct Timer {
@@ -81,7 +83,6 @@ struct mlap_prolog {
     int N1;       // down-projection width
     int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
     int bn_q, bn_kv;
-    int nt_q;     // up-projection N tiles of q (partial amax entries per token)
     Timer timer;
 
     Plan plan(int T) const {
@@ -107,6 +108,41 @@ struct mlap_prolog {
         }
         p.up_q = {small ? 128 : 256, bn_q, small ? 3 : 1};
         p.up_kv = {small ? 128 : 256, bn_kv, small ? 3 : 1};
+        const InType it = w8a8 ? InType::kInt8 : InType::kBf16;
+        if (!small) {
+            // MFMA-bound: the large-batch kernel wherever the shapes suit it
+            GemmArgs d{};
+            d.K = cfg.hidden;
+            d.N = N1;
+            d.ldo = N1;
+            p.big_down = gemm_big_fits(d, it, Epi::kStoreBf16);
+            if (p.big_down) {
+                p.down_epi = Epi::kStoreBf16;
+                p.down_splits = 1;
+            }
+            if (cfg.q_lora > 0) {
+                GemmArgs u{};
+                u.K = cfg.q_lora;
+                u.head_w = QH;
+                u.d0 = cfg.nope_dim;
+                u.d1 = cfg.rope_dim;
+                u.rope = 1;
+                p.big_q = gemm_big_fits(u, it, Epi::kHeads);
+            }
+            if (cfg.v_dim > 0) {
+                GemmArgs u{};
+                u.K = cfg.kv_lora;
+                u.head_w = KH;
+                u.d0 = cfg.nope_dim;
+                u.d1 = cfg.v_dim;
+                u.rope = 0;
+                p.big_kv = gemm_big_fits(u, it, Epi::kHeads);
+            }
+        }
+        if (cfg.q_lora > 0) {
+            const int nq = cfg.n_heads * QH;
+            p.nt_q = p.big_q ? (nq + kBigTile - 1) / kBigTile : (nq + bn_q - 1) / bn_q;
+        }
         return p;
     }
 
@@ -123,7 +159,7 @@ struct mlap_prolog {
         L.a1 = take(p.down_epi == Epi::kStoreF32 ? t * N1 * 4 * p.down_splits : t * N1 * 2);
         if (cfg.q_lora > 0) L.qn = take(t * cfg.q_lora * 2);
         if (cfg.v_dim > 0) L.kvn = take(t * cfg.kv_lora * 2);
-        if (cfg.q_lora > 0) L.qpart = take(t * nt_q * 4);
+        if (cfg.q_lora > 0) L.qpart = take(t * p.nt_q * 4);
         if (w8a8) {
             L.xq = take(t * cfg.hidden);
             L.xs = take(t * 4);
@@ -208,7 +244,6 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
     h->KH = cfg->nope_dim + cfg->v_dim;
     h->bn_q = cfg->q_lora > 0 ? heads_tile(h->QH) : 0;
     h->bn_kv = cfg->v_dim > 0 ? heads_tile(h->KH) : 0;
-    h->nt_q = cfg->q_lora > 0 ? (cfg->n_heads * h->QH + h->bn_q - 1) / h->bn_q : 0;
     *out = h;
     return MLAP_OK;
 }
@@ -333,10 +368,14 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         g.a_scale = xs;
         g.b_scale0 = has_q ? in->ws_qa : in->ws_kva;
         g.b_scale1 = in->ws_kva;
-        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
+        MLAP_LAUNCH(kKGemmDown, plan.big_down
+                                    ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
+                                    : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
     } else {
         g.A = in->x;
-        MLAP_LAUNCH(kKGemmDown, launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
+        MLAP_LAUNCH(kKGemmDown, plan.big_down
+                                    ? launch_gemm_big(g, InType::kBf16, Epi::kStoreBf16, s)
+                                    : launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
     }
 
     // 2. row stage
@@ -400,16 +439,17 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.sin = in->sin;
         u.max_pos = c.max_pos;
         u.part_amax = quant_q ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
-        u.n_tiles = h->nt_q;
+        u.n_tiles = plan.nt_q;
+        const InType it = w8 ? InType::kInt8 : InType::kBf16;
         if (w8) {
             u.A = na.qn_i8;
             u.a_scale = na.qn_scale;
             u.b_scale0 = u.b_scale1 = in->ws_qb;
-            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kInt8, plan.up_q, Epi::kHeads, s));
         } else {
             u.A = qn;
-            MLAP_LAUNCH(kKGemmUpQ, launch_gemm(u, InType::kBf16, plan.up_q, Epi::kHeads, s));
         }
+        MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s)
+                                          : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
     }
 
     // 4. kv_b up projection (KV-Prolog mode): per head [k_nope | value]
@@ -431,15 +471,16 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.n_heads = H;
         u.out0 = out->k_nope;
         u.out1 = out->value;
+        const InType it = w8 ? InType::kInt8 : InType::kBf16;
         if (w8) {
             u.A = na.kv_i8_b;
             u.a_scale = na.kv_scale_b;
             u.b_scale0 = u.b_scale1 = in->ws_kvb;
-            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kInt8, plan.up_kv, Epi::kHeads, s));
         } else {
             u.A = kvn;
-            MLAP_LAUNCH(kKGemmUpKv, launch_gemm(u, InType::kBf16, plan.up_kv, Epi::kHeads, s));
         }
+        MLAP_LAUNCH(kKGemmUpKv, plan.big_kv ? launch_gemm_big(u, it, Epi::kHeads, s)
+                                            : launch_gemm(u, it, plan.up_kv, Epi::kHeads, s));
     }
 
     // 5. per-token INT8 quant of q (after RoPE), one scale over all heads
@@ -449,7 +490,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         qa.H = H;
         qa.Dn = c.nope_dim;
         qa.R = R;
-        qa.n_tiles = h->nt_q;
+        qa.n_tiles = plan.nt_q;
         qa.part_amax = reinterpret_cast<const float*>(wsb + L.qpart);
         qa.q_nope = static_cast<const uint16_t*>(out->q_nope);
         qa.q_pe = static_cast<const uint16_t*>(out->q_pe);

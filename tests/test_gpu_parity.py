@@ -113,17 +113,23 @@ def sample_rows(T, n_random=40, seed=0):
     return np.array(sorted(rows), dtype=np.int32)
 
 
-@pytest.mark.parametrize("name", ["v3_prefill", "v3_w8a8"])
-def test_prolog_parity_full_size_sampled_rows(name):
-    cfg = synth.get_config(name)
+# Batches past the weight-streaming bucket run the large-batch GEMM (256 x 256 tiles):
+# mid sizes with ragged last tiles, and the full benchmark sizes.
+@pytest.mark.parametrize("name,T", [("v3_prefill", 1000), ("v3_w8a8", 700),
+                                    ("v2lite_kv_decode", 1000), ("v3_prefill", None),
+                                    ("v3_w8a8", None)])
+def test_prolog_parity_full_size_sampled_rows(name, T):
+    cfg = synth.get_config(name, T=T)
     say("prolog full-size", name, "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
     out = run_gpu(cfg, inp)
     rows = sample_rows(cfg.T)
+    rows = np.union1d(rows, [r for r in (255, 256, 511, 512, 767, 768) if r < cfg.T]).astype(np.int32)
     stats = check_prolog(cfg, inp, out, rows=rows)
     say("  rows", len(rows), {k: round(v, 4) for k, v in stats.items()})
-    # the outlier channels make per-token amax large: every row still reaches |code| = 127
-    assert (out["q_i8"].abs().reshape(cfg.T, -1).amax(1) == 127).all()
+    # every row with a nonzero amax reaches |code| = 127
+    if "q_i8" in out:
+        assert (out["q_i8"].abs().reshape(cfg.T, -1).amax(1) == 127).all()
     assert (out["kv_i8"].abs().amax(1) == 127).all()
 
 
