@@ -39,6 +39,8 @@ struct GemmArgs {
     int ldb;
     int k_splits;  // each split covers K/k_splits (kStoreF32 only)
     int group_m;   // M-tiles per group in the workgroup -> tile order
+    int n_major;   // large-batch kernel: split the tile space over XCDs by N rather than M
+                   // (each XCD then streams a 1/8 share of B and all of A)
     // W8A8 dequant: y = f32(acc) * (a_scale[m] * b_scale[n]); b_scale split like B.
     const float* a_scale;
     const float* b_scale0;

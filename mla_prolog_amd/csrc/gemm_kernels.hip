@@ -64,7 +64,7 @@ template <typename Tin, Epi EPI>
 hipError_t launch_big_one(const GemmArgs& g, hipStream_t s) {
     constexpr int BM = kBigTile, BN = kBigTile, WM = 4, WN = 2, KB = 128, S = 2;
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, KB, S, EPI>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, KB, S, 0, EPI>), dim3(tiles),
                        dim3(64 * WM * WN), 0, s, g);
     return hipGetLastError();
 }
@@ -85,6 +85,30 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi) {
 hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (!gemm_big_fits(g, t, epi)) return hipErrorInvalidValue;
+    if (epi == Epi::kStoreBf16 && g.N > kBigTile && g.N % kBigTile && g.N % 64 == 0) {
+        // A ragged last column tile (the 64-wide k_pe slice of the down projection) would
+        // cost a whole extra round of 256x256 tiles: run the full-width columns here and
+        // the remainder with 256 x 64 tiles.
+        const int nm = g.N / kBigTile * kBigTile;
+        GemmArgs a = g;
+        a.N = nm;
+        hipError_t e = launch_gemm_big(a, t, epi, s);
+        if (e != hipSuccess) return e;
+        GemmArgs r = g;
+        r.N = g.N - nm;
+        const size_t eb = t == InType::kInt8 ? 1 : 2;
+        if (nm >= g.b_split) {  // the remainder rows all come from the second segment
+            r.B0 = r.B1 = static_cast<const char*>(g.B1) + static_cast<size_t>(nm - g.b_split) * g.ldb * eb;
+            r.b_scale0 = r.b_scale1 = g.b_scale1 ? g.b_scale1 + (nm - g.b_split) : nullptr;
+            r.b_split = r.N;
+        } else {
+            r.B0 = static_cast<const char*>(g.B0) + static_cast<size_t>(nm) * g.ldb * eb;
+            r.b_scale0 = g.b_scale0 ? g.b_scale0 + nm : nullptr;
+            r.b_split = g.b_split - nm;
+        }
+        r.out = static_cast<uint16_t*>(g.out) + nm;
+        return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
+    }
     if (t == InType::kBf16)
         return epi == Epi::kStoreBf16 ? launch_big_one<uint16_t, Epi::kStoreBf16>(g, s)
                                       : launch_big_one<uint16_t, Epi::kHeads>(g, s);

@@ -37,6 +37,10 @@ struct NormArgs {
     int T, Lq, Lkv, R, N1, k_splits;
     const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output, or
     const float* a_f32;      // [k_splits, T, N1] fp32 split-K partial sums (used when set)
+    // Columns [tail_c0, N1) of the down projection, when set, come from their own split-K
+    // fp32 partials [tail_splits, T, N1 - tail_c0] instead (tail_c0 a multiple of 8).
+    const float* tail_f32;
+    int tail_c0, tail_splits;
     const uint16_t* gamma_q;
     const uint16_t* gamma_kv;
     float eps;

@@ -38,6 +38,7 @@ const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope"
 constexpr size_t kAlign = 256;
 constexpr int kSmallBatch = 512;  // token counts up to this use the weight-streaming tiles
 constexpr int kGroupM = 4;        // M-tiles per group in the XCD-aware tile order
+constexpr int kGroupNq = 8;       // N-tiles per group for the q up projection (N-major split)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -59,6 +60,10 @@ struct Plan {
     int down_splits;
     GemmTile up_q, up_kv;
     bool big_down = false, big_q = false, big_kv = false;  // large-batch kernel (gemm_big.hpp)
+    // bf16 large batches: the down projection's columns past the last whole 256-wide tile
+    // (the k_pe slice at V3 and V2-Lite widths) run as a split-K GEMM with fp32 partials
+    // that the row kernel sums, instead of a second, mostly idle round of tiles.
+    int tail_c0 = 0, tail_splits = 0;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
 };
 
@@ -71,7 +76,7 @@ struct Timer {
 
 // Workspace carve-up for T tokens.
 struct WsLayout {
-    size_t a1 = 0, qn = 0, kvn = 0, qpart = 0, xq = 0, xs = 0, qnq = 0, qns = 0, kvq = 0, kvs = 0;
+    size_t a1 = 0, tail = 0, qn = 0, kvn = 0, qpart = 0, xq = 0, xs = 0, qnq = 0, qns = 0, kvq = 0, kvs = 0;
     size_t total = 0;
 };
 
@@ -119,6 +124,18 @@ struct mlap_prolog {
             if (p.big_down) {
                 p.down_epi = Epi::kStoreBf16;
                 p.down_splits = 1;
+                const int c0 = N1 / kBigTile * kBigTile;
+                if (!w8a8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
+                    p.tail_c0 = c0;
+                    const int tiles = (T + 255) / 256 * ((N1 - c0) / 64);
+                    int sp = 1;
+                    for (int c = 1; c <= 16; ++c) {
+                        if (nk % c) continue;
+                        sp = c;
+                        if (tiles * c >= 256) break;
+                    }
+                    p.tail_splits = sp;
+                }
             }
             if (cfg.q_lora > 0) {
                 GemmArgs u{};
@@ -157,6 +174,7 @@ struct mlap_prolog {
         };
         const size_t t = static_cast<size_t>(T);
         L.a1 = take(p.down_epi == Epi::kStoreF32 ? t * N1 * 4 * p.down_splits : t * N1 * 2);
+        if (p.tail_splits) L.tail = take(t * (N1 - p.tail_c0) * 4 * p.tail_splits);
         if (cfg.q_lora > 0) L.qn = take(t * cfg.q_lora * 2);
         if (cfg.v_dim > 0) L.kvn = take(t * cfg.kv_lora * 2);
         if (cfg.q_lora > 0) L.qpart = take(t * p.nt_q * 4);
@@ -371,6 +389,26 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         MLAP_LAUNCH(kKGemmDown, plan.big_down
                                     ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
                                     : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
+    } else if (plan.tail_splits) {
+        g.A = in->x;
+        GemmArgs r = g;  // columns [tail_c0, N1): split-K fp32 partials
+        r.N = h->N1 - plan.tail_c0;
+        r.k_splits = plan.tail_splits;
+        if (plan.tail_c0 >= g.b_split) {
+            r.B0 = r.B1 = static_cast<const char*>(g.B1) +
+                          static_cast<size_t>(plan.tail_c0 - g.b_split) * g.ldb * 2;
+            r.b_split = r.N;
+        } else {
+            r.B0 = static_cast<const char*>(g.B0) + static_cast<size_t>(plan.tail_c0) * g.ldb * 2;
+            r.b_split = g.b_split - plan.tail_c0;
+        }
+        r.out = wsb + L.tail;
+        r.ldo = r.N;
+        g.N = plan.tail_c0;
+        MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, InType::kBf16, Epi::kStoreBf16, s) != hipSuccess
+                                    ? hipErrorInvalidValue
+                                    : launch_gemm(r, InType::kBf16, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
+        g.N = h->N1;
     } else {
         g.A = in->x;
         MLAP_LAUNCH(kKGemmDown, plan.big_down
@@ -386,6 +424,11 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     na.R = R;
     na.N1 = h->N1;
     na.k_splits = plan.down_splits;
+    if (plan.tail_splits) {
+        na.tail_f32 = reinterpret_cast<const float*>(wsb + L.tail);
+        na.tail_c0 = plan.tail_c0;
+        na.tail_splits = plan.tail_splits;
+    }
     if (plan.down_epi == Epi::kStoreF32)
         na.a_f32 = reinterpret_cast<const float*>(a1);
     else
@@ -427,6 +470,8 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
+        u.n_major = 1;   // B (75 MB at V3) dwarfs A: give each XCD a 1/8 share of B
+        u.group_m = kGroupNq;
         u.head_w = h->QH;
         u.d0 = c.nope_dim;
         u.d1 = R;

@@ -47,6 +47,20 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 // 8 consecutive down-projection outputs of token t starting at column col, as the fp32
 // values of their bf16 rounding (the GEMM's bf16 output cast point).
 __device__ __forceinline__ void load_a8(const NormArgs& a, int t, int col, float* f) {
+    if (a.tail_f32 && col >= a.tail_c0) {
+        const int w = a.N1 - a.tail_c0;
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < a.tail_splits; ++sp) {
+            const float4* p = reinterpret_cast<const float4*>(
+                a.tail_f32 + (static_cast<size_t>(sp) * a.T + t) * w + (col - a.tail_c0));
+            const float4 x0 = p[0], x1 = p[1];
+            s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
+            s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+        return;
+    }
     if (!a.a_f32) {
         unpack8(*reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col), f);
         return;
@@ -190,6 +204,145 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
     }
 }
 
+// Same stage with one 64-wide wave per token (four tokens per workgroup) for segment
+// widths up to 64 * 8 * QC (q) and 64 * 8 * KC (kv): every reduction is a wave butterfly,
+// there is no workgroup barrier, and 2048 workgroups of four short waves fill the chip.
+template <int QC, int KC>
+__global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;  // the whole wave leaves; nothing below synchronises the workgroup
+    const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
+
+    float qv[QC > 0 ? QC : 1][8], kv[KC][8];
+    float sq = 0.f, skv = 0.f;
+    const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
+    const float invkv = 1.0f / static_cast<float>(a.Lkv);
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nq) {
+            load_a8(a, t, c * 8, qv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = qv[i][e] * qv[i][e];
+                sq += p * invq;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nkv) {
+            load_a8(a, t, a.Lq + c * 8, kv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = kv[i][e] * kv[i][e];
+                skv += p * invkv;
+            }
+        }
+    }
+    const float msq = QC > 0 ? wave_sum(sq) : 0.f;
+    const float mskv = wave_sum(skv);
+    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
+    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+
+    float qmax = 0.f, kvmax = 0.f;
+    uint4 qo[QC > 0 ? QC : 1], kvo[KC];
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nq) {
+            float g[8], o[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.gamma_q + c * 8), g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = qv[i][e] * rstd_q;
+                o[e] = y * g[e];
+            }
+            qo[i] = pack8(o);
+            if (a.q_norm)
+                *reinterpret_cast<uint4*>(a.q_norm + static_cast<size_t>(t) * a.Lq + c * 8) = qo[i];
+            qmax = fmaxf(qmax, absmax8(qo[i]));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nkv) {
+            float g[8], o[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.gamma_kv + c * 8), g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = kv[i][e] * rstd_kv;
+                o[e] = y * g[e];
+            }
+            kvo[i] = pack8(o);
+            if (a.kv_norm)
+                *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
+            kvmax = fmaxf(kvmax, absmax8(kvo[i]));
+        }
+    }
+
+    // rotate-half RoPE of the k_pe slice (pairs i, i + R/2), one cos/sin row per token
+    const int half = a.R >> 1;
+    if (a.k_pe && lane < (half >> 3)) {
+        const int i0 = lane * 8;
+        const int p = clamp_pos(a.positions[t], a.max_pos);
+        const float* cr = a.cos + static_cast<size_t>(p) * a.R;
+        const float* sr = a.sin + static_cast<size_t>(p) * a.R;
+        float x1[8], x2[8], lo[8], hi[8];
+        load_a8(a, t, a.Lq + a.Lkv + i0, x1);
+        load_a8(a, t, a.Lq + a.Lkv + half + i0, x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float p1 = x1[e] * cr[i0 + e];
+            float p2 = (-x2[e]) * sr[i0 + e];
+            lo[e] = p1 + p2;
+            float p3 = x2[e] * cr[half + i0 + e];
+            float p4 = x1[e] * sr[half + i0 + e];
+            hi[e] = p3 + p4;
+        }
+        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
+        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
+        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+    }
+
+    // per-token INT8 quant of kv_norm
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+        const float amax = wave_max(kvmax);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nkv) {
+                const uint2 codes = quant8(kvo[i], mult);
+                const size_t off = static_cast<size_t>(t) * a.Lkv + c * 8;
+                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+            }
+        }
+        if (lane == 0) {
+            const float sc = amax / 127.0f;
+            if (a.kv_scale) a.kv_scale[t] = sc;
+            if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+        }
+    }
+    // W8A8: per-token activation quant of q_norm for the int8 up projection
+    if (QC > 0 && a.qn_i8) {
+        const float amax = wave_max(qmax);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+        for (int i = 0; i < QC; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nq)
+                *reinterpret_cast<uint2*>(a.qn_i8 + static_cast<size_t>(t) * a.Lq + c * 8) =
+                    quant8(qo[i], mult);
+        }
+        if (lane == 0) a.qn_scale[t] = amax / 127.0f;
+    }
+}
+
 __global__ __launch_bounds__(kRowThreads) void act_quant_kernel(const uint16_t* x, int K,
                                                                 int8_t* codes, float* scale) {
     __shared__ float red[kRowWaves];
@@ -231,6 +384,19 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
 
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
+    const int qc = (a.Lq / 8 + 63) / 64, kc = (a.Lkv / 8 + 63) / 64;
+    const dim3 grid((a.T + 3) / 4), block(kRowThreads);
+    if (a.R <= 1024 && kc >= 1 && kc <= 4 && qc <= 4) {
+#define MLAP_NORM_WAVE(Q, K)                                                  \
+    if (qc == Q && kc == K) {                                                 \
+        hipLaunchKernelGGL((norm_rope_wave_kernel<Q, K>), grid, block, 0, s, a); \
+        return hipGetLastError();                                             \
+    }
+        MLAP_NORM_WAVE(0, 1) MLAP_NORM_WAVE(0, 2) MLAP_NORM_WAVE(0, 3) MLAP_NORM_WAVE(0, 4)
+        MLAP_NORM_WAVE(1, 1) MLAP_NORM_WAVE(2, 1) MLAP_NORM_WAVE(3, 1) MLAP_NORM_WAVE(4, 1)
+        MLAP_NORM_WAVE(3, 2) MLAP_NORM_WAVE(4, 2) MLAP_NORM_WAVE(2, 2) MLAP_NORM_WAVE(1, 2)
+#undef MLAP_NORM_WAVE
+    }
     hipLaunchKernelGGL(norm_rope_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
 }

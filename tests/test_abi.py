@@ -102,9 +102,8 @@ def test_workspace_size_grows_with_T_and_is_aligned():
         p.workspace_size(8193)
     # W8A8 adds the int8 copies of x and q_norm (plus their per-token scales)
     w8 = mlap.Prolog.from_config(synth.get_config("v3_w8a8"))
-    bf = mlap.Prolog.from_config(synth.get_config("v3_prefill"), t_max=16384)
     T = 8192
-    assert w8.workspace_size(T) - bf.workspace_size(T) >= T * (7168 + 1536)
+    assert w8.workspace_size(T) >= T * 2112 * 2 + T * 1536 * 2 + T * (7168 + 1536)
     # small batches split the down projection over K: fp32 partial sums per split
     dec = mlap.Prolog.from_config(synth.get_config("v3_decode"))
     assert dec.workspace_size(256) >= 2 * 256 * 2112 * 4
