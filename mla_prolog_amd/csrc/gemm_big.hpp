@@ -60,7 +60,9 @@ struct Shape {
     static constexpr int ROUNDS = ROWS / RROWS;
     static constexpr int STAGE = ROWS * KB;
     static constexpr int MAIN = S * STAGE;
-    static constexpr int LDS = MAIN > BM * BN * 2 ? MAIN : BM * BN * 2;
+    static constexpr int EPI_PITCH = BN * 2 + 16;             // bytes per staged bf16 row
+    static constexpr int EPI = BM * EPI_PITCH + BM * 4;       // staged tile + row amax
+    static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
     static_assert(KB == 64 || KB == 128, "stage row bytes");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave block must be whole 32x32 fragments");
     static_assert(BM % RROWS == 0 && BN % RROWS == 0, "tile rows must fill whole copy rounds");
@@ -130,12 +132,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     const int tiles_n = (g.N + BN - 1) / BN;
     int m_tile, n_tile, split;
     if (g.n_major)
-        tile_of(blockIdx.x, tiles_n, tiles_m, 1, g.group_m, n_tile, m_tile, split);
+        tile_of(blockIdx.x, tiles_n, tiles_m, g.k_splits, g.group_m, n_tile, m_tile, split);
     else
-        tile_of(blockIdx.x, tiles_m, tiles_n, 1, g.group_m, m_tile, n_tile, split);
+        tile_of(blockIdx.x, tiles_m, tiles_n, g.k_splits, g.group_m, m_tile, n_tile, split);
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
-    const int nk = g.K * static_cast<int>(sizeof(Tin)) / KB;
+    // split-K (fp32 partial epilogue only): this workgroup covers K bytes
+    // [split * kbs, (split + 1) * kbs) of every row
+    const int kbs = g.K * static_cast<int>(sizeof(Tin)) / g.k_splits;
+    const int nk = kbs / KB;
+    const size_t k0 = static_cast<size_t>(split) * kbs;
 
     // Copy sources: round i moves tile row i*RROWS + tid/LPR, physical chunk tid%LPR.
     // Rows past the matrix edge re-read its last row; their results are never stored.
@@ -149,14 +155,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             const int c = (tid % LPR) ^ big::swz<KB>(r);
             if constexpr (i * SH::RROWS < BM) {
                 const int m = min(m0 + r, g.M - 1);
-                src[i] = static_cast<const char*>(g.A) + static_cast<size_t>(m) * lda_b + c * 16;
+                src[i] = static_cast<const char*>(g.A) + static_cast<size_t>(m) * lda_b + k0 + c * 16;
             } else {
                 const int n = min(n0 + r - BM, g.N - 1);
                 const char* row = n < g.b_split
                                       ? static_cast<const char*>(g.B0) + static_cast<size_t>(n) * ldb_b
                                       : static_cast<const char*>(g.B1) +
                                             static_cast<size_t>(n - g.b_split) * ldb_b;
-                src[i] = row + c * 16;
+                src[i] = row + k0 + c * 16;
             }
         });
     }
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     });
     auto prefetch = [&](int kt) __attribute__((always_inline)) {
         static_for<PF>([&](auto p_c) __attribute__((always_inline)) {
-            big::copy4_to_lds(prow[decltype(p_c)::value] + kt * KB, smem + SH::LDS + wave * 256);
+            big::copy4_to_lds(prow[decltype(p_c)::value] + k0 + kt * KB, smem + SH::LDS + wave * 256);
         });
     };
     // Copy rounds [R0, R1) of stage kt into `slot`.
@@ -326,13 +332,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         }
     };
 
+    if constexpr (EPI == Epi::kStoreF32) {
+        // split-K partial sums, fp32 [k_splits][M][ldo]: four consecutive columns per lane
+        float* out = static_cast<float*>(g.out) + static_cast<size_t>(split) * g.M * g.ldo;
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                const int m = mb + 32 * i;
+                if (m < g.M) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int n = nb + 32 * j + 8 * gq;
+                        if (n < g.N)  // N is a multiple of 4
+                            *reinterpret_cast<float4*>(out + static_cast<size_t>(m) * g.ldo + n) =
+                                make_float4(acc[j][i][4 * gq], acc[j][i][4 * gq + 1],
+                                            acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
+                    }
+                }
+            });
+        });
+        return;
+    }
+
     // The bf16 tile is transposed through LDS (the stage buffers are free now) so that
-    // stores leave as whole 16-byte chunks, a row's chunks on consecutive lanes: row r's
-    // 16-byte chunk c sits at chunk c ^ (r % CPR) of its BN*2-byte LDS row.
-    constexpr int CPR = BN / 8;            // 16-byte chunks per tile row
-    constexpr int RPP = SH::NT / CPR;      // rows per read-back pass
-    static_assert(CPR <= 64 && SH::NT % CPR == 0 && BM % RPP == 0, "read-back geometry");
-    static_assert(BM * BN * 2 <= SH::LDS, "LDS holds the bf16 tile");
+    // stores leave as whole 16-byte chunks, a row's chunks on consecutive lanes. Rows are
+    // padded by 16 bytes against bank conflicts.
+    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+    constexpr int PITCH = SH::EPI_PITCH;
+    uint32_t* row_amax = reinterpret_cast<uint32_t*>(smem + BM * PITCH);
     big::lds_barrier();  // every wave is done reading the last stage
     static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
         constexpr int j = decltype(j_c)::value;
@@ -343,49 +371,52 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             const int row = wm * TM + 32 * i + lr;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int chunk = (wn * TN + 32 * j + 8 * gq) >> 3;
-                *reinterpret_cast<uint2*>(smem + row * (BN * 2) + ((chunk ^ (row % CPR)) << 4) + 8 * lh) =
-                    make_uint2(w[2 * gq], w[2 * gq + 1]);
+                const int col = wn * TN + 32 * j + 8 * gq + 4 * lh;
+                *reinterpret_cast<uint2*>(smem + row * PITCH + col * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
             }
         });
     });
+    if constexpr (EPI == Epi::kHeads) {
+        for (int r = tid; r < BM; r += SH::NT) row_amax[r] = 0u;
+    }
     big::lds_barrier();
 
-    const int c = tid % CPR;          // this thread's chunk of each row
-    const int n = n0 + 8 * c;         // its first output column
     auto tile_chunk = [&](int row, int ch) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(smem + row * (BN * 2) + ((ch ^ (row % CPR)) << 4));
+        return *reinterpret_cast<const uint4*>(smem + row * PITCH + ch * 16);
     };
     if constexpr (EPI == Epi::kStoreBf16) {
         uint16_t* out = static_cast<uint16_t*>(g.out);
-        for (int row = tid / CPR; row < BM; row += RPP) {
-            const int m = m0 + row;
+        for (int idx = tid; idx < BM * CPR; idx += SH::NT) {
+            const int row = idx / CPR, c = idx - row * CPR;
+            const int m = m0 + row, n = n0 + 8 * c;
             if (m < g.M && n < g.N)  // N is a multiple of 8
                 *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) = tile_chunk(row, c);
         }
     } else if constexpr (EPI == Epi::kHeads) {
-        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the 64-wide
-        // rotate-half slice. Head width and d0 are multiples of 64 and tiles start on
-        // multiples of 64, so a chunk lies in one segment and the rotate-half partner of
-        // chunk c (32 columns away) is chunk c ^ 4 of the same tile row.
+        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the
+        // rotate-half slice. The host picks tiles that hold whole 8-column chunks of one
+        // segment and a whole rope slice, so the rotate-half partner of a chunk (d1/2
+        // columns away) is in the same tile row.
         const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
+        const int pc = d1 / 16;  // partner distance in chunks
         uint16_t* out0 = static_cast<uint16_t*>(g.out0);
         uint16_t* out1 = static_cast<uint16_t*>(g.out1);
-        const bool nok = n < g.N;
-        const int h = nok ? n / HW : 0;
-        const int d = n - h * HW;
-        const bool seg0 = d < d0;
-        const int dr = d - d0;  // column within seg1
-        for (int row = tid / CPR; row < BM; row += RPP) {
-            const int m = m0 + row;
-            const bool ok = nok && m < g.M;
+        for (int idx = tid; idx < BM * CPR; idx += SH::NT) {
+            const int row = idx / CPR, c = idx - row * CPR;
+            const int m = m0 + row, n = n0 + 8 * c;
+            const bool ok = n < g.N && m < g.M;
+            const int h = n / HW;
+            const int d = n - h * HW;
+            const bool seg0 = d < d0;
+            const int dr = d - d0;  // column within seg1
             const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
             const uint4 v = tile_chunk(row, c);
             uint4 o = v;
             if (!seg0 && g.rope) {
                 // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
                 // cos/sin at this chunk's own columns; the partner is the other half.
-                const uint4 pv = tile_chunk(row, c ^ 4);
+                const bool low = dr < (d1 >> 1);
+                const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
                 const int p = clamp_pos(g.positions[min(m, g.M - 1)], g.max_pos);
                 const float* cr = g.cos + static_cast<size_t>(p) * d1 + dr;
                 const float* sr = g.sin + static_cast<size_t>(p) * d1 + dr;
@@ -398,7 +429,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 const float4 s1 = *reinterpret_cast<const float4*>(sr + 4);
                 const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
                 const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-                const bool low = dr < (d1 >> 1);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float t1 = own[e] * cs[e];
@@ -414,14 +444,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 } else if (out1) {
                     *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
                 }
+                // |values| are non-negative floats, whose bit patterns order like unsigned ints
+                if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
             }
-            if (g.part_amax) {
-                // the token's amax over this tile's columns: max over the CPR lanes of the row
-                float amax = ok ? absmax8(o) : 0.f;
-#pragma unroll
-                for (int o2 = CPR / 2; o2 > 0; o2 >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o2, kWave));
-                if (c == 0 && m < g.M) g.part_amax[static_cast<size_t>(m) * g.n_tiles + n_tile] = amax;
-            }
+        }
+        if (g.part_amax) {
+            big::lds_barrier();
+            for (int r = tid; r < BM; r += SH::NT)
+                if (m0 + r < g.M)
+                    g.part_amax[static_cast<size_t>(m0 + r) * g.n_tiles + n_tile] = __uint_as_float(row_amax[r]);
         }
     }
 }

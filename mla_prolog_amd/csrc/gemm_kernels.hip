@@ -60,39 +60,54 @@ hipError_t dispatch(const GemmArgs& g, const GemmTile& t, Epi epi, hipStream_t s
     return hipErrorInvalidValue;
 }
 
-template <typename Tin, Epi EPI>
+template <typename Tin, int BM, int BN, int WM, int WN, int S, Epi EPI>
 hipError_t launch_big_one(const GemmArgs& g, hipStream_t s) {
-    constexpr int BM = kBigTile, BN = kBigTile, WM = 4, WN = 2, KB = 128, S = 2;
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, KB, S, 0, EPI>), dim3(tiles),
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.k_splits;
+    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, 128, S, 0, EPI>), dim3(tiles),
                        dim3(64 * WM * WN), 0, s, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi) {
+int big_tile_n(BigShape shape) {
+    return shape == BigShape::kWide ? 256 : shape == BigShape::kHalfHead ? 96 : 64;
+}
+
+bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
     const int kbytes = g.K * (t == InType::kInt8 ? 1 : 2);
-    if (g.K <= 0 || kbytes % 128) return false;  // whole 128-byte stages
-    if (epi == Epi::kStoreBf16) return g.N % 8 == 0 && g.ldo % 8 == 0;
-    if (epi == Epi::kHeads) {
-        if (g.head_w % 64 || g.d0 % 64) return false;
-        return g.rope ? g.d1 == 64 : g.d1 % 8 == 0;
+    const int splits = g.k_splits > 0 ? g.k_splits : 1;
+    if (g.K <= 0 || kbytes % (128 * splits)) return false;  // whole 128-byte stages per split
+    if (splits > 1 && epi != Epi::kStoreF32) return false;
+    switch (shape) {
+        case BigShape::kWide:
+            if (epi == Epi::kStoreBf16) return g.N % 8 == 0 && g.ldo % 8 == 0;
+            if (epi == Epi::kHeads) {
+                if (g.head_w % 64 || g.d0 % 64) return false;
+                return g.rope ? g.d1 == 64 : g.d1 % 8 == 0;
+            }
+            return false;
+        case BigShape::kHalfHead:
+            // 96-column tiles, two per head: [0, 96) all seg0, [96, HW) the rest of seg0
+            // and the whole rope slice
+            return t == InType::kBf16 && epi == Epi::kHeads && g.head_w == 192 && g.rope &&
+                   g.d0 >= 96 && g.d0 % 8 == 0 && g.d1 == 192 - g.d0 && g.d1 % 16 == 0;
+        case BigShape::kSplitK:
+            return t == InType::kBf16 && epi == Epi::kStoreF32 && g.N % 4 == 0 && g.ldo % 4 == 0;
     }
     return false;
 }
 
-hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s) {
+hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, BigShape shape) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    if (!gemm_big_fits(g, t, epi)) return hipErrorInvalidValue;
-    if (epi == Epi::kStoreBf16 && g.N > kBigTile && g.N % kBigTile && g.N % 64 == 0) {
-        // A ragged last column tile (the 64-wide k_pe slice of the down projection) would
-        // cost a whole extra round of 256x256 tiles: run the full-width columns here and
-        // the remainder with 256 x 64 tiles.
+    if (shape == BigShape::kWide && epi == Epi::kStoreBf16 && g.N > kBigTile && g.N % kBigTile &&
+        g.N % 64 == 0) {
+        // A ragged last column tile would cost a whole extra round of 256x256 tiles: run the
+        // full-width columns here and the remainder with 256 x 64 tiles.
         const int nm = g.N / kBigTile * kBigTile;
         GemmArgs a = g;
         a.N = nm;
-        hipError_t e = launch_gemm_big(a, t, epi, s);
+        hipError_t e = launch_gemm_big(a, t, epi, s, shape);
         if (e != hipSuccess) return e;
         GemmArgs r = g;
         r.N = g.N - nm;
@@ -109,11 +124,20 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s) 
         r.out = static_cast<uint16_t*>(g.out) + nm;
         return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
     }
-    if (t == InType::kBf16)
-        return epi == Epi::kStoreBf16 ? launch_big_one<uint16_t, Epi::kStoreBf16>(g, s)
-                                      : launch_big_one<uint16_t, Epi::kHeads>(g, s);
-    return epi == Epi::kStoreBf16 ? launch_big_one<int8_t, Epi::kStoreBf16>(g, s)
-                                  : launch_big_one<int8_t, Epi::kHeads>(g, s);
+    if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
+    switch (shape) {
+        case BigShape::kWide:
+            if (t == InType::kBf16)
+                return epi == Epi::kStoreBf16 ? launch_big_one<uint16_t, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s)
+                                              : launch_big_one<uint16_t, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
+            return epi == Epi::kStoreBf16 ? launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s)
+                                          : launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
+        case BigShape::kHalfHead:
+            return launch_big_one<uint16_t, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
+        case BigShape::kSplitK:
+            return launch_big_one<uint16_t, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, InType type, const GemmTile& t, Epi epi, hipStream_t s) {

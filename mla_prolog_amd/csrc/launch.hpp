@@ -21,14 +21,21 @@ struct GemmTile {
 // (type, tile, epilogue) combination that has no instantiation.
 hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi epi, hipStream_t s);
 
-// Large-batch GEMM (gemm_big.hpp): kBigTile x kBigTile output tiles. Epilogues kStoreBf16
-// and kHeads; with kHeads, g.n_tiles must be ceil(N / kBigTile) (one partial amax per
-// token and tile). gemm_big_fits says whether the shapes suit it (K a whole number of
-// 128-byte stages; N a multiple of 8; for heads, head width and d0 multiples of 64 and
-// a 64-wide rope slice).
+// LDS-DMA GEMM (gemm_big.hpp) in three shapes:
+//   kWide     -- 256 x 256 tiles, eight waves (large batches, MFMA-bound); kStoreBf16 and
+//                kHeads (head width and d0 multiples of 64, a 64-wide rope slice);
+//   kHalfHead -- 256 x 96 tiles, four waves: one tile per half of a 192-wide q head, a
+//                decode batch's whole T in one tile row (bf16, kHeads);
+//   kSplitK   -- 256 x 64 tiles, four waves, split-K fp32 partials (bf16, kStoreF32).
+// With kHeads, g.n_tiles must be ceil(N / big_tile_n(shape)) (one partial amax per token
+// and tile). gemm_big_fits says whether the shapes suit it (K a whole number of 128-byte
+// stages per split).
+enum class BigShape : int { kWide = 0, kHalfHead = 1, kSplitK = 2 };
 constexpr int kBigTile = 256;
-bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi);
-hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s);
+int big_tile_n(BigShape shape);
+bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape = BigShape::kWide);
+hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s,
+                           BigShape shape = BigShape::kWide);
 
 // Per-token row stage after the down projection: RMSNorm*gamma -> bf16 for the q and kv
 // segments, rotate-half RoPE of the k_pe segment, per-token INT8 quant of kv_norm and (W8A8)

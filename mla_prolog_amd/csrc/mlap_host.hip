@@ -64,6 +64,7 @@ struct Plan {
     // (the k_pe slice at V3 and V2-Lite widths) run as a split-K GEMM with fp32 partials
     // that the row kernel sums, instead of a second, mostly idle round of tiles.
     int tail_c0 = 0, tail_splits = 0;
+    BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
 };
 
@@ -155,10 +156,35 @@ struct mlap_prolog {
                 u.rope = 0;
                 p.big_kv = gemm_big_fits(u, it, Epi::kHeads);
             }
+        } else if (!w8a8) {
+            // weight streaming: the LDS-DMA kernel with split-K fp32 partials for the down
+            // projection and half-head tiles spanning the whole batch for the q up projection
+            GemmArgs d{};
+            d.K = cfg.hidden;
+            d.N = N1;
+            d.ldo = N1;
+            d.k_splits = p.down_splits;
+            if (gemm_big_fits(d, it, Epi::kStoreF32, BigShape::kSplitK)) {
+                p.big_down = true;
+                p.down_shape = BigShape::kSplitK;
+            }
+            if (cfg.q_lora > 0) {
+                GemmArgs u{};
+                u.K = cfg.q_lora;
+                u.head_w = QH;
+                u.d0 = cfg.nope_dim;
+                u.d1 = cfg.rope_dim;
+                u.rope = 1;
+                if (gemm_big_fits(u, it, Epi::kHeads, BigShape::kHalfHead)) {
+                    p.big_q = true;
+                    p.q_shape = BigShape::kHalfHead;
+                }
+            }
         }
         if (cfg.q_lora > 0) {
             const int nq = cfg.n_heads * QH;
-            p.nt_q = p.big_q ? (nq + kBigTile - 1) / kBigTile : (nq + bn_q - 1) / bn_q;
+            const int bn = p.big_q ? big_tile_n(p.q_shape) : bn_q;
+            p.nt_q = (nq + bn - 1) / bn;
         }
         return p;
     }
@@ -412,7 +438,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     } else {
         g.A = in->x;
         MLAP_LAUNCH(kKGemmDown, plan.big_down
-                                    ? launch_gemm_big(g, InType::kBf16, Epi::kStoreBf16, s)
+                                    ? launch_gemm_big(g, InType::kBf16, plan.down_epi, s, plan.down_shape)
                                     : launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
     }
 
@@ -493,7 +519,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         } else {
             u.A = qn;
         }
-        MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s)
+        MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
                                           : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
     }
 

@@ -386,7 +386,9 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     const int qc = (a.Lq / 8 + 63) / 64, kc = (a.Lkv / 8 + 63) / 64;
     const dim3 grid((a.T + 3) / 4), block(kRowThreads);
-    if (a.R <= 1024 && kc >= 1 && kc <= 4 && qc <= 4) {
+    // A wave per token needs thousands of tokens to fill 256 CUs; small batches keep a
+    // whole workgroup per token.
+    if (a.T >= 2048 && a.R <= 1024 && kc >= 1 && kc <= 4 && qc <= 4) {
 #define MLAP_NORM_WAVE(Q, K)                                                  \
     if (qc == Q && kc == K) {                                                 \
         hipLaunchKernelGGL((norm_rope_wave_kernel<Q, K>), grid, block, 0, s, a); \
