@@ -95,11 +95,6 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, (lds_ptr)(lds), 16, 0, 0);
 }
 
-// One 4-byte-per-lane copy global -> LDS (global_load_lds_dword); lane l writes lds + 4 l.
-__device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(lds), 4, 0, 0);
-}
-
 // An empty statement that needs `v` in VGPRs (an allocation hint, no instruction).
 __device__ __forceinline__ void pin_vgpr(i32x4& v) { asm volatile("" : "+v"(v)); }
 
@@ -114,15 +109,13 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 
 }  // namespace big
 
-template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, int PD, Epi EPI>
+template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     using SH = big::Shape<BM, BN, WM, WN, KB, S>;
-    static_assert(PD == 0 || (S == 2 && PD >= 2), "L2 prefetch runs ahead of a two-stage ring");
     using Op = MfmaOp<Tin>;
     constexpr int TM = SH::TM, TN = SH::TN, FM = SH::FM, FN = SH::FN, KS = SH::KS;
     constexpr int ROUNDS = SH::ROUNDS, LPR = SH::LPR;
-    constexpr int PF = PD > 0 ? (SH::ROWS + SH::NT - 1) / SH::NT : 0;  // prefetch copies per stage
-    __shared__ __attribute__((aligned(1024))) char smem[SH::LDS + (PD > 0 ? SH::NT * 4 : 0)];
+    __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -166,29 +159,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             }
         });
     }
-    // L2 prefetch of stage kt: one 4-byte copy per 128-byte line (the first bytes of every
-    // tile row's stage) into a scratch corner of LDS that nothing reads, so the lines are on
-    // chip when the real copy of that stage is issued.
-    const char* prow[PF > 0 ? PF : 1];
-    static_for<PF>([&](auto p_c) __attribute__((always_inline)) {
-        constexpr int p = decltype(p_c)::value;
-        const int r = min(p * SH::NT + tid, SH::ROWS - 1);
-        if (r < BM) {
-            prow[p] = static_cast<const char*>(g.A) +
-                      static_cast<size_t>(min(m0 + r, g.M - 1)) * g.lda * sizeof(Tin);
-        } else {
-            const int n = min(n0 + r - BM, g.N - 1);
-            prow[p] = n < g.b_split
-                          ? static_cast<const char*>(g.B0) + static_cast<size_t>(n) * g.ldb * sizeof(Tin)
-                          : static_cast<const char*>(g.B1) +
-                                static_cast<size_t>(n - g.b_split) * g.ldb * sizeof(Tin);
-        }
-    });
-    auto prefetch = [&](int kt) __attribute__((always_inline)) {
-        static_for<PF>([&](auto p_c) __attribute__((always_inline)) {
-            big::copy4_to_lds(prow[decltype(p_c)::value] + k0 + kt * KB, smem + SH::LDS + wave * 256);
-        });
-    };
     // Copy rounds [R0, R1) of stage kt into `slot`.
     auto issue_part = [&](int kt, int slot, auto r0_c, auto r1_c) __attribute__((always_inline)) {
         constexpr int R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
@@ -258,27 +228,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // of iteration kt certifies that stage kt has landed for every wave and that every wave
     // is done with slot (kt - 1) % S, which the copy of stage kt + S - 1 then reuses.
     // Inside a stage, the fragments of k-step ks + 1 are read while k-step ks multiplies.
-    if constexpr (PD > 0) {
-        for (int s = 1; s < PD && s < nk; ++s) prefetch(s);
-    }
     static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         if (s < nk) issue(s, s);
     });
     int slot = 0;  // kt % S
     for (int kt = 0; kt < nk; ++kt) {
-        if constexpr (PD > 0) {
-            // stage kt was copied before the prefetch issued at the end of iteration kt - 1
-            if (kt >= 1 && kt - 1 + PD < nk)
-                big::wait_vmcnt<PF>();
-            else
-                big::wait_vmcnt<0>();
-        } else {
-            if (kt + S - 2 < nk)
-                big::wait_vmcnt<(S - 2) * ROUNDS>();
-            else
-                big::wait_vmcnt<0>();
-        }
+        if (kt + S - 2 < nk)
+            big::wait_vmcnt<(S - 2) * ROUNDS>();
+        else
+            big::wait_vmcnt<0>();
         big::lds_barrier();
         // The next copy is spread over the k-steps so that a busy memory pipeline never
         // holds up all MFMA issue at once.
@@ -294,9 +253,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             if constexpr (ks + 1 < KS) read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
             multiply(f[ks & 1]);
         });
-        if constexpr (PD > 0) {
-            if (kt + PD < nk) prefetch(kt + PD);
-        }
         slot = slot + 1 == S ? 0 : slot + 1;
     }
 

@@ -36,11 +36,22 @@ const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope"
                                            "gemm_up_q", "gemm_up_kv", "quant_q"};
 
 constexpr size_t kAlign = 256;
+constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kSmallBatch = 512;  // token counts up to this use the weight-streaming tiles
 constexpr int kGroupM = 4;        // M-tiles per group in the XCD-aware tile order
 constexpr int kGroupNq = 8;       // N-tiles per group for the q up projection (N-major split)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Split-K factor for `tiles` output tiles over `nk` K-tiles: the largest divisor of nk (at
+// most 16) that keeps the grid within one round of the 256 CUs -- a grid just past 256
+// workgroups runs a second, nearly empty round -- or 1 if the tiles alone fill a round.
+int one_round_splits(int tiles, int nk) {
+    int best = 1;
+    for (int c = 1; c <= 16; ++c)
+        if (nk % c == 0 && tiles * c <= kCUs) best = c;
+    return best;
+}
 
 // Widest supported up-projection tile that holds whole heads.
 int heads_tile(int head_w) {
@@ -99,14 +110,7 @@ struct mlap_prolog {
         if (!w8a8 && small) {
             p.down = {256, 64, 3};
             p.down_epi = Epi::kStoreF32;
-            const int tiles = ((T + 255) / 256) * ((N1 + 63) / 64);
-            int s = 1;
-            for (int c = 1; c <= 16; ++c) {
-                if (nk % c) continue;
-                s = c;
-                if (tiles * c >= 256) break;
-            }
-            p.down_splits = s;
+            p.down_splits = one_round_splits(((T + 255) / 256) * ((N1 + 63) / 64), nk);
         } else {
             p.down = (cfg.q_lora % 192 == 0 && !small) ? GemmTile{256, 192, 1} : GemmTile{256, 64, 1};
             p.down_epi = Epi::kStoreBf16;
@@ -128,14 +132,7 @@ struct mlap_prolog {
                 const int c0 = N1 / kBigTile * kBigTile;
                 if (!w8a8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
                     p.tail_c0 = c0;
-                    const int tiles = (T + 255) / 256 * ((N1 - c0) / 64);
-                    int sp = 1;
-                    for (int c = 1; c <= 16; ++c) {
-                        if (nk % c) continue;
-                        sp = c;
-                        if (tiles * c >= 256) break;
-                    }
-                    p.tail_splits = sp;
+                    p.tail_splits = one_round_splits((T + 255) / 256 * ((N1 - c0) / 64), nk);
                 }
             }
             if (cfg.q_lora > 0) {
