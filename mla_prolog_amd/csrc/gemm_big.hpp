@@ -353,57 +353,90 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         // rotate-half slice. The host picks tiles that hold whole 8-column chunks of one
         // segment and a whole rope slice, so the rotate-half partner of a chunk (d1/2
         // columns away) is in the same tile row.
+        //
+        // A thread keeps one chunk column c for the whole tile and walks the rows (RPP rows
+        // per pass), so its segment, head offset and rope role are fixed. Every gather the
+        // rope needs is issued ahead: all of the thread's token positions at once, and the
+        // cos/sin rows of pass p + L while pass p is rotated.
+        constexpr int RPP = SH::NT / CPR;                 // rows per pass
+        constexpr int PASSES = (BM + RPP - 1) / RPP;
+        constexpr int L = PASSES < 4 ? PASSES : 4;        // cos/sin lookahead (passes)
         const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
         const int pc = d1 / 16;  // partner distance in chunks
         uint16_t* out0 = static_cast<uint16_t*>(g.out0);
         uint16_t* out1 = static_cast<uint16_t*>(g.out1);
-        for (int idx = tid; idx < BM * CPR; idx += SH::NT) {
-            const int row = idx / CPR, c = idx - row * CPR;
-            const int m = m0 + row, n = n0 + 8 * c;
-            const bool ok = n < g.N && m < g.M;
-            const int h = n / HW;
-            const int d = n - h * HW;
-            const bool seg0 = d < d0;
-            const int dr = d - d0;  // column within seg1
-            const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
-            const uint4 v = tile_chunk(row, c);
-            uint4 o = v;
-            if (!seg0 && g.rope) {
-                // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
-                // cos/sin at this chunk's own columns; the partner is the other half.
-                const bool low = dr < (d1 >> 1);
-                const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
-                const int p = clamp_pos(g.positions[min(m, g.M - 1)], g.max_pos);
-                const float* cr = g.cos + static_cast<size_t>(p) * d1 + dr;
-                const float* sr = g.sin + static_cast<size_t>(p) * d1 + dr;
-                float own[8], oth[8], res[8];
-                unpack8(v, own);
-                unpack8(pv, oth);
-                const float4 c0 = *reinterpret_cast<const float4*>(cr);
-                const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
-                const float4 s0 = *reinterpret_cast<const float4*>(sr);
-                const float4 s1 = *reinterpret_cast<const float4*>(sr + 4);
-                const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const int c = tid % CPR, r_in = tid / CPR;
+        const bool active = tid < RPP * CPR;
+        const int n = n0 + 8 * c;
+        const bool nok = active && n < g.N;
+        const int h = n / HW;
+        const int d = n - h * HW;
+        const bool seg0 = d < d0;
+        const int dr = d - d0;  // column within seg1
+        const bool rot = nok && !seg0 && g.rope;
+        const bool low = dr < (d1 >> 1);
+        int pos[PASSES];
+        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            const int m = min(m0 + p * RPP + r_in, g.M - 1);
+            pos[p] = rot ? clamp_pos(g.positions[m], g.max_pos) : 0;
+        });
+        float4 cs[L][2], sn[L][2];
+        auto gather = [&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            if constexpr (p < PASSES) {
+                if (rot) {
+                    const float* cr = g.cos + static_cast<size_t>(pos[p]) * d1 + dr;
+                    const float* sr = g.sin + static_cast<size_t>(pos[p]) * d1 + dr;
+                    cs[p % L][0] = *reinterpret_cast<const float4*>(cr);
+                    cs[p % L][1] = *reinterpret_cast<const float4*>(cr + 4);
+                    sn[p % L][0] = *reinterpret_cast<const float4*>(sr);
+                    sn[p % L][1] = *reinterpret_cast<const float4*>(sr + 4);
+                }
+            }
+        };
+        static_for<L>([&](auto p_c) __attribute__((always_inline)) { gather(p_c); });
+        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            const int row = p * RPP + r_in;
+            const int m = m0 + row;
+            if (active && row < BM) {
+                const bool ok = nok && m < g.M;
+                const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
+                const uint4 v = tile_chunk(row, c);
+                uint4 o = v;
+                if (rot) {
+                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
+                    // cos/sin at this chunk's own columns; the partner is the other half.
+                    const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
+                    float own[8], oth[8], res[8];
+                    unpack8(v, own);
+                    unpack8(pv, oth);
+                    const float4 c0 = cs[p % L][0], c1 = cs[p % L][1];
+                    const float4 s0 = sn[p % L][0], s1 = sn[p % L][1];
+                    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float t1 = own[e] * cs[e];
-                    const float t2 = (low ? -oth[e] : oth[e]) * sn[e];
-                    res[e] = t1 + t2;
+                    for (int e = 0; e < 8; ++e) {
+                        const float t1 = own[e] * cv[e];
+                        const float t2 = (low ? -oth[e] : oth[e]) * sv[e];
+                        res[e] = t1 + t2;
+                    }
+                    o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
+                                   big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
                 }
-                o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
-                               big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
-            }
-            if (ok) {
-                if (seg0) {
-                    if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
-                } else if (out1) {
-                    *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
+                if (ok) {
+                    if (seg0) {
+                        if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
+                    } else if (out1) {
+                        *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
+                    }
+                    // |values| are non-negative floats, whose bit patterns order like unsigned ints
+                    if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
                 }
-                // |values| are non-negative floats, whose bit patterns order like unsigned ints
-                if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
             }
-        }
+            gather(std::integral_constant<int, p + L>{});
+        });
         if (g.part_amax) {
             big::lds_barrier();
             for (int r = tid; r < BM; r += SH::NT)

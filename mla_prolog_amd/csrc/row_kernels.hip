@@ -44,37 +44,47 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
     return t;
 }
 
+// Sum over `splits` split-K fp32 partials (8 values at p + sp * stride each, split 0 first)
+// then round to bf16 (the GEMM's output cast point). Loads go out in groups of eight so a
+// group costs one memory latency; the additions stay in split order.
+__device__ __forceinline__ void sum_partials8(const float* p, size_t stride, int splits, float* f) {
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        float4 x[8][2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int sp = min(s0 + j, splits - 1);
+            const float4* q = reinterpret_cast<const float4*>(p + static_cast<size_t>(sp) * stride);
+            x[j][0] = q[0];
+            x[j][1] = q[1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (s0 + j < splits) {
+                s[0] += x[j][0].x; s[1] += x[j][0].y; s[2] += x[j][0].z; s[3] += x[j][0].w;
+                s[4] += x[j][1].x; s[5] += x[j][1].y; s[6] += x[j][1].z; s[7] += x[j][1].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+}
+
 // 8 consecutive down-projection outputs of token t starting at column col, as the fp32
 // values of their bf16 rounding (the GEMM's bf16 output cast point).
 __device__ __forceinline__ void load_a8(const NormArgs& a, int t, int col, float* f) {
     if (a.tail_f32 && col >= a.tail_c0) {
         const int w = a.N1 - a.tail_c0;
-        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < a.tail_splits; ++sp) {
-            const float4* p = reinterpret_cast<const float4*>(
-                a.tail_f32 + (static_cast<size_t>(sp) * a.T + t) * w + (col - a.tail_c0));
-            const float4 x0 = p[0], x1 = p[1];
-            s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
-            s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+        sum_partials8(a.tail_f32 + static_cast<size_t>(t) * w + (col - a.tail_c0),
+                      static_cast<size_t>(a.T) * w, a.tail_splits, f);
         return;
     }
     if (!a.a_f32) {
         unpack8(*reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col), f);
         return;
     }
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < a.k_splits; ++sp) {
-        const float4* p = reinterpret_cast<const float4*>(
-            a.a_f32 + (static_cast<size_t>(sp) * a.T + t) * a.N1 + col);
-        const float4 x0 = p[0], x1 = p[1];
-        s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
-        s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+    sum_partials8(a.a_f32 + static_cast<size_t>(t) * a.N1 + col, static_cast<size_t>(a.T) * a.N1,
+                  a.k_splits, f);
 }
 
 __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
@@ -362,7 +372,26 @@ __global__ __launch_bounds__(kRowThreads) void act_quant_kernel(const uint16_t* 
 
 __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     __shared__ float red[kRowWaves];
+    constexpr int kHeld = 16;  // q chunks a thread loads before the amax is known
     const int t = blockIdx.x;
+    const int QH = a.Dn + a.R;
+    const int cph = QH >> 3, cn = a.Dn >> 3;
+    const int total = a.H * cph;
+    auto chunk_at = [&](int c) -> const uint4* {
+        const int h = c / cph, j = c - h * cph;
+        const size_t th = static_cast<size_t>(t) * a.H + h;
+        return (j < cn) ? reinterpret_cast<const uint4*>(a.q_nope + th * a.Dn + j * 8)
+                        : reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
+    };
+    // the token's q values do not depend on its amax: start fetching them first
+    uint4 held[kHeld];
+    if (a.q_i8) {
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) {
+            const int c = threadIdx.x + k * kRowThreads;
+            if (c < total) held[k] = *chunk_at(c);
+        }
+    }
     float m = 0.f;
     for (int i = threadIdx.x; i < a.n_tiles; i += kRowThreads)
         m = fmaxf(m, a.part_amax[static_cast<size_t>(t) * a.n_tiles + i]);
@@ -370,16 +399,17 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     if (threadIdx.x == 0 && a.q_scale) a.q_scale[t] = amax / 127.0f;
     if (!a.q_i8) return;
     const float mult = amax > 0.f ? 127.0f / amax : 0.f;
-    const int QH = a.Dn + a.R;
-    const int cph = QH >> 3, cn = a.Dn >> 3;
-    const int total = a.H * cph;
-    for (int c = threadIdx.x; c < total; c += kRowThreads) {
+    auto store = [&](int c, const uint4& v) {
         const int h = c / cph, j = c - h * cph;
         const size_t th = static_cast<size_t>(t) * a.H + h;
-        const uint4 v = (j < cn) ? *reinterpret_cast<const uint4*>(a.q_nope + th * a.Dn + j * 8)
-                                 : *reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
         *reinterpret_cast<uint2*>(a.q_i8 + th * QH + j * 8) = quant8(v, mult);
+    };
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) store(c, held[k]);
     }
+    for (int c = threadIdx.x + kHeld * kRowThreads; c < total; c += kRowThreads) store(c, *chunk_at(c));
 }
 
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
