@@ -1,33 +1,30 @@
-// gemm_big.hpp -- MFMA-bound GEMM for large token batches on gfx950: C = A . B^T.
+// gemm_big.hpp -- GEMM C = A . B^T on gfx950 matrix cores with global->LDS DMA staging.
 //
 // A [M, K] holds token activations, B [N, K] the weights (the AT-10 card's b_trans
-// layout), both K-contiguous. One workgroup of four 64-wide waves (2 x 2) computes a
-// BM x BN output tile; each wave owns a (BM/2) x (BN/2) block held in accumulator
-// registers (128 x 128 fp32 = 256 registers per lane at BM = BN = 256), so the
-// workgroup runs alone on its CU with one wave per SIMD.
+// layout), both K-contiguous. One workgroup of WM x WN 64-wide waves computes a BM x BN
+// output tile; each wave owns a (BM/WM) x (BN/WN) block held in accumulator registers.
+// Shapes in use: 256 x 256 with 4 x 2 waves for large token batches (64 x 128 per wave,
+// two waves per SIMD), and 256-row tiles 64 or 96 columns wide with 4 x 1 waves for
+// weight streaming at small batches.
 //
-// Operand staging. A K-stage is 64 bytes of every tile row (32 bf16 or 64 int8):
-// (BM + BN) rows x 64 B = 32 KB at 256 x 256. S stages form a ring in LDS. Every stage
-// is copied HBM -> LDS directly by the buffer unit (global_load_lds_dwordx4: each
-// lane moves 16 bytes and a wave writes 1 KB of consecutive LDS), so no register holds
-// operands in flight and S - 1 stages are in the air while one is multiplied. A lane
-// fetches the global chunk that lands on its fixed LDS slot: 16-byte chunk c of tile
-// row r lives at chunk c ^ swz(r), which spreads the 128-bit operand reads of the 16
-// lanes the LDS serves per cycle over distinct banks.
+// Operand staging. A K-stage is KB bytes of every tile row (KB = 128: 64 bf16 or 128
+// int8), (BM + BN) rows x KB bytes; S stages form a ring in LDS. Every stage is copied
+// global -> LDS directly by the load unit (global_load_lds_dwordx4: each lane moves 16
+// bytes and a wave writes 1 KB of consecutive LDS), so no register holds operands in
+// flight. A lane fetches the global chunk that lands on its fixed LDS slot: 16-byte
+// chunk c of tile row r lives at chunk c ^ swz(r), which spreads the 128-bit operand
+// reads of the 16 lanes the LDS serves per cycle over distinct banks.
 //
-// Per stage a wave runs two k-steps of v_mfma_f32_32x32x16_bf16 (or
+// Per stage a wave runs KB / 32 k-steps of v_mfma_f32_32x32x16_bf16 (or
 // v_mfma_i32_32x32x32_i8). The weight fragment is the MFMA's first operand and the
 // activation fragment its second, so the accumulator is the transposed tile: lane l,
 // register 4g + q holds token (l % 32) and output column 8g + 4(l / 32) + q. Every lane
-// therefore owns runs of four consecutive output columns of its tokens, and the
-// epilogue works in registers: one 8-byte store per run, rotate-half pairs (i, i + 32)
-// in the same lane one fragment apart, and a token's row amax as a lane-local max plus
-// one exchange with lane l ^ 32.
+// therefore owns runs of four consecutive output columns of its tokens.
 //
-// Synchronisation per stage: wait until this wave's copies of the stage have landed
-// (vmcnt), one workgroup barrier (all waves' copies visible, and every wave is done
-// reading the slot the next copy overwrites), issue the copy S - 1 stages ahead,
-// multiply.
+// The k-step schedule is explicit (waits placed by hand, sched_group_barrier templates):
+// one MFMA, then one LDS read of the next k-step's fragments or one copy instruction,
+// and so on, so LDS latency and copy issue hide under the matrix pipe; one workgroup
+// barrier per stage, placed inside the last k-step.
 #pragma once
 
 #include "gemm.hpp"
@@ -76,6 +73,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Workgroup barrier that orders LDS traffic without waiting for outstanding global
 // loads (a __syncthreads() fence would drain the copy ring).
@@ -206,55 +206,109 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             f.x[i] = *reinterpret_cast<const i32x4*>(base + a_rd[ks] + i * 32 * KB);
         });
     };
-    auto multiply = [&](Frags& f) __attribute__((always_inline)) {
-        // Pin the operand fragments to VGPRs: left to itself the register allocator may
-        // park them in AGPRs, which the accumulators fill completely.
+    // Pin a k-step's operand fragments to VGPRs: left to itself the register allocator
+    // may park them in AGPRs, which the accumulators fill. The pins sit at the head of a
+    // k-step (an empty asm is an ordering point for memory instructions), so the reads
+    // and copies after them stay free to interleave with the MFMAs.
+    auto pin = [&](Frags& f) __attribute__((always_inline)) {
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
             big::pin_vgpr(f.w[decltype(j_c)::value]);
         });
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             big::pin_vgpr(f.x[decltype(i_c)::value]);
         });
-        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = decltype(j_c)::value;
+    };
+    // MFMAs of weight fragments [J0, J1) against every activation fragment.
+    auto multiply = [&](Frags& f, auto j0_c, auto j1_c) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
+        static_for<J1 - J0>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = J0 + decltype(j_c)::value;
             static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                 constexpr int i = decltype(i_c)::value;
                 Op::mma(acc[j][i], f.w[j], f.x[i]);
             });
         });
     };
+    // Scheduling template for the region just emitted: N MFMAs, after the i-th of which
+    // go one LDS read while i < NR, else one global->LDS copy while i - NR < NC.
+    auto interleave = [&](auto n_c, auto nr_c, auto nc_c) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value, NR = decltype(nr_c)::value, NC = decltype(nc_c)::value;
+        static_for<N>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if constexpr (i < NR)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            else if constexpr (i - NR < NC)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // Stage j goes to slot j % S and is copied S - 1 stages ahead. The barrier at the top
-    // of iteration kt certifies that stage kt has landed for every wave and that every wave
-    // is done with slot (kt - 1) % S, which the copy of stage kt + S - 1 then reuses.
-    // Inside a stage, the fragments of k-step ks + 1 are read while k-step ks multiplies.
+    // Stage j goes to slot j % S and is copied S - 1 stages ahead. Every k-step first waits
+    // for its own fragments (read during the previous k-step), then issues the next
+    // k-step's reads and its share of the copy of stage kt + S - 1 between its MFMAs. The
+    // stage barrier sits inside the last k-step, after its first half of MFMAs: it
+    // certifies that stage kt + 1 has landed for every wave (each wave first waits for its
+    // own copies) and that every wave is done reading slot kt % S, which the copy issued
+    // in the next stage reuses; the next stage's first reads then run under the second
+    // half. With two slots the whole copy goes out at the head of the stage, so it has
+    // the most time to land; with more it is spread over the k-steps.
     static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         if (s < nk) issue(s, s);
     });
-    int slot = 0;  // kt % S
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + S - 2 < nk)
-            big::wait_vmcnt<(S - 2) * ROUNDS>();
-        else
-            big::wait_vmcnt<0>();
+    constexpr int SPREAD = S == 2 ? 1 : KS;
+    constexpr int NR = FN + FM, NM = FN * FM;
+    Frags f[2];
+    if (nk > 0) {
+        if (nk >= S - 1) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
         big::lds_barrier();
-        // The next copy is spread over the k-steps so that a busy memory pipeline never
-        // holds up all MFMA issue at once.
-        const bool copy = kt + S - 1 < nk;
+        read(smem, std::integral_constant<int, 0>{}, f[0]);
+    }
+    int slot = 0;  // kt % S
+    auto stage = [&](int kt, auto copy_c) __attribute__((always_inline)) {
+        constexpr bool copy = decltype(copy_c)::value;
         const int cslot = slot == 0 ? S - 1 : slot - 1;
+        const int nslot = slot + 1 == S ? 0 : slot + 1;
         const char* base = smem + slot * SH::STAGE;
-        Frags f[2];
-        read(base, std::integral_constant<int, 0>{}, f[0]);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
-            constexpr int r0 = ROUNDS * ks / KS, r1 = ROUNDS * (ks + 1) / KS;
-            if (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
-            if constexpr (ks + 1 < KS) read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
-            multiply(f[ks & 1]);
+            constexpr int r0 = ks < SPREAD ? ROUNDS * ks / SPREAD : ROUNDS;
+            constexpr int r1 = ks < SPREAD ? ROUNDS * (ks + 1) / SPREAD : ROUNDS;
+            constexpr int NC = copy ? r1 - r0 : 0;
+            using I0 = std::integral_constant<int, 0>;
+            using IH = std::integral_constant<int, FN / 2>;
+            using IF = std::integral_constant<int, FN>;
+            big::wait_lgkmcnt0();
+            __builtin_amdgcn_sched_barrier(0);
+            pin(f[ks & 1]);
+            if constexpr (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
+            if constexpr (ks + 1 < KS) {
+                read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
+                multiply(f[ks & 1], I0{}, IF{});
+                interleave(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{},
+                           std::integral_constant<int, NC>{});
+            } else {
+                multiply(f[ks & 1], I0{}, IH{});
+                interleave(std::integral_constant<int, FN / 2 * FM>{},
+                           std::integral_constant<int, 0>{}, std::integral_constant<int, NC>{});
+                const bool more = kt + 1 < nk;
+                if (more) {
+                    if (copy) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
+                    big::lds_barrier();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) read(smem + nslot * SH::STAGE, I0{}, f[(ks + 1) & 1]);
+                multiply(f[ks & 1], IH{}, IF{});
+                interleave(std::integral_constant<int, (FN - FN / 2) * FM>{}, std::integral_constant<int, NR>{},
+                           std::integral_constant<int, 0>{});
+            }
         });
-        slot = slot + 1 == S ? 0 : slot + 1;
-    }
+        slot = nslot;
+    };
+    int kt = 0;
+    for (; kt + S - 1 < nk; ++kt) stage(kt, std::true_type{});
+    for (; kt < nk; ++kt) stage(kt, std::false_type{});
 
     // ------------------------------------------------------------- epilogues --
     // Lane view of the transposed accumulator: token m = mb + 32 i + lr, columns
