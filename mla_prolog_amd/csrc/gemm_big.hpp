@@ -45,6 +45,10 @@ __device__ __forceinline__ int swz(int r) {
         return (r >> 1) & 7;
 }
 
+// Epilogue LDS: the bf16 tile with rows padded by 16 bytes, then one row-amax word per row.
+constexpr int epi_pitch(int bn) { return bn * 2 + 16; }
+constexpr int epi_lds(int bm, int bn) { return bm * epi_pitch(bn) + bm * 4; }
+
 template <int BM, int BN, int WM, int WN, int KB, int S>
 struct Shape {
     static constexpr int NT = 64 * WM * WN;
@@ -57,8 +61,7 @@ struct Shape {
     static constexpr int ROUNDS = ROWS / RROWS;
     static constexpr int STAGE = ROWS * KB;
     static constexpr int MAIN = S * STAGE;
-    static constexpr int EPI_PITCH = BN * 2 + 16;             // bytes per staged bf16 row
-    static constexpr int EPI = BM * EPI_PITCH + BM * 4;       // staged tile + row amax
+    static constexpr int EPI = epi_lds(BM, BN);               // staged tile + row amax
     static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
     static_assert(KB == 64 || KB == 128, "stage row bytes");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave block must be whole 32x32 fragments");
@@ -108,6 +111,209 @@ __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 }  // namespace big
+
+// Output stage of a BM x BN tile held in the transposed accumulator layout (lane l,
+// register 4g + q of fragment (j, i): token 32 i + l % 32 of the wave's rows, column
+// 32 j + 8 g + 4 (l / 32) + q of its columns). `smem` must hold
+// big::epi_lds(BM, BN) bytes and be free: every wave is done with the operand stages.
+template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, typename AccT, int FN, int FM>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN][FM], char* smem,
+                                              int m0, int n0, int n_tile, int split) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    static_assert(FM == TM / 32 && FN == TN / 32, "accumulator shape");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 31, lh = lane >> 5;
+    // Lane view of the transposed accumulator: token m = mb + 32 i + lr, columns
+    // nb + 32 j + 8 g + 4 lh + q for register 4 g + q.
+    const int mb = m0 + wm * TM + lr;
+    const int nb = n0 + wn * TN + 4 * lh;
+
+    // Fragment (j, i) as eight packed bf16 pairs (the GEMM's bf16 output cast), with the
+    // W8A8 dequantisation f32(acc) * (a_scale[m] * b_scale[n]) applied first.
+    auto frag_bf16 = [&](int j, int i, uint32_t* w) __attribute__((always_inline)) {
+        const int m = mb + 32 * i;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            float v[4];
+            if constexpr (sizeof(Tin) == 1) {
+                const int n = nb + 32 * j + 8 * gq;
+                const float as = m < g.M ? g.a_scale[min(m, g.M - 1)] : 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nn = min(n + q, g.N - 1);
+                    const float bs = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
+                    const float sc = as * bs;
+                    v[q] = static_cast<float>(acc[j][i][4 * gq + q]) * sc;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = acc[j][i][4 * gq + q];
+            }
+            w[2 * gq] = big::pack_bf16x2(v[0], v[1]);
+            w[2 * gq + 1] = big::pack_bf16x2(v[2], v[3]);
+        }
+    };
+
+    if constexpr (EPI == Epi::kStoreF32) {
+        // split-K partial sums, fp32 [k_splits][M][ldo]: four consecutive columns per lane
+        float* out = static_cast<float*>(g.out) + static_cast<size_t>(split) * g.M * g.ldo;
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                const int m = mb + 32 * i;
+                if (m < g.M) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int n = nb + 32 * j + 8 * gq;
+                        if (n < g.N)  // N is a multiple of 4
+                            *reinterpret_cast<float4*>(out + static_cast<size_t>(m) * g.ldo + n) =
+                                make_float4(acc[j][i][4 * gq], acc[j][i][4 * gq + 1],
+                                            acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
+                    }
+                }
+            });
+        });
+        return;
+    }
+
+    // The bf16 tile is transposed through LDS (the stage buffers are free now) so that
+    // stores leave as whole 16-byte chunks, a row's chunks on consecutive lanes. Rows are
+    // padded by 16 bytes against bank conflicts.
+    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+    constexpr int PITCH = big::epi_pitch(BN);
+    uint32_t* row_amax = reinterpret_cast<uint32_t*>(smem + BM * PITCH);
+    big::lds_barrier();  // every wave is done reading the last stage
+    static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            uint32_t w[8];
+            frag_bf16(j, i, w);
+            const int row = wm * TM + 32 * i + lr;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int col = wn * TN + 32 * j + 8 * gq + 4 * lh;
+                *reinterpret_cast<uint2*>(smem + row * PITCH + col * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
+            }
+        });
+    });
+    if constexpr (EPI == Epi::kHeads) {
+        for (int r = tid; r < BM; r += NT) row_amax[r] = 0u;
+    }
+    big::lds_barrier();
+
+    auto tile_chunk = [&](int row, int ch) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(smem + row * PITCH + ch * 16);
+    };
+    if constexpr (EPI == Epi::kStoreBf16) {
+        uint16_t* out = static_cast<uint16_t*>(g.out);
+        for (int idx = tid; idx < BM * CPR; idx += NT) {
+            const int row = idx / CPR, c = idx - row * CPR;
+            const int m = m0 + row, n = n0 + 8 * c;
+            if (m < g.M && n < g.N)  // N is a multiple of 8
+                *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) = tile_chunk(row, c);
+        }
+    } else if constexpr (EPI == Epi::kHeads) {
+        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the
+        // rotate-half slice. The host picks tiles that hold whole 8-column chunks of one
+        // segment and a whole rope slice, so the rotate-half partner of a chunk (d1/2
+        // columns away) is in the same tile row.
+        //
+        // A thread keeps one chunk column c for the whole tile and walks the rows (RPP rows
+        // per pass), so its segment, head offset and rope role are fixed. Every gather the
+        // rope needs is issued ahead: all of the thread's token positions at once, and the
+        // cos/sin rows of pass p + L while pass p is rotated.
+        constexpr int RPP = NT / CPR;                 // rows per pass
+        constexpr int PASSES = (BM + RPP - 1) / RPP;
+        constexpr int L = PASSES < 4 ? PASSES : 4;        // cos/sin lookahead (passes)
+        const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
+        const int pc = d1 / 16;  // partner distance in chunks
+        uint16_t* out0 = static_cast<uint16_t*>(g.out0);
+        uint16_t* out1 = static_cast<uint16_t*>(g.out1);
+        const int c = tid % CPR, r_in = tid / CPR;
+        const bool active = tid < RPP * CPR;
+        const int n = n0 + 8 * c;
+        const bool nok = active && n < g.N;
+        const int h = n / HW;
+        const int d = n - h * HW;
+        const bool seg0 = d < d0;
+        const int dr = d - d0;  // column within seg1
+        const bool rot = nok && !seg0 && g.rope;
+        const bool low = dr < (d1 >> 1);
+        int pos[PASSES];
+        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            const int m = min(m0 + p * RPP + r_in, g.M - 1);
+            pos[p] = rot ? clamp_pos(g.positions[m], g.max_pos) : 0;
+        });
+        float4 cs[L][2], sn[L][2];
+        auto gather = [&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            if constexpr (p < PASSES) {
+                if (rot) {
+                    const float* cr = g.cos + static_cast<size_t>(pos[p]) * d1 + dr;
+                    const float* sr = g.sin + static_cast<size_t>(pos[p]) * d1 + dr;
+                    cs[p % L][0] = *reinterpret_cast<const float4*>(cr);
+                    cs[p % L][1] = *reinterpret_cast<const float4*>(cr + 4);
+                    sn[p % L][0] = *reinterpret_cast<const float4*>(sr);
+                    sn[p % L][1] = *reinterpret_cast<const float4*>(sr + 4);
+                }
+            }
+        };
+        static_for<L>([&](auto p_c) __attribute__((always_inline)) { gather(p_c); });
+        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int p = decltype(p_c)::value;
+            const int row = p * RPP + r_in;
+            const int m = m0 + row;
+            if (active && row < BM) {
+                const bool ok = nok && m < g.M;
+                const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
+                const uint4 v = tile_chunk(row, c);
+                uint4 o = v;
+                if (rot) {
+                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
+                    // cos/sin at this chunk's own columns; the partner is the other half.
+                    const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
+                    float own[8], oth[8], res[8];
+                    unpack8(v, own);
+                    unpack8(pv, oth);
+                    const float4 c0 = cs[p % L][0], c1 = cs[p % L][1];
+                    const float4 s0 = sn[p % L][0], s1 = sn[p % L][1];
+                    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float t1 = own[e] * cv[e];
+                        const float t2 = (low ? -oth[e] : oth[e]) * sv[e];
+                        res[e] = t1 + t2;
+                    }
+                    o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
+                                   big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
+                }
+                if (ok) {
+                    if (seg0) {
+                        if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
+                    } else if (out1) {
+                        *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
+                    }
+                    // |values| are non-negative floats, whose bit patterns order like unsigned ints
+                    if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
+                }
+            }
+            gather(std::integral_constant<int, p + L>{});
+        });
+        if (g.part_amax) {
+            big::lds_barrier();
+            for (int r = tid; r < BM; r += NT)
+                if (m0 + r < g.M)
+                    g.part_amax[static_cast<size_t>(m0 + r) * g.n_tiles + n_tile] = __uint_as_float(row_amax[r]);
+        }
+    }
+}
 
 template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
@@ -310,194 +516,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     for (; kt + S - 1 < nk; ++kt) stage(kt, std::true_type{});
     for (; kt < nk; ++kt) stage(kt, std::false_type{});
 
-    // ------------------------------------------------------------- epilogues --
-    // Lane view of the transposed accumulator: token m = mb + 32 i + lr, columns
-    // nb + 32 j + 8 g + 4 lh + q for register 4 g + q.
-    const int mb = m0 + wm * TM + lr;
-    const int nb = n0 + wn * TN + 4 * lh;
-
-    // Fragment (j, i) as eight packed bf16 pairs (the GEMM's bf16 output cast), with the
-    // W8A8 dequantisation f32(acc) * (a_scale[m] * b_scale[n]) applied first.
-    auto frag_bf16 = [&](int j, int i, uint32_t* w) __attribute__((always_inline)) {
-        const int m = mb + 32 * i;
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            float v[4];
-            if constexpr (sizeof(Tin) == 1) {
-                const int n = nb + 32 * j + 8 * gq;
-                const float as = m < g.M ? g.a_scale[min(m, g.M - 1)] : 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nn = min(n + q, g.N - 1);
-                    const float bs = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
-                    const float sc = as * bs;
-                    v[q] = static_cast<float>(acc[j][i][4 * gq + q]) * sc;
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = acc[j][i][4 * gq + q];
-            }
-            w[2 * gq] = big::pack_bf16x2(v[0], v[1]);
-            w[2 * gq + 1] = big::pack_bf16x2(v[2], v[3]);
-        }
-    };
-
-    if constexpr (EPI == Epi::kStoreF32) {
-        // split-K partial sums, fp32 [k_splits][M][ldo]: four consecutive columns per lane
-        float* out = static_cast<float*>(g.out) + static_cast<size_t>(split) * g.M * g.ldo;
-        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = decltype(j_c)::value;
-            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-                constexpr int i = decltype(i_c)::value;
-                const int m = mb + 32 * i;
-                if (m < g.M) {
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int n = nb + 32 * j + 8 * gq;
-                        if (n < g.N)  // N is a multiple of 4
-                            *reinterpret_cast<float4*>(out + static_cast<size_t>(m) * g.ldo + n) =
-                                make_float4(acc[j][i][4 * gq], acc[j][i][4 * gq + 1],
-                                            acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
-                    }
-                }
-            });
-        });
-        return;
-    }
-
-    // The bf16 tile is transposed through LDS (the stage buffers are free now) so that
-    // stores leave as whole 16-byte chunks, a row's chunks on consecutive lanes. Rows are
-    // padded by 16 bytes against bank conflicts.
-    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-    constexpr int PITCH = SH::EPI_PITCH;
-    uint32_t* row_amax = reinterpret_cast<uint32_t*>(smem + BM * PITCH);
-    big::lds_barrier();  // every wave is done reading the last stage
-    static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-        constexpr int j = decltype(j_c)::value;
-        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-            constexpr int i = decltype(i_c)::value;
-            uint32_t w[8];
-            frag_bf16(j, i, w);
-            const int row = wm * TM + 32 * i + lr;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int col = wn * TN + 32 * j + 8 * gq + 4 * lh;
-                *reinterpret_cast<uint2*>(smem + row * PITCH + col * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
-            }
-        });
-    });
-    if constexpr (EPI == Epi::kHeads) {
-        for (int r = tid; r < BM; r += SH::NT) row_amax[r] = 0u;
-    }
-    big::lds_barrier();
-
-    auto tile_chunk = [&](int row, int ch) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(smem + row * PITCH + ch * 16);
-    };
-    if constexpr (EPI == Epi::kStoreBf16) {
-        uint16_t* out = static_cast<uint16_t*>(g.out);
-        for (int idx = tid; idx < BM * CPR; idx += SH::NT) {
-            const int row = idx / CPR, c = idx - row * CPR;
-            const int m = m0 + row, n = n0 + 8 * c;
-            if (m < g.M && n < g.N)  // N is a multiple of 8
-                *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) = tile_chunk(row, c);
-        }
-    } else if constexpr (EPI == Epi::kHeads) {
-        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the
-        // rotate-half slice. The host picks tiles that hold whole 8-column chunks of one
-        // segment and a whole rope slice, so the rotate-half partner of a chunk (d1/2
-        // columns away) is in the same tile row.
-        //
-        // A thread keeps one chunk column c for the whole tile and walks the rows (RPP rows
-        // per pass), so its segment, head offset and rope role are fixed. Every gather the
-        // rope needs is issued ahead: all of the thread's token positions at once, and the
-        // cos/sin rows of pass p + L while pass p is rotated.
-        constexpr int RPP = SH::NT / CPR;                 // rows per pass
-        constexpr int PASSES = (BM + RPP - 1) / RPP;
-        constexpr int L = PASSES < 4 ? PASSES : 4;        // cos/sin lookahead (passes)
-        const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
-        const int pc = d1 / 16;  // partner distance in chunks
-        uint16_t* out0 = static_cast<uint16_t*>(g.out0);
-        uint16_t* out1 = static_cast<uint16_t*>(g.out1);
-        const int c = tid % CPR, r_in = tid / CPR;
-        const bool active = tid < RPP * CPR;
-        const int n = n0 + 8 * c;
-        const bool nok = active && n < g.N;
-        const int h = n / HW;
-        const int d = n - h * HW;
-        const bool seg0 = d < d0;
-        const int dr = d - d0;  // column within seg1
-        const bool rot = nok && !seg0 && g.rope;
-        const bool low = dr < (d1 >> 1);
-        int pos[PASSES];
-        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            const int m = min(m0 + p * RPP + r_in, g.M - 1);
-            pos[p] = rot ? clamp_pos(g.positions[m], g.max_pos) : 0;
-        });
-        float4 cs[L][2], sn[L][2];
-        auto gather = [&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            if constexpr (p < PASSES) {
-                if (rot) {
-                    const float* cr = g.cos + static_cast<size_t>(pos[p]) * d1 + dr;
-                    const float* sr = g.sin + static_cast<size_t>(pos[p]) * d1 + dr;
-                    cs[p % L][0] = *reinterpret_cast<const float4*>(cr);
-                    cs[p % L][1] = *reinterpret_cast<const float4*>(cr + 4);
-                    sn[p % L][0] = *reinterpret_cast<const float4*>(sr);
-                    sn[p % L][1] = *reinterpret_cast<const float4*>(sr + 4);
-                }
-            }
-        };
-        static_for<L>([&](auto p_c) __attribute__((always_inline)) { gather(p_c); });
-        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            const int row = p * RPP + r_in;
-            const int m = m0 + row;
-            if (active && row < BM) {
-                const bool ok = nok && m < g.M;
-                const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
-                const uint4 v = tile_chunk(row, c);
-                uint4 o = v;
-                if (rot) {
-                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
-                    // cos/sin at this chunk's own columns; the partner is the other half.
-                    const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
-                    float own[8], oth[8], res[8];
-                    unpack8(v, own);
-                    unpack8(pv, oth);
-                    const float4 c0 = cs[p % L][0], c1 = cs[p % L][1];
-                    const float4 s0 = sn[p % L][0], s1 = sn[p % L][1];
-                    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float t1 = own[e] * cv[e];
-                        const float t2 = (low ? -oth[e] : oth[e]) * sv[e];
-                        res[e] = t1 + t2;
-                    }
-                    o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
-                                   big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
-                }
-                if (ok) {
-                    if (seg0) {
-                        if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
-                    } else if (out1) {
-                        *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
-                    }
-                    // |values| are non-negative floats, whose bit patterns order like unsigned ints
-                    if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
-                }
-            }
-            gather(std::integral_constant<int, p + L>{});
-        });
-        if (g.part_amax) {
-            big::lds_barrier();
-            for (int r = tid; r < BM; r += SH::NT)
-                if (m0 + r < g.M)
-                    g.part_amax[static_cast<size_t>(m0 + r) * g.n_tiles + n_tile] = __uint_as_float(row_amax[r]);
-        }
-    }
+    tile_epilogue<Tin, BM, BN, WM, WN, EPI>(g, acc, smem, m0, n0, n_tile, split);
 }
 
 }  // namespace mlap

@@ -70,6 +70,27 @@ __device__ __forceinline__ void sum_partials8(const float* p, size_t stride, int
     for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
 }
 
+// sum_partials8 with the split count known at compile time: straight-line code, so the
+// loads of several chunks can all be in flight before the first sum.
+template <int SPL>
+__device__ __forceinline__ void sum_partials8_n(const float* p, size_t stride, float* f) {
+    float4 x[SPL][2];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const float4* q = reinterpret_cast<const float4*>(p + static_cast<size_t>(j) * stride);
+        x[j][0] = q[0];
+        x[j][1] = q[1];
+    }
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        s[0] += x[j][0].x; s[1] += x[j][0].y; s[2] += x[j][0].z; s[3] += x[j][0].w;
+        s[4] += x[j][1].x; s[5] += x[j][1].y; s[6] += x[j][1].z; s[7] += x[j][1].w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s[e]));
+}
+
 // 8 consecutive down-projection outputs of token t starting at column col, as the fp32
 // values of their bf16 rounding (the GEMM's bf16 output cast point).
 __device__ __forceinline__ void load_a8(const NormArgs& a, int t, int col, float* f) {
@@ -212,6 +233,227 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
         }
         if (tid == 0) a.qn_scale[t] = amax / 127.0f;
     }
+}
+
+// The same stage for small batches, one workgroup per token, shaped for latency: the
+// token's whole input (down-projection values, gamma chunks, the rope slice and its
+// position) is requested in one burst before anything is reduced, and the cos/sin row
+// right after the position returns, so a token costs two memory round trips instead of
+// one per dependent step. Thread i owns q chunks i + 256 c (c < QC) and kv chunks
+// i + 256 c (c < KC); chunk indexes past a segment are clamped for the loads (in bounds,
+// straight-line code) and masked out of the sums and stores. SPL > 0 selects SPL fp32
+// split-K partials as input, SPL = 0 the bf16 down-projection output; no tail partials.
+template <int QC, int KC, int SPL>
+__device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* red) {
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
+    const int half = a.R >> 1;
+    // A chunk's raw input: SPL pairs of float4 partials, or one uint4 of bf16.
+    constexpr int NX = SPL > 0 ? SPL : 1;
+    struct Raw {
+        float4 x[NX][2];
+        uint4 b;
+    };
+    auto fetch = [&](int col, Raw& r) __attribute__((always_inline)) {
+        if constexpr (SPL > 0) {
+            const float* p = a.a_f32 + static_cast<size_t>(t) * a.N1 + col;
+            const size_t stride = static_cast<size_t>(a.T) * a.N1;
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                const float4* q = reinterpret_cast<const float4*>(p + static_cast<size_t>(j) * stride);
+                r.x[j][0] = q[0];
+                r.x[j][1] = q[1];
+            }
+        } else {
+            r.b = *reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col);
+        }
+    };
+    // the chunk's 8 values as the fp32 of their bf16 rounding (splits summed in order)
+    auto finish = [&](const Raw& r, float* f) __attribute__((always_inline)) {
+        if constexpr (SPL > 0) {
+            float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < SPL; ++j) {
+                s8[0] += r.x[j][0].x; s8[1] += r.x[j][0].y; s8[2] += r.x[j][0].z; s8[3] += r.x[j][0].w;
+                s8[4] += r.x[j][1].x; s8[5] += r.x[j][1].y; s8[6] += r.x[j][1].z; s8[7] += r.x[j][1].w;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s8[e]));
+        } else {
+            unpack8(r.b, f);
+        }
+    };
+
+    // round trip 1: everything that depends on no other load, all requested before any use
+    const bool rope = a.k_pe != nullptr && half >= 8;
+    const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
+    Raw rq[QC > 0 ? QC : 1], rkv[KC], r1, r2;
+    uint4 gq[QC > 0 ? QC : 1], gkv[KC];
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        const int ch = min(tid + kRowThreads * c, nq - 1);
+        fetch(ch * 8, rq[c]);
+        gq[c] = *reinterpret_cast<const uint4*>(a.gamma_q + ch * 8);
+    });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        const int ch = min(tid + kRowThreads * c, nkv - 1);
+        fetch(a.Lq + ch * 8, rkv[c]);
+        gkv[c] = *reinterpret_cast<const uint4*>(a.gamma_kv + ch * 8);
+    });
+    const bool roper = rope && tid < (half >> 3);
+    const int i0 = rope ? min(tid, (half >> 3) - 1) * 8 : 0;
+    if (rope) {
+        fetch(a.Lq + a.Lkv + i0, r1);
+        fetch(a.Lq + a.Lkv + half + i0, r2);
+    }
+    // round trip 2: the token's cos/sin row
+    float4 cl[2], ch_[2], sl[2], sh[2];
+    if (rope) {
+        const float* cr = a.cos + static_cast<size_t>(pos) * a.R;
+        const float* sr = a.sin + static_cast<size_t>(pos) * a.R;
+        cl[0] = *reinterpret_cast<const float4*>(cr + i0);
+        cl[1] = *reinterpret_cast<const float4*>(cr + i0 + 4);
+        ch_[0] = *reinterpret_cast<const float4*>(cr + half + i0);
+        ch_[1] = *reinterpret_cast<const float4*>(cr + half + i0 + 4);
+        sl[0] = *reinterpret_cast<const float4*>(sr + i0);
+        sl[1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
+        sh[0] = *reinterpret_cast<const float4*>(sr + half + i0);
+        sh[1] = *reinterpret_cast<const float4*>(sr + half + i0 + 4);
+    }
+
+    float qv[QC > 0 ? QC : 1][8], kv[KC][8], x1[8], x2[8];
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) { finish(rq[decltype(c_c)::value], qv[decltype(c_c)::value]); });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) { finish(rkv[decltype(c_c)::value], kv[decltype(c_c)::value]); });
+    if (rope) {
+        finish(r1, x1);
+        finish(r2, x2);
+    }
+
+    // RMS statistics: per thread in element order, then the fixed-order block sum
+    float sq = 0.f, skv = 0.f;
+    const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
+    const float invkv = 1.0f / static_cast<float>(a.Lkv);
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        if (tid + kRowThreads * c < nq) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = qv[c][e] * qv[c][e];
+                sq += p * invq;
+            }
+        }
+    });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        if (tid + kRowThreads * c < nkv) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float p = kv[c][e] * kv[c][e];
+                skv += p * invkv;
+            }
+        }
+    });
+    const float msq = QC > 0 ? block_sum(sq, red) : 0.f;
+    const float mskv = block_sum(skv, red);
+    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
+    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+
+    float qmax = 0.f, kvmax = 0.f;
+    uint4 qo[QC > 0 ? QC : 1], kvo[KC];
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        const int ch = tid + kRowThreads * c;
+        float g[8], o[8];
+        unpack8(gq[c], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float y = qv[c][e] * rstd_q;
+            o[e] = y * g[e];
+        }
+        qo[c] = pack8(o);
+        if (ch < nq) {
+            if (a.q_norm) *reinterpret_cast<uint4*>(a.q_norm + static_cast<size_t>(t) * a.Lq + ch * 8) = qo[c];
+            qmax = fmaxf(qmax, absmax8(qo[c]));
+        }
+    });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+        constexpr int c = decltype(c_c)::value;
+        const int ch = tid + kRowThreads * c;
+        float g[8], o[8];
+        unpack8(gkv[c], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float y = kv[c][e] * rstd_kv;
+            o[e] = y * g[e];
+        }
+        kvo[c] = pack8(o);
+        if (ch < nkv) {
+            if (a.kv_norm) *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + ch * 8) = kvo[c];
+            kvmax = fmaxf(kvmax, absmax8(kvo[c]));
+        }
+    });
+
+    // rotate-half RoPE of the k_pe slice (pairs i, i + R/2)
+    if (roper) {
+        const float cv[8] = {cl[0].x, cl[0].y, cl[0].z, cl[0].w, cl[1].x, cl[1].y, cl[1].z, cl[1].w};
+        const float chv[8] = {ch_[0].x, ch_[0].y, ch_[0].z, ch_[0].w, ch_[1].x, ch_[1].y, ch_[1].z, ch_[1].w};
+        const float sv[8] = {sl[0].x, sl[0].y, sl[0].z, sl[0].w, sl[1].x, sl[1].y, sl[1].z, sl[1].w};
+        const float shv[8] = {sh[0].x, sh[0].y, sh[0].z, sh[0].w, sh[1].x, sh[1].y, sh[1].z, sh[1].w};
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float p1 = x1[e] * cv[e];
+            float p2 = (-x2[e]) * sv[e];
+            lo[e] = p1 + p2;
+            float p3 = x2[e] * chv[e];
+            float p4 = x1[e] * shv[e];
+            hi[e] = p3 + p4;
+        }
+        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
+        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
+        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+    }
+
+    // per-token INT8 quant of kv_norm
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+        const float amax = block_max(kvmax, red);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+        static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_c)::value;
+            const int ch = tid + kRowThreads * c;
+            if (ch < nkv) {
+                const uint2 codes = quant8(kvo[c], mult);
+                const size_t off = static_cast<size_t>(t) * a.Lkv + ch * 8;
+                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+            }
+        });
+        if (tid == 0) {
+            const float sc = amax / 127.0f;
+            if (a.kv_scale) a.kv_scale[t] = sc;
+            if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+        }
+    }
+    // W8A8: per-token activation quant of q_norm for the int8 up projection
+    if (QC > 0 && a.qn_i8) {
+        const float amax = block_max(qmax, red);
+        const float mult = amax > 0.f ? 127.0f / amax : 0.f;
+        static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_c)::value;
+            const int ch = tid + kRowThreads * c;
+            if (ch < nq)
+                *reinterpret_cast<uint2*>(a.qn_i8 + static_cast<size_t>(t) * a.Lq + ch * 8) = quant8(qo[c], mult);
+        });
+        if (tid == 0) a.qn_scale[t] = amax / 127.0f;
+    }
+}
+
+template <int QC, int KC, int SPL>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void norm_rope_block_kernel(NormArgs a) {
+    __shared__ float red[kRowWaves];
+    norm_rope_block_body<QC, KC, SPL>(a, red);
 }
 
 // Same stage with one 64-wide wave per token (four tokens per workgroup) for segment
@@ -428,6 +670,19 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
         MLAP_NORM_WAVE(1, 1) MLAP_NORM_WAVE(2, 1) MLAP_NORM_WAVE(3, 1) MLAP_NORM_WAVE(4, 1)
         MLAP_NORM_WAVE(3, 2) MLAP_NORM_WAVE(4, 2) MLAP_NORM_WAVE(2, 2) MLAP_NORM_WAVE(1, 2)
 #undef MLAP_NORM_WAVE
+    }
+    const int qb = (a.Lq / 8 + kRowThreads - 1) / kRowThreads, kb = (a.Lkv / 8 + kRowThreads - 1) / kRowThreads;
+    const int spl = a.a_f32 ? a.k_splits : 0;
+    if (!a.tail_f32 && a.R / 16 <= kRowThreads && kb == 1 && qb <= 1) {
+#define MLAP_NORM_BLOCK(Q, P)                                                                      \
+    if (qb == Q && spl == P) {                                                                     \
+        hipLaunchKernelGGL((norm_rope_block_kernel<Q, 1, P>), dim3(a.T), dim3(kRowThreads), 0, s, a); \
+        return hipGetLastError();                                                                  \
+    }
+        MLAP_NORM_BLOCK(0, 0) MLAP_NORM_BLOCK(1, 0) MLAP_NORM_BLOCK(0, 2) MLAP_NORM_BLOCK(1, 2)
+        MLAP_NORM_BLOCK(0, 4) MLAP_NORM_BLOCK(1, 4) MLAP_NORM_BLOCK(0, 7) MLAP_NORM_BLOCK(1, 7)
+        MLAP_NORM_BLOCK(0, 8) MLAP_NORM_BLOCK(1, 8)
+#undef MLAP_NORM_BLOCK
     }
     hipLaunchKernelGGL(norm_rope_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
