@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DOMINANT = "gemm_up_q"
-KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "gemm_kernels.hip"]
+KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "gemm_big.hpp", "gemm_kernels.hip", "launch.hpp", "mlap_host.hip"]
 
 
 def up_q_work(cfg, T):

@@ -612,9 +612,12 @@ __global__ __launch_bounds__(kRowThreads) void act_quant_kernel(const uint16_t* 
     if (threadIdx.x == 0) scale[t] = amax / 127.0f;
 }
 
+// kHeld q chunks per thread are fetched before the amax is known (a small batch has one
+// workgroup per CU and lives on latency); kHeld = 0 streams the row after the amax, which
+// keeps registers low and occupancy high for large batches.
+template <int kHeld>
 __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     __shared__ float red[kRowWaves];
-    constexpr int kHeld = 16;  // q chunks a thread loads before the amax is known
     const int t = blockIdx.x;
     const int QH = a.Dn + a.R;
     const int cph = QH >> 3, cn = a.Dn >> 3;
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
                         : reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
     };
     // the token's q values do not depend on its amax: start fetching them first
-    uint4 held[kHeld];
+    uint4 held[kHeld > 0 ? kHeld : 1];
     if (a.q_i8) {
 #pragma unroll
         for (int k = 0; k < kHeld; ++k) {
@@ -697,7 +700,10 @@ hipError_t launch_act_quant(const uint16_t* x, int T, int K, int8_t* codes, floa
 
 hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_q_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    if (a.T >= 1024)
+        hipLaunchKernelGGL(quant_q_kernel<0>, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(quant_q_kernel<16>, dim3(a.T), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
 }
 
