@@ -46,6 +46,15 @@ def up_q_work(cfg, T):
     return flops, byts
 
 
+def up_kv_work(cfg, T):
+    """Algorithmic FLOPs and bytes of one gemm_up_kv launch (KV-Prolog mode): the kv_b weight
+    once, kv_norm in, k_nope and value out (bf16)."""
+    N = cfg.n_heads * (cfg.nope_dim + cfg.v_dim)
+    flops = 2.0 * T * N * cfg.kv_lora
+    byts = N * cfg.kv_lora * 2 + T * cfg.kv_lora * 2 + T * N * 2
+    return flops, byts
+
+
 def path_work(cfg, T):
     """Algorithmic FLOPs and HBM bytes of the whole prolog (weights, x and outputs once)."""
     H, Dn, R, Lq, Lkv, Hd = cfg.n_heads, cfg.nope_dim, cfg.rope_dim, cfg.q_lora, cfg.kv_lora, cfg.hidden
@@ -102,22 +111,26 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT):
         p.run(sets[i % rotate], outputs=outs, workspace=ws)
     torch.cuda.synchronize()
     p.timing_begin(dominant, steps)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
     for i in range(steps):
         p.run(sets[i % rotate], outputs=outs, workspace=ws)
-    stop.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / steps
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    pct = {"p10": round(per[int(0.1 * (steps - 1))], 5), "p50": round(per[int(0.5 * (steps - 1))], 5),
+           "p90": round(per[int(0.9 * (steps - 1))], 5)}
     kms = p.timing_end()
     k_avg = sum(kms) / len(kms)
     del sets
-    return cfg, ms_step, k_avg, len(kms)
+    return cfg, ms_step, k_avg, pct
 
 
 def roofline_for(cfg, T, k_ms, workload):
-    flops, byts = up_q_work(cfg, T)
+    kv_mode = cfg.q_lora == 0
+    flops, byts = (up_kv_work if kv_mode else up_q_work)(cfg, T)
+    kernel = "gemm_up_kv" if kv_mode else DOMINANT
     intensity = flops / byts
     peak_c = PEAK_I8_TOPS if cfg.w8a8 else PEAK_BF16_TFLOPS
     ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -126,11 +139,11 @@ def roofline_for(cfg, T, k_ms, workload):
         ach = flops / (k_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_c,
                 "unit": "TOP/s" if cfg.w8a8 else "TFLOP/s", "frac": round(ach / peak_c, 4),
-                "traffic": traffic, "kernel": DOMINANT, "kernel_ms": round(k_ms, 5),
+                "traffic": traffic, "kernel": kernel, "kernel_ms": round(k_ms, 5),
                 "algorithmic_flops": flops, "algorithmic_bytes": byts}
     ach = byts / (k_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": DOMINANT,
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kernel,
             "kernel_ms": round(k_ms, 5), "algorithmic_flops": flops, "algorithmic_bytes": byts}
 
 
@@ -165,6 +178,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode",
+                    help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rotate", type=int, default=1,
@@ -189,7 +204,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg, ms, k_ms, nk = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate)
+    cfg, ms, k_ms, pct = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate)
     T = cfg.T
     pf, pb = path_work(cfg, T)
     line = {
@@ -200,6 +215,7 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -215,18 +231,38 @@ def main():
                  "frac_bf16_peak": round(pf / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     if a.decode_workload:
-        dcfg, dms, dk_ms, _ = bench_workload(a.decode_workload, a.decode_steps, a.warmup, rotate=4)
+        dcfg, dms, dk_ms, dpct = bench_workload(a.decode_workload, a.decode_steps, a.warmup, rotate=4)
         dpf, dpb = path_work(dcfg, dcfg.T)
         line["decode"] = {
             "workload": "%s: DeepSeek-V3 MLA Prolog decode batch, T=%d, 4 rotating weight sets"
                         % (dcfg.name, dcfg.T),
             "value": round(dcfg.T / (dms * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(dms, 5), "steps": a.decode_steps,
+            "ms_per_step": round(dms, 5), "step_ms_percentiles": dpct, "steps": a.decode_steps,
             "roofline": roofline_for(dcfg, dcfg.T, dk_ms, dcfg.name),
             "path": {"hbm_gbs": round(dpb / (dms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(dpb / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": dpb},
         }
+    extra = {}
+    for name in [w for w in a.extra_workloads.split(",") if w]:
+        import synth
+        ecfg0 = synth.get_config(name)
+        dom = "gemm_up_kv" if ecfg0.q_lora == 0 else DOMINANT
+        # decode-sized batches rotate weight sets so the last-level cache cannot hold them
+        rot = 4 if ecfg0.T <= 512 else 1
+        ecfg, ems, ek_ms, epct = bench_workload(name, a.steps, a.warmup, rotate=rot, dominant=dom)
+        epf, epb = path_work(ecfg, ecfg.T) if ecfg.q_lora else (None, None)
+        ent = {"value": round(ecfg.T / (ems * 1e-3), 1), "unit": "tokens/s", "tokens": ecfg.T,
+               "dtype": "int8" if ecfg.w8a8 else "bf16", "ms_per_step": round(ems, 5),
+               "step_ms_percentiles": epct, "steps": a.steps, "rotating_sets": rot,
+               "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
+        if epf:
+            peak = PEAK_I8_TOPS if ecfg.w8a8 else PEAK_BF16_TFLOPS
+            ent["path"] = {"tops": round(epf / (ems * 1e-3) / 1e12, 2),
+                           "frac_peak": round(epf / (ems * 1e-3) / 1e12 / peak, 4)}
+        extra[name] = ent
+    if extra:
+        line["extra_workloads"] = extra
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
     print(json.dumps(line), flush=True)
