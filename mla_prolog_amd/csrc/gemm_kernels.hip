@@ -71,7 +71,13 @@ hipError_t launch_big_one(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 int big_tile_n(BigShape shape) {
-    return shape == BigShape::kWide ? 256 : shape == BigShape::kHalfHead ? 96 : 64;
+    switch (shape) {
+        case BigShape::kWide: return 256;
+        case BigShape::kHalfHead: return 96;
+        case BigShape::kSplitK: return 64;
+        case BigShape::kNarrowHeads: return 32;
+    }
+    return 0;
 }
 
 bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
@@ -94,6 +100,10 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
                    g.d0 >= 96 && g.d0 % 8 == 0 && g.d1 == 192 - g.d0 && g.d1 % 16 == 0;
         case BigShape::kSplitK:
             return t == InType::kBf16 && epi == Epi::kStoreF32 && g.N % 4 == 0 && g.ldo % 4 == 0;
+        case BigShape::kNarrowHeads:
+            // 32-column tiles that never straddle a segment; no rotate-half pairs
+            return t == InType::kBf16 && epi == Epi::kHeads && !g.rope && g.head_w % 32 == 0 &&
+                   g.d0 % 32 == 0 && g.d1 % 8 == 0;
     }
     return false;
 }
@@ -125,6 +135,9 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
         return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
     }
     if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
+    // Weight-streaming shapes cover the whole batch in one row tile; at most 64 tokens take
+    // 64-row tiles (two waves), so no copy bandwidth goes to clamped duplicate rows.
+    const bool m64 = g.M <= 64;
     switch (shape) {
         case BigShape::kWide:
             if (t == InType::kBf16)
@@ -133,9 +146,14 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
             return epi == Epi::kStoreBf16 ? launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s)
                                           : launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
         case BigShape::kHalfHead:
-            return launch_big_one<uint16_t, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
+            return m64 ? launch_big_one<uint16_t, 64, 96, 2, 1, 3, Epi::kHeads>(g, s)
+                       : launch_big_one<uint16_t, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
         case BigShape::kSplitK:
-            return launch_big_one<uint16_t, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
+            return m64 ? launch_big_one<uint16_t, 64, 64, 2, 1, 3, Epi::kStoreF32>(g, s)
+                       : launch_big_one<uint16_t, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
+        case BigShape::kNarrowHeads:
+            return m64 ? launch_big_one<uint16_t, 64, 32, 2, 1, 3, Epi::kHeads>(g, s)
+                       : launch_big_one<uint16_t, 256, 32, 4, 1, 3, Epi::kHeads>(g, s);
     }
     return hipErrorInvalidValue;
 }

@@ -30,7 +30,7 @@ hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi ep
 // With kHeads, g.n_tiles must be ceil(N / big_tile_n(shape)) (one partial amax per token
 // and tile). gemm_big_fits says whether the shapes suit it (K a whole number of 128-byte
 // stages per split).
-enum class BigShape : int { kWide = 0, kHalfHead = 1, kSplitK = 2 };
+enum class BigShape : int { kWide = 0, kHalfHead = 1, kSplitK = 2, kNarrowHeads = 3 };
 constexpr int kBigTile = 256;
 int big_tile_n(BigShape shape);
 bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape = BigShape::kWide);

@@ -75,7 +75,7 @@ struct Plan {
     // (the k_pe slice at V3 and V2-Lite widths) run as a split-K GEMM with fp32 partials
     // that the row kernel sums, instead of a second, mostly idle round of tiles.
     int tail_c0 = 0, tail_splits = 0;
-    BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide;
+    BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide, kv_shape = BigShape::kWide;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
 };
 
@@ -175,6 +175,18 @@ struct mlap_prolog {
                 if (gemm_big_fits(u, it, Epi::kHeads, BigShape::kHalfHead)) {
                     p.big_q = true;
                     p.q_shape = BigShape::kHalfHead;
+                }
+            }
+            if (cfg.v_dim > 0) {
+                GemmArgs u{};
+                u.K = cfg.kv_lora;
+                u.head_w = KH;
+                u.d0 = cfg.nope_dim;
+                u.d1 = cfg.v_dim;
+                u.rope = 0;
+                if (gemm_big_fits(u, it, Epi::kHeads, BigShape::kNarrowHeads)) {
+                    p.big_kv = true;
+                    p.kv_shape = BigShape::kNarrowHeads;
                 }
             }
         }
@@ -547,7 +559,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         } else {
             u.A = kvn;
         }
-        MLAP_LAUNCH(kKGemmUpKv, plan.big_kv ? launch_gemm_big(u, it, Epi::kHeads, s)
+        MLAP_LAUNCH(kKGemmUpKv, plan.big_kv ? launch_gemm_big(u, it, Epi::kHeads, s, plan.kv_shape)
                                             : launch_gemm(u, it, plan.up_kv, Epi::kHeads, s));
     }
 

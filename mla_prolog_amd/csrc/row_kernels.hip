@@ -249,19 +249,24 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
     const int tid = threadIdx.x;
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
     const int half = a.R >> 1;
-    // A chunk's raw input: SPL pairs of float4 partials, or one uint4 of bf16.
-    constexpr int NX = SPL > 0 ? SPL : 1;
+    // A chunk's raw input: up to 8 splits of float4 pairs (one fetch group), or one uint4 of
+    // bf16. More than 8 splits are fetched in groups of 8 (a round trip per group) so the
+    // registers in flight stay bounded; the sums still run in split order.
+    constexpr int GS = SPL > 8 ? 8 : (SPL > 0 ? SPL : 1);
+    constexpr int NG = SPL > 0 ? (SPL + 7) / 8 : 1;
     struct Raw {
-        float4 x[NX][2];
+        float4 x[GS][2];
         uint4 b;
     };
-    auto fetch = [&](int col, Raw& r) __attribute__((always_inline)) {
+    auto fetch = [&](int col, Raw& r, auto g_c) __attribute__((always_inline)) {
+        constexpr int g = decltype(g_c)::value;
         if constexpr (SPL > 0) {
+            constexpr int n = SPL - 8 * g < GS ? SPL - 8 * g : GS;
             const float* p = a.a_f32 + static_cast<size_t>(t) * a.N1 + col;
             const size_t stride = static_cast<size_t>(a.T) * a.N1;
 #pragma unroll
-            for (int j = 0; j < SPL; ++j) {
-                const float4* q = reinterpret_cast<const float4*>(p + static_cast<size_t>(j) * stride);
+            for (int j = 0; j < n; ++j) {
+                const float4* q = reinterpret_cast<const float4*>(p + static_cast<size_t>(8 * g + j) * stride);
                 r.x[j][0] = q[0];
                 r.x[j][1] = q[1];
             }
@@ -269,67 +274,96 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
             r.b = *reinterpret_cast<const uint4*>(a.a_bf16 + static_cast<size_t>(t) * a.N1 + col);
         }
     };
-    // the chunk's 8 values as the fp32 of their bf16 rounding (splits summed in order)
-    auto finish = [&](const Raw& r, float* f) __attribute__((always_inline)) {
+    // add fetch group g to the running split sums s8 (split order)
+    auto accum = [&](const Raw& r, float* s8, auto g_c) __attribute__((always_inline)) {
+        constexpr int g = decltype(g_c)::value;
         if constexpr (SPL > 0) {
-            float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            constexpr int n = SPL - 8 * g < GS ? SPL - 8 * g : GS;
 #pragma unroll
-            for (int j = 0; j < SPL; ++j) {
+            for (int j = 0; j < n; ++j) {
                 s8[0] += r.x[j][0].x; s8[1] += r.x[j][0].y; s8[2] += r.x[j][0].z; s8[3] += r.x[j][0].w;
                 s8[4] += r.x[j][1].x; s8[5] += r.x[j][1].y; s8[6] += r.x[j][1].z; s8[7] += r.x[j][1].w;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = bf2f(f2bf(s8[e]));
         } else {
-            unpack8(r.b, f);
+            unpack8(r.b, s8);
+        }
+    };
+    // the chunk's 8 values as the fp32 of their bf16 rounding (the GEMM's output cast)
+    auto finish = [&](float* s8) __attribute__((always_inline)) {
+        if constexpr (SPL > 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = bf2f(f2bf(s8[e]));
         }
     };
 
-    // round trip 1: everything that depends on no other load, all requested before any use
     const bool rope = a.k_pe != nullptr && half >= 8;
     const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
-    Raw rq[QC > 0 ? QC : 1], rkv[KC], r1, r2;
-    uint4 gq[QC > 0 ? QC : 1], gkv[KC];
-    static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
-        constexpr int c = decltype(c_c)::value;
-        const int ch = min(tid + kRowThreads * c, nq - 1);
-        fetch(ch * 8, rq[c]);
-        gq[c] = *reinterpret_cast<const uint4*>(a.gamma_q + ch * 8);
-    });
-    static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
-        constexpr int c = decltype(c_c)::value;
-        const int ch = min(tid + kRowThreads * c, nkv - 1);
-        fetch(a.Lq + ch * 8, rkv[c]);
-        gkv[c] = *reinterpret_cast<const uint4*>(a.gamma_kv + ch * 8);
-    });
     const bool roper = rope && tid < (half >> 3);
     const int i0 = rope ? min(tid, (half >> 3) - 1) * 8 : 0;
-    if (rope) {
-        fetch(a.Lq + a.Lkv + i0, r1);
-        fetch(a.Lq + a.Lkv + half + i0, r2);
-    }
-    // round trip 2: the token's cos/sin row
-    float4 cl[2], ch_[2], sl[2], sh[2];
-    if (rope) {
-        const float* cr = a.cos + static_cast<size_t>(pos) * a.R;
-        const float* sr = a.sin + static_cast<size_t>(pos) * a.R;
-        cl[0] = *reinterpret_cast<const float4*>(cr + i0);
-        cl[1] = *reinterpret_cast<const float4*>(cr + i0 + 4);
-        ch_[0] = *reinterpret_cast<const float4*>(cr + half + i0);
-        ch_[1] = *reinterpret_cast<const float4*>(cr + half + i0 + 4);
-        sl[0] = *reinterpret_cast<const float4*>(sr + i0);
-        sl[1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
-        sh[0] = *reinterpret_cast<const float4*>(sr + half + i0);
-        sh[1] = *reinterpret_cast<const float4*>(sr + half + i0 + 4);
-    }
-
     float qv[QC > 0 ? QC : 1][8], kv[KC][8], x1[8], x2[8];
-    static_for<QC>([&](auto c_c) __attribute__((always_inline)) { finish(rq[decltype(c_c)::value], qv[decltype(c_c)::value]); });
-    static_for<KC>([&](auto c_c) __attribute__((always_inline)) { finish(rkv[decltype(c_c)::value], kv[decltype(c_c)::value]); });
-    if (rope) {
-        finish(r1, x1);
-        finish(r2, x2);
-    }
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[decltype(c_c)::value][e] = 0.f;
+    });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[decltype(c_c)::value][e] = 0.f;
+    });
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x1[e] = x2[e] = 0.f;
+    uint4 gq[QC > 0 ? QC : 1], gkv[KC];
+    float4 cl[2], ch_[2], sl[2], sh[2];
+    static_for<NG>([&](auto g_c) __attribute__((always_inline)) {
+        constexpr int g = decltype(g_c)::value;
+        // one round trip: every load of this group (and, with the first, γ and the position)
+        // is requested before any of them is used
+        Raw rq[QC > 0 ? QC : 1], rkv[KC], r1, r2;
+        static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_c)::value;
+            const int ch = min(tid + kRowThreads * c, nq - 1);
+            fetch(ch * 8, rq[c], g_c);
+            if constexpr (g == 0) gq[c] = *reinterpret_cast<const uint4*>(a.gamma_q + ch * 8);
+        });
+        static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+            constexpr int c = decltype(c_c)::value;
+            const int ch = min(tid + kRowThreads * c, nkv - 1);
+            fetch(a.Lq + ch * 8, rkv[c], g_c);
+            if constexpr (g == 0) gkv[c] = *reinterpret_cast<const uint4*>(a.gamma_kv + ch * 8);
+        });
+        if (rope) {
+            fetch(a.Lq + a.Lkv + i0, r1, g_c);
+            fetch(a.Lq + a.Lkv + half + i0, r2, g_c);
+        }
+        if constexpr (g == 0) {
+            // the token's cos/sin row, requested as soon as the position is back
+            if (rope) {
+                const float* cr = a.cos + static_cast<size_t>(pos) * a.R;
+                const float* sr = a.sin + static_cast<size_t>(pos) * a.R;
+                cl[0] = *reinterpret_cast<const float4*>(cr + i0);
+                cl[1] = *reinterpret_cast<const float4*>(cr + i0 + 4);
+                ch_[0] = *reinterpret_cast<const float4*>(cr + half + i0);
+                ch_[1] = *reinterpret_cast<const float4*>(cr + half + i0 + 4);
+                sl[0] = *reinterpret_cast<const float4*>(sr + i0);
+                sl[1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
+                sh[0] = *reinterpret_cast<const float4*>(sr + half + i0);
+                sh[1] = *reinterpret_cast<const float4*>(sr + half + i0 + 4);
+            }
+        }
+        static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+            accum(rq[decltype(c_c)::value], qv[decltype(c_c)::value], g_c);
+        });
+        static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+            accum(rkv[decltype(c_c)::value], kv[decltype(c_c)::value], g_c);
+        });
+        if (rope) {
+            accum(r1, x1, g_c);
+            accum(r2, x2, g_c);
+        }
+    });
+    static_for<QC>([&](auto c_c) __attribute__((always_inline)) { finish(qv[decltype(c_c)::value]); });
+    static_for<KC>([&](auto c_c) __attribute__((always_inline)) { finish(kv[decltype(c_c)::value]); });
+    finish(x1);
+    finish(x2);
 
     // RMS statistics: per thread in element order, then the fixed-order block sum
     float sq = 0.f, skv = 0.f;
@@ -682,9 +716,10 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((norm_rope_block_kernel<Q, 1, P>), dim3(a.T), dim3(kRowThreads), 0, s, a); \
         return hipGetLastError();                                                                  \
     }
-        MLAP_NORM_BLOCK(0, 0) MLAP_NORM_BLOCK(1, 0) MLAP_NORM_BLOCK(0, 2) MLAP_NORM_BLOCK(1, 2)
-        MLAP_NORM_BLOCK(0, 4) MLAP_NORM_BLOCK(1, 4) MLAP_NORM_BLOCK(0, 7) MLAP_NORM_BLOCK(1, 7)
-        MLAP_NORM_BLOCK(0, 8) MLAP_NORM_BLOCK(1, 8)
+        MLAP_NORM_BLOCK(0, 0) MLAP_NORM_BLOCK(1, 0) MLAP_NORM_BLOCK(0, 1) MLAP_NORM_BLOCK(1, 1)
+        MLAP_NORM_BLOCK(0, 2) MLAP_NORM_BLOCK(1, 2) MLAP_NORM_BLOCK(0, 4) MLAP_NORM_BLOCK(1, 4)
+        MLAP_NORM_BLOCK(0, 7) MLAP_NORM_BLOCK(1, 7) MLAP_NORM_BLOCK(0, 8) MLAP_NORM_BLOCK(1, 8)
+        MLAP_NORM_BLOCK(0, 14) MLAP_NORM_BLOCK(1, 14) MLAP_NORM_BLOCK(0, 16) MLAP_NORM_BLOCK(1, 16)
 #undef MLAP_NORM_BLOCK
     }
     hipLaunchKernelGGL(norm_rope_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
