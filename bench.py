@@ -9,6 +9,10 @@ same line carries the V3 decode batch (T=256) as a second measurement, timed
 with four rotating weight/input sets (423 MB) so the 256 MB last-level cache
 cannot hold the weights between steps.
 
+Each workload is timed twice: eager launches (one prepared mlap_run call per
+step) and a replay of the same steps from a HIP graph captured once; the graph
+figure is the headline (``launch``), the eager one is reported beside it.
+
 Prints ONE JSON line. ``roofline`` is for the dominant kernel (the q up
 projection, gemm_up_q): algorithmic FLOPs (or bytes) per launch divided by the
 kernel's average duration, measured with HIP events recorded around that
@@ -90,7 +94,13 @@ def measured_traffic(workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT):
+def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True):
+    """Times `steps` whole prolog runs of workload `name`, cycling through `rotate` input and
+    weight sets. Two timed passes: eager (one mlap_run per step from a prepared call, with
+    HIP events around every launch of the dominant kernel) and, when `graph`, the same
+    steps replayed from a HIP graph that captured `rotate` consecutive runs (no host
+    launch cost between kernels). Returns (cfg, eager ms/step, dominant kernel ms, eager
+    percentiles, graph ms/step or None, graph percentiles or None)."""
     import torch
 
     import mla_prolog_amd as mlap
@@ -107,24 +117,45 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT):
     p = mlap.Prolog.from_config(cfg)
     outs = p.alloc_outputs(T)
     ws = p.workspace(T)
+    runs = [p.bind(sets[r], outputs=outs, workspace=ws) for r in range(rotate)]
     for i in range(warmup):
-        p.run(sets[i % rotate], outputs=outs, workspace=ws)
+        runs[i % rotate]()
     torch.cuda.synchronize()
+
+    def timed(step_fn, n):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        marks[0].record()
+        for i in range(n):
+            step_fn(i)
+            marks[i + 1].record()
+        torch.cuda.synchronize()
+        per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(n))
+        pct = {"p10": round(per[int(0.1 * (n - 1))], 5), "p50": round(per[int(0.5 * (n - 1))], 5),
+               "p90": round(per[int(0.9 * (n - 1))], 5)}
+        return marks[0].elapsed_time(marks[-1]), pct
+
     p.timing_begin(dominant, steps)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    marks[0].record()
-    for i in range(steps):
-        p.run(sets[i % rotate], outputs=outs, workspace=ws)
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    ms_step = marks[0].elapsed_time(marks[-1]) / steps
-    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
-    pct = {"p10": round(per[int(0.1 * (steps - 1))], 5), "p50": round(per[int(0.5 * (steps - 1))], 5),
-           "p90": round(per[int(0.9 * (steps - 1))], 5)}
+    total, pct = timed(lambda i: runs[i % rotate](), steps)
+    ms_step = total / steps
     kms = p.timing_end()
     k_avg = sum(kms) / len(kms)
+
+    g_ms = g_pct = None
+    if graph:
+        assert steps % rotate == 0, "graph replay covers whole rotations"
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(rotate):
+                p.bind(sets[r], outputs=outs, workspace=ws)()  # bound to the capture stream
+        g.replay()
+        torch.cuda.synchronize()
+        gtotal, g_pct = timed(lambda i: g.replay(), steps // rotate)
+        g_ms = gtotal / steps
+        g_pct = {k: round(v / rotate, 5) for k, v in g_pct.items()}
+        del g
     del sets
-    return cfg, ms_step, k_avg, pct
+    return cfg, ms_step, k_avg, pct, g_ms, g_pct
 
 
 def roofline_for(cfg, T, k_ms, workload):
@@ -181,6 +212,8 @@ def main():
     ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP graph replay pass)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--rotate", type=int, default=1,
                     help="weight/input sets the headline workload cycles through")
@@ -204,7 +237,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg, ms, k_ms, pct = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate)
+    cfg, e_ms, k_ms, e_pct, g_ms, g_pct = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate,
+                                                         graph=not a.no_graph)
+    ms, pct = (g_ms, g_pct) if g_ms else (e_ms, e_pct)
     T = cfg.T
     pf, pb = path_work(cfg, T)
     line = {
@@ -216,6 +251,8 @@ def main():
         "warmup": a.warmup,
         "ms_per_step": round(ms, 5),
         "step_ms_percentiles": pct,
+        "launch": "hip_graph" if g_ms else "eager",
+        "eager_ms_per_step": round(e_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -231,13 +268,16 @@ def main():
                  "frac_bf16_peak": round(pf / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     if a.decode_workload:
-        dcfg, dms, dk_ms, dpct = bench_workload(a.decode_workload, a.decode_steps, a.warmup, rotate=4)
+        dcfg, de_ms, dk_ms, de_pct, dg_ms, dg_pct = bench_workload(a.decode_workload, a.decode_steps,
+                                                                   a.warmup, rotate=4, graph=not a.no_graph)
+        dms, dpct = (dg_ms, dg_pct) if dg_ms else (de_ms, de_pct)
         dpf, dpb = path_work(dcfg, dcfg.T)
         line["decode"] = {
             "workload": "%s: DeepSeek-V3 MLA Prolog decode batch, T=%d, 4 rotating weight sets"
                         % (dcfg.name, dcfg.T),
             "value": round(dcfg.T / (dms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(dms, 5), "step_ms_percentiles": dpct, "steps": a.decode_steps,
+            "launch": "hip_graph" if dg_ms else "eager", "eager_ms_per_step": round(de_ms, 5),
             "roofline": roofline_for(dcfg, dcfg.T, dk_ms, dcfg.name),
             "path": {"hbm_gbs": round(dpb / (dms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(dpb / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -250,11 +290,14 @@ def main():
         dom = "gemm_up_kv" if ecfg0.q_lora == 0 else DOMINANT
         # decode-sized batches rotate weight sets so the last-level cache cannot hold them
         rot = 4 if ecfg0.T <= 512 else 1
-        ecfg, ems, ek_ms, epct = bench_workload(name, a.steps, a.warmup, rotate=rot, dominant=dom)
+        ecfg, ee_ms, ek_ms, ee_pct, eg_ms, eg_pct = bench_workload(name, a.steps, a.warmup, rotate=rot,
+                                                                   dominant=dom, graph=not a.no_graph)
+        ems, epct = (eg_ms, eg_pct) if eg_ms else (ee_ms, ee_pct)
         epf, epb = path_work(ecfg, ecfg.T) if ecfg.q_lora else (None, None)
         ent = {"value": round(ecfg.T / (ems * 1e-3), 1), "unit": "tokens/s", "tokens": ecfg.T,
                "dtype": "int8" if ecfg.w8a8 else "bf16", "ms_per_step": round(ems, 5),
                "step_ms_percentiles": epct, "steps": a.steps, "rotating_sets": rot,
+               "launch": "hip_graph" if eg_ms else "eager", "eager_ms_per_step": round(ee_ms, 5),
                "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
         if epf:
             peak = PEAK_I8_TOPS if ecfg.w8a8 else PEAK_BF16_TFLOPS

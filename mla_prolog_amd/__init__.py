@@ -189,11 +189,7 @@ class Prolog:
             want = [k for k in shapes if k != "q_norm"]
         return {k: torch.empty(shapes[k][0], dtype=shapes[k][1], device=device) for k in want}
 
-    def run(self, inputs, outputs=None, workspace=None, stream=None):
-        """Enqueue one prolog run. ``inputs``: dict with x, positions, w_kva, gamma_kv,
-        cos, sin and (as configured) w_qa, w_qb, gamma_q, w_kvb, and ``*_scale`` for
-        W8A8. ``outputs``: dict of preallocated tensors (default: alloc_outputs).
-        Returns the outputs dict."""
+    def _marshal(self, inputs, outputs, workspace):
         x = inputs["x"]
         T = int(x.shape[0])
         w8 = self.cfg["w8a8"]
@@ -217,10 +213,24 @@ class Prolog:
                "kv_scale": torch.float32}
         o = _Outputs(**{k: _ptr(outputs.get(k), dts.get(k, torch.bfloat16), k) for k in OUTPUTS})
         ws = self.workspace(T, device=x.device) if workspace is None else workspace
+        return i, o, ws, outputs
+
+    def run(self, inputs, outputs=None, workspace=None, stream=None):
+        """Enqueue one prolog run. ``inputs``: dict with x, positions, w_kva, gamma_kv,
+        cos, sin and (as configured) w_qa, w_qb, gamma_q, w_kvb, and ``*_scale`` for
+        W8A8. ``outputs``: dict of preallocated tensors (default: alloc_outputs).
+        Returns the outputs dict."""
+        i, o, ws, outputs = self._marshal(inputs, outputs, workspace)
         _check(_lib.mlap_run(self._h, _stream(stream), C.byref(i), C.byref(o),
                              C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel() * ws.element_size())),
                "mlap_run")
         return outputs
+
+    def bind(self, inputs, outputs=None, workspace=None, stream=None):
+        """Marshal the arguments once; the returned callable enqueues the same run with one
+        foreign call (for tight loops and for capture into a HIP graph). The tensors must
+        stay alive and in place while it is used."""
+        return BoundRun(self, inputs, outputs, workspace, stream)
 
     # -- per-kernel timing ---------------------------------------------------
     def timing_begin(self, kernel, max_launches):
@@ -258,3 +268,21 @@ def gemm_bf16(A, B, out=None, stream=None):
                                C.c_void_p(_ptr(out, torch.bfloat16, "C")), M, N, K),
            "mlap_gemm_bf16")
     return out
+
+
+class BoundRun:
+    """A prolog run with its arguments marshalled once (see ``Prolog.bind``)."""
+
+    def __init__(self, prolog, inputs, outputs, workspace, stream):
+        self.prolog = prolog
+        self._i, self._o, self._ws, self.outputs = prolog._marshal(inputs, outputs, workspace)
+        self._keep = (inputs, self.outputs, self._ws)
+        self._stream = _stream(stream)
+        self._args = (prolog._h, self._stream, C.byref(self._i), C.byref(self._o),
+                      C.c_void_p(self._ws.data_ptr()),
+                      C.c_size_t(self._ws.numel() * self._ws.element_size()))
+
+    def __call__(self):
+        _check(_lib.mlap_run(*self._args), "mlap_run")
+        return self.outputs
+
