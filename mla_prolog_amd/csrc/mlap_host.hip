@@ -442,7 +442,9 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         g.N = plan.tail_c0;
         MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, InType::kBf16, Epi::kStoreBf16, s) != hipSuccess
                                     ? hipErrorInvalidValue
-                                    : launch_gemm(r, InType::kBf16, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
+                                    : gemm_big_fits(r, InType::kBf16, Epi::kStoreF32, BigShape::kSplitK)
+                                          ? launch_gemm_big(r, InType::kBf16, Epi::kStoreF32, s, BigShape::kSplitK)
+                                          : launch_gemm(r, InType::kBf16, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
         g.N = h->N1;
     } else {
         g.A = in->x;

@@ -491,24 +491,80 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // Same stage with one 64-wide wave per token (four tokens per workgroup) for segment
-// widths up to 64 * 8 * QC (q) and 64 * 8 * KC (kv): every reduction is a wave butterfly,
-// there is no workgroup barrier, and 2048 workgroups of four short waves fill the chip.
+// widths up to 64 * 8 * QC (q) and 64 * 8 * KC (kv), for a bf16 down-projection output
+// (with an optional fp32 split-K tail): every reduction is a wave butterfly, there is no
+// workgroup barrier, and 2048 workgroups of four short waves fill the chip. Every input
+// of the token is requested before any is used; when the rope slice lies in the split-K
+// tail, its chunk x split partials are spread one per lane and summed across lanes in
+// split order.
 template <int QC, int KC>
 __global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T) return;  // the whole wave leaves; nothing below synchronises the workgroup
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
+    const int half = a.R >> 1;
+    const int rc = half >> 3;  // rope chunks per half
+    const bool rope = a.k_pe != nullptr && rc > 0;
+    const uint16_t* arow = a.a_bf16 + static_cast<size_t>(t) * a.N1;
+    const int c_rope = a.Lq + a.Lkv;  // first column of the rope slice
+    // rope slice from the tail partials, one (chunk, split) pair per lane
+    const int S = a.tail_splits;
+    const bool lane_tail = rope && a.tail_f32 && c_rope >= a.tail_c0 && 2 * rc * S <= 64;
 
+    // ---- one burst of loads: rows, gamma, position, rope inputs
+    const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
+    uint4 rq[QC > 0 ? QC : 1], rkv[KC], gq[QC > 0 ? QC : 1], gkv[KC];
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+        const int c = min(lane + 64 * i, nq - 1);
+        rq[i] = *reinterpret_cast<const uint4*>(arow + c * 8);
+        gq[i] = *reinterpret_cast<const uint4*>(a.gamma_q + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int c = min(lane + 64 * i, nkv - 1);
+        rkv[i] = *reinterpret_cast<const uint4*>(arow + a.Lq + c * 8);
+        gkv[i] = *reinterpret_cast<const uint4*>(a.gamma_kv + c * 8);
+    }
+    const int i0 = rope ? min(lane, rc - 1) * 8 : 0;
+    float4 tp[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    float x1[8], x2[8];
+    if (lane_tail) {
+        const int j = min(lane / S, 2 * rc - 1), sp = lane - j * S;
+        if (sp < S) {
+            const int w = a.N1 - a.tail_c0;
+            const float* pp = a.tail_f32 + (static_cast<size_t>(sp) * a.T + t) * w + (c_rope - a.tail_c0) + 8 * j;
+            tp[0] = *reinterpret_cast<const float4*>(pp);
+            tp[1] = *reinterpret_cast<const float4*>(pp + 4);
+        }
+    } else if (rope) {
+        load_a8(a, t, c_rope + i0, x1);
+        load_a8(a, t, c_rope + half + i0, x2);
+    }
+    float4 cl[2], chh[2], sl[2], shh[2];
+    if (rope) {
+        const float* cr = a.cos + static_cast<size_t>(pos) * a.R;
+        const float* sr = a.sin + static_cast<size_t>(pos) * a.R;
+        cl[0] = *reinterpret_cast<const float4*>(cr + i0);
+        cl[1] = *reinterpret_cast<const float4*>(cr + i0 + 4);
+        chh[0] = *reinterpret_cast<const float4*>(cr + half + i0);
+        chh[1] = *reinterpret_cast<const float4*>(cr + half + i0 + 4);
+        sl[0] = *reinterpret_cast<const float4*>(sr + i0);
+        sl[1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
+        shh[0] = *reinterpret_cast<const float4*>(sr + half + i0);
+        shh[1] = *reinterpret_cast<const float4*>(sr + half + i0 + 4);
+    }
+
+    // ---- RMSNorm of both segments
     float qv[QC > 0 ? QC : 1][8], kv[KC][8];
     float sq = 0.f, skv = 0.f;
     const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
     const float invkv = 1.0f / static_cast<float>(a.Lkv);
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nq) {
-            load_a8(a, t, c * 8, qv[i]);
+        unpack8(rq[i], qv[i]);
+        if (lane + 64 * i < nq) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = qv[i][e] * qv[i][e];
@@ -518,9 +574,8 @@ __global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nkv) {
-            load_a8(a, t, a.Lq + c * 8, kv[i]);
+        unpack8(rkv[i], kv[i]);
+        if (lane + 64 * i < nkv) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = kv[i][e] * kv[i][e];
@@ -538,55 +593,67 @@ __global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nq) {
-            float g[8], o[8];
-            unpack8(*reinterpret_cast<const uint4*>(a.gamma_q + c * 8), g);
+        float g[8], o[8];
+        unpack8(gq[i], g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float y = qv[i][e] * rstd_q;
-                o[e] = y * g[e];
-            }
-            qo[i] = pack8(o);
-            if (a.q_norm)
-                *reinterpret_cast<uint4*>(a.q_norm + static_cast<size_t>(t) * a.Lq + c * 8) = qo[i];
+        for (int e = 0; e < 8; ++e) {
+            float y = qv[i][e] * rstd_q;
+            o[e] = y * g[e];
+        }
+        qo[i] = pack8(o);
+        if (c < nq) {
+            if (a.q_norm) *reinterpret_cast<uint4*>(a.q_norm + static_cast<size_t>(t) * a.Lq + c * 8) = qo[i];
             qmax = fmaxf(qmax, absmax8(qo[i]));
         }
     }
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nkv) {
-            float g[8], o[8];
-            unpack8(*reinterpret_cast<const uint4*>(a.gamma_kv + c * 8), g);
+        float g[8], o[8];
+        unpack8(gkv[i], g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float y = kv[i][e] * rstd_kv;
-                o[e] = y * g[e];
-            }
-            kvo[i] = pack8(o);
-            if (a.kv_norm)
-                *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
+        for (int e = 0; e < 8; ++e) {
+            float y = kv[i][e] * rstd_kv;
+            o[e] = y * g[e];
+        }
+        kvo[i] = pack8(o);
+        if (c < nkv) {
+            if (a.kv_norm) *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
             kvmax = fmaxf(kvmax, absmax8(kvo[i]));
         }
     }
 
-    // rotate-half RoPE of the k_pe slice (pairs i, i + R/2), one cos/sin row per token
-    const int half = a.R >> 1;
-    if (a.k_pe && lane < (half >> 3)) {
-        const int i0 = lane * 8;
-        const int p = clamp_pos(a.positions[t], a.max_pos);
-        const float* cr = a.cos + static_cast<size_t>(p) * a.R;
-        const float* sr = a.sin + static_cast<size_t>(p) * a.R;
-        float x1[8], x2[8], lo[8], hi[8];
-        load_a8(a, t, a.Lq + a.Lkv + i0, x1);
-        load_a8(a, t, a.Lq + a.Lkv + half + i0, x2);
+    // ---- rotate-half RoPE of the k_pe slice (pairs i, i + R/2)
+    if (lane_tail) {
+        // chunk j's sum over its S splits, in split order, in every lane of its group; then
+        // lane i < rc takes chunks i (x1) and i + rc (x2), rounded to bf16 (the GEMM's cast)
+        const int j = min(lane / S, 2 * rc - 1);
+        float v[8] = {tp[0].x, tp[0].y, tp[0].z, tp[0].w, tp[1].x, tp[1].y, tp[1].z, tp[1].w};
+        float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < S; ++sp) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[e] += __shfl(v[e], j * S + sp);
+        }
+        const int il = min(lane, rc - 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float p1 = x1[e] * cr[i0 + e];
-            float p2 = (-x2[e]) * sr[i0 + e];
+            x1[e] = bf2f(f2bf(__shfl(sum[e], il * S)));
+            x2[e] = bf2f(f2bf(__shfl(sum[e], (il + rc) * S)));
+        }
+    }
+    if (rope && lane < rc) {
+        const float cv[8] = {cl[0].x, cl[0].y, cl[0].z, cl[0].w, cl[1].x, cl[1].y, cl[1].z, cl[1].w};
+        const float chv[8] = {chh[0].x, chh[0].y, chh[0].z, chh[0].w, chh[1].x, chh[1].y, chh[1].z, chh[1].w};
+        const float sv[8] = {sl[0].x, sl[0].y, sl[0].z, sl[0].w, sl[1].x, sl[1].y, sl[1].z, sl[1].w};
+        const float shv[8] = {shh[0].x, shh[0].y, shh[0].z, shh[0].w, shh[1].x, shh[1].y, shh[1].z, shh[1].w};
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float p1 = x1[e] * cv[e];
+            float p2 = (-x2[e]) * sv[e];
             lo[e] = p1 + p2;
-            float p3 = x2[e] * cr[half + i0 + e];
-            float p4 = x1[e] * sr[half + i0 + e];
+            float p3 = x2[e] * chv[e];
+            float p4 = x1[e] * shv[e];
             hi[e] = p3 + p4;
         }
         uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
@@ -594,7 +661,7 @@ __global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
         *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
     }
 
-    // per-token INT8 quant of kv_norm
+    // ---- per-token INT8 quant of kv_norm
     if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
         const float amax = wave_max(kvmax);
         const float mult = amax > 0.f ? 127.0f / amax : 0.f;
@@ -697,7 +764,7 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     const dim3 grid((a.T + 3) / 4), block(kRowThreads);
     // A wave per token needs thousands of tokens to fill 256 CUs; small batches keep a
     // whole workgroup per token.
-    if (a.T >= 2048 && a.R <= 1024 && kc >= 1 && kc <= 4 && qc <= 4) {
+    if (a.T >= 2048 && !a.a_f32 && a.R <= 1024 && kc >= 1 && kc <= 4 && qc <= 4) {
 #define MLAP_NORM_WAVE(Q, K)                                                  \
     if (qc == Q && kc == K) {                                                 \
         hipLaunchKernelGGL((norm_rope_wave_kernel<Q, K>), grid, block, 0, s, a); \
