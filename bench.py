@@ -283,6 +283,14 @@ def main():
                      "frac_hbm_peak": round(dpb / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": dpb},
         }
+        # the same batch with one weight set, which stays in the 256 MB last-level cache
+        # between steps (a serving loop that runs nothing else): the warm figure
+        _, we_ms, wk_ms, _, wg_ms, _ = bench_workload(a.decode_workload, a.decode_steps, a.warmup,
+                                                      rotate=1, graph=not a.no_graph)
+        wms = wg_ms or we_ms
+        line["decode"]["warm"] = {"value": round(dcfg.T / (wms * 1e-3), 1), "unit": "tokens/s",
+                                  "ms_per_step": round(wms, 5), "eager_ms_per_step": round(we_ms, 5),
+                                  "gemm_up_q_ms": round(wk_ms, 5)}
     extra = {}
     for name in [w for w in a.extra_workloads.split(",") if w]:
         import synth

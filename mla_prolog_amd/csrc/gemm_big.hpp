@@ -131,21 +131,50 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     const int mb = m0 + wm * TM + lr;
     const int nb = n0 + wn * TN + 4 * lh;
 
+    // W8A8 dequantisation scales of this lane's rows and columns, fetched in one burst:
+    // a_scale of each of its FM tokens, b_scale of its 4-column runs (float4 when the run
+    // lies inside one weight segment and inside N).
+    float asc[sizeof(Tin) == 1 ? FM : 1];
+    float4 bsc[sizeof(Tin) == 1 ? FN : 1][4];
+    if constexpr (sizeof(Tin) == 1) {
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            asc[i] = g.a_scale[min(mb + 32 * i, g.M - 1)];
+        });
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = nb + 32 * j + 8 * gq;
+                if (n + 3 < g.N && (n + 3 < g.b_split || n >= g.b_split)) {
+                    const float* src = n < g.b_split ? g.b_scale0 + n : g.b_scale1 + (n - g.b_split);
+                    bsc[j][gq] = *reinterpret_cast<const float4*>(src);
+                } else {
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nn = min(n + q, g.N - 1);
+                        v[q] = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
+                    }
+                    bsc[j][gq] = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        });
+    }
+
     // Fragment (j, i) as eight packed bf16 pairs (the GEMM's bf16 output cast), with the
     // W8A8 dequantisation f32(acc) * (a_scale[m] * b_scale[n]) applied first.
-    auto frag_bf16 = [&](int j, int i, uint32_t* w) __attribute__((always_inline)) {
-        const int m = mb + 32 * i;
+    auto frag_bf16 = [&](auto j_c, auto i_c, uint32_t* w) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value, i = decltype(i_c)::value;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             float v[4];
             if constexpr (sizeof(Tin) == 1) {
-                const int n = nb + 32 * j + 8 * gq;
-                const float as = m < g.M ? g.a_scale[min(m, g.M - 1)] : 0.f;
+                const float as = asc[i];
+                const float bs[4] = {bsc[j][gq].x, bsc[j][gq].y, bsc[j][gq].z, bsc[j][gq].w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int nn = min(n + q, g.N - 1);
-                    const float bs = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
-                    const float sc = as * bs;
+                    const float sc = as * bs[q];
                     v[q] = static_cast<float>(acc[j][i][4 * gq + q]) * sc;
                 }
             } else {
@@ -192,7 +221,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
             uint32_t w[8];
-            frag_bf16(j, i, w);
+            frag_bf16(j_c, i_c, w);
             const int row = wm * TM + 32 * i + lr;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
