@@ -132,6 +132,10 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
             r.b_split = g.b_split - nm;
         }
         r.out = static_cast<uint16_t*>(g.out) + nm;
+        // 64 x 64 tiles: one per 64 tokens, so the narrow remainder still spreads over the CUs
+        if ((static_cast<size_t>(r.K) * eb) % 128 == 0)
+            return t == InType::kInt8 ? launch_big_one<int8_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s)
+                                      : launch_big_one<uint16_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s);
         return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
     }
     if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
