@@ -14,9 +14,9 @@ step) and a replay of the same steps from a HIP graph captured once; the graph
 figure is the headline (``launch``), the eager one is reported beside it.
 
 Prints ONE JSON line. ``roofline`` is for the dominant kernel (the q up
-projection, gemm_up_q): algorithmic FLOPs (or bytes) per launch divided by the
-kernel's average duration, measured with HIP events recorded around that
-kernel on the stream it runs on. ``cpu_baseline`` times the CPU oracle on a
+projection, gemm_up_q): its algorithmic FLOPs (or bytes) per step divided by its
+time per step, measured with HIP events recorded around each of its launches on
+the stream it runs on (large batches launch it once per token block). ``cpu_baseline`` times the CPU oracle on a
 bounded sample of token rows of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
@@ -135,11 +135,13 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True):
                "p90": round(per[int(0.9 * (n - 1))], 5)}
         return marks[0].elapsed_time(marks[-1]), pct
 
-    p.timing_begin(dominant, steps)
+    # the dominant kernel may run as several launches per step (token blocks at large
+    # batches): its time per step is the sum of its launches over the step
+    p.timing_begin(dominant, steps * 8)
     total, pct = timed(lambda i: runs[i % rotate](), steps)
     ms_step = total / steps
     kms = p.timing_end()
-    k_avg = sum(kms) / len(kms)
+    k_avg = sum(kms) / steps
 
     g_ms = g_pct = None
     if graph:

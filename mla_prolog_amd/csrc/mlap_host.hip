@@ -39,7 +39,10 @@ constexpr size_t kAlign = 256;
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kSmallBatch = 512;  // token counts up to this use the weight-streaming tiles
 constexpr int kGroupM = 4;        // M-tiles per group in the XCD-aware tile order
-constexpr int kGroupNq = 8;       // N-tiles per group for the q up projection (N-major split)
+constexpr int kGroupNq = 8;
+// token blocks of the q up projection whose quant overlaps the next block (large batches)
+constexpr int kQBlocks = 4;
+constexpr int kQBlockMinT = 2048;       // N-tiles per group for the q up projection (N-major split)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -101,6 +104,12 @@ struct mlap_prolog {
     int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
     int bn_q, bn_kv;
     Timer timer;
+    // Large int8 batches quantise finished token blocks of q on a second stream while the q up
+    // projection continues with the next block (fork/join through events on the caller's
+    // stream, so the run stays ordered on it and can be captured into a graph). Created on
+    // the first run that uses them, on that run's device.
+    hipStream_t aux = nullptr;
+    hipEvent_t fork[kQBlocks + 1] = {};
 
     Plan plan(int T) const {
         Plan p{};
@@ -304,6 +313,9 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
 MLAP_API void mlap_destroy(mlap_handle h) {
     if (!h) return;
     for (hipEvent_t e : h->timer.ev) (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->fork)
+        if (e) (void)hipEventDestroy(e);
+    if (h->aux) (void)hipStreamDestroy(h->aux);
     delete h;
 }
 
@@ -372,6 +384,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     if (!has_kvb && (out->k_nope || out->value)) return MLAP_ERR_INVALID_ARG;
     // the q quant reads the q tensors back
     const bool quant_q = out->q_i8 || out->q_scale;
+    bool quant_done = false;  // the q quant already ran per token block
     if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
     const WsLayout L = h->layout(T);
     if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign))
@@ -530,8 +543,57 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         } else {
             u.A = qn;
         }
-        MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
-                                          : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
+        // Only the int8 projection gains from the overlap: it is twice as fast per FLOP, so
+        // its quant is a larger share of the step; the bf16 projection slows under the
+        // concurrent quant by about what the overlap saves (measured at T=8192).
+        const bool blocks = quant_q && w8 && plan.big_q && plan.q_shape == BigShape::kWide && T >= kQBlockMinT;
+        if (!blocks) {
+            MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
+                                              : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
+        } else {
+            // q in kQBlocks token blocks (whole 256-row tiles); block b's quant runs on the
+            // second stream as soon as its projection is done, under block b + 1's GEMM
+            if (!h->aux) {
+                if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess) return MLAP_ERR_HIP;
+                for (hipEvent_t& ev : h->fork)
+                    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return MLAP_ERR_HIP;
+            }
+            const int rows = (T / kQBlocks + kBigTile - 1) / kBigTile * kBigTile;
+            const size_t ea = w8 ? 1 : 2;
+            for (int b = 0; b * rows < T; ++b) {
+                const int r0 = b * rows, nr = std::min(rows, T - r0);
+                GemmArgs ub = u;
+                ub.M = nr;
+                ub.A = static_cast<const char*>(u.A) + static_cast<size_t>(r0) * Lq * ea;
+                if (w8) ub.a_scale = u.a_scale + r0;
+                ub.out0 = out->q_nope ? static_cast<uint16_t*>(out->q_nope) + static_cast<size_t>(r0) * H * c.nope_dim : nullptr;
+                ub.out1 = out->q_pe ? static_cast<uint16_t*>(out->q_pe) + static_cast<size_t>(r0) * H * R : nullptr;
+                ub.positions = in->positions + r0;
+                ub.part_amax = u.part_amax + static_cast<size_t>(r0) * plan.nt_q;
+                MLAP_LAUNCH(kKGemmUpQ, launch_gemm_big(ub, it, Epi::kHeads, s, plan.q_shape));
+                if (hipEventRecord(h->fork[b], s) != hipSuccess || hipStreamWaitEvent(h->aux, h->fork[b], 0) != hipSuccess)
+                    return MLAP_ERR_HIP;
+                QuantQArgs qa{};
+                qa.T = nr;
+                qa.H = H;
+                qa.Dn = c.nope_dim;
+                qa.R = R;
+                qa.n_tiles = plan.nt_q;
+                qa.part_amax = ub.part_amax;
+                qa.q_nope = static_cast<const uint16_t*>(ub.out0);
+                qa.q_pe = static_cast<const uint16_t*>(ub.out1);
+                qa.q_i8 = out->q_i8 ? out->q_i8 + static_cast<size_t>(r0) * H * (c.nope_dim + R) : nullptr;
+                qa.q_scale = out->q_scale ? out->q_scale + r0 : nullptr;
+                hipStream_t s_main = s;
+                s = h->aux;  // MLAP_LAUNCH records the quant's timing on the stream it runs on
+                MLAP_LAUNCH(kKQuantQ, launch_quant_q(qa, s));
+                s = s_main;
+            }
+            if (hipEventRecord(h->fork[kQBlocks], h->aux) != hipSuccess ||
+                hipStreamWaitEvent(s, h->fork[kQBlocks], 0) != hipSuccess)
+                return MLAP_ERR_HIP;
+            quant_done = true;
+        }
     }
 
     // 4. kv_b up projection (KV-Prolog mode): per head [k_nope | value]
@@ -566,7 +628,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     }
 
     // 5. per-token INT8 quant of q (after RoPE), one scale over all heads
-    if (has_q && quant_q) {
+    if (has_q && quant_q && !quant_done) {
         QuantQArgs qa{};
         qa.T = T;
         qa.H = H;

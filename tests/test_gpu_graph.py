@@ -17,8 +17,10 @@ def say(*a):
     print(*a, flush=True)
 
 
+# v3_w8a8 at T=2048 runs the q up projection in token blocks whose quant forks onto a
+# second stream and joins back, so the capture must carry that fork/join
 @pytest.mark.parametrize("name,T", [("v3_decode", 64), ("v3_decode", 256), ("v2lite_kv_decode", None),
-                                    ("v3_prefill", 1000)])
+                                    ("v3_prefill", 1000), ("v3_w8a8", 2048)])
 def test_graph_replay_matches_eager(name, T):
     cfg = synth.get_config(name, T=T)
     say("graph replay", name, "T=%d" % cfg.T)
