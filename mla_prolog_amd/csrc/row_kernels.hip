@@ -729,21 +729,28 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
         return (j < cn) ? reinterpret_cast<const uint4*>(a.q_nope + th * a.Dn + j * 8)
                         : reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
     };
-    // the token's q values do not depend on its amax: start fetching them first
-    uint4 held[kHeld > 0 ? kHeld : 1];
-    if (a.q_i8) {
-#pragma unroll
-        for (int k = 0; k < kHeld; ++k) {
-            const int c = threadIdx.x + k * kRowThreads;
-            if (c < total) held[k] = *chunk_at(c);
-        }
+    if (!a.q_i8) {  // scale only
+        float m = 0.f;
+        for (int i = threadIdx.x; i < a.n_tiles; i += kRowThreads)
+            m = fmaxf(m, a.part_amax[static_cast<size_t>(t) * a.n_tiles + i]);
+        const float amax = block_max(m, red);
+        if (threadIdx.x == 0 && a.q_scale) a.q_scale[t] = amax / 127.0f;
+        return;
     }
-    float m = 0.f;
-    for (int i = threadIdx.x; i < a.n_tiles; i += kRowThreads)
+    // The partial amaxes go out first and the token's q values right behind them (they do
+    // not depend on the amax), so the amax reduction runs while the row is in flight.
+    // Clamped indexes keep the loads unconditional (straight-line code, exact waits): a
+    // repeated partial amax does not change the max, repeated chunks are not stored.
+    const int i0 = threadIdx.x;
+    const float pa = a.part_amax[static_cast<size_t>(t) * a.n_tiles + min(i0, a.n_tiles - 1)];
+    uint4 held[kHeld > 0 ? kHeld : 1];
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) held[k] = *chunk_at(min(static_cast<int>(threadIdx.x) + k * kRowThreads, total - 1));
+    float m = pa;
+    for (int i = i0 + kRowThreads; i < a.n_tiles; i += kRowThreads)
         m = fmaxf(m, a.part_amax[static_cast<size_t>(t) * a.n_tiles + i]);
     const float amax = block_max(m, red);
     if (threadIdx.x == 0 && a.q_scale) a.q_scale[t] = amax / 127.0f;
-    if (!a.q_i8) return;
     const float mult = amax > 0.f ? 127.0f / amax : 0.f;
     auto store = [&](int c, const uint4& v) {
         const int h = c / cph, j = c - h * cph;
