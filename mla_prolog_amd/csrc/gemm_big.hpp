@@ -107,6 +107,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 16-byte store marked non-temporal: output tiles are written once and not read again by
+// the kernel, so they should not displace operand lines from the L2.
+__device__ __forceinline__ void store_nt(void* p, const uint4& v) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -244,7 +252,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             const int row = idx / CPR, c = idx - row * CPR;
             const int m = m0 + row, n = n0 + 8 * c;
             if (m < g.M && n < g.N)  // N is a multiple of 8
-                *reinterpret_cast<uint4*>(out + static_cast<size_t>(m) * g.ldo + n) = tile_chunk(row, c);
+                big::store_nt(out + static_cast<size_t>(m) * g.ldo + n, tile_chunk(row, c));
         }
     } else if constexpr (EPI == Epi::kHeads) {
         // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the
@@ -325,9 +333,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
                 }
                 if (ok) {
                     if (seg0) {
-                        if (out0) *reinterpret_cast<uint4*>(out0 + th * d0 + d) = o;
+                        if (out0) big::store_nt(out0 + th * d0 + d, o);
                     } else if (out1) {
-                        *reinterpret_cast<uint4*>(out1 + th * d1 + dr) = o;
+                        big::store_nt(out1 + th * d1 + dr, o);
                     }
                     // |values| are non-negative floats, whose bit patterns order like unsigned ints
                     if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
