@@ -106,6 +106,13 @@ __device__ __forceinline__ uint2 quant8(const uint4& v, float m) {
     return make_uint2(w[0], w[1]);
 }
 
+// 8-byte store marked non-temporal (a final output, not read again by the path).
+__device__ __forceinline__ void store_nt8(void* p, const uint2& v) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, static_cast<u32x2*>(p));
+}
+
 __device__ __forceinline__ int clamp_pos(int p, int max_pos) {
     return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
 }

@@ -755,7 +755,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     auto store = [&](int c, const uint4& v) {
         const int h = c / cph, j = c - h * cph;
         const size_t th = static_cast<size_t>(t) * a.H + h;
-        *reinterpret_cast<uint2*>(a.q_i8 + th * QH + j * 8) = quant8(v, mult);
+        store_nt8(a.q_i8 + th * QH + j * 8, quant8(v, mult));
     };
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
