@@ -92,6 +92,7 @@ CASES = [
     ("v3_decode", 37),
     ("v3_decode", 64),        # last batch size of the 64-row weight-streaming tiles
     ("v3_decode", 65),        # first batch size of the 256-row weight-streaming tiles
+    ("v3_decode", 200),       # 128-row head tiles with a ragged second row tile
     ("v3_decode", None),      # T = 256, every row
     ("v2lite_kv_decode", 200),
     ("v2lite_kv_decode", 300),  # two row tiles of the narrow kv_b tiles
