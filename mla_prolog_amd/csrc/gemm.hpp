@@ -1,4 +1,7 @@
-// gemm.hpp -- LDS-staged MFMA GEMM for gfx950, C = A . B^T with A [M,K], B [N,K].
+// gemm.hpp -- GEMM arguments, tile order and MFMA wrappers shared by the GEMM kernels,
+// and the register-staged MFMA GEMM for gfx950, C = A . B^T with A [M,K], B [N,K], which
+// serves the int8 small-batch projections, the test exports and shapes the LDS-DMA kernel
+// (gemm_big.hpp) does not cover.
 //
 // Both operands are K-contiguous (activations [T, K], weights [N, K] as the
 // AT-10 card's b_trans layout), so every lane fetches 16-byte runs along K for

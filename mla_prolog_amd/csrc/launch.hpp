@@ -21,15 +21,19 @@ struct GemmTile {
 // (type, tile, epilogue) combination that has no instantiation.
 hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi epi, hipStream_t s);
 
-// LDS-DMA GEMM (gemm_big.hpp) in three shapes:
-//   kWide     -- 256 x 256 tiles, eight waves (large batches, MFMA-bound); kStoreBf16 and
-//                kHeads (head width and d0 multiples of 64, a 64-wide rope slice);
-//   kHalfHead -- 256 x 96 tiles, four waves: one tile per half of a 192-wide q head, a
-//                decode batch's whole T in one tile row (bf16, kHeads);
-//   kSplitK   -- 256 x 64 tiles, four waves, split-K fp32 partials (bf16, kStoreF32).
-// With kHeads, g.n_tiles must be ceil(N / big_tile_n(shape)) (one partial amax per token
-// and tile). gemm_big_fits says whether the shapes suit it (K a whole number of 128-byte
-// stages per split).
+// LDS-DMA GEMM (gemm_big.hpp) in four shapes:
+//   kWide        -- 256 x 256 tiles, eight waves (large batches, MFMA-bound); kStoreBf16 and
+//                   kHeads (head width and d0 multiples of 64, a 64-wide rope slice);
+//   kHalfHead    -- 96-column tiles: one per half of a 192-wide q head, the whole batch in
+//                   one tile row (bf16, kHeads);
+//   kSplitK      -- 64-column tiles, split-K fp32 partials (bf16, kStoreF32);
+//   kNarrowHeads -- 32-column tiles that stay inside one head segment, no rope (bf16,
+//                   kHeads; the kv_b projection of small batches).
+// The weight-streaming shapes (all but kWide) use 256-row tiles with four waves, or 64-row
+// tiles with two waves when M <= 64. A ragged column remainder of a kWide kStoreBf16 launch
+// runs on 64 x 64 tiles. With kHeads, g.n_tiles must be ceil(N / big_tile_n(shape)) (one
+// partial amax per token and tile). gemm_big_fits says whether the shapes suit it (K a whole
+// number of 128-byte stages per split).
 enum class BigShape : int { kWide = 0, kHalfHead = 1, kSplitK = 2, kNarrowHeads = 3 };
 constexpr int kBigTile = 256;
 int big_tile_n(BigShape shape);
@@ -39,7 +43,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s,
 
 // Per-token row stage after the down projection: RMSNorm*gamma -> bf16 for the q and kv
 // segments, rotate-half RoPE of the k_pe segment, per-token INT8 quant of kv_norm and (W8A8)
-// of q_norm. One workgroup per token.
+// of q_norm. One wave per token for large batches, one workgroup per token otherwise.
 struct NormArgs {
     int T, Lq, Lkv, R, N1, k_splits;
     const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output, or

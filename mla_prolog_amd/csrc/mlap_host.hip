@@ -1,6 +1,7 @@
 // mlap_host.hip -- the C ABI of libmlap.so: validation, per-run plan and launches.
 //
-// The run is a fixed chain of kernels on the caller's stream (no host sync):
+// The run is a fixed chain of kernels on the caller's stream (no host sync; at large int8
+// batches the q quant of each token block forks onto a second stream and joins back):
 //   [W8A8: act_quant(x)] -> gemm_down (x . [W_qa; W_kva]^T, bf16 out)
 //   -> norm_rope (RMSNorm*gamma -> bf16 for q_a and c_kv, RoPE of k_pe, kv quant)
 //   -> gemm_up_q (q_norm . W_qb^T; per head: q_nope, RoPE'd q_pe, partial amax)
@@ -65,9 +66,12 @@ int heads_tile(int head_w) {
 }
 
 // Kernel shapes for one run of T tokens: the counterpart of a tile table bucketed by token
-// count. Small batches stream the weights (the projection is bound by HBM bandwidth):
-// 128-row tiles with 3 K-tiles in flight, and a split-K down projection whose fp32 partial
-// sums the row kernel adds up. Large batches are bound by MFMA throughput: 256-row tiles.
+// count. Small batches stream the weights (the projections are bound by reading them):
+// tiles that span the whole batch (256 rows, or 64 at most 64 tokens) with three stages in
+// flight, a split-K down projection whose fp32 partial sums the row kernel adds up, half-head
+// q tiles and 32-column kv_b tiles so every CU has work. Large batches are bound by MFMA
+// throughput: 256 x 256 tiles. The int8 small-batch projections keep the register-staged
+// kernel of gemm.hpp (GemmTile fields).
 struct Plan {
     GemmTile down;
     Epi down_epi;
