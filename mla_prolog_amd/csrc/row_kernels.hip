@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // tail, its chunk x split partials are spread one per lane and summed across lanes in
 // split order.
 template <int QC, int KC>
-__global__ __launch_bounds__(256) void norm_rope_wave_kernel(NormArgs a) {
+__global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T) return;  // the whole wave leaves; nothing below synchronises the workgroup
