@@ -134,11 +134,16 @@ MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes);
 
 /* Enqueue the whole prolog for in->T tokens on `stream`. `ws` must hold at least
  * mlap_workspace_size(h, in->T) bytes, 256-byte aligned. T == 0 is a no-op.
- * Runs on one handle must not overlap in time unless they use distinct workspaces. */
+ * Runs on one handle must not overlap in time unless they use distinct workspaces, and a
+ * handle is not for concurrent calls from several host threads.
+ * Large int8 (W8A8) batches also use a second stream, created by the handle on its first
+ * such run on the current device: the run forks onto it and joins back to `stream` through
+ * events, so all work stays ordered on `stream` and the run can be captured into a HIP
+ * graph on `stream`. */
 MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
              void* ws, size_t ws_bytes);
 
-/* Free the handle (host memory and any timing events). NULL is allowed. */
+/* Free the handle (host memory, timing events and its second stream). NULL is allowed. */
 MLAP_API void mlap_destroy(mlap_handle h);
 
 /* Static description of a status code. */
