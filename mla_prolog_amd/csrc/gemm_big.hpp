@@ -45,9 +45,10 @@ __device__ __forceinline__ int swz(int r) {
         return (r >> 1) & 7;
 }
 
-// Epilogue LDS: the bf16 tile with rows padded by 16 bytes, then one row-amax word per row.
+// Epilogue LDS: the bf16 tile with rows padded by 16 bytes, then one row-amax word per row
+// and wave column.
 constexpr int epi_pitch(int bn) { return bn * 2 + 16; }
-constexpr int epi_lds(int bm, int bn) { return bm * epi_pitch(bn) + bm * 4; }
+constexpr int epi_lds(int bm, int bn, int wn) { return bm * epi_pitch(bn) + wn * bm * 4; }
 
 template <int BM, int BN, int WM, int WN, int KB, int S>
 struct Shape {
@@ -61,7 +62,7 @@ struct Shape {
     static constexpr int ROUNDS = ROWS / RROWS;
     static constexpr int STAGE = ROWS * KB;
     static constexpr int MAIN = S * STAGE;
-    static constexpr int EPI = epi_lds(BM, BN);               // staged tile + row amax
+    static constexpr int EPI = epi_lds(BM, BN, WN);           // staged tile + row amaxes
     static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
     static_assert(KB == 64 || KB == 128, "stage row bytes");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave block must be whole 32x32 fragments");
@@ -81,9 +82,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Workgroup barrier that orders LDS traffic without waiting for outstanding global
-// loads (a __syncthreads() fence would drain the copy ring).
+// loads (a __syncthreads() fence would drain the copy ring). s_barrier itself does not
+// wait for this wave's LDS operations, so they are drained first (lgkmcnt(0)): without
+// that, a write issued just before the barrier (a staged tile chunk, a cleared row amax)
+// can land after another wave's access that the barrier was meant to order behind it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -120,13 +125,57 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 
 }  // namespace big
 
+// Operands of the in-register rotate-half of the heads epilogue (64-wide rope slices that
+// start on a 32-column fragment). Lane l holds, for each of its FM tokens, columns
+// 8g + 4(l / 32) + q of both 32-column halves of a slice: their cos/sin values depend on
+// the token and the column only. The positions are read when the workgroup starts; the
+// cos/sin values either under the last K-stage (gather: shapes with registers to hold
+// them) or one token fragment at a time in the epilogue (load).
+template <int FM>
+struct RopeOps {
+    bool on;        // the tile holds a rope slice (wave-uniform)
+    int pos[FM];
+    float4 c[FM][2][4], s[FM][2][4];  // [token fragment][half][column group g]
+    __device__ __forceinline__ void fetch_positions(const GemmArgs& g, int mb) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) pos[i] = g.positions[min(mb + 32 * i, g.M - 1)];
+    }
+    // cos/sin of token fragment i into (cc, ss)
+    __device__ __forceinline__ void load(const GemmArgs& g, int lh, int i, float4 (&cc)[2][4],
+                                         float4 (&ss)[2][4]) const {
+        const size_t row = static_cast<size_t>(clamp_pos(pos[i], g.max_pos)) * 64 + 4 * lh;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                cc[h][gq] = *reinterpret_cast<const float4*>(g.cos + row + 32 * h + 8 * gq);
+                ss[h][gq] = *reinterpret_cast<const float4*>(g.sin + row + 32 * h + 8 * gq);
+            }
+    }
+    // every token fragment at once (shapes with registers to hold them)
+    __device__ __forceinline__ void gather(const GemmArgs& g, int lh) {
+        if (!on) return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) load(g, lh, i, c[i], s[i]);
+    }
+};
+template <>
+struct RopeOps<0> {
+    static constexpr bool on = false;
+    __device__ __forceinline__ void fetch_positions(const GemmArgs&, int) {}
+    __device__ __forceinline__ void gather(const GemmArgs&, int) {}
+};
+
 // Output stage of a BM x BN tile held in the transposed accumulator layout (lane l,
 // register 4g + q of fragment (j, i): token 32 i + l % 32 of the wave's rows, column
 // 32 j + 8 g + 4 (l / 32) + q of its columns). `smem` must hold
-// big::epi_lds(BM, BN) bytes and be free: every wave is done with the operand stages.
-template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, typename AccT, int FN, int FM>
+// big::epi_lds(BM, BN, WN) bytes and be free: every wave is done with the operand stages.
+// EARLY: the cos/sin operands were gathered under the last K-stage (else they are gathered
+// here, after the accumulators have been packed to bf16 and freed their registers).
+template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, bool EARLY, typename AccT, int FN, int FM, int RF>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN][FM], char* smem,
-                                              int m0, int n0, int n_tile, int split) {
+                                              int m0, int n0, int n_tile, int split,
+                                              RopeOps<RF>& rope_ops) {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     static_assert(FM == TM / 32 && FN == TN / 32, "accumulator shape");
@@ -222,132 +271,188 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     // padded by 16 bytes against bank conflicts.
     constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
     constexpr int PITCH = big::epi_pitch(BN);
-    uint32_t* row_amax = reinterpret_cast<uint32_t*>(smem + BM * PITCH);
-    big::lds_barrier();  // every wave is done reading the last stage
-    static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-        constexpr int j = decltype(j_c)::value;
-        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-            constexpr int i = decltype(i_c)::value;
-            uint32_t w[8];
-            frag_bf16(j_c, i_c, w);
-            const int row = wm * TM + 32 * i + lr;
+    auto stage_frag = [&](int row, int col, const uint32_t* w) __attribute__((always_inline)) {
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int col = wn * TN + 32 * j + 8 * gq + 4 * lh;
-                *reinterpret_cast<uint2*>(smem + row * PITCH + col * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
-            }
-        });
-    });
-    if constexpr (EPI == Epi::kHeads) {
-        for (int r = tid; r < BM; r += NT) row_amax[r] = 0u;
-    }
-    big::lds_barrier();
-
-    auto tile_chunk = [&](int row, int ch) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(smem + row * PITCH + ch * 16);
+        for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<uint2*>(smem + row * PITCH + (col + 8 * gq) * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
     };
+    big::lds_barrier();  // every wave is done reading the last stage
     if constexpr (EPI == Epi::kStoreBf16) {
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                uint32_t w[8];
+                frag_bf16(j_c, i_c, w);
+                stage_frag(wm * TM + 32 * decltype(i_c)::value + lr, wn * TN + 32 * j + 4 * lh, w);
+            });
+        });
+        big::lds_barrier();
         uint16_t* out = static_cast<uint16_t*>(g.out);
         for (int idx = tid; idx < BM * CPR; idx += NT) {
             const int row = idx / CPR, c = idx - row * CPR;
             const int m = m0 + row, n = n0 + 8 * c;
             if (m < g.M && n < g.N)  // N is a multiple of 8
-                big::store_nt(out + static_cast<size_t>(m) * g.ldo + n, tile_chunk(row, c));
+                big::store_nt(out + static_cast<size_t>(m) * g.ldo + n,
+                              *reinterpret_cast<const uint4*>(smem + row * PITCH + c * 16));
         }
     } else if constexpr (EPI == Epi::kHeads) {
-        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; with rope, seg1 is the
-        // rotate-half slice. The host picks tiles that hold whole 8-column chunks of one
-        // segment and a whole rope slice, so the rotate-half partner of a chunk (d1/2
-        // columns away) is in the same tile row.
-        //
-        // A thread keeps one chunk column c for the whole tile and walks the rows (RPP rows
-        // per pass), so its segment, head offset and rope role are fixed. Every gather the
-        // rope needs is issued ahead: all of the thread's token positions at once, and the
-        // cos/sin rows of pass p + L while pass p is rotated.
-        constexpr int RPP = NT / CPR;                 // rows per pass
+        // The heads work is done in registers before the tile is staged. A rope slice is 64
+        // columns that start on a 32-column fragment j, so its two halves are fragments j and
+        // j + 1 of the same lane (one register apart per value). A token's amax over the tile
+        // is a lane-local max, one exchange with lane l ^ 32 (the other column runs), and
+        // with several wave columns a max over their per-row entries in LDS.
+        float* wave_amax = reinterpret_cast<float*>(smem + BM * PITCH);  // [WN][BM]
+        const int cw = n0 + wn * TN;  // first column of this wave
+        // Fragment sj starts this wave's rope slice, or sj = -1 (wave-uniform). Slices are
+        // at least 128 columns apart, so a wave's columns hold at most one.
+        int sj = -1;
+        if constexpr (RF > 0) {
+            if (rope_ops.on)
+                for (int j = 0; j + 1 < FN; ++j) {
+                    const int cj = cw + 32 * j;
+                    if (sj < 0 && cj + 64 <= g.N && cj % g.head_w == g.d0) sj = j;
+                }
+        }
+        auto absmax_frag = [&](const uint32_t* w) __attribute__((always_inline)) {
+            // |bf16| values: clear the sign bits, then compare as floats
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t a = w[e] & 0x7fff7fffu;
+                mx = fmaxf(mx, fmaxf(big::lo_bf(a), big::hi_bf(a)));
+            }
+            return mx;
+        };
+        // Every fragment is packed and staged at once, its |max| folded into the token's
+        // running max; only the rope slice's two fragments are kept for the rotation.
+        float amx[FM];
+        uint32_t sw[RF > 0 ? 2 : 1][FM][8];
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) { amx[decltype(i_c)::value] = 0.f; });
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                uint32_t w[8];
+                frag_bf16(j_c, i_c, w);
+                bool keep = false;
+                if constexpr (RF > 0) {
+                    if (sj >= 0 && (j == sj || j == sj + 1)) {
+                        keep = true;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sw[j == sj ? 0 : 1][i][e] = w[e];
+                    }
+                }
+                if (!keep) {
+                    stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w);
+                    amx[i] = fmaxf(amx[i], absmax_frag(w));
+                }
+            });
+        });
+        if constexpr (RF > 0) {
+            if (sj >= 0) {
+                // keep the cos/sin loads below the packing: hoisted above it they would be
+                // live alongside the accumulators (and the W8A8 scales)
+                __builtin_amdgcn_sched_barrier(0);
+                // late shapes: every token fragment's cos/sin in one burst (the accumulators
+                // are packed and staged, so their registers are free)
+                float4 lc[EARLY ? 1 : FM][2][4], ls[EARLY ? 1 : FM][2][4];
+                if constexpr (!EARLY)
+                    static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                        constexpr int i = decltype(i_c)::value;
+                        rope_ops.load(g, lh, i, lc[i], ls[i]);
+                    });
+                static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
+                    // cos/sin at each value's own column
+                    uint32_t(&lo)[8] = sw[0][i];
+                    uint32_t(&hi)[8] = sw[1][i];
+                    auto rotate = [&](const float4(&cc)[2][4], const float4(&ss)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const float4 cl = cc[0][gq], ch = cc[1][gq], sl = ss[0][gq], sh = ss[1][gq];
+                        const float c_lo[4] = {cl.x, cl.y, cl.z, cl.w}, c_hi[4] = {ch.x, ch.y, ch.z, ch.w};
+                        const float s_lo[4] = {sl.x, sl.y, sl.z, sl.w}, s_hi[4] = {sh.x, sh.y, sh.z, sh.w};
+                        float x1[4], x2[4], r1[4], r2[4];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            x1[2 * h] = big::lo_bf(lo[2 * gq + h]);
+                            x1[2 * h + 1] = big::hi_bf(lo[2 * gq + h]);
+                            x2[2 * h] = big::lo_bf(hi[2 * gq + h]);
+                            x2[2 * h + 1] = big::hi_bf(hi[2 * gq + h]);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            r1[q] = x1[q] * c_lo[q] + (-x2[q]) * s_lo[q];
+                            r2[q] = x2[q] * c_hi[q] + x1[q] * s_hi[q];
+                        }
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            lo[2 * gq + h] = big::pack_bf16x2(r1[2 * h], r1[2 * h + 1]);
+                            hi[2 * gq + h] = big::pack_bf16x2(r2[2 * h], r2[2 * h + 1]);
+                        }
+                    }
+                    };
+                    if constexpr (EARLY)
+                        rotate(rope_ops.c[i], rope_ops.s[i]);
+                    else
+                        rotate(lc[i], ls[i]);
+                    const int row = wm * TM + 32 * i + lr;
+                    stage_frag(row, wn * TN + 32 * sj + 4 * lh, lo);
+                    stage_frag(row, wn * TN + 32 * (sj + 1) + 4 * lh, hi);
+                    amx[i] = fmaxf(amx[i], fmaxf(absmax_frag(lo), absmax_frag(hi)));
+                });
+            }
+        }
+        if (g.part_amax) {
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                const float mx = fmaxf(amx[i], __shfl_xor(amx[i], 32));
+                const int row = wm * TM + 32 * i + lr;
+                if constexpr (WN == 1) {
+                    const int m = m0 + row;
+                    if (lh == 0 && m < g.M) g.part_amax[static_cast<size_t>(m) * g.n_tiles + n_tile] = mx;
+                } else {
+                    if (lh == 0) wave_amax[wn * BM + row] = mx;
+                }
+            });
+        }
+        big::lds_barrier();
+        if constexpr (WN > 1) {
+            if (g.part_amax)
+                for (int r = tid; r < BM; r += NT)
+                    if (m0 + r < g.M) {
+                        float mx = wave_amax[r];
+#pragma unroll
+                        for (int k = 1; k < WN; ++k) mx = fmaxf(mx, wave_amax[k * BM + r]);
+                        g.part_amax[static_cast<size_t>(m0 + r) * g.n_tiles + n_tile] = mx;
+                    }
+        }
+        // Per head [seg0 (d0 columns) | seg1 (d1 columns)]; the host picks tiles whose
+        // 8-column chunks each lie inside one segment. A thread keeps one chunk column c for
+        // the whole tile and walks the rows, RPP rows per pass.
+        constexpr int RPP = NT / CPR;
         constexpr int PASSES = (BM + RPP - 1) / RPP;
-        constexpr int L = PASSES < 4 ? PASSES : 4;        // cos/sin lookahead (passes)
         const int HW = g.head_w, d0 = g.d0, d1 = g.d1;
-        const int pc = d1 / 16;  // partner distance in chunks
         uint16_t* out0 = static_cast<uint16_t*>(g.out0);
         uint16_t* out1 = static_cast<uint16_t*>(g.out1);
         const int c = tid % CPR, r_in = tid / CPR;
-        const bool active = tid < RPP * CPR;
         const int n = n0 + 8 * c;
-        const bool nok = active && n < g.N;
+        const bool nok = tid < RPP * CPR && n < g.N;
         const int h = n / HW;
         const int d = n - h * HW;
         const bool seg0 = d < d0;
-        const int dr = d - d0;  // column within seg1
-        const bool rot = nok && !seg0 && g.rope;
-        const bool low = dr < (d1 >> 1);
-        int pos[PASSES];
-        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            const int m = min(m0 + p * RPP + r_in, g.M - 1);
-            pos[p] = rot ? clamp_pos(g.positions[m], g.max_pos) : 0;
-        });
-        float4 cs[L][2], sn[L][2];
-        auto gather = [&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            if constexpr (p < PASSES) {
-                if (rot) {
-                    const float* cr = g.cos + static_cast<size_t>(pos[p]) * d1 + dr;
-                    const float* sr = g.sin + static_cast<size_t>(pos[p]) * d1 + dr;
-                    cs[p % L][0] = *reinterpret_cast<const float4*>(cr);
-                    cs[p % L][1] = *reinterpret_cast<const float4*>(cr + 4);
-                    sn[p % L][0] = *reinterpret_cast<const float4*>(sr);
-                    sn[p % L][1] = *reinterpret_cast<const float4*>(sr + 4);
-                }
-            }
-        };
-        static_for<L>([&](auto p_c) __attribute__((always_inline)) { gather(p_c); });
-        static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
-            constexpr int p = decltype(p_c)::value;
-            const int row = p * RPP + r_in;
-            const int m = m0 + row;
-            if (active && row < BM) {
-                const bool ok = nok && m < g.M;
-                const size_t th = static_cast<size_t>(min(m, g.M - 1)) * g.n_heads + h;
-                const uint4 v = tile_chunk(row, c);
-                uint4 o = v;
-                if (rot) {
-                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
-                    // cos/sin at this chunk's own columns; the partner is the other half.
-                    const uint4 pv = tile_chunk(row, low ? c + pc : c - pc);
-                    float own[8], oth[8], res[8];
-                    unpack8(v, own);
-                    unpack8(pv, oth);
-                    const float4 c0 = cs[p % L][0], c1 = cs[p % L][1];
-                    const float4 s0 = sn[p % L][0], s1 = sn[p % L][1];
-                    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float t1 = own[e] * cv[e];
-                        const float t2 = (low ? -oth[e] : oth[e]) * sv[e];
-                        res[e] = t1 + t2;
-                    }
-                    o = make_uint4(big::pack_bf16x2(res[0], res[1]), big::pack_bf16x2(res[2], res[3]),
-                                   big::pack_bf16x2(res[4], res[5]), big::pack_bf16x2(res[6], res[7]));
-                }
-                if (ok) {
-                    if (seg0) {
-                        if (out0) big::store_nt(out0 + th * d0 + d, o);
-                    } else if (out1) {
-                        big::store_nt(out1 + th * d1 + dr, o);
-                    }
-                    // |values| are non-negative floats, whose bit patterns order like unsigned ints
-                    if (g.part_amax) atomicMax(row_amax + row, __float_as_uint(absmax8(o)));
-                }
-            }
-            gather(std::integral_constant<int, p + L>{});
-        });
-        if (g.part_amax) {
-            big::lds_barrier();
-            for (int r = tid; r < BM; r += NT)
-                if (m0 + r < g.M)
-                    g.part_amax[static_cast<size_t>(m0 + r) * g.n_tiles + n_tile] = __uint_as_float(row_amax[r]);
+        uint16_t* const dst = seg0 ? out0 : out1;
+        const int dw = seg0 ? d0 : d1, dd = seg0 ? d : d - d0;
+        if (nok && dst) {
+            static_for<PASSES>([&](auto p_c) __attribute__((always_inline)) {
+                constexpr int p = decltype(p_c)::value;
+                const int row = p * RPP + r_in;
+                const int m = m0 + row;
+                if (row < BM && m < g.M)
+                    big::store_nt(dst + (static_cast<size_t>(m) * g.n_heads + h) * dw + dd,
+                                  *reinterpret_cast<const uint4*>(smem + row * PITCH + c * 16));
+            });
         }
     }
 }
@@ -373,6 +478,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         tile_of(blockIdx.x, tiles_m, tiles_n, g.k_splits, g.group_m, m_tile, n_tile, split);
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
+    // In-register rope operands of the heads epilogue: whether this wave's columns hold a
+    // 64-wide rope slice, and if so its tokens' positions now. With one wave per SIMD (a
+    // 512-register budget) the cos/sin values are gathered under the last K-stage; the
+    // two-waves-per-SIMD shape has no registers to spare there and gathers them in the
+    // epilogue.
+    constexpr int RF = EPI == Epi::kHeads && FN > 1 ? FM : 0;
+    constexpr bool EARLY = WM * WN <= 4;
+    RopeOps<RF> rope_ops;
+    if constexpr (RF > 0) {
+        rope_ops.on = false;
+        if (g.rope && g.d1 == 64)
+            for (int j = 0; j + 1 < FN; ++j) {
+                const int cj = n0 + wn * TN + 32 * j;
+                rope_ops.on |= cj + 64 <= g.N && cj % g.head_w == g.d0;
+            }
+        if (rope_ops.on) rope_ops.fetch_positions(g, m0 + wm * TM + (lane & 31));
+    }
     // split-K (fp32 partial epilogue only): this workgroup covers K bytes
     // [split * kbs, (split + 1) * kbs) of every row
     const int kbs = g.K * static_cast<int>(sizeof(Tin)) / g.k_splits;
@@ -551,9 +673,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     };
     int kt = 0;
     for (; kt + S - 1 < nk; ++kt) stage(kt, std::true_type{});
-    for (; kt < nk; ++kt) stage(kt, std::false_type{});
+    for (; kt < nk; ++kt) {
+        if (EARLY && kt + 1 == nk) rope_ops.gather(g, lh);  // lands under the last stage's MFMAs
+        stage(kt, std::false_type{});
+    }
+    if (EARLY && nk == 0) rope_ops.gather(g, lh);
 
-    tile_epilogue<Tin, BM, BN, WM, WN, EPI>(g, acc, smem, m0, n0, n_tile, split);
+    tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, m0, n0, n_tile, split, rope_ops);
 }
 
 }  // namespace mlap

@@ -94,10 +94,10 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
             }
             return false;
         case BigShape::kHalfHead:
-            // 96-column tiles, two per head: [0, 96) all seg0, [96, HW) the rest of seg0
-            // and the whole rope slice
+            // 96-column tiles, two per head: [0, 96) all seg0, [96, 192) the rest of seg0
+            // (32 columns) and the 64-wide rope slice, rotated in registers
             return t == InType::kBf16 && epi == Epi::kHeads && g.head_w == 192 && g.rope &&
-                   g.d0 >= 96 && g.d0 % 8 == 0 && g.d1 == 192 - g.d0 && g.d1 % 16 == 0;
+                   g.d0 == 128 && g.d1 == 64;
         case BigShape::kSplitK:
             return t == InType::kBf16 && epi == Epi::kStoreF32 && g.N % 4 == 0 && g.ldo % 4 == 0;
         case BigShape::kNarrowHeads:

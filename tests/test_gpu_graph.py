@@ -17,6 +17,14 @@ def say(*a):
     print(*a, flush=True)
 
 
+def _diff(a, b):
+    """Where two equal-shaped tensors differ: count and the first few indexes and values."""
+    ne = (a != b).nonzero()
+    first = [(tuple(i.tolist()), a[tuple(i)].item(), b[tuple(i)].item()) for i in ne[:6]]
+    rows = sorted(set(ne[:, 0].tolist()))
+    return {"count": int(ne.shape[0]), "rows": rows[:12], "n_rows": len(rows), "first": first}
+
+
 # v3_w8a8 at T=2048 runs the q up projection in token blocks whose quant forks onto a
 # second stream and joins back, so the capture must carry that fork/join
 @pytest.mark.parametrize("name,T", [("v3_decode", 64), ("v3_decode", 256), ("v2lite_kv_decode", None),
@@ -46,6 +54,6 @@ def test_graph_replay_matches_eager(name, T):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for k, v in ref.items():
-            assert torch.equal(outs[k], v), "replay %d: %s differs from the eager run" % (rep, k)
+        bad = {k: _diff(outs[k], v) for k, v in ref.items() if not torch.equal(outs[k], v)}
+        assert not bad, "replay %d differs from the eager run: %s" % (rep, bad)
     say("  3 replays bit-identical to eager")
