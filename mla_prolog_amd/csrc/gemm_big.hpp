@@ -129,8 +129,8 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 // start on a 32-column fragment). Lane l holds, for each of its FM tokens, columns
 // 8g + 4(l / 32) + q of both 32-column halves of a slice: their cos/sin values depend on
 // the token and the column only. The positions are read when the workgroup starts; the
-// cos/sin values either under the last K-stage (gather: shapes with registers to hold
-// them) or one token fragment at a time in the epilogue (load).
+// cos/sin values under the last K-stage (gather) on shapes with registers to hold them,
+// else the epilogue stages the tile's cos/sin rows in LDS.
 template <int FM>
 struct RopeOps {
     bool on;        // the tile holds a rope slice (wave-uniform)
@@ -140,23 +140,20 @@ struct RopeOps {
 #pragma unroll
         for (int i = 0; i < FM; ++i) pos[i] = g.positions[min(mb + 32 * i, g.M - 1)];
     }
-    // cos/sin of token fragment i into (cc, ss)
-    __device__ __forceinline__ void load(const GemmArgs& g, int lh, int i, float4 (&cc)[2][4],
-                                         float4 (&ss)[2][4]) const {
-        const size_t row = static_cast<size_t>(clamp_pos(pos[i], g.max_pos)) * 64 + 4 * lh;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                cc[h][gq] = *reinterpret_cast<const float4*>(g.cos + row + 32 * h + 8 * gq);
-                ss[h][gq] = *reinterpret_cast<const float4*>(g.sin + row + 32 * h + 8 * gq);
-            }
-    }
-    // every token fragment at once (shapes with registers to hold them)
+    // every token fragment's cos/sin (shapes with registers to hold them)
     __device__ __forceinline__ void gather(const GemmArgs& g, int lh) {
         if (!on) return;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) load(g, lh, i, c[i], s[i]);
+        for (int i = 0; i < FM; ++i) {
+            const size_t row = static_cast<size_t>(clamp_pos(pos[i], g.max_pos)) * 64 + 4 * lh;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    c[i][h][gq] = *reinterpret_cast<const float4*>(g.cos + row + 32 * h + 8 * gq);
+                    s[i][h][gq] = *reinterpret_cast<const float4*>(g.sin + row + 32 * h + 8 * gq);
+                }
+        }
     }
 };
 template <>
@@ -170,8 +167,8 @@ struct RopeOps<0> {
 // register 4g + q of fragment (j, i): token 32 i + l % 32 of the wave's rows, column
 // 32 j + 8 g + 4 (l / 32) + q of its columns). `smem` must hold
 // big::epi_lds(BM, BN, WN) bytes and be free: every wave is done with the operand stages.
-// EARLY: the cos/sin operands were gathered under the last K-stage (else they are gathered
-// here, after the accumulators have been packed to bf16 and freed their registers).
+// EARLY: the cos/sin operands were gathered under the last K-stage (else the epilogue
+// copies the tile's cos/sin rows into LDS while it packs the accumulators).
 template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, bool EARLY, typename AccT, int FN, int FM, int RF>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN][FM], char* smem,
                                               int m0, int n0, int n_tile, int split,
@@ -323,85 +320,135 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             }
             return mx;
         };
-        // Every fragment is packed and staged at once, its |max| folded into the token's
-        // running max; only the rope slice's two fragments are kept for the rotation.
-        float amx[FM];
-        uint32_t sw[RF > 0 ? 2 : 1][FM][8];
-        static_for<FM>([&](auto i_c) __attribute__((always_inline)) { amx[decltype(i_c)::value] = 0.f; });
-        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = decltype(j_c)::value;
-            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-                constexpr int i = decltype(i_c)::value;
-                uint32_t w[8];
-                frag_bf16(j_c, i_c, w);
-                bool keep = false;
-                if constexpr (RF > 0) {
-                    if (sj >= 0 && (j == sj || j == sj + 1)) {
-                        keep = true;
+        // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half), cos/sin at
+        // each value's own column: cc/ss[half][g] hold columns 32 half + 8 g + 4 (l / 32) + q
+        auto rotate = [&](uint32_t(&lo)[8], uint32_t(&hi)[8], const float4(&cc)[2][4],
+                          const float4(&ss)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) sw[j == sj ? 0 : 1][i][e] = w[e];
-                    }
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 cl = cc[0][gq], ch = cc[1][gq], sl = ss[0][gq], sh = ss[1][gq];
+                const float c_lo[4] = {cl.x, cl.y, cl.z, cl.w}, c_hi[4] = {ch.x, ch.y, ch.z, ch.w};
+                const float s_lo[4] = {sl.x, sl.y, sl.z, sl.w}, s_hi[4] = {sh.x, sh.y, sh.z, sh.w};
+                float x1[4], x2[4], r1[4], r2[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    x1[2 * h] = big::lo_bf(lo[2 * gq + h]);
+                    x1[2 * h + 1] = big::hi_bf(lo[2 * gq + h]);
+                    x2[2 * h] = big::lo_bf(hi[2 * gq + h]);
+                    x2[2 * h + 1] = big::hi_bf(hi[2 * gq + h]);
                 }
-                if (!keep) {
-                    stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w);
-                    amx[i] = fmaxf(amx[i], absmax_frag(w));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    r1[q] = x1[q] * c_lo[q] + (-x2[q]) * s_lo[q];
+                    r2[q] = x2[q] * c_hi[q] + x1[q] * s_hi[q];
                 }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    lo[2 * gq + h] = big::pack_bf16x2(r1[2 * h], r1[2 * h + 1]);
+                    hi[2 * gq + h] = big::pack_bf16x2(r2[2 * h], r2[2 * h + 1]);
+                }
+            }
+        };
+        float amx[FM];
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) { amx[decltype(i_c)::value] = 0.f; });
+        if constexpr (RF > 0 && !EARLY) {
+            // Two waves per SIMD: no registers to hold cos/sin through the main loop. The
+            // tile's cos and sin rows (256 B each per token) are copied into the free LDS
+            // by the load unit while the accumulators are packed: per wave row, cos rows of
+            // its TM tokens then sin rows, one table per wave column, 16-byte chunk c of
+            // token row t at chunk c ^ (t % 16) so that 16 lanes reading 16 consecutive
+            // tokens' chunk hit distinct banks. Each row is fetched once per tile (instead of
+            // once per rope slice and wave, scattered over 32 tokens per load).
+            constexpr int CS_ROWS = 2 * TM;                  // rows per wave row
+            constexpr int PER = CS_ROWS * 256 / 1024 / WN;   // 1 KB copies per wave
+            static_assert(WN == 2 && 4 * PER == TM && TM <= 64, "one table per wave column");
+            static_assert(BM * 512 <= big::epi_lds(BM, BN, WN), "cos/sin rows fit the epilogue LDS");
+            char* const cs_lds = smem;
+            if (rope_ops.on) {  // tile-uniform
+                const float* table = wn == 0 ? g.cos : g.sin;
+                char* const dst = cs_lds + (wm * CS_ROWS + wn * TM) * 256;
+                static_for<PER>([&](auto k_c) __attribute__((always_inline)) {
+                    constexpr int k = decltype(k_c)::value;
+                    const int t = 4 * k + (lane >> 4);  // token within the wave row
+                    const int p = clamp_pos(__shfl(rope_ops.pos[k / 8], (4 * k) % 32 + (lane >> 4)), g.max_pos);
+                    const int c = (lane & 15) ^ (t & 15);
+                    big::copy16_to_lds(table + static_cast<size_t>(p) * 64 + c * 4, dst + k * 1024);
+                });
+            }
+            uint32_t w[FN][FM][8];
+            static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+                static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                    frag_bf16(j_c, i_c, w[decltype(j_c)::value][decltype(i_c)::value]);
+                });
             });
-        });
-        if constexpr (RF > 0) {
+            big::wait_vmcnt<0>();
+            big::lds_barrier();  // every wave's cos/sin rows have landed
             if (sj >= 0) {
-                // keep the cos/sin loads below the packing: hoisted above it they would be
-                // live alongside the accumulators (and the W8A8 scales)
-                __builtin_amdgcn_sched_barrier(0);
-                // late shapes: every token fragment's cos/sin in one burst (the accumulators
-                // are packed and staged, so their registers are free)
-                float4 lc[EARLY ? 1 : FM][2][4], ls[EARLY ? 1 : FM][2][4];
-                if constexpr (!EARLY)
-                    static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-                        constexpr int i = decltype(i_c)::value;
-                        rope_ops.load(g, lh, i, lc[i], ls[i]);
-                    });
                 static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
-                    // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half),
-                    // cos/sin at each value's own column
-                    uint32_t(&lo)[8] = sw[0][i];
-                    uint32_t(&hi)[8] = sw[1][i];
-                    auto rotate = [&](const float4(&cc)[2][4], const float4(&ss)[2][4]) __attribute__((always_inline)) {
+                    const int t = 32 * i + lr;
+                    const char* crow = cs_lds + (wm * CS_ROWS + t) * 256;
+                    const char* srow = crow + TM * 256;
+                    float4 cc[2][4], ss[2][4];
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const float4 cl = cc[0][gq], ch = cc[1][gq], sl = ss[0][gq], sh = ss[1][gq];
-                        const float c_lo[4] = {cl.x, cl.y, cl.z, cl.w}, c_hi[4] = {ch.x, ch.y, ch.z, ch.w};
-                        const float s_lo[4] = {sl.x, sl.y, sl.z, sl.w}, s_hi[4] = {sh.x, sh.y, sh.z, sh.w};
-                        float x1[4], x2[4], r1[4], r2[4];
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            x1[2 * h] = big::lo_bf(lo[2 * gq + h]);
-                            x1[2 * h + 1] = big::hi_bf(lo[2 * gq + h]);
-                            x2[2 * h] = big::lo_bf(hi[2 * gq + h]);
-                            x2[2 * h + 1] = big::hi_bf(hi[2 * gq + h]);
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int off = ((8 * h + 2 * gq + lh) ^ (t & 15)) * 16;
+                            cc[h][gq] = *reinterpret_cast<const float4*>(crow + off);
+                            ss[h][gq] = *reinterpret_cast<const float4*>(srow + off);
                         }
+                    static_for<FN - 1>([&](auto j_c) __attribute__((always_inline)) {
+                        constexpr int j = decltype(j_c)::value;
+                        if (j == sj) rotate(w[j][i], w[j + 1][i], cc, ss);
+                    });
+                });
+            }
+            big::lds_barrier();  // every wave is done reading cos/sin: the tile goes over them
+            static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w[j][i]);
+                    amx[i] = fmaxf(amx[i], absmax_frag(w[j][i]));
+                });
+            });
+        } else {
+            // Every fragment is packed and staged at once, its |max| folded into the token's
+            // running max; only the rope slice's two fragments are kept for the rotation,
+            // with the cos/sin values gathered under the last K-stage.
+            uint32_t sw[RF > 0 ? 2 : 1][FM][8];
+            static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    uint32_t w[8];
+                    frag_bf16(j_c, i_c, w);
+                    bool keep = false;
+                    if constexpr (RF > 0) {
+                        if (sj >= 0 && (j == sj || j == sj + 1)) {
+                            keep = true;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            r1[q] = x1[q] * c_lo[q] + (-x2[q]) * s_lo[q];
-                            r2[q] = x2[q] * c_hi[q] + x1[q] * s_hi[q];
-                        }
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            lo[2 * gq + h] = big::pack_bf16x2(r1[2 * h], r1[2 * h + 1]);
-                            hi[2 * gq + h] = big::pack_bf16x2(r2[2 * h], r2[2 * h + 1]);
+                            for (int e = 0; e < 8; ++e) sw[j == sj ? 0 : 1][i][e] = w[e];
                         }
                     }
-                    };
-                    if constexpr (EARLY)
-                        rotate(rope_ops.c[i], rope_ops.s[i]);
-                    else
-                        rotate(lc[i], ls[i]);
-                    const int row = wm * TM + 32 * i + lr;
-                    stage_frag(row, wn * TN + 32 * sj + 4 * lh, lo);
-                    stage_frag(row, wn * TN + 32 * (sj + 1) + 4 * lh, hi);
-                    amx[i] = fmaxf(amx[i], fmaxf(absmax_frag(lo), absmax_frag(hi)));
+                    if (!keep) {
+                        stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w);
+                        amx[i] = fmaxf(amx[i], absmax_frag(w));
+                    }
                 });
+            });
+            if constexpr (RF > 0) {
+                if (sj >= 0) {
+                    static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                        constexpr int i = decltype(i_c)::value;
+                        rotate(sw[0][i], sw[1][i], rope_ops.c[i], rope_ops.s[i]);
+                        const int row = wm * TM + 32 * i + lr;
+                        stage_frag(row, wn * TN + 32 * sj + 4 * lh, sw[0][i]);
+                        stage_frag(row, wn * TN + 32 * (sj + 1) + 4 * lh, sw[1][i]);
+                        amx[i] = fmaxf(amx[i], fmaxf(absmax_frag(sw[0][i]), absmax_frag(sw[1][i])));
+                    });
+                }
             }
         }
         if (g.part_amax) {
@@ -478,21 +525,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         tile_of(blockIdx.x, tiles_m, tiles_n, g.k_splits, g.group_m, m_tile, n_tile, split);
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
-    // In-register rope operands of the heads epilogue: whether this wave's columns hold a
-    // 64-wide rope slice, and if so its tokens' positions now. With one wave per SIMD (a
-    // 512-register budget) the cos/sin values are gathered under the last K-stage; the
-    // two-waves-per-SIMD shape has no registers to spare there and gathers them in the
-    // epilogue.
+    // In-register rope operands of the heads epilogue: whether the columns hold a 64-wide
+    // rope slice, and if so the tokens' positions now. With one wave per SIMD (a
+    // 512-register budget) each wave with a slice gathers its cos/sin values under the last
+    // K-stage; the two-waves-per-SIMD shape has no registers to spare there, and all of
+    // its waves copy the tile's cos/sin rows into LDS in the epilogue if any wave needs
+    // them.
     constexpr int RF = EPI == Epi::kHeads && FN > 1 ? FM : 0;
     constexpr bool EARLY = WM * WN <= 4;
     RopeOps<RF> rope_ops;
     if constexpr (RF > 0) {
         rope_ops.on = false;
-        if (g.rope && g.d1 == 64)
-            for (int j = 0; j + 1 < FN; ++j) {
-                const int cj = n0 + wn * TN + 32 * j;
+        if (g.rope && g.d1 == 64) {
+            const int c0 = EARLY ? n0 + wn * TN : n0;  // this wave's columns, or the tile's
+            constexpr int NF = EARLY ? FN : BN / 32;
+            for (int j = 0; j + 1 < NF; ++j) {
+                const int cj = c0 + 32 * j;
                 rope_ops.on |= cj + 64 <= g.N && cj % g.head_w == g.d0;
             }
+        }
         if (rope_ops.on) rope_ops.fetch_positions(g, m0 + wm * TM + (lane & 31));
     }
     // split-K (fp32 partial epilogue only): this workgroup covers K bytes
