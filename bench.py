@@ -96,13 +96,15 @@ def measured_traffic(workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True):
+def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, kv_cache=False):
     """Times `steps` whole prolog runs of workload `name`, cycling through `rotate` input and
     weight sets. Two timed passes: eager (one mlap_run per step from a prepared call, with
     HIP events around every launch of the dominant kernel) and, when `graph`, the same
     steps replayed from a HIP graph that captured `rotate` consecutive runs (no host
-    launch cost between kernels). Returns (cfg, eager ms/step, dominant kernel ms, eager
-    percentiles, graph ms/step or None, graph percentiles or None)."""
+    launch cost between kernels). With `kv_cache`, every step also writes the kv rows of its
+    tokens into KV caches of 4 T slots (all four caches, every token cached). Returns (cfg,
+    eager ms/step, dominant kernel ms, eager percentiles, graph ms/step or None, graph
+    percentiles or None)."""
     import torch
 
     import mla_prolog_amd as mlap
@@ -118,6 +120,15 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True):
         del inp
     p = mlap.Prolog.from_config(cfg)
     outs = p.alloc_outputs(T)
+    if kv_cache:
+        n_slots = 4 * T
+        slots = synth.slot_mapping(T, n_slots, seed=1, pad_frac=0.0, out_of_range=0).cuda()
+        for st in sets:
+            st["slot_mapping"] = slots
+        outs.update(kv_cache=torch.zeros(n_slots, cfg.kv_lora, dtype=torch.bfloat16, device="cuda"),
+                    kv_cache_i8=torch.zeros(n_slots, cfg.kv_lora, dtype=torch.int8, device="cuda"),
+                    kv_cache_scale=torch.zeros(n_slots, dtype=torch.float32, device="cuda"),
+                    kr_cache=torch.zeros(n_slots, cfg.rope_dim, dtype=torch.bfloat16, device="cuda"))
     ws = p.workspace(T)
     runs = [p.bind(sets[r], outputs=outs, workspace=ws) for r in range(rotate)]
     for i in range(warmup):
@@ -213,7 +224,7 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode",
+    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -303,12 +314,14 @@ def main():
     extra = {}
     for name in [w for w in a.extra_workloads.split(",") if w]:
         import synth
-        ecfg0 = synth.get_config(name)
+        base, _, opt = name.partition("+")
+        ecfg0 = synth.get_config(base)
         dom = "gemm_up_kv" if ecfg0.q_lora == 0 else DOMINANT
         # decode-sized batches rotate weight sets so the last-level cache cannot hold them
         rot = 4 if ecfg0.T <= 512 else 1
-        ecfg, ee_ms, ek_ms, ee_pct, eg_ms, eg_pct = bench_workload(name, a.steps, a.warmup, rotate=rot,
-                                                                   dominant=dom, graph=not a.no_graph)
+        ecfg, ee_ms, ek_ms, ee_pct, eg_ms, eg_pct = bench_workload(base, a.steps, a.warmup, rotate=rot,
+                                                                   dominant=dom, graph=not a.no_graph,
+                                                                   kv_cache=opt == "kvcache")
         e_use_g = eg_ms is not None and eg_ms < ee_ms
         ems, epct = (eg_ms, eg_pct) if e_use_g else (ee_ms, ee_pct)
         epf, epb = path_work(ecfg, ecfg.T) if ecfg.q_lora else (None, None)
@@ -318,6 +331,9 @@ def main():
                "launch": "hip_graph" if e_use_g else "eager", "eager_ms_per_step": round(ee_ms, 5),
                "graph_ms_per_step": round(eg_ms, 5) if eg_ms else None,
                "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
+        if opt == "kvcache":
+            ent["kv_cache"] = {"slots": 4 * ecfg.T, "caches": "kv_norm bf16, kv codes, kv scale, k_pe",
+                               "bytes_per_token": ecfg.kv_lora * 3 + 4 + ecfg.rope_dim * 2}
         if epf:
             peak = PEAK_I8_TOPS if ecfg.w8a8 else PEAK_BF16_TFLOPS
             ent["path"] = {"tops": round(epf / (ems * 1e-3) / 1e12, 2),

@@ -102,6 +102,13 @@ typedef struct {
     const void* gamma_kv;      /* [Lkv] bf16 RMSNorm weight of the kv branch */
     const float* cos;          /* [max_pos, R] fp32, the rotate-half table (both halves) */
     const float* sin;          /* [max_pos, R] fp32 */
+    /* KV cache write (optional; the caches are in mlap_outputs). slot_mapping[t] is the cache
+       row of token t: a flat slot index (for a paged cache, block * block_size + offset). A
+       negative slot, or one >= cache_slots, leaves the caches untouched for that token
+       (padding). Slots of one run must be distinct; with duplicates the row holds one of the
+       tokens' entries. Needed (with cache_slots > 0) when any cache pointer is set. */
+    const int32_t* slot_mapping; /* [T] int32 */
+    int32_t cache_slots;         /* rows of every cache */
 } mlap_inputs;
 
 /*
@@ -120,6 +127,14 @@ typedef struct {
     float* q_scale;   /* [T] fp32, amax/127 over the token's H*(Dn+R) values */
     int8_t* kv_i8;    /* [T, Lkv] int8 codes of kv_norm */
     float* kv_scale;  /* [T] fp32 */
+    /* KV cache rows written at mlap_inputs.slot_mapping: the ScatterUpdate of the prolog's kv
+       results into the cache ([V32] page, section 2.4; the [BLOG] page's step 2 caches the
+       per-row quantised rows). Each is optional and holds exactly what the same-named
+       per-token output holds, at row slot_mapping[t] instead of t; other rows are untouched. */
+    void* kv_cache;         /* [cache_slots, Lkv] bf16 kv_norm */
+    int8_t* kv_cache_i8;    /* [cache_slots, Lkv] int8 codes of kv_norm */
+    float* kv_cache_scale;  /* [cache_slots] fp32 kv scale */
+    void* kr_cache;         /* [cache_slots, R] bf16 k_pe, after RoPE */
 } mlap_outputs;
 
 typedef struct mlap_prolog* mlap_handle;

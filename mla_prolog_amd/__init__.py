@@ -44,15 +44,20 @@ class _Config(C.Structure):
 class _Inputs(C.Structure):
     _fields_ = [("T", C.c_int32)] + [(n, C.c_void_p) for n in (
         "x", "positions", "w_qa", "w_qb", "w_kva", "w_kvb", "ws_qa", "ws_qb", "ws_kva", "ws_kvb",
-        "gamma_q", "gamma_kv", "cos", "sin")]
+        "gamma_q", "gamma_kv", "cos", "sin", "slot_mapping")] + [("cache_slots", C.c_int32)]
 
 
 OUTPUTS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_i8", "q_scale",
            "kv_i8", "kv_scale")
+# KV cache rows written at inputs["slot_mapping"]: [cache_slots, Lkv] bf16, [cache_slots, Lkv]
+# int8, [cache_slots] fp32, [cache_slots, R] bf16
+CACHES = ("kv_cache", "kv_cache_i8", "kv_cache_scale", "kr_cache")
+_DTYPES = {"q_i8": torch.int8, "kv_i8": torch.int8, "q_scale": torch.float32,
+           "kv_scale": torch.float32, "kv_cache_i8": torch.int8, "kv_cache_scale": torch.float32}
 
 
 class _Outputs(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in OUTPUTS]
+    _fields_ = [(n, C.c_void_p) for n in OUTPUTS + CACHES]
 
 
 def _load():
@@ -208,18 +213,24 @@ class Prolog:
                     gamma_q=_ptr(g("gamma_q"), torch.bfloat16, "gamma_q"),
                     gamma_kv=_ptr(inputs["gamma_kv"], torch.bfloat16, "gamma_kv"),
                     cos=_ptr(inputs["cos"], torch.float32, "cos"),
-                    sin=_ptr(inputs["sin"], torch.float32, "sin"))
-        dts = {"q_i8": torch.int8, "kv_i8": torch.int8, "q_scale": torch.float32,
-               "kv_scale": torch.float32}
-        o = _Outputs(**{k: _ptr(outputs.get(k), dts.get(k, torch.bfloat16), k) for k in OUTPUTS})
+                    sin=_ptr(inputs["sin"], torch.float32, "sin"),
+                    slot_mapping=_ptr(g("slot_mapping"), torch.int32, "slot_mapping"))
+        caches = [outputs[k] for k in CACHES if outputs.get(k) is not None]
+        if caches:
+            i.cache_slots = int(caches[0].shape[0])
+            if any(int(c.shape[0]) != i.cache_slots for c in caches):
+                raise ValueError("every KV cache must have the same number of rows")
+        o = _Outputs(**{k: _ptr(outputs.get(k), _DTYPES.get(k, torch.bfloat16), k)
+                        for k in OUTPUTS + CACHES})
         ws = self.workspace(T, device=x.device) if workspace is None else workspace
         return i, o, ws, outputs
 
     def run(self, inputs, outputs=None, workspace=None, stream=None):
         """Enqueue one prolog run. ``inputs``: dict with x, positions, w_kva, gamma_kv,
         cos, sin and (as configured) w_qa, w_qb, gamma_q, w_kvb, and ``*_scale`` for
-        W8A8. ``outputs``: dict of preallocated tensors (default: alloc_outputs).
-        Returns the outputs dict."""
+        W8A8; ``slot_mapping`` (int32 [T]) with a KV cache write. ``outputs``: dict of
+        preallocated tensors (default: alloc_outputs), plus any of the caches in CACHES
+        (rows = cache slots). Returns the outputs dict."""
         i, o, ws, outputs = self._marshal(inputs, outputs, workspace)
         _check(_lib.mlap_run(self._h, _stream(stream), C.byref(i), C.byref(o),
                              C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel() * ws.element_size())),

@@ -68,6 +68,14 @@ struct NormArgs {
     float* kv_scale_b;
     int8_t* qn_i8;       // [T, Lq] W8A8 activation codes of q_norm, or null
     float* qn_scale;     // [T]
+    // KV cache rows: token t's kv_norm / codes and scale / k_pe also go to row slots[t] of
+    // these when 0 <= slots[t] < n_slots (each pointer optional)
+    const int* slots;
+    int n_slots;
+    uint16_t* kv_cache;     // [n_slots, Lkv]
+    int8_t* kv_cache_i8;    // [n_slots, Lkv]
+    float* kv_cache_scale;  // [n_slots]
+    uint16_t* kr_cache;     // [n_slots, R]
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 

@@ -386,6 +386,9 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     if (!has_q && (out->q_nope || out->q_pe || out->q_norm || out->q_i8 || out->q_scale))
         return MLAP_ERR_INVALID_ARG;
     if (!has_kvb && (out->k_nope || out->value)) return MLAP_ERR_INVALID_ARG;
+    // a KV cache write needs the slots and the cache size
+    const bool cache = out->kv_cache || out->kv_cache_i8 || out->kv_cache_scale || out->kr_cache;
+    if (cache && (!in->slot_mapping || in->cache_slots <= 0)) return MLAP_ERR_INVALID_ARG;
     // the q quant reads the q tensors back
     const bool quant_q = out->q_i8 || out->q_scale;
     bool quant_done = false;  // the q quant already ran per token block
@@ -499,6 +502,14 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     na.k_pe = static_cast<uint16_t*>(out->k_pe);
     na.kv_i8 = out->kv_i8;
     na.kv_scale = out->kv_scale;
+    if (cache) {
+        na.slots = in->slot_mapping;
+        na.n_slots = in->cache_slots;
+        na.kv_cache = static_cast<uint16_t*>(out->kv_cache);
+        na.kv_cache_i8 = out->kv_cache_i8;
+        na.kv_cache_scale = out->kv_cache_scale;
+        na.kr_cache = static_cast<uint16_t*>(out->kr_cache);
+    }
     const bool need_q = has_q && (out->q_nope || out->q_pe || quant_q);
     const bool need_kvb = has_kvb && (out->k_nope || out->value);
     if (need_kvb && !w8) na.kv_norm = kvn;  // the bf16 kv_b reads it

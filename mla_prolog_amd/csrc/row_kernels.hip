@@ -44,6 +44,22 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
     return t;
 }
 
+// Cache row of token t: slots[t] when the run writes a KV cache and the slot is in range,
+// else -1.
+__device__ __forceinline__ int cache_row(const NormArgs& a, int t) {
+    if (!a.slots) return -1;
+    const int s = a.slots[t];
+    return (s >= 0 && s < a.n_slots) ? s : -1;
+}
+
+// Store v at element `off` of row t of `out` and, for a token with a cache row, of row `cr`
+// of `cache` (the same row width); either pointer may be null.
+template <typename E, typename V>
+__device__ __forceinline__ void put_row(E* out, E* cache, int t, int cr, int width, int off, const V& v) {
+    if (out) *reinterpret_cast<V*>(out + static_cast<size_t>(t) * width + off) = v;
+    if (cache && cr >= 0) *reinterpret_cast<V*>(cache + static_cast<size_t>(cr) * width + off) = v;
+}
+
 // Sum over `splits` split-K fp32 partials (8 values at p + sp * stride each, split 0 first)
 // then round to bf16 (the GEMM's output cast point). Loads go out in groups of eight so a
 // group costs one memory latency; the additions stay in split order.
@@ -113,6 +129,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
+    const int cache_r = cache_row(a, t);
 
     float qv[kMaxChunks][8], kv[kMaxChunks][8];
     float sq = 0.f, skv = 0.f;
@@ -170,15 +187,14 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
                 o[e] = y * g[e];
             }
             kvo[i] = pack8(o);
-            if (a.kv_norm)
-                *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
+            put_row(a.kv_norm, a.kv_cache, t, cache_r, a.Lkv, c * 8, kvo[i]);
             kvmax = fmaxf(kvmax, absmax8(kvo[i]));
         }
     }
 
     // rotate-half RoPE of the k_pe slice (pairs i, i + R/2), one cos/sin row per token
     const int half = a.R >> 1;
-    if (a.k_pe && tid < (half >> 3)) {
+    if ((a.k_pe || a.kr_cache) && tid < (half >> 3)) {
         const int i0 = tid * 8;
         const int p = clamp_pos(a.positions[t], a.max_pos);
         const float* cr = a.cos + static_cast<size_t>(p) * a.R;
@@ -195,13 +211,12 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
             float p4 = x1[e] * sr[half + i0 + e];
             hi[e] = p3 + p4;
         }
-        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
-        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
-        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, i0, pack8(lo));
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, half + i0, pack8(hi));
     }
 
     // per-token INT8 quant of kv_norm
-    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b || a.kv_cache_i8 || a.kv_cache_scale) {
         const float amax = block_max(kvmax, red);
         const float mult = amax > 0.f ? 127.0f / amax : 0.f;
 #pragma unroll
@@ -209,15 +224,15 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
             const int c = tid + i * kRowThreads;
             if (c < nkv) {
                 const uint2 codes = quant8(kvo[i], mult);
-                const size_t off = static_cast<size_t>(t) * a.Lkv + c * 8;
-                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
-                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+                put_row(a.kv_i8, a.kv_cache_i8, t, cache_r, a.Lkv, c * 8, codes);
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + static_cast<size_t>(t) * a.Lkv + c * 8) = codes;
             }
         }
         if (tid == 0) {
             const float sc = amax / 127.0f;
             if (a.kv_scale) a.kv_scale[t] = sc;
             if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+            if (a.kv_cache_scale && cache_r >= 0) a.kv_cache_scale[cache_r] = sc;
         }
     }
     // W8A8: per-token activation quant of q_norm for the int8 up projection
@@ -247,6 +262,7 @@ template <int QC, int KC, int SPL>
 __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* red) {
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int cache_r = cache_row(a, t);
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
     const int half = a.R >> 1;
     // A chunk's raw input: up to 8 splits of float4 pairs (one fetch group), or one uint4 of
@@ -296,7 +312,7 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
         }
     };
 
-    const bool rope = a.k_pe != nullptr && half >= 8;
+    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr) && half >= 8;
     const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
     const bool roper = rope && tid < (half >> 3);
     const int i0 = rope ? min(tid, (half >> 3) - 1) * 8 : 0;
@@ -424,7 +440,7 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
         }
         kvo[c] = pack8(o);
         if (ch < nkv) {
-            if (a.kv_norm) *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + ch * 8) = kvo[c];
+            put_row(a.kv_norm, a.kv_cache, t, cache_r, a.Lkv, ch * 8, kvo[c]);
             kvmax = fmaxf(kvmax, absmax8(kvo[c]));
         }
     });
@@ -445,13 +461,12 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
             float p4 = x1[e] * shv[e];
             hi[e] = p3 + p4;
         }
-        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
-        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
-        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, i0, pack8(lo));
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, half + i0, pack8(hi));
     }
 
     // per-token INT8 quant of kv_norm
-    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b || a.kv_cache_i8 || a.kv_cache_scale) {
         const float amax = block_max(kvmax, red);
         const float mult = amax > 0.f ? 127.0f / amax : 0.f;
         static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
@@ -459,15 +474,15 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
             const int ch = tid + kRowThreads * c;
             if (ch < nkv) {
                 const uint2 codes = quant8(kvo[c], mult);
-                const size_t off = static_cast<size_t>(t) * a.Lkv + ch * 8;
-                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
-                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+                put_row(a.kv_i8, a.kv_cache_i8, t, cache_r, a.Lkv, ch * 8, codes);
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + static_cast<size_t>(t) * a.Lkv + ch * 8) = codes;
             }
         });
         if (tid == 0) {
             const float sc = amax / 127.0f;
             if (a.kv_scale) a.kv_scale[t] = sc;
             if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+            if (a.kv_cache_scale && cache_r >= 0) a.kv_cache_scale[cache_r] = sc;
         }
     }
     // W8A8: per-token activation quant of q_norm for the int8 up projection
@@ -502,10 +517,11 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T) return;  // the whole wave leaves; nothing below synchronises the workgroup
+    const int cache_r = cache_row(a, t);
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
     const int half = a.R >> 1;
     const int rc = half >> 3;  // rope chunks per half
-    const bool rope = a.k_pe != nullptr && rc > 0;
+    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr) && rc > 0;
     const uint16_t* arow = a.a_bf16 + static_cast<size_t>(t) * a.N1;
     const int c_rope = a.Lq + a.Lkv;  // first column of the rope slice
     // rope slice from the tail partials, one (chunk, split) pair per lane
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
         }
         kvo[i] = pack8(o);
         if (c < nkv) {
-            if (a.kv_norm) *reinterpret_cast<uint4*>(a.kv_norm + static_cast<size_t>(t) * a.Lkv + c * 8) = kvo[i];
+            put_row(a.kv_norm, a.kv_cache, t, cache_r, a.Lkv, c * 8, kvo[i]);
             kvmax = fmaxf(kvmax, absmax8(kvo[i]));
         }
     }
@@ -656,13 +672,12 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
             float p4 = x1[e] * shv[e];
             hi[e] = p3 + p4;
         }
-        uint16_t* dst = a.k_pe + static_cast<size_t>(t) * a.R;
-        *reinterpret_cast<uint4*>(dst + i0) = pack8(lo);
-        *reinterpret_cast<uint4*>(dst + half + i0) = pack8(hi);
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, i0, pack8(lo));
+        put_row(a.k_pe, a.kr_cache, t, cache_r, a.R, half + i0, pack8(hi));
     }
 
     // ---- per-token INT8 quant of kv_norm
-    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b) {
+    if (a.kv_i8 || a.kv_scale || a.kv_i8_b || a.kv_scale_b || a.kv_cache_i8 || a.kv_cache_scale) {
         const float amax = wave_max(kvmax);
         const float mult = amax > 0.f ? 127.0f / amax : 0.f;
 #pragma unroll
@@ -670,15 +685,15 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
             const int c = lane + 64 * i;
             if (c < nkv) {
                 const uint2 codes = quant8(kvo[i], mult);
-                const size_t off = static_cast<size_t>(t) * a.Lkv + c * 8;
-                if (a.kv_i8) *reinterpret_cast<uint2*>(a.kv_i8 + off) = codes;
-                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + off) = codes;
+                put_row(a.kv_i8, a.kv_cache_i8, t, cache_r, a.Lkv, c * 8, codes);
+                if (a.kv_i8_b) *reinterpret_cast<uint2*>(a.kv_i8_b + static_cast<size_t>(t) * a.Lkv + c * 8) = codes;
             }
         }
         if (lane == 0) {
             const float sc = amax / 127.0f;
             if (a.kv_scale) a.kv_scale[t] = sc;
             if (a.kv_scale_b) a.kv_scale_b[t] = sc;
+            if (a.kv_cache_scale && cache_r >= 0) a.kv_cache_scale[cache_r] = sc;
         }
     }
     // W8A8: per-token activation quant of q_norm for the int8 up projection

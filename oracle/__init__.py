@@ -75,6 +75,9 @@ def load():
                                             C.c_void_p]
             lib.orc_rope_row.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
             lib.orc_quant_row.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+            lib.orc_cache_scatter.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
+                                              C.c_int64, C.c_void_p]
+            lib.orc_cache_scatter.restype = C.c_int
             lib.orc_prolog.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p, C.c_int32,
                                        C.POINTER(_Outputs)]
             lib.orc_prolog.restype = C.c_int
@@ -263,3 +266,36 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
     if rc != 0:
         raise ValueError("oracle rejected the inputs (rc=%d)" % rc)
     return outs
+
+
+# --------------------------------------------------------------- KV cache ----
+
+# cache name -> the per-token output whose rows it holds
+CACHE_OF = {"kv_cache": "kv_norm", "kv_cache_i8": "kv_i8", "kv_cache_scale": "kv_scale",
+            "kr_cache": "k_pe"}
+
+
+def cache_scatter(slots, rows, cache):
+    """Row t of ``rows`` into row ``slots[t]`` of ``cache`` (in place) when the slot is in
+    [0, len(cache)); other rows untouched. The ScatterUpdate of the prolog's results into
+    the K cache ([V32] page, section 2.4; [BLOG] page, step 2). Raises on repeated slots."""
+    slots = np.ascontiguousarray(slots, np.int32)
+    rows = np.ascontiguousarray(rows)
+    assert cache.flags.c_contiguous and cache.dtype == rows.dtype
+    assert rows.shape[0] == slots.size and cache.shape[1:] == rows.shape[1:]
+    row_bytes = rows.dtype.itemsize * int(np.prod(rows.shape[1:], dtype=np.int64))
+    rc = load().orc_cache_scatter(_p(slots), int(slots.size), int(cache.shape[0]), _p(rows),
+                                  row_bytes, _p(cache))
+    if rc != 0:
+        raise ValueError("two tokens share a cache slot")
+    return cache
+
+
+def kv_cache_write(outs, slots, caches):
+    """Apply the KV cache write of one run: ``outs`` the oracle's per-token outputs of all
+    T tokens (``prolog``), ``caches`` a dict name -> numpy cache (see CACHE_OF), updated in
+    place and returned."""
+    for name, cache in caches.items():
+        cache_scatter(slots, outs[CACHE_OF[name]], cache)
+    return caches
+

@@ -361,6 +361,27 @@ ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* 
     return orc_prolog_from(cfg, in, rows, nrows, NULL, NULL, out);
 }
 
+/* ------------------------------------------------------------ KV cache --- */
+
+/* The KV cache write: the prolog's per-token rows placed at their tokens' cache rows, the
+ * ScatterUpdate of the results into the K cache named in the [V32] page (section 2.4) and
+ * the caching of the per-row quantised rows in step 2 of the [BLOG] page. Row t of src
+ * (row_bytes each) goes to row slots[t] of dst when 0 <= slots[t] < n_slots; every other
+ * row of dst is left as it was. Returns -1 if two in-range slots of the run coincide (the
+ * caller's contract), else 0. */
+ORC_API int orc_cache_scatter(const int32_t* slots, int32_t T, int32_t n_slots, const void* src,
+                              int64_t row_bytes, void* dst) {
+    for (int32_t t = 0; t < T; ++t) {
+        const int32_t s = slots[t];
+        if (s < 0 || s >= n_slots) continue;
+        for (int32_t u = 0; u < t; ++u)
+            if (slots[u] == s) return -1;
+        memcpy((char*)dst + (size_t)s * (size_t)row_bytes, (const char*)src + (size_t)t * (size_t)row_bytes,
+               (size_t)row_bytes);
+    }
+    return 0;
+}
+
 ORC_API int orc_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

@@ -40,7 +40,8 @@ from dataclasses import dataclass, asdict, replace
 
 import torch
 
-__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "rope_table", "seed_for"]
+__all__ = ["Config", "CONFIGS", "get_config", "make_inputs", "rope_table", "seed_for",
+           "slot_mapping"]
 
 
 @dataclass(frozen=True)
@@ -122,6 +123,21 @@ def rope_table(max_pos: int, rope_dim: int, base: float = 10000.0):
     ang = pos[:, None] * inv[None, :]
     ang = torch.cat([ang, ang], dim=1)
     return torch.cos(ang).to(torch.float32).contiguous(), torch.sin(ang).to(torch.float32).contiguous()
+
+
+def slot_mapping(T: int, n_slots: int, seed: int = 0, pad_frac: float = 0.08,
+                 out_of_range: int = 2):
+    """KV cache slots [T] int32 for a run of T tokens: distinct rows of a cache of n_slots
+    (n_slots >= T) in random order, about pad_frac of them -1 (padding tokens), and
+    `out_of_range` tokens at n_slots or beyond (not written)."""
+    g = torch.Generator().manual_seed(int(seed))
+    slots = torch.randperm(n_slots, generator=g)[:T].to(torch.int32)
+    pad = torch.rand(T, generator=g) < pad_frac
+    slots[pad] = -1
+    if T > 0 and out_of_range > 0:
+        idx = torch.randperm(T, generator=g)[:out_of_range]
+        slots[idx] = n_slots + torch.arange(idx.numel(), dtype=torch.int32) * 7
+    return slots.contiguous()
 
 
 def _normal(g, shape, std):

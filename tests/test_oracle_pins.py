@@ -377,3 +377,40 @@ def test_golden_v2lite_case_shapes():
     assert out["value"].shape == (b * s, cfg.n_heads, cfg.v_dim)
     assert out["k_pe"].shape == (b * s, cfg.rope_dim)
     assert case["eps"] == cfg.eps
+
+
+# ------------------------------------------------------------------ KV cache ----
+
+def test_cache_scatter_hand_example():
+    """The cache write on a hand-made run: token rows land at their slots; padding (-1) and
+    out-of-range slots write nothing; the other rows keep their contents."""
+    rows = np.array([[11, 12, 13], [21, 22, 23], [31, 32, 33], [41, 42, 43], [51, 52, 53]],
+                    dtype=np.uint16)
+    slots = [4, -1, 0, 6, 2]          # 6 is past a 5-row cache
+    cache = np.full((5, 3), 7, dtype=np.uint16)
+    oracle.cache_scatter(slots, rows, cache)
+    expect = np.array([[31, 32, 33], [7, 7, 7], [51, 52, 53], [7, 7, 7], [11, 12, 13]],
+                      dtype=np.uint16)
+    np.testing.assert_array_equal(cache, expect)
+    # one value per row (the scales) and int8 rows take the same path
+    sc = np.zeros(5, np.float32)
+    oracle.cache_scatter(slots, np.array([1.5, 2.5, 3.5, 4.5, 5.5], np.float32), sc)
+    np.testing.assert_array_equal(sc, [3.5, 0, 5.5, 0, 1.5])
+    c8 = np.zeros((5, 2), np.int8)
+    oracle.cache_scatter(slots, np.array([[1, -1], [2, -2], [3, -3], [4, -4], [5, -5]], np.int8), c8)
+    np.testing.assert_array_equal(c8, [[3, -3], [0, 0], [5, -5], [0, 0], [1, -1]])
+
+
+def test_cache_scatter_rejects_repeated_slots():
+    with pytest.raises(ValueError):
+        oracle.cache_scatter([1, 3, 1], np.zeros((3, 2), np.uint16), np.zeros((4, 2), np.uint16))
+    # padding may repeat
+    oracle.cache_scatter([-1, 3, -1], np.ones((3, 2), np.uint16), np.zeros((4, 2), np.uint16))
+
+
+def test_slot_mapping_generator():
+    s = synth.slot_mapping(300, 1024, seed=3).numpy()
+    valid = s[(s >= 0) & (s < 1024)]
+    assert len(np.unique(valid)) == valid.size          # distinct in-range slots
+    assert (s == -1).any() and (s >= 1024).sum() == 2   # padding and out-of-range tokens
+    np.testing.assert_array_equal(s, synth.slot_mapping(300, 1024, seed=3).numpy())
