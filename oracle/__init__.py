@@ -39,7 +39,8 @@ def build(force: bool = True) -> str:
 class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("hidden", "q_lora", "kv_lora", "rope_dim", "nope_dim",
                                           "v_dim", "n_heads", "max_pos")] + \
-               [("eps", C.c_float), ("w8a8", C.c_int32)]
+               [("eps", C.c_float), ("w8a8", C.c_int32), ("norm_rsqrt", C.c_int32),
+                ("rope_chunk", C.c_int32), ("q_quant_per_head", C.c_int32)]
 
 
 class _Inputs(C.Structure):
@@ -74,6 +75,10 @@ def load():
             lib.orc_rmsnorm_row.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_float,
                                             C.c_void_p]
             lib.orc_rope_row.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+            lib.orc_rmsnorm_row_rsqrt.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_float,
+                                                  C.c_void_p]
+            lib.orc_rope_row_chunked.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                                 C.c_int64, C.c_void_p]
             lib.orc_quant_row.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
             lib.orc_cache_scatter.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
                                               C.c_int64, C.c_void_p]
@@ -167,6 +172,27 @@ def rmsnorm_row(v, gamma, eps):
     return out
 
 
+def rmsnorm_row_rsqrt(v, gamma, eps):
+    """RMSNorm variant A: sum of squares, times 1/D, + eps, rsqrt (one rounding), times
+    fp32(gamma), cast to bf16. AT-10 card, section 三 (variant A)."""
+    v = _np(v, np.uint16).reshape(-1)
+    g = None if gamma is None else _np(gamma, np.uint16).reshape(-1)
+    out = np.empty_like(v)
+    load().orc_rmsnorm_row_rsqrt(_p(v), _p(g), v.size, C.c_float(eps), _p(out))
+    return out
+
+
+def rope_row_chunked(u, c, s, chunk=2):
+    """The QuantRope3D form: the slice viewed as [R/chunk, chunk], the two axes transposed,
+    then rotate-half; output in the transposed order. "PyPTO Operator 深度解析", section 3.3."""
+    u = _np(u, np.uint16).reshape(-1)
+    c = np.ascontiguousarray(c, np.float32).reshape(-1)
+    s = np.ascontiguousarray(s, np.float32).reshape(-1)
+    out = np.empty_like(u)
+    load().orc_rope_row_chunked(_p(u), _p(c), _p(s), u.size, int(chunk), _p(out))
+    return out
+
+
 def rope_row(u, c, s):
     """Rotate-half RoPE of one slice: x*cos + rotate_half(x)*sin, fp32, back to bf16.
 
@@ -253,11 +279,14 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
     if Lq > 0:
         outs.update(q_nope=np.empty((n, H, Dn), np.uint16), q_pe=np.empty((n, H, R), np.uint16),
                     q_norm=np.empty((n, Lq), np.uint16), q_i8=np.empty((n, H, Dn + R), np.int8),
-                    q_scale=np.empty((n,), np.float32))
+                    q_scale=np.empty((n, H) if getattr(cfg, "q_quant_per_head", False) else (n,),
+                                     np.float32))
     if Dv > 0:
         outs.update(k_nope=np.empty((n, H, Dn), np.uint16), value=np.empty((n, H, Dv), np.uint16))
 
-    c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8))
+    c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8),
+             int(getattr(cfg, "norm_rsqrt", False)), 2 if getattr(cfg, "rope_interleaved", False) else 0,
+             int(getattr(cfg, "q_quant_per_head", False)))
     i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
     o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
     qn = None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq)

@@ -155,6 +155,28 @@ ORC_API void orc_rmsnorm_row(const uint16_t* v, const uint16_t* gamma, int64_t D
     }
 }
 
+/* Variant A ([AT-10] section 三, AT-03 rsqrt_mode): sum of the squares (fp64, rounded once to
+ * fp32), times 1/D in fp32 (= mean_sq), + eps, rstd = 1/sqrt(var) rounded once to fp32 (the
+ * rsqrt), out_k = bf16((y_k*rstd)*f32(gamma_k)). */
+ORC_API void orc_rmsnorm_row_rsqrt(const uint16_t* v, const uint16_t* gamma, int64_t D, float eps,
+                                   uint16_t* out) {
+    const float invD = 1.0f / (float)D;
+    double s = 0.0;
+    for (int64_t k = 0; k < D; ++k) {
+        float y = orc_f32(v[k]);
+        float sq = y * y;
+        s += (double)sq;
+    }
+    float mean_sq = (float)s * invD;
+    float var = mean_sq + eps;
+    float rstd = (float)(1.0 / sqrt((double)var));
+    for (int64_t k = 0; k < D; ++k) {
+        float y = orc_f32(v[k]) * rstd;
+        if (gamma) y = y * orc_f32(gamma[k]);
+        out[k] = orc_bf16(y);
+    }
+}
+
 /* ---------------------------------------------------------------- RoPE ---- */
 
 /* Rotate-half RoPE of one R-wide slice u (bf16) with the token's cos/sin rows:
@@ -175,6 +197,20 @@ ORC_API void orc_rope_row(const uint16_t* u, const float* c, const float* s, int
         out[i] = orc_bf16(lo);
         out[i + h] = orc_bf16(hi);
     }
+}
+
+/* The QuantRope3D form ([V32] section 3.3): the slice is viewed as R/CHUNK chunks of CHUNK
+ * values, the two axes are transposed, and rotate-half is applied to the result. With
+ * CHUNK = 2 the transpose de-interleaves adjacent pairs (u_0 u_2 u_4 ... | u_1 u_3 ...), so
+ * pair (2i, 2i+1) rotates with the cos/sin of columns i and i + R/2; the output keeps the
+ * transposed (half-split) order. */
+ORC_API void orc_rope_row_chunked(const uint16_t* u, const float* c, const float* s, int64_t R,
+                                  int64_t chunk, uint16_t* out) {
+    uint16_t t[1024];
+    const int64_t nch = R / chunk;
+    for (int64_t a = 0; a < nch; ++a)          /* [nch, chunk] -> [chunk, nch] */
+        for (int64_t b = 0; b < chunk; ++b) t[b * nch + a] = u[a * chunk + b];
+    orc_rope_row(t, c, s, R, out);
 }
 
 /* --------------------------------------------------------------- Quant ---- */
@@ -215,6 +251,9 @@ typedef struct {
     int32_t hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads, max_pos;
     float eps;
     int32_t w8a8;
+    int32_t norm_rsqrt;       /* RMSNorm variant A instead of B */
+    int32_t rope_chunk;       /* 0: rotate-half on the slice as is; else the QuantRope3D form */
+    int32_t q_quant_per_head; /* q codes and scales per (token, head) instead of per token */
 } orc_cfg;
 
 typedef struct {
@@ -243,10 +282,26 @@ typedef struct { /* every array is [nrows, ...] in the order of rows[] */
     uint16_t* value;    /* [nrows, H, v] (kv_b) */
     uint16_t* q_norm;   /* [nrows, q_lora] */
     int8_t* q_i8;       /* [nrows, H, nope+rope] */
-    float* q_scale;     /* [nrows] */
+    float* q_scale;     /* [nrows], or [nrows, H] per head */
     int8_t* kv_i8;      /* [nrows, kv_lora] */
     float* kv_scale;    /* [nrows] */
 } orc_outputs;
+
+static void orc_norm(const orc_cfg* cfg, const uint16_t* v, const uint16_t* gamma, int64_t D,
+                     uint16_t* out) {
+    if (cfg->norm_rsqrt)
+        orc_rmsnorm_row_rsqrt(v, gamma, D, cfg->eps, out);
+    else
+        orc_rmsnorm_row(v, gamma, D, cfg->eps, out);
+}
+
+static void orc_rope(const orc_cfg* cfg, const uint16_t* u, const float* c, const float* s,
+                     int64_t R, uint16_t* out) {
+    if (cfg->rope_chunk > 0)
+        orc_rope_row_chunked(u, c, s, R, cfg->rope_chunk, out);
+    else
+        orc_rope_row(u, c, s, R, out);
+}
 
 /* One projection of one bf16 row v (length K) through W [N,K]: bf16 or W8A8. */
 static void orc_project(const orc_cfg* cfg, const uint16_t* v, int64_t K, const void* W,
@@ -279,6 +334,7 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
     const int64_t Dn = cfg->nope_dim, Dv = cfg->v_dim, H = cfg->n_heads;
     const int64_t QH = Dn + R, KH = Dn + Dv;
     if (R <= 0 || (R & 1) || Lkv <= 0 || Hd <= 0) return -1;
+    if (cfg->rope_chunk < 0 || (cfg->rope_chunk > 0 && (R % cfg->rope_chunk || R > 1024))) return -1;
     for (int32_t i = 0; i < nrows; ++i) {
         int32_t p = in->positions[rows[i]];
         if (p < 0 || p >= cfg->max_pos) return -1;
@@ -309,9 +365,9 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
 
         /* kv branch: kv_a projection -> [c_kv | k_pe] */
         orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, Lkv + R, a, codes);
-        orc_rmsnorm_row(a, in->gamma_kv, Lkv, cfg->eps, kvn);
+        orc_norm(cfg, a, in->gamma_kv, Lkv, kvn);
         if (out->kv_norm) memcpy(out->kv_norm + i * Lkv, kvn, sizeof(uint16_t) * (size_t)Lkv);
-        if (out->k_pe) orc_rope_row(a + Lkv, c, s, R, out->k_pe + i * R);
+        if (out->k_pe) orc_rope(cfg, a + Lkv, c, s, R, out->k_pe + i * R);
         if (out->kv_i8 || out->kv_scale) {
             float sc;
             orc_quant_row(kvn, Lkv, codes, &sc);
@@ -332,7 +388,7 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
         /* q branch: q_a projection -> RMSNorm*gamma -> q_b projection -> split, RoPE */
         if (Lq > 0) {
             orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, Lq, a, codes);
-            orc_rmsnorm_row(a, in->gamma_q, Lq, cfg->eps, qn);
+            orc_norm(cfg, a, in->gamma_q, Lq, qn);
             if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
             const uint16_t* q_src = qn_given ? qn_given + i * Lq : qn;
             orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
@@ -340,11 +396,18 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
                 const uint16_t* head = a + h * QH;
                 uint16_t* qh = qrow + h * QH;
                 memcpy(qh, head, sizeof(uint16_t) * (size_t)Dn);
-                orc_rope_row(head + Dn, c, s, R, qh + Dn);
+                orc_rope(cfg, head + Dn, c, s, R, qh + Dn);
                 if (out->q_nope) memcpy(out->q_nope + (i * H + h) * Dn, qh, sizeof(uint16_t) * (size_t)Dn);
                 if (out->q_pe) memcpy(out->q_pe + (i * H + h) * R, qh + Dn, sizeof(uint16_t) * (size_t)R);
             }
-            if (out->q_i8 || out->q_scale) {
+            if ((out->q_i8 || out->q_scale) && cfg->q_quant_per_head) {
+                for (int64_t h = 0; h < H; ++h) {  /* each head's [nope | pe] row on its own */
+                    float sc;
+                    orc_quant_row(qrow + h * QH, QH, codes, &sc);
+                    if (out->q_i8) memcpy(out->q_i8 + (i * H + h) * QH, codes, (size_t)QH);
+                    if (out->q_scale) out->q_scale[i * H + h] = sc;
+                }
+            } else if (out->q_i8 || out->q_scale) {
                 float sc;
                 orc_quant_row(qrow, H * QH, codes, &sc);
                 if (out->q_i8) memcpy(out->q_i8 + i * H * QH, codes, (size_t)(H * QH));

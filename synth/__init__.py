@@ -62,6 +62,10 @@ class Config:
     outlier_frac: float = 0.0    # fraction of hidden channels scaled by outlier_scale
     outlier_scale: float = 20.0
     index: int = 0               # seed = 1000 + index
+    # numeric variants (flags of the prolog, not of the inputs)
+    norm_rsqrt: bool = False        # RMSNorm variant A
+    rope_interleaved: bool = False  # rope slices de-interleaved before rotate-half
+    q_quant_per_head: bool = False  # q codes / scales per (token, head)
 
     def asdict(self):
         return asdict(self)
@@ -104,10 +108,14 @@ CONFIGS = {
 }
 
 
-def get_config(name: str, T: int | None = None) -> Config:
+def get_config(name: str, T: int | None = None, **variants) -> Config:
+    """A named configuration, optionally with another token count and variant flags
+    (norm_rsqrt, rope_interleaved, q_quant_per_head)."""
     cfg = CONFIGS[name]
     if T is not None:
         cfg = replace(cfg, T=int(T))
+    if variants:
+        cfg = replace(cfg, **variants)
     return cfg
 
 

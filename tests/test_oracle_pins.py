@@ -414,3 +414,81 @@ def test_slot_mapping_generator():
     assert len(np.unique(valid)) == valid.size          # distinct in-range slots
     assert (s == -1).any() and (s >= 1024).sum() == 2   # padding and out-of-range tokens
     np.testing.assert_array_equal(s, synth.slot_mapping(300, 1024, seed=3).numpy())
+
+
+# ------------------------------------------------------- numeric variants ----
+
+def test_rmsnorm_variant_a_closed_forms():
+    """Variant A (rsqrt, 1/D after the sum): constant and alternating rows give +-gamma, the
+    eps closed form holds, and it agrees with the fp64 definition within one bf16 ulp."""
+    D = 512
+    gamma = to_bf16_bits(rng.uniform(0.5, 1.5, D))
+    for c in (1.0, -3.5, 0.25, 200.0):
+        out = oracle.rmsnorm_row_rsqrt(to_bf16_bits(np.full(D, c)), gamma, 1e-6)
+        np.testing.assert_array_equal(from_bits(out), np.sign(c) * from_bits(gamma))
+    row = np.where(np.arange(D) % 2 == 0, 0.75, -0.75)
+    np.testing.assert_array_equal(from_bits(oracle.rmsnorm_row_rsqrt(to_bf16_bits(row), None, 1e-6)),
+                                  np.sign(row))
+    y = np.full(64, 1e-3, np.float32)
+    yb = from_bits(to_bf16_bits(y))[0].astype(np.float64)
+    np.testing.assert_allclose(from_bits(oracle.rmsnorm_row_rsqrt(to_bf16_bits(y), None, 1e-6)),
+                               yb / np.sqrt(yb * yb + 1e-6), rtol=2 ** -8)
+    for trial in range(20):
+        y = from_bits(to_bf16_bits(rng.standard_normal(D) * rng.uniform(0.01, 10)))
+        g = from_bits(to_bf16_bits(rng.uniform(0.5, 1.5, D)))
+        ref = y.astype(np.float64) / np.sqrt(np.mean(y.astype(np.float64) ** 2) + 1e-6) * g
+        out = oracle.rmsnorm_row_rsqrt(to_bf16_bits(y), to_bf16_bits(g), 1e-6)
+        d = ulp_diff(out, to_bf16_bits(ref.astype(np.float32)))
+        assert d.max() <= 1 and (d == 0).mean() > 0.98
+        # the two variants differ only in the last bits
+        assert ulp_diff(out, oracle.rmsnorm_row(to_bf16_bits(y), to_bf16_bits(g), 1e-6)).max() <= 1
+
+
+def test_chunked_rope_position_zero_deinterleaves():
+    """QuantRope3D with chunk 2 at cos = 1, sin = 0: the output is the input with adjacent
+    pairs split into the two halves (u0 u2 u4 ... | u1 u3 u5 ...)."""
+    R = 64
+    cos, sin = synth.rope_table(4, R)
+    u = to_bf16_bits(rng.standard_normal(R))
+    out = oracle.rope_row_chunked(u, cos[0].numpy(), sin[0].numpy(), 2)
+    np.testing.assert_array_equal(from_bits(out), np.concatenate([from_bits(u)[0::2], from_bits(u)[1::2]]))
+    # chunk = R is one chunk: no transpose, plain rotate-half
+    p = 3
+    np.testing.assert_array_equal(oracle.rope_row_chunked(u, cos[p].numpy(), sin[p].numpy(), R),
+                                  oracle.rope_row(u, cos[p].numpy(), sin[p].numpy()))
+
+
+def test_chunked_rope_is_the_interleaved_pair_rotation():
+    """With chunk 2, pair (u_2i, u_2i+1) is rotated by p*theta_i as the complex number
+    u_2i + j u_2i+1 (the interleaved-pair RoPE), real parts to column i, imaginary to i + R/2."""
+    R, P = 64, 8192
+    cos, sin = synth.rope_table(P, R)
+    h = R // 2
+    theta = np.array([10000.0 ** (-2.0 * i / R) for i in range(h)])
+    for p in (1, 7, 1000, 8191):
+        u = to_bf16_bits(rng.standard_normal(R))
+        uf = from_bits(u).astype(np.float64)
+        z = (uf[0::2] + 1j * uf[1::2]) * np.exp(1j * p * theta)
+        ref = np.concatenate([z.real, z.imag]).astype(np.float32)
+        out = oracle.rope_row_chunked(u, cos[p].numpy(), sin[p].numpy(), 2)
+        np.testing.assert_allclose(from_bits(out), ref, rtol=2 ** -7, atol=1e-6)
+
+
+def test_per_head_q_quant():
+    """Per-(token, head) q quant: each head's [nope | pe] row is quantised on its own; every
+    head reaches code 127 and the token's q row reconstructs within half a scale per head
+    (plus the fp32 rounding of z * 127/amax, at most 127 * 2^-24 code units)."""
+    cfg = synth.get_config("v3_decode", T=2, q_quant_per_head=True)
+    inp = synth.make_inputs(cfg)
+    out = oracle.prolog(cfg, inp, rows=np.array([1], np.int32))
+    H, QH = cfg.n_heads, cfg.nope_dim + cfg.rope_dim
+    q = np.concatenate([from_bits(out["q_nope"][0]), from_bits(out["q_pe"][0])], axis=1)  # [H, QH]
+    codes = out["q_i8"][0].reshape(H, QH).astype(np.float64)
+    sc = out["q_scale"][0]
+    assert sc.shape == (H,)
+    assert (np.abs(codes).max(1) == 127).all()
+    np.testing.assert_allclose(sc, np.abs(q).max(1) / 127.0, rtol=1e-7)
+    assert (np.abs(q - codes * sc[:, None]) <= sc[:, None] * (0.5 + 2.0 ** -16)).all()
+    # the per-token form of the same run has one scale: the largest head's
+    tok = oracle.prolog(synth.get_config("v3_decode", T=2), inp, rows=np.array([1], np.int32))
+    assert tok["q_scale"][0] == sc.max()
