@@ -96,13 +96,19 @@ def measured_traffic(workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, kv_cache=False):
+VARIANTS = dict(norm_rsqrt=True, rope_interleaved=True, q_quant_per_head=True)
+
+
+def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, kv_cache=False,
+                   variants=False):
     """Times `steps` whole prolog runs of workload `name`, cycling through `rotate` input and
     weight sets. Two timed passes: eager (one mlap_run per step from a prepared call, with
     HIP events around every launch of the dominant kernel) and, when `graph`, the same
     steps replayed from a HIP graph that captured `rotate` consecutive runs (no host
     launch cost between kernels). With `kv_cache`, every step also writes the kv rows of its
-    tokens into KV caches of 4 T slots (all four caches, every token cached). Returns (cfg,
+    tokens into KV caches of 4 T slots (all four caches, every token cached); with
+    `variants`, the run uses RMSNorm variant A, the de-interleaved RoPE and per-head q
+    quant (VARIANTS). Returns (cfg,
     eager ms/step, dominant kernel ms, eager percentiles, graph ms/step or None, graph
     percentiles or None)."""
     import torch
@@ -110,7 +116,7 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, k
     import mla_prolog_amd as mlap
     import synth
 
-    cfg = synth.get_config(name)
+    cfg = synth.get_config(name, **(VARIANTS if variants else {}))
     T = cfg.T
     sets = []
     for r in range(rotate):
@@ -224,7 +230,7 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache",
+    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache,v3_decode+variants",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -321,7 +327,8 @@ def main():
         rot = 4 if ecfg0.T <= 512 else 1
         ecfg, ee_ms, ek_ms, ee_pct, eg_ms, eg_pct = bench_workload(base, a.steps, a.warmup, rotate=rot,
                                                                    dominant=dom, graph=not a.no_graph,
-                                                                   kv_cache=opt == "kvcache")
+                                                                   kv_cache=opt == "kvcache",
+                                                                   variants=opt == "variants")
         e_use_g = eg_ms is not None and eg_ms < ee_ms
         ems, epct = (eg_ms, eg_pct) if e_use_g else (ee_ms, ee_pct)
         epf, epb = path_work(ecfg, ecfg.T) if ecfg.q_lora else (None, None)
@@ -331,6 +338,8 @@ def main():
                "launch": "hip_graph" if e_use_g else "eager", "eager_ms_per_step": round(ee_ms, 5),
                "graph_ms_per_step": round(eg_ms, 5) if eg_ms else None,
                "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
+        if opt == "variants":
+            ent["variants"] = "RMSNorm variant A (rsqrt), de-interleaved RoPE, per-(token, head) q quant"
         if opt == "kvcache":
             ent["kv_cache"] = {"slots": 4 * ecfg.T, "caches": "kv_norm bf16, kv codes, kv scale, k_pe",
                                "bytes_per_token": ecfg.kv_lora * 3 + 4 + ecfg.rope_dim * 2}

@@ -65,6 +65,18 @@ typedef enum {
 
 /* Configuration flags. */
 #define MLAP_W8A8 0x1u /* int8 weights + per-output-channel fp32 scales; W8A8 GEMMs */
+/* Numeric variants the pages describe besides the default path:
+ * MLAP_NORM_RSQRT: RMSNorm variant A of the AT-10 card (section 三): sum of squares, times
+ *   1/D, + eps, rsqrt; the default is variant B (x^2/D summed, sqrt, divide).
+ * MLAP_ROPE_INTERLEAVED: the QuantRope3D form of the [V32] page (section 3.3) with chunk 2:
+ *   each raw rope slice (q_pe per head, k_pe) is de-interleaved (u0 u2 ... | u1 u3 ...) before
+ *   rotate-half; the outputs keep the split-half order. cos/sin as for the default.
+ * MLAP_QUANT_Q_PER_HEAD: q codes and scales per (token, head): the per-row max of [V32]
+ *   section 3.1 over the last axis of the [T, H, Dn+R] q tensor; q_scale is then [T, H].
+ *   Needs H <= 1024 and H*(Dn+R) <= 32768. */
+#define MLAP_NORM_RSQRT 0x2u
+#define MLAP_ROPE_INTERLEAVED 0x4u
+#define MLAP_QUANT_Q_PER_HEAD 0x8u
 
 typedef struct {
     int32_t t_max;    /* largest token count a run may pass (sizes nothing on device) */
@@ -77,7 +89,7 @@ typedef struct {
     int32_t n_heads;  /* attention heads */
     int32_t max_pos;  /* rows of the cos/sin tables */
     float eps;        /* RMSNorm epsilon (added to the mean square) */
-    uint32_t flags;   /* MLAP_W8A8 */
+    uint32_t flags;   /* MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD */
 } mlap_config;
 
 /*
@@ -124,7 +136,7 @@ typedef struct {
     void* value;      /* [T, H, Dv] bf16                      (needs Dv > 0) */
     void* q_norm;     /* [T, Lq]    bf16, the normalised q_a projection (optional) */
     int8_t* q_i8;     /* [T, H, Dn+R] int8 codes of [q_nope | q_pe] per head */
-    float* q_scale;   /* [T] fp32, amax/127 over the token's H*(Dn+R) values */
+    float* q_scale;   /* [T] fp32, amax/127 over the token's H*(Dn+R) values ([T, H] per head) */
     int8_t* kv_i8;    /* [T, Lkv] int8 codes of kv_norm */
     float* kv_scale;  /* [T] fp32 */
     /* KV cache rows written at mlap_inputs.slot_mapping: the ScatterUpdate of the prolog's kv

@@ -23,6 +23,9 @@ _LIB = os.path.join(_HERE, "libmlap.so")
 
 MLAP_OK, MLAP_ERR_INVALID_ARG, MLAP_ERR_UNSUPPORTED, MLAP_ERR_WORKSPACE, MLAP_ERR_HIP = range(5)
 MLAP_W8A8 = 0x1
+MLAP_NORM_RSQRT = 0x2        # RMSNorm variant A
+MLAP_ROPE_INTERLEAVED = 0x4  # rope slices de-interleaved before rotate-half
+MLAP_QUANT_Q_PER_HEAD = 0x8  # q codes / scales per (token, head)
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_timing_begin", "mlap_timing_end",
@@ -136,13 +139,18 @@ class Prolog:
     """One MLA Prolog configuration (a host-side handle; holds no device memory)."""
 
     def __init__(self, t_max, hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads,
-                 max_pos, eps=1e-6, w8a8=False):
+                 max_pos, eps=1e-6, w8a8=False, norm_rsqrt=False, rope_interleaved=False,
+                 q_quant_per_head=False):
         self.cfg = dict(t_max=t_max, hidden=hidden, q_lora=q_lora, kv_lora=kv_lora,
                         rope_dim=rope_dim, nope_dim=nope_dim, v_dim=v_dim, n_heads=n_heads,
-                        max_pos=max_pos, eps=eps, w8a8=bool(w8a8))
+                        max_pos=max_pos, eps=eps, w8a8=bool(w8a8), norm_rsqrt=bool(norm_rsqrt),
+                        rope_interleaved=bool(rope_interleaved),
+                        q_quant_per_head=bool(q_quant_per_head))
+        flags = ((MLAP_W8A8 if w8a8 else 0) | (MLAP_NORM_RSQRT if norm_rsqrt else 0) |
+                 (MLAP_ROPE_INTERLEAVED if rope_interleaved else 0) |
+                 (MLAP_QUANT_Q_PER_HEAD if q_quant_per_head else 0))
         c = _Config(int(t_max), int(hidden), int(q_lora), int(kv_lora), int(rope_dim),
-                    int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps),
-                    MLAP_W8A8 if w8a8 else 0)
+                    int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps), flags)
         h = C.c_void_p()
         _check(_lib.mlap_create(C.byref(c), C.byref(h)), "mlap_create")
         self._h = h
@@ -151,8 +159,10 @@ class Prolog:
     @classmethod
     def from_config(cls, cfg, t_max=None):
         """Build from any object with the fields of ``synth.Config``."""
+        g = lambda k: bool(getattr(cfg, k, False))
         return cls(t_max or cfg.T, cfg.hidden, cfg.q_lora, cfg.kv_lora, cfg.rope_dim,
-                   cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8)
+                   cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8,
+                   g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"))
 
     def close(self):
         if getattr(self, "_h", None):
@@ -187,7 +197,7 @@ class Prolog:
                   "kv_scale": ((T,), f)}
         if Lq > 0:
             shapes.update(q_nope=((T, H, Dn), bf), q_pe=((T, H, R), bf), q_i8=((T, H, Dn + R), i8),
-                          q_scale=((T,), f), q_norm=((T, Lq), bf))
+                          q_scale=((T, H) if c["q_quant_per_head"] else (T,), f), q_norm=((T, Lq), bf))
         if Dv > 0:
             shapes.update(k_nope=((T, H, Dn), bf), value=((T, H, Dv), bf))
         if want is None:

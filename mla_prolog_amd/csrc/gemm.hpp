@@ -61,7 +61,27 @@ struct GemmArgs {
     int max_pos;
     float* part_amax;  // [M, n_tiles] or null
     int n_tiles;
+    // Rope slices read in de-interleaved order (pe_w > 0): in every period of pe_period
+    // columns of the whole projection, columns [pe_off, pe_off + pe_w) take weight rows
+    // pe_off + 2i (first half, i < pe_w/2) and pe_off + 2i + 1 (second half) of their
+    // period, so the output holds the slice of the interleaved-pair layout split into its
+    // halves. pe_c0: the projection column of this launch's column 0 (B, b_scale and out
+    // are offset to it).
+    int pe_period, pe_off, pe_w, pe_c0;
 };
+
+// Weight row (and per-channel scale) feeding output column n of this launch, relative to
+// its B base; a remapped row may lie outside the launch's own columns (a slice cut by the
+// launch boundary) but stays in the slice, inside one weight segment.
+__device__ __forceinline__ int b_row(const GemmArgs& g, int n) {
+    if (g.pe_w == 0) return n;
+    const int c = n + g.pe_c0;
+    const int h = c / g.pe_period;
+    const int d = c - h * g.pe_period - g.pe_off;
+    if (d < 0 || d >= g.pe_w) return n;
+    const int half = g.pe_w >> 1;
+    return h * g.pe_period + g.pe_off + (d < half ? 2 * d : 2 * (d - half) + 1) - g.pe_c0;
+}
 
 template <typename Tin>
 struct MfmaOp;
@@ -256,6 +276,15 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
     const int cc16 = (tid & 7) * 16;
     constexpr int R8 = S::NT / 8;  // rows covered by one pass of the workgroup
     const uint32_t lda32 = static_cast<uint32_t>(lda_b), ldb32 = static_cast<uint32_t>(ldb_b);
+    // byte offsets of this thread's B rows from b_base (signed: a row remapped for a
+    // de-interleaved rope slice may come from outside the tile)
+    int64_t b_off[S::CH > S::A_PER ? S::CH - S::A_PER : 1];
+    static_for<S::CH - S::A_PER>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        const int r = row0 + i * R8;
+        const int n = n0 + (r < b_last ? r : b_last);
+        b_off[i] = static_cast<int64_t>(b_row(g, n) - n0) * static_cast<int64_t>(ldb_b) + cc16;
+    });
 
     i32x4 pre[P][S::CH];
     auto fetch = [&](int kt, auto slot_c) __attribute__((always_inline)) {
@@ -269,9 +298,7 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
                 const uint32_t off = static_cast<uint32_t>(r < a_last ? r : a_last) * lda32 + cc16;
                 pre[slot][i] = *reinterpret_cast<const i32x4*>(ap + off);
             } else {
-                const int r = row0 + (i - S::A_PER) * R8;
-                const uint32_t off = static_cast<uint32_t>(r < b_last ? r : b_last) * ldb32 + cc16;
-                pre[slot][i] = *reinterpret_cast<const i32x4*>(bp + off);
+                pre[slot][i] = *reinterpret_cast<const i32x4*>(bp + b_off[i - S::A_PER]);
             }
         });
     };
@@ -397,11 +424,11 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
                             float v;
                             if constexpr (sizeof(Tin) == 1) {
                                 const int m = m0 + pass * S::TM + lr;
-                                const int n = n0 + lc;
+                                const int n = b_row(g, n0 + lc);
                                 const float as = (m < g.M) ? g.a_scale[m] : 0.f;
-                                const float bs = (n < g.N) ? ((n < g.b_split) ? g.b_scale0[n]
-                                                                              : g.b_scale1[n - g.b_split])
-                                                           : 0.f;
+                                const float bs = (n0 + lc < g.N) ? ((n < g.b_split) ? g.b_scale0[n]
+                                                                                   : g.b_scale1[n - g.b_split])
+                                                                : 0.f;
                                 const float sc = as * bs;
                                 v = static_cast<float>(acc[i][j][r]) * sc;
                             } else {

@@ -200,14 +200,14 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int n = nb + 32 * j + 8 * gq;
-                if (n + 3 < g.N && (n + 3 < g.b_split || n >= g.b_split)) {
+                if (g.pe_w == 0 && n + 3 < g.N && (n + 3 < g.b_split || n >= g.b_split)) {
                     const float* src = n < g.b_split ? g.b_scale0 + n : g.b_scale1 + (n - g.b_split);
                     bsc[j][gq] = *reinterpret_cast<const float4*>(src);
                 } else {
                     float v[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int nn = min(n + q, g.N - 1);
+                        const int nn = b_row(g, min(n + q, g.N - 1));
                         v[q] = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
                     }
                     bsc[j][gq] = make_float4(v[0], v[1], v[2], v[3]);
@@ -566,11 +566,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 const int m = min(m0 + r, g.M - 1);
                 src[i] = static_cast<const char*>(g.A) + static_cast<size_t>(m) * lda_b + k0 + c * 16;
             } else {
-                const int n = min(n0 + r - BM, g.N - 1);
+                const int n = b_row(g, min(n0 + r - BM, g.N - 1));
                 const char* row = n < g.b_split
-                                      ? static_cast<const char*>(g.B0) + static_cast<size_t>(n) * ldb_b
+                                      ? static_cast<const char*>(g.B0) + static_cast<ptrdiff_t>(n) * static_cast<ptrdiff_t>(ldb_b)
                                       : static_cast<const char*>(g.B1) +
-                                            static_cast<size_t>(n - g.b_split) * ldb_b;
+                                            static_cast<ptrdiff_t>(n - g.b_split) * static_cast<ptrdiff_t>(ldb_b);
                 src[i] = row + k0 + c * 16;
             }
         });

@@ -121,6 +121,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
         if (e != hipSuccess) return e;
         GemmArgs r = g;
         r.N = g.N - nm;
+        r.pe_c0 = g.pe_c0 + nm;
         const size_t eb = t == InType::kInt8 ? 1 : 2;
         if (nm >= g.b_split) {  // the remainder rows all come from the second segment
             r.B0 = r.B1 = static_cast<const char*>(g.B1) + static_cast<size_t>(nm - g.b_split) * g.ldb * eb;

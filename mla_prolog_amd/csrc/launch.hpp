@@ -46,6 +46,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s,
 // of q_norm. One wave per token for large batches, one workgroup per token otherwise.
 struct NormArgs {
     int T, Lq, Lkv, R, N1, k_splits;
+    int rsqrt;  // RMSNorm variant A (sum, x 1/D, rsqrt) instead of B (x^2/D summed, sqrt, divide)
     const uint16_t* a_bf16;  // [T, N1] bf16 down-projection output, or
     const float* a_f32;      // [k_splits, T, N1] fp32 split-K partial sums (used when set)
     // Columns [tail_c0, N1) of the down projection, when set, come from their own split-K
@@ -91,8 +92,12 @@ struct QuantQArgs {
     const uint16_t* q_nope;   // [T, H, Dn]
     const uint16_t* q_pe;     // [T, H, R]
     int8_t* q_i8;             // [T, H, Dn+R] or null
-    float* q_scale;           // [T] or null
+    float* q_scale;           // [T] or null; [T, H] with per_head
+    int per_head;             // one scale per (token, head) instead of per token
 };
+// Limits of the per-head q quant (one workgroup holds a token's row).
+constexpr int kMaxQuantHeads = 1024;
+constexpr int kQuantHeadChunks = 16;  // 16-byte chunks per thread: H*(Dn+R) <= 16*8*256
 hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s);
 
 }  // namespace mlap

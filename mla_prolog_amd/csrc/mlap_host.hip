@@ -254,7 +254,8 @@ namespace {
 
 int validate(const mlap_config* c) {
     const bool w8 = (c->flags & MLAP_W8A8) != 0;
-    if (c->flags & ~MLAP_W8A8) return MLAP_ERR_INVALID_ARG;
+    if (c->flags & ~(MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD))
+        return MLAP_ERR_INVALID_ARG;
     if (c->t_max < 1 || c->hidden < 1 || c->kv_lora < 1 || c->rope_dim < 1 || c->n_heads < 1 ||
         c->max_pos < 1 || c->q_lora < 0 || c->v_dim < 0 || c->nope_dim < 0 || !(c->eps >= 0.f))
         return MLAP_ERR_INVALID_ARG;
@@ -267,6 +268,10 @@ int validate(const mlap_config* c) {
     if (c->q_lora > 8192 || c->kv_lora > 8192) return MLAP_ERR_UNSUPPORTED;  // row kernel
     if (c->q_lora > 0 && heads_tile(c->nope_dim + c->rope_dim) == 0) return MLAP_ERR_UNSUPPORTED;
     if (c->v_dim > 0 && heads_tile(c->nope_dim + c->v_dim) == 0) return MLAP_ERR_UNSUPPORTED;
+    if ((c->flags & MLAP_QUANT_Q_PER_HEAD) && c->q_lora > 0 &&
+        (c->n_heads > kMaxQuantHeads ||
+         c->n_heads * (c->nope_dim + c->rope_dim) > kQuantHeadChunks * 8 * 256))
+        return MLAP_ERR_UNSUPPORTED;
     // GEMM sizes and grid dimensions are 32-bit in the kernels
     if (c->t_max > (1 << 24) || c->hidden > (1 << 20) || c->n_heads > 4096 || c->max_pos > (1 << 26))
         return MLAP_ERR_UNSUPPORTED;
@@ -391,6 +396,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     if (cache && (!in->slot_mapping || in->cache_slots <= 0)) return MLAP_ERR_INVALID_ARG;
     // the q quant reads the q tensors back
     const bool quant_q = out->q_i8 || out->q_scale;
+    const int per_head = (c.flags & MLAP_QUANT_Q_PER_HEAD) ? 1 : 0;
     bool quant_done = false;  // the q quant already ran per token block
     if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
     const WsLayout L = h->layout(T);
@@ -427,6 +433,11 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     g.B0 = has_q ? in->w_qa : in->w_kva;
     g.B1 = in->w_kva;
     g.b_split = Lq;
+    if (c.flags & MLAP_ROPE_INTERLEAVED) {  // the k_pe slice of [q_a | c_kv | k_pe]
+        g.pe_period = h->N1;
+        g.pe_off = Lq + Lkv;
+        g.pe_w = R;
+    }
     const Plan plan = h->plan(T);
     g.k_splits = plan.down_splits;
     g.group_m = kGroupM;
@@ -448,6 +459,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         g.A = in->x;
         GemmArgs r = g;  // columns [tail_c0, N1): split-K fp32 partials
         r.N = h->N1 - plan.tail_c0;
+        r.pe_c0 = plan.tail_c0;
         r.k_splits = plan.tail_splits;
         if (plan.tail_c0 >= g.b_split) {
             r.B0 = r.B1 = static_cast<const char*>(g.B1) +
@@ -493,6 +505,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     na.gamma_q = static_cast<const uint16_t*>(in->gamma_q);
     na.gamma_kv = static_cast<const uint16_t*>(in->gamma_kv);
     na.eps = c.eps;
+    na.rsqrt = (c.flags & MLAP_NORM_RSQRT) ? 1 : 0;
     na.positions = in->positions;
     na.cos = in->cos;
     na.sin = in->sin;
@@ -541,6 +554,11 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.d0 = c.nope_dim;
         u.d1 = R;
         u.rope = 1;
+        if (c.flags & MLAP_ROPE_INTERLEAVED) {  // the rope slice of every q head
+            u.pe_period = h->QH;
+            u.pe_off = c.nope_dim;
+            u.pe_w = R;
+        }
         u.n_heads = H;
         u.out0 = out->q_nope;
         u.out1 = out->q_pe;
@@ -548,7 +566,8 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.cos = in->cos;
         u.sin = in->sin;
         u.max_pos = c.max_pos;
-        u.part_amax = quant_q ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+        // per-token q quant: the epilogue's per-tile partial amax (per-head quant reads the rows)
+        u.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
         u.n_tiles = plan.nt_q;
         const InType it = w8 ? InType::kInt8 : InType::kBf16;
         if (w8) {
@@ -584,7 +603,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                 ub.out0 = out->q_nope ? static_cast<uint16_t*>(out->q_nope) + static_cast<size_t>(r0) * H * c.nope_dim : nullptr;
                 ub.out1 = out->q_pe ? static_cast<uint16_t*>(out->q_pe) + static_cast<size_t>(r0) * H * R : nullptr;
                 ub.positions = in->positions + r0;
-                ub.part_amax = u.part_amax + static_cast<size_t>(r0) * plan.nt_q;
+                ub.part_amax = u.part_amax ? u.part_amax + static_cast<size_t>(r0) * plan.nt_q : nullptr;
                 MLAP_LAUNCH(kKGemmUpQ, launch_gemm_big(ub, it, Epi::kHeads, s, plan.q_shape));
                 if (hipEventRecord(h->fork[b], s) != hipSuccess || hipStreamWaitEvent(h->aux, h->fork[b], 0) != hipSuccess)
                     return MLAP_ERR_HIP;
@@ -595,10 +614,11 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                 qa.R = R;
                 qa.n_tiles = plan.nt_q;
                 qa.part_amax = ub.part_amax;
+                qa.per_head = per_head;
                 qa.q_nope = static_cast<const uint16_t*>(ub.out0);
                 qa.q_pe = static_cast<const uint16_t*>(ub.out1);
                 qa.q_i8 = out->q_i8 ? out->q_i8 + static_cast<size_t>(r0) * H * (c.nope_dim + R) : nullptr;
-                qa.q_scale = out->q_scale ? out->q_scale + r0 : nullptr;
+                qa.q_scale = out->q_scale ? out->q_scale + static_cast<size_t>(r0) * (per_head ? H : 1) : nullptr;
                 hipStream_t s_main = s;
                 s = h->aux;  // MLAP_LAUNCH records the quant's timing on the stream it runs on
                 MLAP_LAUNCH(kKQuantQ, launch_quant_q(qa, s));
@@ -651,6 +671,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         qa.R = R;
         qa.n_tiles = plan.nt_q;
         qa.part_amax = reinterpret_cast<const float*>(wsb + L.qpart);
+        qa.per_head = per_head;
         qa.q_nope = static_cast<const uint16_t*>(out->q_nope);
         qa.q_pe = static_cast<const uint16_t*>(out->q_pe);
         qa.q_i8 = out->q_i8;

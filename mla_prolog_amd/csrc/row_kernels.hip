@@ -52,6 +52,12 @@ __device__ __forceinline__ int cache_row(const NormArgs& a, int t) {
     return (s >= 0 && s < a.n_slots) ? s : -1;
 }
 
+// 1/rms of a row from its sum s: variant B (the default) summed x^2/D and takes
+// 1/sqrt(s + eps); variant A (rsqrt) summed x^2, scales the sum by 1/D, then rsqrt.
+__device__ __forceinline__ float norm_rstd(const NormArgs& a, float s, float invD) {
+    return a.rsqrt ? rsqrtf(s * invD + a.eps) : 1.0f / sqrtf(s + a.eps);
+}
+
 // Store v at element `off` of row t of `out` and, for a token with a cache row, of row `cr`
 // of `cache` (the same row width); either pointer may be null.
 template <typename E, typename V>
@@ -135,6 +141,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
     float sq = 0.f, skv = 0.f;
     const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
     const float invkv = 1.0f / static_cast<float>(a.Lkv);
+    const float eq = a.rsqrt ? 1.0f : invq, ekv = a.rsqrt ? 1.0f : invkv;  // per-element 1/D (B)
 #pragma unroll
     for (int i = 0; i < kMaxChunks; ++i) {
         const int c = tid + i * kRowThreads;
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = qv[i][e] * qv[i][e];
-                sq += p * invq;
+                sq += p * eq;
             }
         }
         if (c < nkv) {
@@ -151,14 +158,14 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = kv[i][e] * kv[i][e];
-                skv += p * invkv;
+                skv += p * ekv;
             }
         }
     }
     const float msq = (a.Lq > 0) ? block_sum(sq, red) : 0.f;
     const float mskv = block_sum(skv, red);
-    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
-    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+    const float rstd_q = norm_rstd(a, msq, invq);
+    const float rstd_kv = norm_rstd(a, mskv, invkv);
 
     float qmax = 0.f, kvmax = 0.f;
     uint4 qo[kMaxChunks], kvo[kMaxChunks];
@@ -385,13 +392,14 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
     float sq = 0.f, skv = 0.f;
     const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
     const float invkv = 1.0f / static_cast<float>(a.Lkv);
+    const float eq = a.rsqrt ? 1.0f : invq, ekv = a.rsqrt ? 1.0f : invkv;  // per-element 1/D (B)
     static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
         constexpr int c = decltype(c_c)::value;
         if (tid + kRowThreads * c < nq) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = qv[c][e] * qv[c][e];
-                sq += p * invq;
+                sq += p * eq;
             }
         }
     });
@@ -401,14 +409,14 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = kv[c][e] * kv[c][e];
-                skv += p * invkv;
+                skv += p * ekv;
             }
         }
     });
     const float msq = QC > 0 ? block_sum(sq, red) : 0.f;
     const float mskv = block_sum(skv, red);
-    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
-    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+    const float rstd_q = norm_rstd(a, msq, invq);
+    const float rstd_kv = norm_rstd(a, mskv, invkv);
 
     float qmax = 0.f, kvmax = 0.f;
     uint4 qo[QC > 0 ? QC : 1], kvo[KC];
@@ -577,6 +585,7 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
     float sq = 0.f, skv = 0.f;
     const float invq = a.Lq > 0 ? 1.0f / static_cast<float>(a.Lq) : 0.f;
     const float invkv = 1.0f / static_cast<float>(a.Lkv);
+    const float eq = a.rsqrt ? 1.0f : invq, ekv = a.rsqrt ? 1.0f : invkv;  // per-element 1/D (B)
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
         unpack8(rq[i], qv[i]);
@@ -584,7 +593,7 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = qv[i][e] * qv[i][e];
-                sq += p * invq;
+                sq += p * eq;
             }
         }
     }
@@ -595,14 +604,14 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = kv[i][e] * kv[i][e];
-                skv += p * invkv;
+                skv += p * ekv;
             }
         }
     }
     const float msq = QC > 0 ? wave_sum(sq) : 0.f;
     const float mskv = wave_sum(skv);
-    const float rstd_q = 1.0f / sqrtf(msq + a.eps);
-    const float rstd_kv = 1.0f / sqrtf(mskv + a.eps);
+    const float rstd_q = norm_rstd(a, msq, invq);
+    const float rstd_kv = norm_rstd(a, mskv, invkv);
 
     float qmax = 0.f, kvmax = 0.f;
     uint4 qo[QC > 0 ? QC : 1], kvo[KC];
@@ -780,6 +789,52 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     for (int c = threadIdx.x + kHeld * kRowThreads; c < total; c += kRowThreads) store(c, *chunk_at(c));
 }
 
+// Per-(token, head) INT8 quant of q: each head's [q_nope | q_pe] row on its own (the row
+// max of the [t, heads, d] q tensor over its last axis). One workgroup per token holds the
+// whole row (kHeld chunks per thread); chunk maxima go through LDS to one maximum per head.
+template <int kHeld>
+__global__ __launch_bounds__(kRowThreads) void quant_q_head_kernel(QuantQArgs a) {
+    __shared__ float cmax[kHeld * kRowThreads];
+    __shared__ float hmax[kMaxQuantHeads];
+    const int t = blockIdx.x;
+    const int QH = a.Dn + a.R;
+    const int cph = QH >> 3, cn = a.Dn >> 3;
+    const int total = a.H * cph;
+    auto chunk_at = [&](int c) -> const uint4* {
+        const int h = c / cph, j = c - h * cph;
+        const size_t th = static_cast<size_t>(t) * a.H + h;
+        return (j < cn) ? reinterpret_cast<const uint4*>(a.q_nope + th * a.Dn + j * 8)
+                        : reinterpret_cast<const uint4*>(a.q_pe + th * a.R + (j - cn) * 8);
+    };
+    uint4 held[kHeld];
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) held[k] = *chunk_at(min(static_cast<int>(threadIdx.x) + k * kRowThreads, total - 1));
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) cmax[c] = absmax8(held[k]);
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < a.H; h += kRowThreads) {
+        float m = 0.f;
+        for (int j = 0; j < cph; ++j) m = fmaxf(m, cmax[h * cph + j]);
+        hmax[h] = m;
+        if (a.q_scale) a.q_scale[static_cast<size_t>(t) * a.H + h] = m / 127.0f;
+    }
+    __syncthreads();
+    if (!a.q_i8) return;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) {
+            const int h = c / cph, j = c - h * cph;
+            const float m = hmax[h];
+            const float mult = m > 0.f ? 127.0f / m : 0.f;
+            store_nt8(a.q_i8 + (static_cast<size_t>(t) * a.H + h) * QH + j * 8, quant8(held[k], mult));
+        }
+    }
+}
+
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     const int qc = (a.Lq / 8 + 63) / 64, kc = (a.Lkv / 8 + 63) / 64;
@@ -824,6 +879,12 @@ hipError_t launch_act_quant(const uint16_t* x, int T, int K, int8_t* codes, floa
 
 hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
+    if (a.per_head) {
+        if (a.H > kMaxQuantHeads || a.H * ((a.Dn + a.R) >> 3) > kQuantHeadChunks * kRowThreads)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(quant_q_head_kernel<kQuantHeadChunks>, dim3(a.T), dim3(kRowThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.T >= 1024)
         hipLaunchKernelGGL(quant_q_kernel<0>, dim3(a.T), dim3(kRowThreads), 0, s, a);
     else

@@ -189,11 +189,14 @@ def check_prolog(cfg, inp, gpu, rows=None):
                                    extra=rope_allowance(st2["q_pe"], R))
     if has_q and "q_i8" in G:
         gq = q_rows(G["q_nope"], G["q_pe"])
-        check_self_consistent_quant("q", gq, G["q_i8"], G["q_scale"])
         oq = np.concatenate([st2["q_nope"], st2["q_pe"]], axis=2).reshape(len(rows), -1)
+        gc, gs, os_ = G["q_i8"], G["q_scale"], np.asarray(st2["q_scale"])
+        if getattr(cfg, "q_quant_per_head", False):  # one quant row per (token, head)
+            QH = cfg.nope_dim + cfg.rope_dim
+            gq, oq, gs, os_ = gq.reshape(-1, QH), oq.reshape(-1, QH), gs.reshape(-1), os_.reshape(-1)
+        check_self_consistent_quant("q", gq, gc, gs)
         stats["q_excused"] = check_quant_vs_oracle(
-            "q", bits(gq), G["q_i8"].numpy(), G["q_scale"].numpy(), oq, st2["q_i8"],
-            st2["q_scale"])
+            "q", bits(gq), gc.numpy(), gs.numpy(), oq, st2["q_i8"], os_)
 
     # end to end against the independent chain, with the measured stage-1 differences
     # propagated linearly through the up projection (and RoPE's pair mixing)
@@ -203,6 +206,8 @@ def check_prolog(cfg, inp, gpu, rows=None):
         casc = (dqn @ np.abs(_w_f64(inp, "w_qb", cfg)).T).reshape(len(rows), H, Dn + R)
         h = R // 2
         pe = casc[..., Dn:]
+        if getattr(cfg, "rope_interleaved", False):  # raw pairs (2i, 2i+1) feed outputs (i, i+h)
+            pe = np.concatenate([pe[..., 0::2], pe[..., 1::2]], axis=-1)
         pe_pair = pe + np.concatenate([pe[..., h:], pe[..., :h]], axis=-1)
         stats["q_nope_e2e"] = check_bf16("q_nope[e2e]", G["q_nope"], ref["q_nope"],
                                          extra=2 * casc[..., :Dn])

@@ -73,6 +73,11 @@ def create(**kw):
     (dict(nope_dim=100), mlap.MLAP_ERR_UNSUPPORTED),
     (dict(nope_dim=120, rope_dim=64), mlap.MLAP_ERR_UNSUPPORTED),  # head 184 fits no tile
     (dict(q_lora=16384), mlap.MLAP_ERR_UNSUPPORTED),
+    (dict(flags=mlap.MLAP_NORM_RSQRT | mlap.MLAP_ROPE_INTERLEAVED | mlap.MLAP_QUANT_Q_PER_HEAD),
+     mlap.MLAP_OK),
+    (dict(flags=0x10), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=mlap.MLAP_QUANT_Q_PER_HEAD, n_heads=2048), mlap.MLAP_ERR_UNSUPPORTED),
+    (dict(flags=mlap.MLAP_QUANT_Q_PER_HEAD, n_heads=256), mlap.MLAP_ERR_UNSUPPORTED),  # 49152 values
 ])
 def test_create_validation(kw, status):
     rc, h = create(**kw)

@@ -111,6 +111,29 @@ def test_prolog_parity(name, T):
     say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
 
 
+# Numeric variants (configuration flags): RMSNorm variant A, the QuantRope3D de-interleaved
+# rope, per-(token, head) q quant; alone and together, on each path (weight streaming,
+# 64-row tiles, KV-Prolog mode, W8A8).
+ALL3 = dict(norm_rsqrt=True, rope_interleaved=True, q_quant_per_head=True)
+VARIANTS = [("v3_decode", 64, ALL3),
+            ("v3_decode", None, dict(rope_interleaved=True)),
+            ("v3_decode", 200, dict(q_quant_per_head=True)),
+            ("v3_decode", 37, dict(norm_rsqrt=True)),
+            ("v2lite_kv_decode", None, dict(norm_rsqrt=True, rope_interleaved=True)),
+            ("tiny_kv", None, dict(rope_interleaved=True)),
+            ("v3_w8a8", 130, ALL3)]
+
+
+@pytest.mark.parametrize("name,T,var", VARIANTS)
+def test_prolog_variants_parity(name, T, var):
+    cfg = synth.get_config(name, T=T, **var)
+    say("prolog parity", name, "T=%d" % cfg.T, var)
+    inp = synth.make_inputs(cfg)
+    out = run_gpu(cfg, inp)
+    stats = check_prolog(cfg, inp, out)
+    say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
+
+
 def sample_rows(T, n_random=40, seed=0):
     rng = np.random.default_rng(seed)
     edges = [0, 1, 127, 128, 129, T // 2, T - 129, T - 128, T - 2, T - 1]
@@ -247,3 +270,17 @@ def test_empty_batch_is_a_noop():
     torch.cuda.synchronize()
     for v in out.values():
         assert (v.float() == 7).all()
+
+
+# the variants on the large-batch kernels: the 256 x 256 heads epilogue (late cos/sin in LDS),
+# the split-K tail of the down projection (its column range starts at the k_pe slice), the
+# wave-per-token row kernel and the W8A8 token blocks with their forked quant
+@pytest.mark.parametrize("name,T", [("v3_prefill", 1000), ("v3_prefill", 2048), ("v3_w8a8", 2048)])
+def test_prolog_variants_large_batch_sampled_rows(name, T):
+    cfg = synth.get_config(name, T=T, **ALL3)
+    say("variants, sampled rows", name, "T=%d" % cfg.T)
+    inp = synth.make_inputs(cfg)
+    out = run_gpu(cfg, inp)
+    stats = check_prolog(cfg, inp, out, rows=sample_rows(cfg.T, n_random=24))
+    say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
+
