@@ -40,7 +40,8 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("hidden", "q_lora", "kv_lora", "rope_dim", "nope_dim",
                                           "v_dim", "n_heads", "max_pos")] + \
                [("eps", C.c_float), ("w8a8", C.c_int32), ("norm_rsqrt", C.c_int32),
-                ("rope_chunk", C.c_int32), ("q_quant_per_head", C.c_int32)]
+                ("rope_chunk", C.c_int32), ("q_quant_per_head", C.c_int32),
+                ("q_head_norm", C.c_int32)]
 
 
 class _Inputs(C.Structure):
@@ -286,7 +287,7 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
 
     c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8),
              int(getattr(cfg, "norm_rsqrt", False)), 2 if getattr(cfg, "rope_interleaved", False) else 0,
-             int(getattr(cfg, "q_quant_per_head", False)))
+             int(getattr(cfg, "q_quant_per_head", False)), int(getattr(cfg, "q_head_norm", False)))
     i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
     o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
     qn = None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq)

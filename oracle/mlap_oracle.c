@@ -254,6 +254,7 @@ typedef struct {
     int32_t norm_rsqrt;       /* RMSNorm variant A instead of B */
     int32_t rope_chunk;       /* 0: rotate-half on the slice as is; else the QuantRope3D form */
     int32_t q_quant_per_head; /* q codes and scales per (token, head) instead of per token */
+    int32_t q_head_norm;      /* RMSNorm (no gamma) of every q head after q_b, before RoPE */
 } orc_cfg;
 
 typedef struct {
@@ -392,6 +393,8 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
             if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
             const uint16_t* q_src = qn_given ? qn_given + i * Lq : qn;
             orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
+            if (cfg->q_head_norm) /* [AT-10] section 九: q_b -> reshape (heads, head_dim) -> RMSNorm */
+                for (int64_t h = 0; h < H; ++h) orc_norm(cfg, a + h * QH, NULL, QH, a + h * QH);
             for (int64_t h = 0; h < H; ++h) {
                 const uint16_t* head = a + h * QH;
                 uint16_t* qh = qrow + h * QH;

@@ -66,6 +66,7 @@ class Config:
     norm_rsqrt: bool = False        # RMSNorm variant A
     rope_interleaved: bool = False  # rope slices de-interleaved before rotate-half
     q_quant_per_head: bool = False  # q codes / scales per (token, head)
+    q_head_norm: bool = False       # RMSNorm of every q head after q_b (the V4-shape prolog)
 
     def asdict(self):
         return asdict(self)
@@ -101,6 +102,12 @@ CONFIGS = {
     "v3_prefill": Config("v3_prefill", T=8192, hidden=7168, q_lora=1536, kv_lora=512,
                          rope_dim=64, nope_dim=128, v_dim=0, n_heads=128, max_pos=8192,
                          positions="arange", outlier_frac=0.01, index=3),
+    # The V4-shape MLA Prolog of the AT-10 card's test case (t=16, 64 heads of 512 with a
+    # 64-wide rope slice, hidden 4096, q_lora 1024) with the per-head q RMSNorm after q_b; the
+    # card gives no kv dimensions: kv_lora 512 and the same rope width.
+    "v4_decode": Config("v4_decode", T=16, hidden=4096, q_lora=1024, kv_lora=512, rope_dim=64,
+                        nope_dim=448, v_dim=0, n_heads=64, max_pos=8192, positions="uniform",
+                        q_head_norm=True, index=5),
     # Same shape with int8 W8A8 projections.
     "v3_w8a8": Config("v3_w8a8", T=16384, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
                       nope_dim=128, v_dim=0, n_heads=128, max_pos=16384,
@@ -110,7 +117,7 @@ CONFIGS = {
 
 def get_config(name: str, T: int | None = None, **variants) -> Config:
     """A named configuration, optionally with another token count and variant flags
-    (norm_rsqrt, rope_interleaved, q_quant_per_head)."""
+    (norm_rsqrt, rope_interleaved, q_quant_per_head, q_head_norm)."""
     cfg = CONFIGS[name]
     if T is not None:
         cfg = replace(cfg, T=int(T))

@@ -492,3 +492,55 @@ def test_per_head_q_quant():
     # the per-token form of the same run has one scale: the largest head's
     tok = oracle.prolog(synth.get_config("v3_decode", T=2), inp, rows=np.array([1], np.int32))
     assert tok["q_scale"][0] == sc.max()
+
+
+# ----------------------------------------------------- V4-shape head norm ----
+
+def test_golden_v4_case_shapes():
+    """Sizes of the card's V4 test case; the q row reshapes to (num_heads, head_dim)."""
+    import json
+    import os
+    case = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "v4_mla_prolog_t16_shapes.json")))
+    cfg = synth.get_config("v4_decode")
+    assert (cfg.T, cfg.n_heads, cfg.hidden, cfg.q_lora) == (case["t"], case["num_heads"], case["h"],
+                                                           case["q_lora_rank"])
+    assert cfg.nope_dim + cfg.rope_dim == case["head_dim"] and cfg.rope_dim == case["qk_rope_head_dim"]
+    inp = synth.make_inputs(cfg)
+    assert list(inp["w_qb"].shape) == [case["num_heads"] * case["head_dim"], case["q_lora_rank"]]
+    out = oracle.prolog(cfg, inp, rows=np.array([0, 15], np.int32))
+    assert out["q_nope"].shape[1:] == (case["num_heads"], case["head_dim"] - case["qk_rope_head_dim"])
+    assert out["q_pe"].shape[1:] == (case["num_heads"], case["qk_rope_head_dim"])
+
+
+def test_head_norm_is_scale_invariant_per_head():
+    """With eps = 0 the per-head RMSNorm undoes a power-of-two scale of one head's q_b rows
+    bit for bit (every step scales exactly); without the head norm the head scales by it."""
+    from dataclasses import replace
+    cfg = replace(synth.get_config("v4_decode", T=3), eps=0.0)
+    inp = synth.make_inputs(cfg)
+    QH = cfg.nope_dim + cfg.rope_dim
+    h = 5
+    scaled = dict(inp)
+    w = inp["w_qb"].clone()
+    w[h * QH:(h + 1) * QH] *= 8
+    scaled["w_qb"] = w
+    rows = np.array([0, 2], np.int32)
+    a, b = oracle.prolog(cfg, inp, rows=rows), oracle.prolog(cfg, scaled, rows=rows)
+    for k in ("q_nope", "q_pe", "q_i8", "q_scale"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    plain = replace(cfg, q_head_norm=False)
+    a, b = oracle.prolog(plain, inp, rows=rows), oracle.prolog(plain, scaled, rows=rows)
+    np.testing.assert_array_equal(from_bits(b["q_nope"][:, h]), 8 * from_bits(a["q_nope"][:, h]))
+
+
+def test_head_norm_gives_unit_rms_heads():
+    """At position 0 (RoPE is the identity) every head of q has mean square 1 up to the bf16
+    rounding of its values."""
+    cfg = synth.get_config("v4_decode", T=2)
+    inp = synth.make_inputs(cfg)
+    inp["positions"] = torch.zeros_like(inp["positions"])
+    out = oracle.prolog(cfg, inp)
+    q = np.concatenate([from_bits(out["q_nope"]), from_bits(out["q_pe"])], axis=2).astype(np.float64)
+    ms = (q ** 2).mean(axis=2)
+    assert np.abs(ms - 1).max() < 2.0 ** -7
