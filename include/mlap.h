@@ -77,6 +77,11 @@ typedef enum {
 #define MLAP_NORM_RSQRT 0x2u
 #define MLAP_ROPE_INTERLEAVED 0x4u
 #define MLAP_QUANT_Q_PER_HEAD 0x8u
+/* MLAP_Q_HEAD_NORM: the V4-shape prolog of the AT-10 card (sections 五, 九): after q_b the q
+ *   row is reshaped to its heads and every head (Dn + R values) goes through RMSNorm without
+ *   gamma (the configured variant) before RoPE. bf16 only; Dn and Dn + R multiples of 64,
+ *   H <= 1024, H*(Dn+R) <= 32768, H*R <= 8192. */
+#define MLAP_Q_HEAD_NORM 0x10u
 
 typedef struct {
     int32_t t_max;    /* largest token count a run may pass (sizes nothing on device) */
@@ -89,7 +94,8 @@ typedef struct {
     int32_t n_heads;  /* attention heads */
     int32_t max_pos;  /* rows of the cos/sin tables */
     float eps;        /* RMSNorm epsilon (added to the mean square) */
-    uint32_t flags;   /* MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD */
+    uint32_t flags;   /* MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
+                         MLAP_Q_HEAD_NORM */
 } mlap_config;
 
 /*

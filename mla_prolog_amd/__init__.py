@@ -26,6 +26,7 @@ MLAP_W8A8 = 0x1
 MLAP_NORM_RSQRT = 0x2        # RMSNorm variant A
 MLAP_ROPE_INTERLEAVED = 0x4  # rope slices de-interleaved before rotate-half
 MLAP_QUANT_Q_PER_HEAD = 0x8  # q codes / scales per (token, head)
+MLAP_Q_HEAD_NORM = 0x10      # RMSNorm of every q head after q_b (the V4-shape prolog)
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_timing_begin", "mlap_timing_end",
@@ -140,15 +141,16 @@ class Prolog:
 
     def __init__(self, t_max, hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads,
                  max_pos, eps=1e-6, w8a8=False, norm_rsqrt=False, rope_interleaved=False,
-                 q_quant_per_head=False):
+                 q_quant_per_head=False, q_head_norm=False):
         self.cfg = dict(t_max=t_max, hidden=hidden, q_lora=q_lora, kv_lora=kv_lora,
                         rope_dim=rope_dim, nope_dim=nope_dim, v_dim=v_dim, n_heads=n_heads,
                         max_pos=max_pos, eps=eps, w8a8=bool(w8a8), norm_rsqrt=bool(norm_rsqrt),
                         rope_interleaved=bool(rope_interleaved),
-                        q_quant_per_head=bool(q_quant_per_head))
+                        q_quant_per_head=bool(q_quant_per_head), q_head_norm=bool(q_head_norm))
         flags = ((MLAP_W8A8 if w8a8 else 0) | (MLAP_NORM_RSQRT if norm_rsqrt else 0) |
                  (MLAP_ROPE_INTERLEAVED if rope_interleaved else 0) |
-                 (MLAP_QUANT_Q_PER_HEAD if q_quant_per_head else 0))
+                 (MLAP_QUANT_Q_PER_HEAD if q_quant_per_head else 0) |
+                 (MLAP_Q_HEAD_NORM if q_head_norm else 0))
         c = _Config(int(t_max), int(hidden), int(q_lora), int(kv_lora), int(rope_dim),
                     int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps), flags)
         h = C.c_void_p()
@@ -162,7 +164,7 @@ class Prolog:
         g = lambda k: bool(getattr(cfg, k, False))
         return cls(t_max or cfg.T, cfg.hidden, cfg.q_lora, cfg.kv_lora, cfg.rope_dim,
                    cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8,
-                   g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"))
+                   g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"), g("q_head_norm"))
 
     def close(self):
         if getattr(self, "_h", None):

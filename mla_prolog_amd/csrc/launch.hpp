@@ -100,4 +100,25 @@ constexpr int kMaxQuantHeads = 1024;
 constexpr int kQuantHeadChunks = 16;  // 16-byte chunks per thread: H*(Dn+R) <= 16*8*256
 hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s);
 
+// Per-head RMSNorm (no gamma) of q after the up projection, then rotate-half RoPE of each
+// head's rope slice, in place on q_nope / q_pe (the raw projection output), and the token's
+// |q| max as a single partial amax (the V4-shape prolog: q_b -> reshape to heads -> RMSNorm).
+struct QHeadNormArgs {
+    int T, H, Dn, R;
+    float eps;
+    int rsqrt;                // RMSNorm variant A instead of B
+    const int* positions;
+    const float* cos;
+    const float* sin;
+    int max_pos;
+    uint16_t* q_nope;         // [T, H, Dn], in place
+    uint16_t* q_pe;           // [T, H, R], in place
+    float* part_amax;         // [T] or null
+};
+// Limits of the per-head norm (one workgroup holds a token's q row): H*(Dn+R) <= 32768 and
+// H*R <= 8192 (the rope chunks staged in LDS).
+constexpr int kHeadNormChunks = 16;
+constexpr int kHeadNormPeChunks = 1024;
+hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s);
+
 }  // namespace mlap

@@ -31,10 +31,11 @@ enum KernelId : int32_t {
     kKGemmUpQ = 3,
     kKGemmUpKv = 4,
     kKQuantQ = 5,
-    kKCount = 6
+    kKQHeadNorm = 6,
+    kKCount = 7
 };
 const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope",
-                                           "gemm_up_q", "gemm_up_kv", "quant_q"};
+                                           "gemm_up_q", "gemm_up_kv", "quant_q", "q_head_norm"};
 
 constexpr size_t kAlign = 256;
 constexpr int kCUs = 256;          // MI355X compute units
@@ -115,6 +116,8 @@ struct mlap_prolog {
     hipStream_t aux = nullptr;
     hipEvent_t fork[kQBlocks + 1] = {};
 
+    bool head_norm() const { return (cfg.flags & MLAP_Q_HEAD_NORM) && cfg.q_lora > 0; }
+
     Plan plan(int T) const {
         Plan p{};
         const bool small = T <= kSmallBatch;
@@ -154,7 +157,7 @@ struct mlap_prolog {
                 u.head_w = QH;
                 u.d0 = cfg.nope_dim;
                 u.d1 = cfg.rope_dim;
-                u.rope = 1;
+                u.rope = head_norm() ? 0 : 1;
                 p.big_q = gemm_big_fits(u, it, Epi::kHeads);
             }
             if (cfg.v_dim > 0) {
@@ -184,10 +187,13 @@ struct mlap_prolog {
                 u.head_w = QH;
                 u.d0 = cfg.nope_dim;
                 u.d1 = cfg.rope_dim;
-                u.rope = 1;
+                u.rope = head_norm() ? 0 : 1;
                 if (gemm_big_fits(u, it, Epi::kHeads, BigShape::kHalfHead)) {
                     p.big_q = true;
                     p.q_shape = BigShape::kHalfHead;
+                } else if (head_norm() && gemm_big_fits(u, it, Epi::kHeads, BigShape::kNarrowHeads)) {
+                    p.big_q = true;  // raw heads: no rope slice to keep whole
+                    p.q_shape = BigShape::kNarrowHeads;
                 }
             }
             if (cfg.v_dim > 0) {
@@ -254,8 +260,10 @@ namespace {
 
 int validate(const mlap_config* c) {
     const bool w8 = (c->flags & MLAP_W8A8) != 0;
-    if (c->flags & ~(MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD))
+    if (c->flags & ~(MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
+                     MLAP_Q_HEAD_NORM))
         return MLAP_ERR_INVALID_ARG;
+    const bool head_norm = (c->flags & MLAP_Q_HEAD_NORM) && c->q_lora > 0;
     if (c->t_max < 1 || c->hidden < 1 || c->kv_lora < 1 || c->rope_dim < 1 || c->n_heads < 1 ||
         c->max_pos < 1 || c->q_lora < 0 || c->v_dim < 0 || c->nope_dim < 0 || !(c->eps >= 0.f))
         return MLAP_ERR_INVALID_ARG;
@@ -266,7 +274,13 @@ int validate(const mlap_config* c) {
     if (c->rope_dim % 16) return MLAP_ERR_UNSUPPORTED;
     if (c->nope_dim % 8 || c->v_dim % 8) return MLAP_ERR_UNSUPPORTED;
     if (c->q_lora > 8192 || c->kv_lora > 8192) return MLAP_ERR_UNSUPPORTED;  // row kernel
-    if (c->q_lora > 0 && heads_tile(c->nope_dim + c->rope_dim) == 0) return MLAP_ERR_UNSUPPORTED;
+    if (c->q_lora > 0 && !head_norm && heads_tile(c->nope_dim + c->rope_dim) == 0) return MLAP_ERR_UNSUPPORTED;
+    // per-head q norm: raw heads from the LDS-DMA GEMM (32-column tiles at small batches,
+    // 256 x 256 at large), then the head-norm row kernel
+    if (head_norm && (w8 || c->nope_dim % 64 || (c->nope_dim + c->rope_dim) % 64 || c->n_heads > kMaxQuantHeads ||
+                      c->n_heads * (c->nope_dim + c->rope_dim) > kHeadNormChunks * 8 * 256 ||
+                      c->n_heads * (c->rope_dim >> 3) > kHeadNormPeChunks))
+        return MLAP_ERR_UNSUPPORTED;
     if (c->v_dim > 0 && heads_tile(c->nope_dim + c->v_dim) == 0) return MLAP_ERR_UNSUPPORTED;
     if ((c->flags & MLAP_QUANT_Q_PER_HEAD) && c->q_lora > 0 &&
         (c->n_heads > kMaxQuantHeads ||
@@ -397,6 +411,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     // the q quant reads the q tensors back
     const bool quant_q = out->q_i8 || out->q_scale;
     const int per_head = (c.flags & MLAP_QUANT_Q_PER_HEAD) ? 1 : 0;
+    const bool head_norm = h->head_norm();
     bool quant_done = false;  // the q quant already ran per token block
     if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
     const WsLayout L = h->layout(T);
@@ -524,6 +539,8 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         na.kr_cache = static_cast<uint16_t*>(out->kr_cache);
     }
     const bool need_q = has_q && (out->q_nope || out->q_pe || quant_q);
+    // the per-head norm rewrites the raw heads in place: it needs both q tensors
+    if (head_norm && need_q && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
     const bool need_kvb = has_kvb && (out->k_nope || out->value);
     if (need_kvb && !w8) na.kv_norm = kvn;  // the bf16 kv_b reads it
     if (w8 && need_q) {
@@ -553,7 +570,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.head_w = h->QH;
         u.d0 = c.nope_dim;
         u.d1 = R;
-        u.rope = 1;
+        u.rope = head_norm ? 0 : 1;  // with the per-head norm, RoPE follows it in the row kernel
         if (c.flags & MLAP_ROPE_INTERLEAVED) {  // the rope slice of every q head
             u.pe_period = h->QH;
             u.pe_off = c.nope_dim;
@@ -567,7 +584,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.sin = in->sin;
         u.max_pos = c.max_pos;
         // per-token q quant: the epilogue's per-tile partial amax (per-head quant reads the rows)
-        u.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+        u.part_amax = quant_q && !per_head && !head_norm ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
         u.n_tiles = plan.nt_q;
         const InType it = w8 ? InType::kInt8 : InType::kBf16;
         if (w8) {
@@ -584,6 +601,23 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         if (!blocks) {
             MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
                                               : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
+            if (head_norm) {
+                QHeadNormArgs hn{};
+                hn.T = T;
+                hn.H = H;
+                hn.Dn = c.nope_dim;
+                hn.R = R;
+                hn.eps = c.eps;
+                hn.rsqrt = (c.flags & MLAP_NORM_RSQRT) ? 1 : 0;
+                hn.positions = in->positions;
+                hn.cos = in->cos;
+                hn.sin = in->sin;
+                hn.max_pos = c.max_pos;
+                hn.q_nope = static_cast<uint16_t*>(out->q_nope);
+                hn.q_pe = static_cast<uint16_t*>(out->q_pe);
+                hn.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+                MLAP_LAUNCH(kKQHeadNorm, launch_q_head_norm(hn, s));
+            }
         } else {
             // q in kQBlocks token blocks (whole 256-row tiles); block b's quant runs on the
             // second stream as soon as its projection is done, under block b + 1's GEMM
@@ -669,7 +703,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         qa.H = H;
         qa.Dn = c.nope_dim;
         qa.R = R;
-        qa.n_tiles = plan.nt_q;
+        qa.n_tiles = head_norm ? 1 : plan.nt_q;  // the head-norm kernel leaves one partial per token
         qa.part_amax = reinterpret_cast<const float*>(wsb + L.qpart);
         qa.per_head = per_head;
         qa.q_nope = static_cast<const uint16_t*>(out->q_nope);

@@ -835,6 +835,113 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_head_kernel(QuantQArgs a)
     }
 }
 
+// One workgroup per token: the q row (H heads of Dn + R raw values) is held in registers; each
+// chunk's sum of squares goes to LDS and one thread per head adds its chunks in order; the
+// normalised rope chunks are staged in LDS so each can read its rotate-half partner (R/2
+// columns away in the same head); the token's |q| max closes the kernel.
+__global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs a) {
+    __shared__ float csq[kHeadNormChunks * kRowThreads];
+    __shared__ float hrstd[kMaxQuantHeads];
+    __shared__ uint4 pe_stage[kHeadNormPeChunks];
+    __shared__ float red[kRowWaves];
+    const int t = blockIdx.x;
+    const int QH = a.Dn + a.R;
+    const int cph = QH >> 3, cn = a.Dn >> 3, cr = a.R >> 3;
+    const int total = a.H * cph;
+    const float invD = 1.0f / static_cast<float>(QH);
+    const float e = a.rsqrt ? 1.0f : invD;  // per-element 1/D (variant B)
+    auto chunk_ptr = [&](int c) -> uint16_t* {
+        const int h = c / cph, j = c - h * cph;
+        const size_t th = static_cast<size_t>(t) * a.H + h;
+        return (j < cn) ? a.q_nope + th * a.Dn + j * 8 : a.q_pe + th * a.R + (j - cn) * 8;
+    };
+    const int p = clamp_pos(a.positions[t], a.max_pos);
+    uint4 held[kHeadNormChunks];
+#pragma unroll
+    for (int k = 0; k < kHeadNormChunks; ++k)
+        held[k] = *reinterpret_cast<const uint4*>(chunk_ptr(min(static_cast<int>(threadIdx.x) + k * kRowThreads, total - 1)));
+#pragma unroll
+    for (int k = 0; k < kHeadNormChunks; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) {
+            float f[8], s = 0.f;
+            unpack8(held[k], f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float sq = f[q] * f[q];
+                s += sq * e;
+            }
+            csq[c] = s;
+        }
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < a.H; h += kRowThreads) {
+        float s = 0.f;
+        for (int j = 0; j < cph; ++j) s += csq[h * cph + j];
+        hrstd[h] = a.rsqrt ? rsqrtf(s * invD + a.eps) : 1.0f / sqrtf(s + a.eps);
+    }
+    __syncthreads();
+    // normalise (bf16 cast point); rope chunks go to LDS for their partners
+#pragma unroll
+    for (int k = 0; k < kHeadNormChunks; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) {
+            const int h = c / cph, j = c - h * cph;
+            const float r = hrstd[h];
+            float f[8];
+            unpack8(held[k], f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[q] = f[q] * r;
+            held[k] = pack8(f);
+            if (j >= cn) pe_stage[h * cr + (j - cn)] = held[k];
+        }
+    }
+    __syncthreads();
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHeadNormChunks; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < total) {
+            const int h = c / cph, j = c - h * cph;
+            uint4 o = held[k];
+            if (j >= cn) {
+                // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half), cos/sin
+                // at this chunk's own columns; the partner is the other half
+                const int jr = j - cn;
+                const bool low = jr < (cr >> 1);
+                const uint4 pv = pe_stage[h * cr + (low ? jr + (cr >> 1) : jr - (cr >> 1))];
+                float own[8], oth[8], res[8];
+                unpack8(o, own);
+                unpack8(pv, oth);
+                const float* cs = a.cos + static_cast<size_t>(p) * a.R + jr * 8;
+                const float* sn = a.sin + static_cast<size_t>(p) * a.R + jr * 8;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float t1 = own[q] * cs[q];
+                    const float t2 = (low ? -oth[q] : oth[q]) * sn[q];
+                    res[q] = t1 + t2;
+                }
+                o = pack8(res);
+            }
+            *reinterpret_cast<uint4*>(chunk_ptr(c)) = o;
+            mx = fmaxf(mx, absmax8(o));
+        }
+    }
+    if (a.part_amax) {
+        const float amax = block_max(mx, red);
+        if (threadIdx.x == 0) a.part_amax[t] = amax;
+    }
+}
+
+hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s) {
+    if (a.T <= 0) return hipSuccess;
+    if (a.H > kMaxQuantHeads || a.H * ((a.Dn + a.R) >> 3) > kHeadNormChunks * kRowThreads ||
+        a.H * (a.R >> 3) > kHeadNormPeChunks || (a.R >> 3) % 2)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(q_head_norm_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
     if (a.T <= 0) return hipSuccess;
     const int qc = (a.Lq / 8 + 63) / 64, kc = (a.Lkv / 8 + 63) / 64;

@@ -13,7 +13,9 @@ point. Parity is therefore checked per stage on identical stage inputs:
 * stage 2, from the GPU's own q_norm / kv_norm rows (themselves checked in
   stage 1): q_nope, q_pe, k_nope, value, q codes/scales;
 
-each against the bounds above. A normalised output (kv_norm, q_norm) reads raw
+each against the bounds above (with a per-head q norm, the raw q_b values it reads are a
+cast point inside stage 2 and q gets the normalised-output allowance below; the end-to-end
+propagation is then left to the staged checks). A normalised output (kv_norm, q_norm) reads raw
 projection values that are bf16 cast points: one of them rounded the other way
 moves the output by at most |o| 2^-7, which its bound adds. A RoPE output
 (q_pe, k_pe) reads a raw projection value that is itself a bf16 cast point, and
@@ -181,12 +183,16 @@ def check_prolog(cfg, inp, gpu, rows=None):
     st2 = oracle.prolog(cfg, inp, rows=rows,
                         q_norm=bits(G["q_norm"]) if has_q else None,
                         kv_norm=bits(G["kv_norm"]) if has_kvb else None)
+    # with the per-head q norm the raw q_b values are a cast point inside stage 2
+    hn = getattr(cfg, "q_head_norm", False)
     for k in ("q_nope", "k_nope", "value"):
         if k in st2 and k in G:
-            stats[k] = check_bf16(k + "[stage2]", G[k], st2[k])
+            stats[k] = check_bf16(k + "[stage2]", G[k], st2[k],
+                                  extra=norm_allowance(st2[k]) if hn and k == "q_nope" else None)
     if has_q and "q_pe" in G:
         stats["q_pe"] = check_bf16("q_pe[stage2]", G["q_pe"], st2["q_pe"],
-                                   extra=rope_allowance(st2["q_pe"], R))
+                                   extra=rope_allowance(st2["q_pe"], R) +
+                                   (norm_allowance(st2["q_pe"]) if hn else 0))
     if has_q and "q_i8" in G:
         gq = q_rows(G["q_nope"], G["q_pe"])
         oq = np.concatenate([st2["q_nope"], st2["q_pe"]], axis=2).reshape(len(rows), -1)
@@ -201,7 +207,9 @@ def check_prolog(cfg, inp, gpu, rows=None):
     # end to end against the independent chain, with the measured stage-1 differences
     # propagated linearly through the up projection (and RoPE's pair mixing)
     H, Dn, Dv = cfg.n_heads, cfg.nope_dim, cfg.v_dim
-    if has_q and "q_nope" in G:
+    # (the linear propagation models a raw q_b output; a per-head norm divides each head by
+    # its own rms, so head-normed configs rely on the two staged checks above)
+    if has_q and "q_nope" in G and not hn:
         dqn = _act_diff(cfg, bits(G["q_norm"]), ref["q_norm"])
         casc = (dqn @ np.abs(_w_f64(inp, "w_qb", cfg)).T).reshape(len(rows), H, Dn + R)
         h = R // 2

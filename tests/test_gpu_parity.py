@@ -121,7 +121,11 @@ VARIANTS = [("v3_decode", 64, ALL3),
             ("v3_decode", 37, dict(norm_rsqrt=True)),
             ("v2lite_kv_decode", None, dict(norm_rsqrt=True, rope_interleaved=True)),
             ("tiny_kv", None, dict(rope_interleaved=True)),
-            ("v3_w8a8", 130, ALL3)]
+            ("v3_w8a8", 130, ALL3),
+            # the V4-shape prolog (per-head q RMSNorm after q_b), alone and with the variants
+            ("v4_decode", None, {}),
+            ("v4_decode", 100, dict(norm_rsqrt=True, rope_interleaved=True)),
+            ("v4_decode", 64, dict(q_quant_per_head=True))]
 
 
 @pytest.mark.parametrize("name,T,var", VARIANTS)
@@ -275,9 +279,11 @@ def test_empty_batch_is_a_noop():
 # the variants on the large-batch kernels: the 256 x 256 heads epilogue (late cos/sin in LDS),
 # the split-K tail of the down projection (its column range starts at the k_pe slice), the
 # wave-per-token row kernel and the W8A8 token blocks with their forked quant
-@pytest.mark.parametrize("name,T", [("v3_prefill", 1000), ("v3_prefill", 2048), ("v3_w8a8", 2048)])
-def test_prolog_variants_large_batch_sampled_rows(name, T):
-    cfg = synth.get_config(name, T=T, **ALL3)
+@pytest.mark.parametrize("name,T,var", [("v3_prefill", 1000, ALL3), ("v3_prefill", 2048, ALL3),
+                                        ("v3_w8a8", 2048, ALL3), ("v4_decode", 1000, {}),
+                                        ("v4_decode", 2048, ALL3)])
+def test_prolog_variants_large_batch_sampled_rows(name, T, var):
+    cfg = synth.get_config(name, T=T, **var)
     say("variants, sampled rows", name, "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
     out = run_gpu(cfg, inp)
