@@ -41,13 +41,14 @@ class _Cfg(C.Structure):
                                           "v_dim", "n_heads", "max_pos")] + \
                [("eps", C.c_float), ("w8a8", C.c_int32), ("norm_rsqrt", C.c_int32),
                 ("rope_chunk", C.c_int32), ("q_quant_per_head", C.c_int32),
-                ("q_head_norm", C.c_int32)]
+                ("q_head_norm", C.c_int32), ("mxfp8", C.c_int32)]
 
 
 class _Inputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("x", "positions", "w_qa", "w_qb", "w_kva", "w_kvb",
                                           "ws_qa", "ws_qb", "ws_kva", "ws_kvb", "gamma_q",
-                                          "gamma_kv", "cos", "sin")]
+                                          "gamma_kv", "cos", "sin", "ms_qa", "ms_qb", "ms_kva",
+                                          "ms_kvb")]
 
 
 _OUT_FIELDS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_i8",
@@ -81,6 +82,11 @@ def load():
             lib.orc_rope_row_chunked.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                                  C.c_int64, C.c_void_p]
             lib.orc_quant_row.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+            lib.orc_e4m3_value.argtypes = [C.c_uint8]
+            lib.orc_e4m3_value.restype = C.c_double
+            lib.orc_e4m3_round.argtypes = [C.c_double]
+            lib.orc_e4m3_round.restype = C.c_double
+            lib.orc_mx_quant_row.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
             lib.orc_cache_scatter.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
                                               C.c_int64, C.c_void_p]
             lib.orc_cache_scatter.restype = C.c_int
@@ -194,6 +200,27 @@ def rope_row_chunked(u, c, s, chunk=2):
     return out
 
 
+def e4m3_value(code):
+    """Value of an OCP E4M3FN byte (NaN for 0x7F / 0xFF). grouped_matmul_swiglu_quant page,
+    section 算子语义 (MXFP8: E4M3 data)."""
+    return load().orc_e4m3_value(int(code) & 0xFF)
+
+
+def e4m3_round(v):
+    """Nearest E4M3 value to v, ties to even, saturating at +-448."""
+    return load().orc_e4m3_round(float(v))
+
+
+def mx_quant_row(v):
+    """MX conversion of a bf16 row (length a multiple of 32), block by block: shared exponent
+    floor(log2(amax)) - 8, values rounded to E4M3. Returns (dequantised bf16 bits, E8M0 bytes)."""
+    v = _np(v, np.uint16).reshape(-1)
+    deq = np.empty_like(v)
+    sc = np.empty(v.size // 32, np.uint8)
+    load().orc_mx_quant_row(_p(v), v.size, _p(deq), _p(sc))
+    return deq, sc
+
+
 def rope_row(u, c, s):
     """Rotate-half RoPE of one slice: x*cos + rotate_half(x)*sin, fp32, back to bf16.
 
@@ -251,7 +278,8 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
     H, Dn, R, Dv = cfg.n_heads, cfg.nope_dim, cfg.rope_dim, cfg.v_dim
     Lq, Lkv = cfg.q_lora, cfg.kv_lora
     w8 = bool(cfg.w8a8)
-    wdt = np.int8 if w8 else np.uint16
+    mx = bool(getattr(cfg, "mxfp8", False))
+    wdt = np.int8 if w8 else (np.uint8 if mx else np.uint16)
 
     arrs = {
         "x": _np(inputs["x"], np.uint16),
@@ -270,6 +298,10 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
         for k in ("w_qa", "w_qb", "w_kva", "w_kvb"):
             if k + "_scale" in inputs:
                 arrs["ws" + k[1:]] = _np(inputs[k + "_scale"], np.float32)
+    if mx:
+        for k in ("w_qa", "w_qb", "w_kva", "w_kvb"):
+            if k + "_mxscale" in inputs:
+                arrs["ms" + k[1:]] = _np(inputs[k + "_mxscale"], np.uint8)
 
     outs = {
         "kv_norm": np.empty((n, Lkv), np.uint16),
@@ -287,7 +319,8 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
 
     c = _Cfg(cfg.hidden, Lq, Lkv, R, Dn, Dv, H, cfg.max_pos, C.c_float(cfg.eps), int(w8),
              int(getattr(cfg, "norm_rsqrt", False)), 2 if getattr(cfg, "rope_interleaved", False) else 0,
-             int(getattr(cfg, "q_quant_per_head", False)), int(getattr(cfg, "q_head_norm", False)))
+             int(getattr(cfg, "q_quant_per_head", False)), int(getattr(cfg, "q_head_norm", False)),
+             int(mx))
     i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
     o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
     qn = None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq)

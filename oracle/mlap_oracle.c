@@ -238,6 +238,68 @@ ORC_API void orc_quant_row(const uint16_t* z, int64_t n, int8_t* codes, float* s
     *scale = amax / 127.0f;
 }
 
+/* ------------------------------------------------------------- MXFP8 ---- */
+
+/* The MXFP8 format of the grouped_matmul_swiglu_quant page (section 算子语义): FP8 E4M3 data
+ * (OCP E4M3FN: sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities, 0x7F and
+ * 0xFF are NaN) and one E8M0 scale 2^(e-127) per 32-element block along K. */
+ORC_API double orc_e4m3_value(uint8_t c) {
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                 /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Nearest E4M3 value to v, ties to even, saturating at +-448 (the largest finite value). */
+ORC_API double orc_e4m3_round(double v) {
+    const double a = fabs(v);
+    double q;
+    if (a >= 448.0) {
+        q = 448.0;
+    } else if (a < 0x1p-6) {
+        q = nearbyint(a * 512.0) / 512.0;        /* subnormal grid: steps of 2^-9 */
+    } else {
+        int e;
+        frexp(a, &e);                            /* a in [2^(e-1), 2^e) */
+        const double step = ldexp(1.0, e - 1 - 3);
+        q = nearbyint(a / step) * step;
+        if (q > 448.0) q = 448.0;
+    }
+    return v < 0 ? -q : q;
+}
+
+/* MX conversion of one row of n bf16 values (n a multiple of 32), block by block: the
+ * shared exponent is floor(log2(amax)) - 8 (8 = the largest exponent of E4M3), clamped to
+ * E8M0's range, and each value divided by 2^shared rounds to E4M3. Writes the dequantised
+ * values (code * 2^shared, exact in bf16 within its exponent range) and the E8M0 bytes. */
+ORC_API void orc_mx_quant_row(const uint16_t* v, int64_t n, uint16_t* deq, uint8_t* scales) {
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double amax = 0.0;
+        for (int k = 0; k < 32; ++k) {
+            const double a = fabs((double)orc_f32(v[b * 32 + k]));
+            if (a > amax) amax = a;
+        }
+        int sh = -127;
+        if (amax > 0.0) {
+            int e;
+            frexp(amax, &e);
+            sh = (e - 1) - 8;
+            if (sh < -127) sh = -127;
+            if (sh > 127) sh = 127;
+        }
+        if (scales) scales[b] = (uint8_t)(sh + 127);
+        for (int k = 0; k < 32; ++k) {
+            const double x = (double)orc_f32(v[b * 32 + k]);
+            const double q = amax > 0.0 ? orc_e4m3_round(ldexp(x, -sh)) : 0.0;
+            deq[b * 32 + k] = orc_bf16((float)ldexp(q, sh));
+        }
+    }
+}
+
 /* Dequant of one int32 accumulator: bf16(fp32(acc) * (xs * ws)). */
 static uint16_t orc_dequant(int32_t acc, float xs, float ws) {
     float sc = xs * ws;
@@ -255,6 +317,7 @@ typedef struct {
     int32_t rope_chunk;       /* 0: rotate-half on the slice as is; else the QuantRope3D form */
     int32_t q_quant_per_head; /* q codes and scales per (token, head) instead of per token */
     int32_t q_head_norm;      /* RMSNorm (no gamma) of every q head after q_b, before RoPE */
+    int32_t mxfp8;            /* MXFP8 projections: E4M3 weights with E8M0 block scales */
 } orc_cfg;
 
 typedef struct {
@@ -272,6 +335,10 @@ typedef struct {
     const uint16_t* gamma_kv; /* [kv_lora] bf16 */
     const float* cos;         /* [max_pos, rope] fp32 */
     const float* sin;
+    const uint8_t* ms_qa;     /* MXFP8: E8M0 block scales [N, K/32] of each weight */
+    const uint8_t* ms_qb;
+    const uint8_t* ms_kva;
+    const uint8_t* ms_kvb;
 } orc_inputs;
 
 typedef struct { /* every array is [nrows, ...] in the order of rows[] */
@@ -304,9 +371,28 @@ static void orc_rope(const orc_cfg* cfg, const uint16_t* u, const float* c, cons
         orc_rope_row(u, c, s, R, out);
 }
 
-/* One projection of one bf16 row v (length K) through W [N,K]: bf16 or W8A8. */
+/* One projection of one bf16 row v (length K) through W [N,K]: bf16, W8A8 or MXFP8
+ * (the AT-09 Linear modes of the AT-10 card, section 四). MXFP8: scaled_mm with an fp32
+ * result, sum_k deq(x_k) * deq(w_nk) with x converted to MX block by block, then the bf16
+ * cast point of the projection. */
 static void orc_project(const orc_cfg* cfg, const uint16_t* v, int64_t K, const void* W,
-                        const float* ws, int64_t N, uint16_t* out, int8_t* tmp_codes) {
+                        const float* ws, const uint8_t* ms, int64_t N, uint16_t* out,
+                        int8_t* tmp_codes) {
+    if (cfg->mxfp8) {
+        uint16_t* xd = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)K);
+        orc_mx_quant_row(v, K, xd, NULL);
+        const uint8_t* Wc = (const uint8_t*)W;
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double w = ldexp(orc_e4m3_value(Wc[n * K + k]), (int)ms[n * (K / 32) + k / 32] - 127);
+                s += (double)orc_f32(xd[k]) * w;
+            }
+            out[n] = orc_bf16((float)s);
+        }
+        free(xd);
+        return;
+    }
     if (!cfg->w8a8) {
         const uint16_t* Wb = (const uint16_t*)W;
         for (int64_t n = 0; n < N; ++n) out[n] = orc_bf16(orc_dot_bf16(v, Wb + n * K, K));
@@ -365,7 +451,7 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
         }
 
         /* kv branch: kv_a projection -> [c_kv | k_pe] */
-        orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, Lkv + R, a, codes);
+        orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, in->ms_kva, Lkv + R, a, codes);
         orc_norm(cfg, a, in->gamma_kv, Lkv, kvn);
         if (out->kv_norm) memcpy(out->kv_norm + i * Lkv, kvn, sizeof(uint16_t) * (size_t)Lkv);
         if (out->k_pe) orc_rope(cfg, a + Lkv, c, s, R, out->k_pe + i * R);
@@ -377,7 +463,7 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
         }
         if (Dv > 0) { /* kv_b projection of the normalised compressed KV */
             const uint16_t* kv_src = kvn_given ? kvn_given + i * Lkv : kvn;
-            orc_project(cfg, kv_src, Lkv, in->w_kvb, in->ws_kvb, H * KH, a, codes);
+            orc_project(cfg, kv_src, Lkv, in->w_kvb, in->ws_kvb, in->ms_kvb, H * KH, a, codes);
             for (int64_t h = 0; h < H; ++h) {
                 if (out->k_nope)
                     memcpy(out->k_nope + (i * H + h) * Dn, a + h * KH, sizeof(uint16_t) * (size_t)Dn);
@@ -388,11 +474,11 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
 
         /* q branch: q_a projection -> RMSNorm*gamma -> q_b projection -> split, RoPE */
         if (Lq > 0) {
-            orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, Lq, a, codes);
+            orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, in->ms_qa, Lq, a, codes);
             orc_norm(cfg, a, in->gamma_q, Lq, qn);
             if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
             const uint16_t* q_src = qn_given ? qn_given + i * Lq : qn;
-            orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, H * QH, a, codes);
+            orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, in->ms_qb, H * QH, a, codes);
             if (cfg->q_head_norm) /* [AT-10] section 九: q_b -> reshape (heads, head_dim) -> RMSNorm */
                 for (int64_t h = 0; h < H; ++h) orc_norm(cfg, a + h * QH, NULL, QH, a + h * QH);
             for (int64_t h = 0; h < H; ++h) {

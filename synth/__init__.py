@@ -67,6 +67,7 @@ class Config:
     rope_interleaved: bool = False  # rope slices de-interleaved before rotate-half
     q_quant_per_head: bool = False  # q codes / scales per (token, head)
     q_head_norm: bool = False       # RMSNorm of every q head after q_b (the V4-shape prolog)
+    mxfp8: bool = False             # MXFP8 weights (E4M3 codes + E8M0 block scales)
 
     def asdict(self):
         return asdict(self)
@@ -109,6 +110,10 @@ CONFIGS = {
                         nope_dim=448, v_dim=0, n_heads=64, max_pos=8192, positions="uniform",
                         q_head_norm=True, index=5),
     # Same shape with int8 W8A8 projections.
+    # Same shape with MXFP8 projections (E4M3 weights, one E8M0 scale per 32 of K).
+    "v3_mxfp8": Config("v3_mxfp8", T=4096, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
+                       nope_dim=128, v_dim=0, n_heads=128, max_pos=8192, positions="arange",
+                       mxfp8=True, index=6),
     "v3_w8a8": Config("v3_w8a8", T=16384, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
                       nope_dim=128, v_dim=0, n_heads=128, max_pos=16384,
                       positions="arange", w8a8=True, index=4),
@@ -153,6 +158,18 @@ def slot_mapping(T: int, n_slots: int, seed: int = 0, pad_frac: float = 0.08,
         idx = torch.randperm(T, generator=g)[:out_of_range]
         slots[idx] = n_slots + torch.arange(idx.numel(), dtype=torch.int32) * 7
     return slots.contiguous()
+
+
+def _mx_weight(g, n, k):
+    """MXFP8 weight [n, k]: E4M3 bytes drawn directly (random sign, exponent field 3..10,
+    mantissa 0..7, so no NaN codes) and one E8M0 byte per 32 of k (2^-9 .. 2^-7): magnitudes
+    from about 1e-4 to 0.12, around the size of the bf16 weights."""
+    sign = torch.randint(0, 2, (n, k), generator=g, dtype=torch.int32) << 7
+    exp = torch.randint(3, 11, (n, k), generator=g, dtype=torch.int32) << 3
+    man = torch.randint(0, 8, (n, k), generator=g, dtype=torch.int32)
+    codes = (sign | exp | man).to(torch.uint8).contiguous()
+    scales = torch.randint(127 - 9, 127 - 6, (n, k // 32), generator=g, dtype=torch.int32)
+    return codes, scales.to(torch.uint8).contiguous()
 
 
 def _normal(g, shape, std):
@@ -203,7 +220,11 @@ def make_inputs(cfg: Config, seed: int | None = None, weights_seed: int | None =
     out["positions"] = pos.contiguous()
 
     def weight(name, n, k):
-        if cfg.w8a8:
+        if cfg.mxfp8:
+            codes, scales = _mx_weight(gw, n, k)
+            out[name] = codes
+            out[name + "_mxscale"] = scales
+        elif cfg.w8a8:
             codes, scale = _int8_weight(gw, n, k)
             out[name] = codes
             out[name + "_scale"] = scale

@@ -544,3 +544,75 @@ def test_head_norm_gives_unit_rms_heads():
     q = np.concatenate([from_bits(out["q_nope"]), from_bits(out["q_pe"])], axis=2).astype(np.float64)
     ms = (q ** 2).mean(axis=2)
     assert np.abs(ms - 1).max() < 2.0 ** -7
+
+
+# ------------------------------------------------------------------ MXFP8 ----
+
+def test_e4m3_decode_all_codes():
+    """Every E4M3FN byte decodes as torch's float8_e4m3fn does (NaN at 0x7F and 0xFF)."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_rounding_matches_torch_and_saturates():
+    """Nearest E4M3 value, ties to even, against torch's conversion inside the finite range
+    (grid points, midpoints, subnormals, random values); beyond 448 the MX conversion
+    saturates to 448."""
+    grid = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    grid = np.unique(grid[~np.isnan(grid)])
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals = np.concatenate([grid, mids, rng.uniform(-440, 440, 2000), rng.uniform(-0.02, 0.02, 2000)])
+    vals = vals[np.abs(vals) < 448]
+    ref = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_round(float(np.float32(v))) for v in vals])
+    np.testing.assert_array_equal(got, ref)
+    for v in (448.0, 449.0, 470.0, 511.9, 1e6):
+        assert oracle.e4m3_round(v) == 448.0 and oracle.e4m3_round(-v) == -448.0
+
+
+def test_mx_block_scale_rule():
+    """Shared exponent floor(log2(amax)) - 8: amax 1.0 gives E8M0 119; the block's largest value
+    lands in [256, 512) before rounding; an all-zero block gives zeros (scale byte 0); values
+    on the E4M3 grid times a power of two come back exactly when the block's largest
+    mantissa is at most 1.75 (1.875 * 2^e lands on 480 > 448 and saturates to 1.75 * 2^e)."""
+    v = np.zeros(128, np.float32)
+    v[:32] = rng.uniform(-1, 1, 32)
+    v[0] = 1.0
+    v[32:64] = rng.uniform(-3e-3, 3e-3, 32)
+    codes = [0x38] + list(range(0x40, 0x5F))                             # 1.0 and 2 .. 28
+    grid = np.array([oracle.e4m3_value(c) for c in codes])
+    v[64:96] = (grid * 2.0 ** -12).astype(np.float32)
+    v[96:128] = v[64:96]
+    v[96] = 30 * 2.0 ** -12                                              # 1.875 * 2^4
+    bitsv = to_bf16_bits(v)
+    deq, sc = oracle.mx_quant_row(bitsv)
+    assert sc[0] == 119
+    b = from_bits(bitsv[32:64]).astype(np.float64)
+    assert 256 <= np.abs(b).max() / 2.0 ** (int(sc[1]) - 127) < 512
+    np.testing.assert_array_equal(from_bits(deq[64:96]), from_bits(bitsv[64:96]))
+    assert from_bits(deq[96:97])[0] == 28 * 2.0 ** -12
+    z, zs = oracle.mx_quant_row(to_bf16_bits(np.zeros(32, np.float32)))
+    assert (z == 0).all() and zs[0] == 0
+
+
+def test_mx_projection_is_the_bf16_gemm_of_dequantised_operands():
+    """An MXFP8 projection equals the bf16 GEMM definition on its dequantised operands: the
+    MX-converted activation row and the weights decoded with torch's E4M3 type times their
+    E8M0 scales (exact in bf16 here). Checked on k_pe at position 0, where RoPE is the
+    identity, of a small KV-Prolog configuration."""
+    from dataclasses import replace
+    cfg = replace(synth.get_config("tiny_kv"), mxfp8=True)
+    inp = synth.make_inputs(cfg)
+    assert int(inp["positions"][0]) == 0
+    out = oracle.prolog(cfg, inp, rows=np.array([0], np.int32))
+    xd, _ = oracle.mx_quant_row(synth.bf16_bits(inp["x"][0]))
+    w = inp["w_kva"].view(torch.float8_e4m3fn).double()
+    s = torch.exp2(inp["w_kva_mxscale"].double() - 127).repeat_interleave(32, dim=1)
+    wd = to_bf16_bits((w * s).float().numpy())
+    assert np.array_equal(from_bits(wd).astype(np.float64), (w * s).numpy())   # exact in bf16
+    ref = oracle.gemm_bf16(xd.reshape(1, -1), wd)[0]
+    np.testing.assert_array_equal(out["k_pe"][0], ref[cfg.kv_lora:cfg.kv_lora + cfg.rope_dim])
