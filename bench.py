@@ -230,7 +230,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache,v3_decode+variants,v4_decode",
+    ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache,v3_decode+variants,v4_decode,"
+                            "v3_mxfp8",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -338,6 +339,9 @@ def main():
                "launch": "hip_graph" if e_use_g else "eager", "eager_ms_per_step": round(ee_ms, 5),
                "graph_ms_per_step": round(eg_ms, 5) if eg_ms else None,
                "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
+        if ecfg.mxfp8:
+            ent["mxfp8"] = ("E4M3 weights with E8M0 scales per 32 of K, decoded to bf16 every step "
+                            "(mx_convert) with the activations' MX conversion; bf16 MFMA GEMMs")
         if opt == "variants":
             ent["variants"] = "RMSNorm variant A (rsqrt), de-interleaved RoPE, per-(token, head) q quant"
         if opt == "kvcache":

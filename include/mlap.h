@@ -82,6 +82,13 @@ typedef enum {
  *   gamma (the configured variant) before RoPE. bf16 only; Dn and Dn + R multiples of 64,
  *   H <= 1024, H*(Dn+R) <= 32768, H*R <= 8192. */
 #define MLAP_Q_HEAD_NORM 0x10u
+/* MLAP_MXFP8: MXFP8 projections (the third Linear mode of the AT-10 card, section 四:
+ *   scaled_mm with an fp32 result; the format of the grouped_matmul_swiglu_quant page,
+ *   section 算子语义: E4M3 data and one E8M0 scale 2^(e-127) per 32 values along K). The
+ *   weights w_* are E4M3FN bytes [N, K] with scales ms_* [N, K/32]; the activations (x, q_norm,
+ *   kv_norm) are converted block by block (shared exponent floor(log2(amax)) - 8, values
+ *   rounded to E4M3, saturating at 448). Not with MLAP_W8A8. */
+#define MLAP_MXFP8 0x20u
 
 typedef struct {
     int32_t t_max;    /* largest token count a run may pass (sizes nothing on device) */
@@ -95,7 +102,7 @@ typedef struct {
     int32_t max_pos;  /* rows of the cos/sin tables */
     float eps;        /* RMSNorm epsilon (added to the mean square) */
     uint32_t flags;   /* MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
-                         MLAP_Q_HEAD_NORM */
+                         MLAP_Q_HEAD_NORM | MLAP_MXFP8 */
 } mlap_config;
 
 /*
@@ -108,7 +115,7 @@ typedef struct {
     const void* x;             /* [T, Hd] bf16 token activations */
     const int32_t* positions;  /* [T] position of each token in [0, max_pos); values outside
                                   are clamped into range (a violated precondition) */
-    const void* w_qa;          /* [Lq, Hd]          bf16 (int8 with W8A8); unused if Lq == 0 */
+    const void* w_qa;          /* [Lq, Hd]          bf16 (int8 with W8A8, E4M3 with MXFP8); unused if Lq == 0 */
     const void* w_qb;          /* [H*(Dn+R), Lq]    bf16 (int8); per head [nope | rope] rows */
     const void* w_kva;         /* [Lkv+R, Hd]       bf16 (int8); rows [c_kv | k_pe] */
     const void* w_kvb;         /* [H*(Dn+Dv), Lkv]  bf16 (int8); per head [nope | v]; if Dv > 0 */
@@ -127,6 +134,10 @@ typedef struct {
        tokens' entries. Needed (with cache_slots > 0) when any cache pointer is set. */
     const int32_t* slot_mapping; /* [T] int32 */
     int32_t cache_slots;         /* rows of every cache */
+    const uint8_t* ms_qa;        /* MLAP_MXFP8 only: E8M0 block scales [Lq, Hd/32] of w_qa */
+    const uint8_t* ms_qb;        /* [H*(Dn+R), Lq/32] */
+    const uint8_t* ms_kva;       /* [Lkv+R, Hd/32] */
+    const uint8_t* ms_kvb;       /* [H*(Dn+Dv), Lkv/32] */
 } mlap_inputs;
 
 /*
@@ -162,7 +173,8 @@ typedef struct mlap_prolog* mlap_handle;
 MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out);
 
 /* Bytes of device workspace a run with T tokens needs (GEMM intermediates, the
- * per-tile partial amax of q, the W8A8 int8 activations). The caller allocates it. */
+ * per-tile partial amax of q, the W8A8 int8 activations; with MXFP8 also the decoded
+ * bf16 weights and converted activations). The caller allocates it. */
 MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes);
 
 /* Enqueue the whole prolog for in->T tokens on `stream`. `ws` must hold at least

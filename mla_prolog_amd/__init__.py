@@ -27,6 +27,7 @@ MLAP_NORM_RSQRT = 0x2        # RMSNorm variant A
 MLAP_ROPE_INTERLEAVED = 0x4  # rope slices de-interleaved before rotate-half
 MLAP_QUANT_Q_PER_HEAD = 0x8  # q codes / scales per (token, head)
 MLAP_Q_HEAD_NORM = 0x10      # RMSNorm of every q head after q_b (the V4-shape prolog)
+MLAP_MXFP8 = 0x20            # E4M3 weights with E8M0 scales per 32 of K; MX-converted activations
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_timing_begin", "mlap_timing_end",
@@ -48,7 +49,8 @@ class _Config(C.Structure):
 class _Inputs(C.Structure):
     _fields_ = [("T", C.c_int32)] + [(n, C.c_void_p) for n in (
         "x", "positions", "w_qa", "w_qb", "w_kva", "w_kvb", "ws_qa", "ws_qb", "ws_kva", "ws_kvb",
-        "gamma_q", "gamma_kv", "cos", "sin", "slot_mapping")] + [("cache_slots", C.c_int32)]
+        "gamma_q", "gamma_kv", "cos", "sin", "slot_mapping")] + [("cache_slots", C.c_int32)] + \
+        [(n, C.c_void_p) for n in ("ms_qa", "ms_qb", "ms_kva", "ms_kvb")]
 
 
 OUTPUTS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_i8", "q_scale",
@@ -141,16 +143,17 @@ class Prolog:
 
     def __init__(self, t_max, hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads,
                  max_pos, eps=1e-6, w8a8=False, norm_rsqrt=False, rope_interleaved=False,
-                 q_quant_per_head=False, q_head_norm=False):
+                 q_quant_per_head=False, q_head_norm=False, mxfp8=False):
         self.cfg = dict(t_max=t_max, hidden=hidden, q_lora=q_lora, kv_lora=kv_lora,
                         rope_dim=rope_dim, nope_dim=nope_dim, v_dim=v_dim, n_heads=n_heads,
                         max_pos=max_pos, eps=eps, w8a8=bool(w8a8), norm_rsqrt=bool(norm_rsqrt),
                         rope_interleaved=bool(rope_interleaved),
-                        q_quant_per_head=bool(q_quant_per_head), q_head_norm=bool(q_head_norm))
+                        q_quant_per_head=bool(q_quant_per_head), q_head_norm=bool(q_head_norm),
+                        mxfp8=bool(mxfp8))
         flags = ((MLAP_W8A8 if w8a8 else 0) | (MLAP_NORM_RSQRT if norm_rsqrt else 0) |
                  (MLAP_ROPE_INTERLEAVED if rope_interleaved else 0) |
                  (MLAP_QUANT_Q_PER_HEAD if q_quant_per_head else 0) |
-                 (MLAP_Q_HEAD_NORM if q_head_norm else 0))
+                 (MLAP_Q_HEAD_NORM if q_head_norm else 0) | (MLAP_MXFP8 if mxfp8 else 0))
         c = _Config(int(t_max), int(hidden), int(q_lora), int(kv_lora), int(rope_dim),
                     int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps), flags)
         h = C.c_void_p()
@@ -164,7 +167,8 @@ class Prolog:
         g = lambda k: bool(getattr(cfg, k, False))
         return cls(t_max or cfg.T, cfg.hidden, cfg.q_lora, cfg.kv_lora, cfg.rope_dim,
                    cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8,
-                   g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"), g("q_head_norm"))
+                   g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"), g("q_head_norm"),
+                   g("mxfp8"))
 
     def close(self):
         if getattr(self, "_h", None):
@@ -210,7 +214,7 @@ class Prolog:
         x = inputs["x"]
         T = int(x.shape[0])
         w8 = self.cfg["w8a8"]
-        wdt = torch.int8 if w8 else torch.bfloat16
+        wdt = torch.int8 if w8 else torch.uint8 if self.cfg["mxfp8"] else torch.bfloat16
         if outputs is None:
             outputs = self.alloc_outputs(T, device=x.device)
         g = inputs.get
@@ -226,7 +230,9 @@ class Prolog:
                     gamma_kv=_ptr(inputs["gamma_kv"], torch.bfloat16, "gamma_kv"),
                     cos=_ptr(inputs["cos"], torch.float32, "cos"),
                     sin=_ptr(inputs["sin"], torch.float32, "sin"),
-                    slot_mapping=_ptr(g("slot_mapping"), torch.int32, "slot_mapping"))
+                    slot_mapping=_ptr(g("slot_mapping"), torch.int32, "slot_mapping"),
+                    **{"ms_" + k: _ptr(g("w_%s_mxscale" % k), torch.uint8, "w_%s_mxscale" % k)
+                       for k in ("qa", "qb", "kva", "kvb")})
         caches = [outputs[k] for k in CACHES if outputs.get(k) is not None]
         if caches:
             i.cache_slots = int(caches[0].shape[0])
@@ -240,7 +246,8 @@ class Prolog:
     def run(self, inputs, outputs=None, workspace=None, stream=None):
         """Enqueue one prolog run. ``inputs``: dict with x, positions, w_kva, gamma_kv,
         cos, sin and (as configured) w_qa, w_qb, gamma_q, w_kvb, and ``*_scale`` for
-        W8A8; ``slot_mapping`` (int32 [T]) with a KV cache write. ``outputs``: dict of
+        W8A8, ``*_mxscale`` (uint8 E8M0 [N, K/32], with uint8 E4M3 weights) for MXFP8;
+        ``slot_mapping`` (int32 [T]) with a KV cache write. ``outputs``: dict of
         preallocated tensors (default: alloc_outputs), plus any of the caches in CACHES
         (rows = cache slots). Returns the outputs dict."""
         i, o, ws, outputs = self._marshal(inputs, outputs, workspace)

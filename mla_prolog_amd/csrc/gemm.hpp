@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kWave* WM* WN) void gemm_nt_kernel(GemmArgs g) {
     const int row0 = tid >> 3;
     const int cc16 = (tid & 7) * 16;
     constexpr int R8 = S::NT / 8;  // rows covered by one pass of the workgroup
-    const uint32_t lda32 = static_cast<uint32_t>(lda_b), ldb32 = static_cast<uint32_t>(ldb_b);
+    const uint32_t lda32 = static_cast<uint32_t>(lda_b);
     // byte offsets of this thread's B rows from b_base (signed: a row remapped for a
     // de-interleaved rope slice may come from outside the tile)
     int64_t b_off[S::CH > S::A_PER ? S::CH - S::A_PER : 1];

@@ -121,4 +121,11 @@ constexpr int kHeadNormChunks = 16;
 constexpr int kHeadNormPeChunks = 1024;
 hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s);
 
+// MXFP8 operands for the bf16 MFMA GEMMs: E4M3 weights [N, K] with E8M0 scales [N, K/32]
+// decoded to bf16 (exact), and the MX conversion of bf16 activations [T, K] (K a multiple of
+// 32), written back as the dequantised bf16 values.
+hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int N, int K, uint16_t* out,
+                             hipStream_t s);
+hipError_t launch_mx_act(const uint16_t* x, int T, int K, uint16_t* out, hipStream_t s);
+
 }  // namespace mlap

@@ -32,10 +32,11 @@ enum KernelId : int32_t {
     kKGemmUpKv = 4,
     kKQuantQ = 5,
     kKQHeadNorm = 6,
-    kKCount = 7
+    kKMxConvert = 7,
+    kKCount = 8
 };
-const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope",
-                                           "gemm_up_q", "gemm_up_kv", "quant_q", "q_head_norm"};
+const char* const kKernelNames[kKCount] = {"act_quant", "gemm_down", "norm_rope", "gemm_up_q",
+                                           "gemm_up_kv", "quant_q", "q_head_norm", "mx_convert"};
 
 constexpr size_t kAlign = 256;
 constexpr int kCUs = 256;          // MI355X compute units
@@ -97,6 +98,7 @@ struct Timer {
 // Workspace carve-up for T tokens.
 struct WsLayout {
     size_t a1 = 0, tail = 0, qn = 0, kvn = 0, qpart = 0, xq = 0, xs = 0, qnq = 0, qns = 0, kvq = 0, kvs = 0;
+    size_t wd_down = 0, wd_qb = 0, wd_kvb = 0, xm = 0, qnm = 0, kvnm = 0;  // MXFP8 operands
     size_t total = 0;
 };
 
@@ -105,6 +107,7 @@ struct WsLayout {
 struct mlap_prolog {
     mlap_config cfg;
     bool w8a8;
+    bool mx;      // MXFP8 projections
     int N1;       // down-projection width
     int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
     int bn_q, bn_kv;
@@ -244,6 +247,18 @@ struct mlap_prolog {
                 L.kvs = take(t * 4);
             }
         }
+        if (mx) {  // decoded weights and converted activations for the bf16 GEMMs
+            L.wd_down = take(static_cast<size_t>(N1) * cfg.hidden * 2);
+            L.xm = take(t * cfg.hidden * 2);
+            if (cfg.q_lora > 0) {
+                L.wd_qb = take(static_cast<size_t>(cfg.n_heads) * QH * cfg.q_lora * 2);
+                L.qnm = take(t * cfg.q_lora * 2);
+            }
+            if (cfg.v_dim > 0) {
+                L.wd_kvb = take(static_cast<size_t>(cfg.n_heads) * KH * cfg.kv_lora * 2);
+                L.kvnm = take(t * cfg.kv_lora * 2);
+            }
+        }
         L.total = std::max<size_t>(off, kAlign);
         return L;
     }
@@ -261,8 +276,9 @@ namespace {
 int validate(const mlap_config* c) {
     const bool w8 = (c->flags & MLAP_W8A8) != 0;
     if (c->flags & ~(MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
-                     MLAP_Q_HEAD_NORM))
+                     MLAP_Q_HEAD_NORM | MLAP_MXFP8))
         return MLAP_ERR_INVALID_ARG;
+    if ((c->flags & MLAP_W8A8) && (c->flags & MLAP_MXFP8)) return MLAP_ERR_INVALID_ARG;
     const bool head_norm = (c->flags & MLAP_Q_HEAD_NORM) && c->q_lora > 0;
     if (c->t_max < 1 || c->hidden < 1 || c->kv_lora < 1 || c->rope_dim < 1 || c->n_heads < 1 ||
         c->max_pos < 1 || c->q_lora < 0 || c->v_dim < 0 || c->nope_dim < 0 || !(c->eps >= 0.f))
@@ -324,6 +340,7 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
     if (!h) return MLAP_ERR_INVALID_ARG;
     h->cfg = *cfg;
     h->w8a8 = (cfg->flags & MLAP_W8A8) != 0;
+    h->mx = (cfg->flags & MLAP_MXFP8) != 0;
     h->N1 = cfg->q_lora + cfg->kv_lora + cfg->rope_dim;
     h->QH = cfg->nope_dim + cfg->rope_dim;
     h->KH = cfg->nope_dim + cfg->v_dim;
@@ -399,6 +416,9 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         return MLAP_ERR_INVALID_ARG;
     if (has_q && (!in->w_qa || !in->w_qb || !in->gamma_q)) return MLAP_ERR_INVALID_ARG;
     if (has_kvb && !in->w_kvb) return MLAP_ERR_INVALID_ARG;
+    const bool mx = h->mx;
+    if (mx && (!in->ms_kva || (has_q && (!in->ms_qa || !in->ms_qb)) || (has_kvb && !in->ms_kvb)))
+        return MLAP_ERR_INVALID_ARG;
     if (w8 && (!in->ws_kva || (has_q && (!in->ws_qa || !in->ws_qb)) || (has_kvb && !in->ws_kvb)))
         return MLAP_ERR_INVALID_ARG;
     // outputs that need a branch this configuration lacks
@@ -438,6 +458,24 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         if (e != hipSuccess) return MLAP_ERR_HIP; \
     } while (0)
 
+    // 0. MXFP8: weights decoded to bf16 and x converted block by block, for the bf16 GEMMs
+    uint16_t* wd_down = mx ? reinterpret_cast<uint16_t*>(wsb + L.wd_down) : nullptr;
+    uint16_t* xm = mx ? reinterpret_cast<uint16_t*>(wsb + L.xm) : nullptr;
+    if (mx) {
+        if (has_q)
+            MLAP_LAUNCH(kKMxConvert, launch_mx_dequant(static_cast<const uint8_t*>(in->w_qa), in->ms_qa, Lq,
+                                                      c.hidden, wd_down, s));
+        MLAP_LAUNCH(kKMxConvert, launch_mx_dequant(static_cast<const uint8_t*>(in->w_kva), in->ms_kva, Lkv + R,
+                                                  c.hidden, wd_down + static_cast<size_t>(Lq) * c.hidden, s));
+        if (has_q)
+            MLAP_LAUNCH(kKMxConvert, launch_mx_dequant(static_cast<const uint8_t*>(in->w_qb), in->ms_qb, H * h->QH,
+                                                      Lq, reinterpret_cast<uint16_t*>(wsb + L.wd_qb), s));
+        if (has_kvb)
+            MLAP_LAUNCH(kKMxConvert, launch_mx_dequant(static_cast<const uint8_t*>(in->w_kvb), in->ms_kvb, H * h->KH,
+                                                      Lkv, reinterpret_cast<uint16_t*>(wsb + L.wd_kvb), s));
+        MLAP_LAUNCH(kKMxConvert, launch_mx_act(static_cast<const uint16_t*>(in->x), T, c.hidden, xm, s));
+    }
+
     // 1. down projection x . [W_qa ; W_kva]^T -> a1 [T, N1] bf16
     GemmArgs g{};
     g.M = T;
@@ -445,8 +483,8 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     g.K = c.hidden;
     g.lda = c.hidden;
     g.ldb = c.hidden;
-    g.B0 = has_q ? in->w_qa : in->w_kva;
-    g.B1 = in->w_kva;
+    g.B0 = mx ? static_cast<const void*>(wd_down) : (has_q ? in->w_qa : in->w_kva);
+    g.B1 = mx ? static_cast<const void*>(wd_down + static_cast<size_t>(Lq) * c.hidden) : in->w_kva;
     g.b_split = Lq;
     if (c.flags & MLAP_ROPE_INTERLEAVED) {  // the k_pe slice of [q_a | c_kv | k_pe]
         g.pe_period = h->N1;
@@ -471,7 +509,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                                     ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
                                     : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
     } else if (plan.tail_splits) {
-        g.A = in->x;
+        g.A = mx ? static_cast<const void*>(xm) : in->x;
         GemmArgs r = g;  // columns [tail_c0, N1): split-K fp32 partials
         r.N = h->N1 - plan.tail_c0;
         r.pe_c0 = plan.tail_c0;
@@ -494,7 +532,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                                           : launch_gemm(r, InType::kBf16, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
         g.N = h->N1;
     } else {
-        g.A = in->x;
+        g.A = mx ? static_cast<const void*>(xm) : in->x;
         MLAP_LAUNCH(kKGemmDown, plan.big_down
                                     ? launch_gemm_big(g, InType::kBf16, plan.down_epi, s, plan.down_shape)
                                     : launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
@@ -561,7 +599,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.K = Lq;
         u.lda = Lq;
         u.ldb = Lq;
-        u.B0 = u.B1 = in->w_qb;
+        u.B0 = u.B1 = mx ? static_cast<const void*>(wsb + L.wd_qb) : in->w_qb;
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
@@ -591,6 +629,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
             u.A = na.qn_i8;
             u.a_scale = na.qn_scale;
             u.b_scale0 = u.b_scale1 = in->ws_qb;
+        } else if (mx) {  // the MX conversion of q_norm
+            uint16_t* qnm = reinterpret_cast<uint16_t*>(wsb + L.qnm);
+            MLAP_LAUNCH(kKMxConvert, launch_mx_act(qn, T, Lq, qnm, s));
+            u.A = qnm;
         } else {
             u.A = qn;
         }
@@ -673,7 +715,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.K = Lkv;
         u.lda = Lkv;
         u.ldb = Lkv;
-        u.B0 = u.B1 = in->w_kvb;
+        u.B0 = u.B1 = mx ? static_cast<const void*>(wsb + L.wd_kvb) : in->w_kvb;
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
@@ -689,6 +731,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
             u.A = na.kv_i8_b;
             u.a_scale = na.kv_scale_b;
             u.b_scale0 = u.b_scale1 = in->ws_kvb;
+        } else if (mx) {  // the MX conversion of kv_norm
+            uint16_t* kvnm = reinterpret_cast<uint16_t*>(wsb + L.kvnm);
+            MLAP_LAUNCH(kKMxConvert, launch_mx_act(kvn, T, Lkv, kvnm, s));
+            u.A = kvnm;
         } else {
             u.A = kvn;
         }

@@ -12,6 +12,8 @@
 // section 3.3). The INT8 quant is the per-row PrologQuant of the same page,
 // section 3.1: multiplier 127/amax, round half to even, saturate, scale amax/127.
 #include "common.hpp"
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace mlap {
@@ -939,6 +941,100 @@ hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s) {
         a.H * (a.R >> 3) > kHeadNormPeChunks || (a.R >> 3) % 2)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(q_head_norm_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---- MXFP8: E4M3 data with one E8M0 scale (2^(e-127)) per 32 values along K ----
+
+// Value of an OCP E4M3FN byte (0x7F / 0xFF are NaN).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15, m = c & 7;
+    float v = (e == 0) ? ldexpf(static_cast<float>(m), -9) : ldexpf(1.0f + 0.125f * m, static_cast<int>(e) - 7);
+    if (e == 15 && m == 7) v = __builtin_nanf("");
+    return (c & 0x80) ? -v : v;
+}
+
+// Nearest E4M3 value to v (|v| < 2^10), ties to even, saturating at +-448; every step is exact
+// in fp32 (scalings by powers of two and a round to an integer).
+__device__ __forceinline__ float e4m3_round(float v) {
+    const float a = fabsf(v);
+    float q;
+    if (a >= 448.0f) {
+        q = 448.0f;
+    } else if (a < 0x1p-6f) {
+        q = rintf(a * 512.0f) * 0x1p-9f;  // subnormal grid: steps of 2^-9
+    } else {
+        const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;  // a in [2^e, 2^(e+1))
+        q = ldexpf(rintf(ldexpf(a, 3 - e)), e - 3);
+        q = fminf(q, 448.0f);
+    }
+    return copysignf(q, v);
+}
+
+// Weights: E4M3 bytes [N, K] with E8M0 bytes [N, K/32] -> bf16 [N, K] (exact within bf16's
+// exponent range); 16 values per thread.
+__global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                         size_t n16, int K, uint16_t* out) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const size_t e0 = i * 16;
+        const size_t row = e0 / K;
+        const int col = static_cast<int>(e0 - row * K);
+        const uint4 c = *reinterpret_cast<const uint4*>(codes + e0);
+        const int sh = static_cast<int>(scales[row * (K / 32) + col / 32]) - 127;
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        float f[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[j] = ldexpf(e4m3_value((w[j >> 2] >> (8 * (j & 3))) & 0xFF), sh);
+        uint4* o = reinterpret_cast<uint4*>(out + e0);
+        o[0] = pack8(f);
+        o[1] = pack8(f + 8);
+    }
+}
+
+// Activations: the MX conversion of a bf16 matrix [T, K], block by block (32 values, one
+// thread each): shared exponent floor(log2(amax)) - 8 clamped to E8M0's range, values divided
+// by 2^shared rounded to E4M3; writes the dequantised values (exact in bf16) for the bf16
+// MFMA GEMM that follows.
+__global__ __launch_bounds__(256) void mx_act_kernel(const uint16_t* x, size_t nblocks, uint16_t* out) {
+    for (size_t b = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; b < nblocks;
+         b += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+        float f[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) unpack8(src[j], f + 8 * j);
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        int sh = -127;
+        if (amax > 0.f) {
+            const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // floor(log2)
+            sh = min(127, max(-127, e - 8));
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) f[j] = amax > 0.f ? ldexpf(e4m3_round(ldexpf(f[j], -sh)), sh) : 0.f;
+        uint4* dst = reinterpret_cast<uint4*>(out + b * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = pack8(f + 8 * j);
+    }
+}
+
+hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int N, int K, uint16_t* out,
+                             hipStream_t s) {
+    if (N <= 0 || K <= 0) return hipSuccess;
+    if (K % 32) return hipErrorInvalidValue;
+    const size_t n16 = static_cast<size_t>(N) * K / 16;
+    const int grid = static_cast<int>(std::min<size_t>((n16 + 255) / 256, 8192));
+    hipLaunchKernelGGL(mx_dequant_kernel, dim3(grid), dim3(256), 0, s, codes, scales, n16, K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_act(const uint16_t* x, int T, int K, uint16_t* out, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (K % 32) return hipErrorInvalidValue;
+    const size_t nb = static_cast<size_t>(T) * K / 32;
+    const int grid = static_cast<int>(std::min<size_t>((nb + 255) / 256, 8192));
+    hipLaunchKernelGGL(mx_act_kernel, dim3(grid), dim3(256), 0, s, x, nb, out);
     return hipGetLastError();
 }
 

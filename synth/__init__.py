@@ -122,7 +122,7 @@ CONFIGS = {
 
 def get_config(name: str, T: int | None = None, **variants) -> Config:
     """A named configuration, optionally with another token count and variant flags
-    (norm_rsqrt, rope_interleaved, q_quant_per_head, q_head_norm)."""
+    (norm_rsqrt, rope_interleaved, q_quant_per_head, q_head_norm, mxfp8)."""
     cfg = CONFIGS[name]
     if T is not None:
         cfg = replace(cfg, T=int(T))

@@ -24,8 +24,8 @@ its pair, 2 ulp(rho) with rho the pair norm (which the rotation preserves). End 
 oracle chain, every bf16 output of stage 2 must lie within the bound plus the
 exact linear propagation of the measured stage-1 differences
 (sum_k |da_k| |W[n,k]|, where a is the activation the up projection reads: the
-normalised bf16 row, or with W8A8 its per-token quantise-dequantise; RoPE pairs
-add their two partners).
+normalised bf16 row, with W8A8 its per-token quantise-dequantise, with MXFP8 its MX
+conversion; RoPE pairs add their two partners).
 
 Where floating point decides an integer (the codes, and the amax behind each
 scale), the decision is checked in the same precision on both sides: the
@@ -136,8 +136,17 @@ def q_rows(q_nope, q_pe):
     return torch.cat([q_nope, q_pe], dim=2).reshape(q_nope.shape[0], -1)
 
 
+_E4M3 = None
+
+
 def _w_f64(inp, name, cfg):
     w = inp[name]
+    if getattr(cfg, "mxfp8", False):  # E4M3 codes times their E8M0 block scale
+        global _E4M3
+        if _E4M3 is None:
+            _E4M3 = np.array([oracle.e4m3_value(c) for c in range(256)], np.float64)
+        sc = np.exp2(inp[name + "_mxscale"].numpy().astype(np.float64) - 127.0)
+        return _E4M3[w.numpy()] * np.repeat(sc, 32, axis=1)
     if cfg.w8a8:
         return w.numpy().astype(np.float64) * inp[name + "_scale"].numpy().astype(np.float64)[:, None]
     return oracle.f32(synth.bf16_bits(w)).astype(np.float64)
@@ -145,7 +154,11 @@ def _w_f64(inp, name, cfg):
 
 def _act_diff(cfg, g_bits, o_bits):
     """|activation seen by the up projection, GPU side - oracle side|, per element:
-    the bf16 rows themselves, or (W8A8) their per-row quantise-dequantise."""
+    the bf16 rows themselves, (W8A8) their per-row quantise-dequantise, or (MXFP8) their
+    MX conversion."""
+    if getattr(cfg, "mxfp8", False):
+        mx = lambda b: oracle.f32(np.stack([oracle.mx_quant_row(r)[0] for r in b])).astype(np.float64)
+        return np.abs(mx(g_bits) - mx(o_bits))
     if not cfg.w8a8:
         return np.abs(oracle.f32(g_bits).astype(np.float64) - oracle.f32(o_bits).astype(np.float64))
     gc, gs = oracle.quant_rows(g_bits)

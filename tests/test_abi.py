@@ -41,7 +41,7 @@ def test_status_strings_and_kernel_names():
         assert lib.mlap_status_str(s)
     assert lib.mlap_status_str(99) == b"unknown status"
     assert mlap.KERNELS == ("act_quant", "gemm_down", "norm_rope", "gemm_up_q", "gemm_up_kv",
-                            "quant_q", "q_head_norm")
+                            "quant_q", "q_head_norm", "mx_convert")
     assert mlap.version().startswith("mlap")
 
 
@@ -75,7 +75,9 @@ def create(**kw):
     (dict(q_lora=16384), mlap.MLAP_ERR_UNSUPPORTED),
     (dict(flags=mlap.MLAP_NORM_RSQRT | mlap.MLAP_ROPE_INTERLEAVED | mlap.MLAP_QUANT_Q_PER_HEAD),
      mlap.MLAP_OK),
-    (dict(flags=0x20), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=0x40), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=mlap.MLAP_MXFP8), mlap.MLAP_OK),
+    (dict(flags=mlap.MLAP_MXFP8 | mlap.MLAP_W8A8), mlap.MLAP_ERR_INVALID_ARG),
     (dict(flags=mlap.MLAP_Q_HEAD_NORM, hidden=4096, q_lora=1024, nope_dim=448, n_heads=64), mlap.MLAP_OK),
     (dict(flags=mlap.MLAP_Q_HEAD_NORM | mlap.MLAP_W8A8, hidden=4096, q_lora=1024, nope_dim=448,
           n_heads=64), mlap.MLAP_ERR_UNSUPPORTED),

@@ -125,7 +125,13 @@ VARIANTS = [("v3_decode", 64, ALL3),
             # the V4-shape prolog (per-head q RMSNorm after q_b), alone and with the variants
             ("v4_decode", None, {}),
             ("v4_decode", 100, dict(norm_rsqrt=True, rope_interleaved=True)),
-            ("v4_decode", 64, dict(q_quant_per_head=True))]
+            ("v4_decode", 64, dict(q_quant_per_head=True)),
+            # MXFP8 projections (E4M3 weights, E8M0 scales per 32 of K, MX-converted activations)
+            ("v3_mxfp8", 64, {}),
+            ("v3_mxfp8", 37, ALL3),
+            ("v2lite_kv_decode", None, dict(mxfp8=True)),
+            ("tiny_kv", None, dict(mxfp8=True)),
+            ("v4_decode", 64, dict(mxfp8=True))]
 
 
 @pytest.mark.parametrize("name,T,var", VARIANTS)
@@ -281,7 +287,8 @@ def test_empty_batch_is_a_noop():
 # wave-per-token row kernel and the W8A8 token blocks with their forked quant
 @pytest.mark.parametrize("name,T,var", [("v3_prefill", 1000, ALL3), ("v3_prefill", 2048, ALL3),
                                         ("v3_w8a8", 2048, ALL3), ("v4_decode", 1000, {}),
-                                        ("v4_decode", 2048, ALL3)])
+                                        ("v4_decode", 2048, ALL3), ("v3_mxfp8", None, {}),
+                                        ("v3_mxfp8", 1000, ALL3)])
 def test_prolog_variants_large_batch_sampled_rows(name, T, var):
     cfg = synth.get_config(name, T=T, **var)
     say("variants, sampled rows", name, "T=%d" % cfg.T)
