@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DOMINANT = "gemm_up_q"
 KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "gemm_big.hpp", "gemm_kernels.hip", "launch.hpp", "mlap_host.hip"]
@@ -46,7 +47,8 @@ def up_q_work(cfg, T):
     FLOPs: 2*T*N*K with N = H*(nope+rope), K = q_lora. Bytes: the q_b weight once,
     q_norm in, q_nope and q_pe out (bf16), and each token's cos/sin row."""
     N = cfg.n_heads * cfg.q_head
-    wbytes = N * cfg.q_lora * (1 if cfg.w8a8 else 2)
+    mfma8 = getattr(cfg, "mxfp8_mfma", False)  # E4M3 weights read directly, one scale per 32
+    wbytes = N * cfg.q_lora * (1 if cfg.w8a8 else 1 + 1 / 32 if mfma8 else 2)
     flops = 2.0 * T * N * cfg.q_lora
     byts = wbytes + T * cfg.q_lora * 2 + T * N * 2 + T * cfg.rope_dim * 8
     return flops, byts
@@ -100,7 +102,7 @@ VARIANTS = dict(norm_rsqrt=True, rope_interleaved=True, q_quant_per_head=True)
 
 
 def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, kv_cache=False,
-                   variants=False):
+                   variants=False, mfma=False):
     """Times `steps` whole prolog runs of workload `name`, cycling through `rotate` input and
     weight sets. Two timed passes: eager (one mlap_run per step from a prepared call, with
     HIP events around every launch of the dominant kernel) and, when `graph`, the same
@@ -108,7 +110,7 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, k
     launch cost between kernels). With `kv_cache`, every step also writes the kv rows of its
     tokens into KV caches of 4 T slots (all four caches, every token cached); with
     `variants`, the run uses RMSNorm variant A, the de-interleaved RoPE and per-head q
-    quant (VARIANTS). Returns (cfg,
+    quant (VARIANTS); with `mfma`, MXFP8 runs on the block-scaled MFMA. Returns (cfg,
     eager ms/step, dominant kernel ms, eager percentiles, graph ms/step or None, graph
     percentiles or None)."""
     import torch
@@ -116,7 +118,7 @@ def bench_workload(name, steps, warmup, rotate, dominant=DOMINANT, graph=True, k
     import mla_prolog_amd as mlap
     import synth
 
-    cfg = synth.get_config(name, **(VARIANTS if variants else {}))
+    cfg = synth.get_config(name, **(VARIANTS if variants else {}), **({"mxfp8_mfma": True} if mfma else {}))
     T = cfg.T
     sets = []
     for r in range(rotate):
@@ -184,7 +186,8 @@ def roofline_for(cfg, T, k_ms, workload):
     flops, byts = (up_kv_work if kv_mode else up_q_work)(cfg, T)
     kernel = "gemm_up_kv" if kv_mode else DOMINANT
     intensity = flops / byts
-    peak_c = PEAK_I8_TOPS if cfg.w8a8 else PEAK_BF16_TFLOPS
+    mfma8 = getattr(cfg, "mxfp8_mfma", False)
+    peak_c = PEAK_I8_TOPS if cfg.w8a8 else PEAK_FP8_TFLOPS if mfma8 else PEAK_BF16_TFLOPS
     ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(workload)
     if intensity >= ridge:
@@ -231,7 +234,7 @@ def main():
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache,v3_decode+variants,v4_decode,"
-                            "v3_mxfp8",
+                            "v3_mxfp8,v3_mxfp8+mfma",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
@@ -329,17 +332,23 @@ def main():
         ecfg, ee_ms, ek_ms, ee_pct, eg_ms, eg_pct = bench_workload(base, a.steps, a.warmup, rotate=rot,
                                                                    dominant=dom, graph=not a.no_graph,
                                                                    kv_cache=opt == "kvcache",
-                                                                   variants=opt == "variants")
+                                                                   variants=opt == "variants",
+                                                                   mfma=opt == "mfma")
         e_use_g = eg_ms is not None and eg_ms < ee_ms
         ems, epct = (eg_ms, eg_pct) if e_use_g else (ee_ms, ee_pct)
         epf, epb = path_work(ecfg, ecfg.T) if ecfg.q_lora else (None, None)
         ent = {"value": round(ecfg.T / (ems * 1e-3), 1), "unit": "tokens/s", "tokens": ecfg.T,
-               "dtype": "int8" if ecfg.w8a8 else "bf16", "ms_per_step": round(ems, 5),
+               "dtype": "int8" if ecfg.w8a8 else "fp8" if ecfg.mxfp8_mfma else "bf16",
+               "ms_per_step": round(ems, 5),
                "step_ms_percentiles": epct, "steps": a.steps, "rotating_sets": rot,
                "launch": "hip_graph" if e_use_g else "eager", "eager_ms_per_step": round(ee_ms, 5),
                "graph_ms_per_step": round(eg_ms, 5) if eg_ms else None,
                "roofline": roofline_for(ecfg, ecfg.T, ek_ms, ecfg.name)}
-        if ecfg.mxfp8:
+        if ecfg.mxfp8 and ecfg.mxfp8_mfma:
+            ent["mxfp8"] = ("E4M3 weights with E8M0 scales per 32 of K on the block-scaled MFMA "
+                            "(v_mfma_scale_f32_32x32x64_f8f6f4); activations converted to E4M3 codes "
+                            "(mx_convert); roofline against the dense fp8 peak")
+        elif ecfg.mxfp8:
             ent["mxfp8"] = ("E4M3 weights with E8M0 scales per 32 of K, decoded to bf16 every step "
                             "(mx_convert) with the activations' MX conversion; bf16 MFMA GEMMs")
         if opt == "variants":
@@ -348,7 +357,7 @@ def main():
             ent["kv_cache"] = {"slots": 4 * ecfg.T, "caches": "kv_norm bf16, kv codes, kv scale, k_pe",
                                "bytes_per_token": ecfg.kv_lora * 3 + 4 + ecfg.rope_dim * 2}
         if epf:
-            peak = PEAK_I8_TOPS if ecfg.w8a8 else PEAK_BF16_TFLOPS
+            peak = PEAK_I8_TOPS if ecfg.w8a8 else PEAK_FP8_TFLOPS if ecfg.mxfp8_mfma else PEAK_BF16_TFLOPS
             ent["path"] = {"tops": round(epf / (ems * 1e-3) / 1e12, 2),
                            "frac_peak": round(epf / (ems * 1e-3) / 1e12 / peak, 4)}
         extra[name] = ent

@@ -89,6 +89,15 @@ typedef enum {
  *   kv_norm) are converted block by block (shared exponent floor(log2(amax)) - 8, values
  *   rounded to E4M3, saturating at 448). Not with MLAP_W8A8. */
 #define MLAP_MXFP8 0x20u
+/* MLAP_MXFP8_MFMA (with MLAP_MXFP8): run the projections on gfx950's block-scaled MFMA
+ * (E4M3 operands with their E8M0 scales, 64 values of K per instruction) instead of decoding
+ * the weights to bf16. Faster, but the instruction's own sum of 64 products is not exact: the
+ * projections then differ from the exact sum by about 1e-4 relative (so bf16 outputs more often
+ * land one ulp away: INT8 codes measured 99.86-99.94% exact at V3 sizes, against >= 99.9% on the
+ * default route). Without this flag the
+ * MXFP8 products and sums are exact up to the fp32 accumulation. Needs hidden, q_lora and (with
+ * kv_b) kv_lora multiples of 128; otherwise the decoded path runs. */
+#define MLAP_MXFP8_MFMA 0x40u
 
 typedef struct {
     int32_t t_max;    /* largest token count a run may pass (sizes nothing on device) */
@@ -102,7 +111,7 @@ typedef struct {
     int32_t max_pos;  /* rows of the cos/sin tables */
     float eps;        /* RMSNorm epsilon (added to the mean square) */
     uint32_t flags;   /* MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
-                         MLAP_Q_HEAD_NORM | MLAP_MXFP8 */
+                         MLAP_Q_HEAD_NORM | MLAP_MXFP8 | MLAP_MXFP8_MFMA */
 } mlap_config;
 
 /*
@@ -134,7 +143,8 @@ typedef struct {
        tokens' entries. Needed (with cache_slots > 0) when any cache pointer is set. */
     const int32_t* slot_mapping; /* [T] int32 */
     int32_t cache_slots;         /* rows of every cache */
-    const uint8_t* ms_qa;        /* MLAP_MXFP8 only: E8M0 block scales [Lq, Hd/32] of w_qa */
+    const uint8_t* ms_qa;        /* MLAP_MXFP8 only: E8M0 block scales [Lq, Hd/32] of w_qa; every
+                                    ms_* pointer 4-byte aligned */
     const uint8_t* ms_qb;        /* [H*(Dn+R), Lq/32] */
     const uint8_t* ms_kva;       /* [Lkv+R, Hd/32] */
     const uint8_t* ms_kvb;       /* [H*(Dn+Dv), Lkv/32] */
@@ -210,6 +220,16 @@ MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, in
  */
 MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C, int32_t M, int32_t N,
                    int32_t K);
+
+/*
+ * Test export of the block-scaled MFMA core (MLAP_MXFP8_MFMA; the MXFP8 scaled_mm of the AT-10
+ * card, section 四, with an fp32 result): C[m, n] = sum_k deq(A[m, k]) * deq(B[n, k]) where
+ * deq(code) = E4M3 value of the byte times 2^(scale - 127), one scale byte per 32 values of K
+ * (A_scale [M, K/32], B_scale [N, K/32], both 4-byte aligned). A [M, K], B [N, K] E4M3 bytes,
+ * C [M, N] fp32, device pointers; K a multiple of 128, N of 4. Enqueued on `stream`.
+ */
+MLAP_API int mlap_gemm_mxfp8_f32(void* stream, const uint8_t* A, const uint8_t* A_scale, const uint8_t* B,
+                                 const uint8_t* B_scale, float* C, int32_t M, int32_t N, int32_t K);
 
 /*
  * Per-kernel timing (measurement support). Kernel ids: see mlap_kernel_name.

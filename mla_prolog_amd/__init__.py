@@ -28,9 +28,10 @@ MLAP_ROPE_INTERLEAVED = 0x4  # rope slices de-interleaved before rotate-half
 MLAP_QUANT_Q_PER_HEAD = 0x8  # q codes / scales per (token, head)
 MLAP_Q_HEAD_NORM = 0x10      # RMSNorm of every q head after q_b (the V4-shape prolog)
 MLAP_MXFP8 = 0x20            # E4M3 weights with E8M0 scales per 32 of K; MX-converted activations
+MLAP_MXFP8_MFMA = 0x40       # ... on the block-scaled MFMA (hardware sums, not exact)
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
-           "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_timing_begin", "mlap_timing_end",
+           "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_gemm_mxfp8_f32", "mlap_timing_begin", "mlap_timing_end",
            "mlap_kernel_name", "mlap_version")
 
 
@@ -83,6 +84,7 @@ def _load():
     lib.mlap_status_str.restype = C.c_char_p
     lib.mlap_gemm_i8_i32.argtypes = [C.c_void_p] * 4 + [C.c_int32] * 3
     lib.mlap_gemm_bf16.argtypes = [C.c_void_p] * 4 + [C.c_int32] * 3
+    lib.mlap_gemm_mxfp8_f32.argtypes = [C.c_void_p] * 6 + [C.c_int32] * 3
     lib.mlap_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
     lib.mlap_timing_end.argtypes = [C.c_void_p, C.POINTER(C.c_float), C.c_int32,
                                     C.POINTER(C.c_int32)]
@@ -143,17 +145,18 @@ class Prolog:
 
     def __init__(self, t_max, hidden, q_lora, kv_lora, rope_dim, nope_dim, v_dim, n_heads,
                  max_pos, eps=1e-6, w8a8=False, norm_rsqrt=False, rope_interleaved=False,
-                 q_quant_per_head=False, q_head_norm=False, mxfp8=False):
+                 q_quant_per_head=False, q_head_norm=False, mxfp8=False, mxfp8_mfma=False):
         self.cfg = dict(t_max=t_max, hidden=hidden, q_lora=q_lora, kv_lora=kv_lora,
                         rope_dim=rope_dim, nope_dim=nope_dim, v_dim=v_dim, n_heads=n_heads,
                         max_pos=max_pos, eps=eps, w8a8=bool(w8a8), norm_rsqrt=bool(norm_rsqrt),
                         rope_interleaved=bool(rope_interleaved),
                         q_quant_per_head=bool(q_quant_per_head), q_head_norm=bool(q_head_norm),
-                        mxfp8=bool(mxfp8))
+                        mxfp8=bool(mxfp8), mxfp8_mfma=bool(mxfp8_mfma))
         flags = ((MLAP_W8A8 if w8a8 else 0) | (MLAP_NORM_RSQRT if norm_rsqrt else 0) |
                  (MLAP_ROPE_INTERLEAVED if rope_interleaved else 0) |
                  (MLAP_QUANT_Q_PER_HEAD if q_quant_per_head else 0) |
-                 (MLAP_Q_HEAD_NORM if q_head_norm else 0) | (MLAP_MXFP8 if mxfp8 else 0))
+                 (MLAP_Q_HEAD_NORM if q_head_norm else 0) | (MLAP_MXFP8 if mxfp8 else 0) |
+                 (MLAP_MXFP8_MFMA if mxfp8_mfma else 0))
         c = _Config(int(t_max), int(hidden), int(q_lora), int(kv_lora), int(rope_dim),
                     int(nope_dim), int(v_dim), int(n_heads), int(max_pos), C.c_float(eps), flags)
         h = C.c_void_p()
@@ -168,7 +171,7 @@ class Prolog:
         return cls(t_max or cfg.T, cfg.hidden, cfg.q_lora, cfg.kv_lora, cfg.rope_dim,
                    cfg.nope_dim, cfg.v_dim, cfg.n_heads, cfg.max_pos, cfg.eps, cfg.w8a8,
                    g("norm_rsqrt"), g("rope_interleaved"), g("q_quant_per_head"), g("q_head_norm"),
-                   g("mxfp8"))
+                   g("mxfp8"), g("mxfp8_mfma"))
 
     def close(self):
         if getattr(self, "_h", None):
@@ -297,6 +300,22 @@ def gemm_bf16(A, B, out=None, stream=None):
                                C.c_void_p(_ptr(B, torch.bfloat16, "B")),
                                C.c_void_p(_ptr(out, torch.bfloat16, "C")), M, N, K),
            "mlap_gemm_bf16")
+    return out
+
+
+def gemm_mxfp8_f32(A, A_scale, B, B_scale, out=None, stream=None):
+    """sum_k deq(A) deq(B) in fp32 on the block-scaled MFMA core (test export): A [M, K], B [N, K]
+    E4M3 bytes (uint8), scales [M, K/32] / [N, K/32] E8M0 bytes."""
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    _check(_lib.mlap_gemm_mxfp8_f32(_stream(stream), C.c_void_p(_ptr(A, torch.uint8, "A")),
+                                    C.c_void_p(_ptr(A_scale, torch.uint8, "A_scale")),
+                                    C.c_void_p(_ptr(B, torch.uint8, "B")),
+                                    C.c_void_p(_ptr(B_scale, torch.uint8, "B_scale")),
+                                    C.c_void_p(_ptr(out, torch.float32, "C")), M, N, K),
+           "mlap_gemm_mxfp8_f32")
     return out
 
 

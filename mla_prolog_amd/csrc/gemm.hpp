@@ -68,6 +68,11 @@ struct GemmArgs {
     // halves. pe_c0: the projection column of this launch's column 0 (B, b_scale and out
     // are offset to it).
     int pe_period, pe_off, pe_w, pe_c0;
+    // MXFP8 operands (E4M3 bytes in A and B): E8M0 block scales, one byte per 32 values
+    // of K, rows of K/32 bytes: a_mx [M, K/32]; b_mx split like B (rows remapped like B).
+    const uint8_t* a_mx;
+    const uint8_t* b_mx0;
+    const uint8_t* b_mx1;
 };
 
 // Weight row (and per-channel scale) feeding output column n of this launch, relative to
@@ -83,8 +88,39 @@ __device__ __forceinline__ int b_row(const GemmArgs& g, int n) {
     return h * g.pe_period + g.pe_off + (d < half ? 2 * d : 2 * (d - half) + 1) - g.pe_c0;
 }
 
+// An OCP E4M3FN byte (the element type of the MXFP8 operands).
+struct fp8e4m3 {
+    uint8_t bits;
+};
+
+template <typename Tin>
+constexpr bool kIsI8 = std::is_same<Tin, int8_t>::value;
+template <typename Tin>
+constexpr bool kIsMx = std::is_same<Tin, fp8e4m3>::value;
+
 template <typename Tin>
 struct MfmaOp;
+
+// MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E4M3 (format 0). Operand
+// layout (checked on gfx950): lane l holds row l % 32, its 32 bytes being K values
+// 16 (l / 32) + [0, 16) and 32 + 16 (l / 32) + [0, 16) of the 64; the scale operand of
+// lane l is the E8M0 byte of row l % 32 and 32-value block l / 32, taken from byte OPSEL
+// of the 32-bit register. The products are exact and the hardware adds the 64 of them
+// into the fp32 accumulator.
+template <>
+struct MfmaOp<fp8e4m3> {
+    typedef f32x16 acc_t;
+    static __device__ __forceinline__ acc_t zero() {
+        acc_t z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+        return z;
+    }
+    template <int OPSEL>
+    static __device__ __forceinline__ void mma(acc_t& c, const i32x8& a, const i32x8& b, int sa, int sb) {
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
+    }
+};
 
 template <>
 struct MfmaOp<uint16_t> {  // bf16

@@ -105,6 +105,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
 
 // An empty statement that needs `v` in VGPRs (an allocation hint, no instruction).
 __device__ __forceinline__ void pin_vgpr(i32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_vgpr(i32x8& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -188,9 +189,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     // W8A8 dequantisation scales of this lane's rows and columns, fetched in one burst:
     // a_scale of each of its FM tokens, b_scale of its 4-column runs (float4 when the run
     // lies inside one weight segment and inside N).
-    float asc[sizeof(Tin) == 1 ? FM : 1];
-    float4 bsc[sizeof(Tin) == 1 ? FN : 1][4];
-    if constexpr (sizeof(Tin) == 1) {
+    float asc[kIsI8<Tin> ? FM : 1];
+    float4 bsc[kIsI8<Tin> ? FN : 1][4];
+    if constexpr (kIsI8<Tin>) {
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
             asc[i] = g.a_scale[min(mb + 32 * i, g.M - 1)];
@@ -223,7 +224,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             float v[4];
-            if constexpr (sizeof(Tin) == 1) {
+            if constexpr (kIsI8<Tin>) {
                 const float as = asc[i];
                 const float bs[4] = {bsc[j][gq].x, bsc[j][gq].y, bsc[j][gq].z, bsc[j][gq].w};
 #pragma unroll
@@ -361,7 +362,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             // once per rope slice and wave, scattered over 32 tokens per load).
             constexpr int CS_ROWS = 2 * TM;                  // rows per wave row
             constexpr int PER = CS_ROWS * 256 / 1024 / WN;   // 1 KB copies per wave
-            static_assert(WN == 2 && 4 * PER == TM && TM <= 64, "one table per wave column");
+            static_assert(WN == 2 && 4 * PER == TM, "one table per wave column");
             static_assert(BM * 512 <= big::epi_lds(BM, BN, WN), "cos/sin rows fit the epilogue LDS");
             char* const cs_lds = smem;
             if (rope_ops.on) {  // tile-uniform
@@ -508,7 +509,11 @@ template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     using SH = big::Shape<BM, BN, WM, WN, KB, S>;
     using Op = MfmaOp<Tin>;
-    constexpr int TM = SH::TM, TN = SH::TN, FM = SH::FM, FN = SH::FN, KS = SH::KS;
+    // MXFP8: a k-step is one 64-deep block-scaled MFMA, 64 bytes of every row, read as two
+    // 16-byte chunks per lane
+    constexpr bool MX = kIsMx<Tin>;
+    constexpr int RPK = MX ? 2 : 1;  // LDS reads per fragment per k-step
+    constexpr int TM = SH::TM, TN = SH::TN, FM = SH::FM, FN = SH::FN, KS = MX ? KB / 64 : SH::KS;
     constexpr int ROUNDS = SH::ROUNDS, LPR = SH::LPR;
     __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
 
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // its waves copy the tile's cos/sin rows into LDS in the epilogue if any wave needs
     // them.
     constexpr int RF = EPI == Epi::kHeads && FN > 1 ? FM : 0;
-    constexpr bool EARLY = WM * WN <= 4;
+    constexpr bool EARLY = WM * WN <= 4 && SH::FM <= 2;
     RopeOps<RF> rope_ops;
     if constexpr (RF > 0) {
         rope_ops.on = false;
@@ -590,15 +595,64 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     };
 
     // LDS read offsets of this lane's operands: row (l % 32) of each 32-row fragment,
-    // logical 16-byte chunk 2*ks + l/32.
+    // logical 16-byte chunk 2*ks + l/32 (MXFP8: chunks 4*ks + l/32 and 4*ks + 2 + l/32).
     const int lr = lane & 31, lh = lane >> 5;
-    int a_rd[KS], b_rd[KS];
+    int a_rd[KS][RPK], b_rd[KS][RPK];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int chunk = ((2 * ks + lh) ^ big::swz<KB>(lr)) * 16;
-        a_rd[ks] = (wm * TM + lr) * KB + chunk;
-        b_rd[ks] = (BM + wn * TN + lr) * KB + chunk;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int h = 0; h < RPK; ++h) {
+            const int logical = MX ? 4 * ks + 2 * h + lh : 2 * ks + lh;
+            const int chunk = (logical ^ big::swz<KB>(lr)) * 16;
+            a_rd[ks][h] = (wm * TM + lr) * KB + chunk;
+            b_rd[ks][h] = (BM + wn * TN + lr) * KB + chunk;
+        }
+
+    // MXFP8 block scales: per stage, one 32-bit word per fragment row holding the E8M0
+    // bytes of its four 32-value blocks, loaded a stage ahead into registers; shifted by
+    // 8 (l / 32) so that byte 2*ks is this lane's block of k-step ks.
+    const uint8_t* a_sp[MX ? FM : 1];
+    const uint8_t* b_sp[MX ? FN : 1];
+    uint32_t sx[MX ? FM : 1], sw[MX ? FN : 1], sx_n[MX ? FM : 1], sw_n[MX ? FN : 1];
+    if constexpr (MX) {
+        const size_t srow = static_cast<size_t>(g.K / 32);
+        const size_t kblk = k0 / 32;
+        static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            const int m = min(m0 + wm * TM + 32 * i + lr, g.M - 1);
+            a_sp[i] = g.a_mx + static_cast<size_t>(m) * srow + kblk;
+        });
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            const int n = b_row(g, min(n0 + wn * TN + 32 * j + lr, g.N - 1));
+            b_sp[j] = n < g.b_split ? g.b_mx0 + static_cast<ptrdiff_t>(n) * static_cast<ptrdiff_t>(srow) + kblk
+                                    : g.b_mx1 + static_cast<ptrdiff_t>(n - g.b_split) * static_cast<ptrdiff_t>(srow) + kblk;
+        });
     }
+    auto load_scales = [&](int kt) __attribute__((always_inline)) {
+        if constexpr (MX) {
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                sx_n[i] = *reinterpret_cast<const uint32_t*>(a_sp[i] + 4 * kt);
+            });
+            static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                sw_n[j] = *reinterpret_cast<const uint32_t*>(b_sp[j] + 4 * kt);
+            });
+        }
+    };
+    auto take_scales = [&]() __attribute__((always_inline)) {
+        if constexpr (MX) {
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                sx[i] = sx_n[i] >> (8 * lh);
+            });
+            static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+                constexpr int j = decltype(j_c)::value;
+                sw[j] = sw_n[j] >> (8 * lh);
+            });
+        }
+    };
 
     typename Op::acc_t acc[FN][FM];
     static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
@@ -608,18 +662,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     });
 
     // One k-step's operands: FN weight and FM activation fragments.
+    using FragT = typename std::conditional<MX, i32x8, i32x4>::type;
     struct Frags {
-        i32x4 w[FN], x[FM];
+        FragT w[FN], x[FM];
+    };
+    auto frag_at = [&](const char* p, const int (&rd)[RPK]) __attribute__((always_inline)) {
+        if constexpr (MX) {
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(p + rd[0]);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(p + rd[1]);
+            return FragT{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        } else {
+            return *reinterpret_cast<const i32x4*>(p + rd[0]);
+        }
     };
     auto read = [&](const char* base, auto ks_c, Frags& f) __attribute__((always_inline)) {
         constexpr int ks = decltype(ks_c)::value;
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
             constexpr int j = decltype(j_c)::value;
-            f.w[j] = *reinterpret_cast<const i32x4*>(base + b_rd[ks] + j * 32 * KB);
+            f.w[j] = frag_at(base + j * 32 * KB, b_rd[ks]);
         });
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
-            f.x[i] = *reinterpret_cast<const i32x4*>(base + a_rd[ks] + i * 32 * KB);
+            f.x[i] = frag_at(base + i * 32 * KB, a_rd[ks]);
         });
     };
     // Pin a k-step's operand fragments to VGPRs: left to itself the register allocator
@@ -634,26 +698,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             big::pin_vgpr(f.x[decltype(i_c)::value]);
         });
     };
-    // MFMAs of weight fragments [J0, J1) against every activation fragment.
-    auto multiply = [&](Frags& f, auto j0_c, auto j1_c) __attribute__((always_inline)) {
+    // MFMAs of weight fragments [J0, J1) against every activation fragment (k-step ks).
+    auto multiply = [&](Frags& f, auto ks_c, auto j0_c, auto j1_c) __attribute__((always_inline)) {
         constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
         static_for<J1 - J0>([&](auto j_c) __attribute__((always_inline)) {
             constexpr int j = J0 + decltype(j_c)::value;
             static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                 constexpr int i = decltype(i_c)::value;
-                Op::mma(acc[j][i], f.w[j], f.x[i]);
+                if constexpr (MX)
+                    Op::template mma<2 * decltype(ks_c)::value>(acc[j][i], f.w[j], f.x[i],
+                                                                static_cast<int>(sw[j]), static_cast<int>(sx[i]));
+                else
+                    Op::mma(acc[j][i], f.w[j], f.x[i]);
             });
         });
     };
     // Scheduling template for the region just emitted: N MFMAs, after the i-th of which
-    // go one LDS read while i < NR, else one global->LDS copy while i - NR < NC.
+    // go the LDS reads of one fragment while i < NR, else one global->LDS copy while
+    // i - NR < NC.
     auto interleave = [&](auto n_c, auto nr_c, auto nc_c) __attribute__((always_inline)) {
         constexpr int N = decltype(n_c)::value, NR = decltype(nr_c)::value, NC = decltype(nc_c)::value;
         static_for<N>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             if constexpr (i < NR)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);  // DS read(s)
             else if constexpr (i - NR < NC)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
         });
@@ -669,6 +738,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // in the next stage reuses; the next stage's first reads then run under the second
     // half. With two slots the whole copy goes out at the head of the stage, so it has
     // the most time to land; with more it is spread over the k-steps.
+    // (the first stage's scales go out ahead of the copies, so the waits below cover them)
+    if (nk > 0) load_scales(0);
     static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
         if (s < nk) issue(s, s);
@@ -679,6 +750,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     if (nk > 0) {
         if (nk >= S - 1) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
         big::lds_barrier();
+        take_scales();
         read(smem, std::integral_constant<int, 0>{}, f[0]);
     }
     int slot = 0;  // kt % S
@@ -687,6 +759,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         const int cslot = slot == 0 ? S - 1 : slot - 1;
         const int nslot = slot + 1 == S ? 0 : slot + 1;
         const char* base = smem + slot * SH::STAGE;
+        // the next stage's scales, ahead of this stage's copies (the stage-end wait covers them)
+        if (kt + 1 < nk) load_scales(kt + 1);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
             constexpr int r0 = ks < SPREAD ? ROUNDS * ks / SPREAD : ROUNDS;
@@ -701,11 +775,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             if constexpr (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
             if constexpr (ks + 1 < KS) {
                 read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
-                multiply(f[ks & 1], I0{}, IF{});
+                multiply(f[ks & 1], ks_c, I0{}, IF{});
                 interleave(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{},
                            std::integral_constant<int, NC>{});
             } else {
-                multiply(f[ks & 1], I0{}, IH{});
+                multiply(f[ks & 1], ks_c, I0{}, IH{});
                 interleave(std::integral_constant<int, FN / 2 * FM>{},
                            std::integral_constant<int, 0>{}, std::integral_constant<int, NC>{});
                 const bool more = kt + 1 < nk;
@@ -715,11 +789,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (more) read(smem + nslot * SH::STAGE, I0{}, f[(ks + 1) & 1]);
-                multiply(f[ks & 1], IH{}, IF{});
+                multiply(f[ks & 1], ks_c, IH{}, IF{});
                 interleave(std::integral_constant<int, (FN - FN / 2) * FM>{}, std::integral_constant<int, NR>{},
                            std::integral_constant<int, 0>{});
             }
         });
+        take_scales();  // the next stage's (its loads were covered by the stage-end wait)
         slot = nslot;
     };
     int kt = 0;

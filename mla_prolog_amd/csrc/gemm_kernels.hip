@@ -81,7 +81,7 @@ int big_tile_n(BigShape shape) {
 }
 
 bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
-    const int kbytes = g.K * (t == InType::kInt8 ? 1 : 2);
+    const int kbytes = g.K * (t == InType::kBf16 ? 2 : 1);
     const int splits = g.k_splits > 0 ? g.k_splits : 1;
     if (g.K <= 0 || kbytes % (128 * splits)) return false;  // whole 128-byte stages per split
     if (splits > 1 && epi != Epi::kStoreF32) return false;
@@ -96,13 +96,13 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
         case BigShape::kHalfHead:
             // 96-column tiles, two per head: [0, 96) all seg0, [96, 192) the rest of seg0
             // (32 columns) and the 64-wide rope slice, rotated in registers
-            return t == InType::kBf16 && epi == Epi::kHeads && g.head_w == 192 && g.rope &&
+            return t != InType::kInt8 && epi == Epi::kHeads && g.head_w == 192 && g.rope &&
                    g.d0 == 128 && g.d1 == 64;
         case BigShape::kSplitK:
-            return t == InType::kBf16 && epi == Epi::kStoreF32 && g.N % 4 == 0 && g.ldo % 4 == 0;
+            return t != InType::kInt8 && epi == Epi::kStoreF32 && g.N % 4 == 0 && g.ldo % 4 == 0;
         case BigShape::kNarrowHeads:
             // 32-column tiles that never straddle a segment; no rotate-half pairs
-            return t == InType::kBf16 && epi == Epi::kHeads && !g.rope && g.head_w % 32 == 0 &&
+            return t != InType::kInt8 && epi == Epi::kHeads && !g.rope && g.head_w % 32 == 0 &&
                    g.d0 % 32 == 0 && g.d1 % 8 == 0;
     }
     return false;
@@ -122,27 +122,49 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
         GemmArgs r = g;
         r.N = g.N - nm;
         r.pe_c0 = g.pe_c0 + nm;
-        const size_t eb = t == InType::kInt8 ? 1 : 2;
+        const size_t eb = t == InType::kBf16 ? 2 : 1;
+        const size_t mxrow = static_cast<size_t>(g.K / 32);  // E8M0 bytes per B row (MXFP8)
         if (nm >= g.b_split) {  // the remainder rows all come from the second segment
             r.B0 = r.B1 = static_cast<const char*>(g.B1) + static_cast<size_t>(nm - g.b_split) * g.ldb * eb;
             r.b_scale0 = r.b_scale1 = g.b_scale1 ? g.b_scale1 + (nm - g.b_split) : nullptr;
+            r.b_mx0 = r.b_mx1 = g.b_mx1 ? g.b_mx1 + static_cast<size_t>(nm - g.b_split) * mxrow : nullptr;
             r.b_split = r.N;
         } else {
             r.B0 = static_cast<const char*>(g.B0) + static_cast<size_t>(nm) * g.ldb * eb;
             r.b_scale0 = g.b_scale0 ? g.b_scale0 + nm : nullptr;
+            r.b_mx0 = g.b_mx0 ? g.b_mx0 + static_cast<size_t>(nm) * mxrow : nullptr;
             r.b_split = g.b_split - nm;
         }
         r.out = static_cast<uint16_t*>(g.out) + nm;
         // 64 x 64 tiles: one per 64 tokens, so the narrow remainder still spreads over the CUs
-        if ((static_cast<size_t>(r.K) * eb) % 128 == 0)
+        if ((static_cast<size_t>(r.K) * eb) % 128 == 0) {
+            if (t == InType::kFp8) return launch_big_one<fp8e4m3, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s);
             return t == InType::kInt8 ? launch_big_one<int8_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s)
                                       : launch_big_one<uint16_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s);
+        }
         return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
     }
     if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
     // Weight-streaming shapes cover the whole batch in one row tile; at most 64 tokens take
     // 64-row tiles (two waves), so no copy bandwidth goes to clamped duplicate rows.
     const bool m64 = g.M <= 64;
+    if (t == InType::kFp8) {  // MXFP8: the same shapes on E4M3 operands
+        switch (shape) {
+            case BigShape::kWide:
+                return epi == Epi::kStoreBf16 ? launch_big_one<fp8e4m3, 256, 256, 2, 2, 2, Epi::kStoreBf16>(g, s)
+                                              : launch_big_one<fp8e4m3, 256, 256, 2, 2, 2, Epi::kHeads>(g, s);
+            case BigShape::kHalfHead:
+                return m64 ? launch_big_one<fp8e4m3, 64, 96, 2, 1, 3, Epi::kHeads>(g, s)
+                           : launch_big_one<fp8e4m3, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
+            case BigShape::kSplitK:
+                return m64 ? launch_big_one<fp8e4m3, 64, 64, 2, 1, 3, Epi::kStoreF32>(g, s)
+                           : launch_big_one<fp8e4m3, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
+            case BigShape::kNarrowHeads:
+                return m64 ? launch_big_one<fp8e4m3, 64, 32, 2, 1, 3, Epi::kHeads>(g, s)
+                           : launch_big_one<fp8e4m3, 256, 32, 4, 1, 3, Epi::kHeads>(g, s);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (shape) {
         case BigShape::kWide:
             if (t == InType::kBf16)
@@ -165,6 +187,7 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
 
 hipError_t launch_gemm(const GemmArgs& g, InType type, const GemmTile& t, Epi epi, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (type == InType::kFp8) return hipErrorInvalidValue;  // MXFP8 runs on the LDS-DMA kernel only
     return type == InType::kBf16 ? dispatch<uint16_t>(g, t, epi, s) : dispatch<int8_t>(g, t, epi, s);
 }
 

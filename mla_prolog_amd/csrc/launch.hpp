@@ -8,7 +8,7 @@
 
 namespace mlap {
 
-enum class InType : int { kBf16 = 0, kInt8 = 1 };
+enum class InType : int { kBf16 = 0, kInt8 = 1, kFp8 = 2 };  // kFp8: MXFP8 (E4M3 + E8M0 block scales)
 
 // Output tile rows x columns and K-tiles of register prefetch.
 struct GemmTile {
@@ -127,5 +127,8 @@ hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s);
 hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int N, int K, uint16_t* out,
                              hipStream_t s);
 hipError_t launch_mx_act(const uint16_t* x, int T, int K, uint16_t* out, hipStream_t s);
+// The same conversion, written as E4M3 codes [T, K] and E8M0 block scales [T, K/32] (the
+// operands of the block-scaled MFMA).
+hipError_t launch_mx_act_codes(const uint16_t* x, int T, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 }  // namespace mlap

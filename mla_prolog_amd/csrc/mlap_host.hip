@@ -86,6 +86,9 @@ struct Plan {
     int tail_c0 = 0, tail_splits = 0;
     BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide, kv_shape = BigShape::kWide;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
+    // MXFP8 on the block-scaled MFMA (E4M3 operands in the GEMMs); else, with MXFP8, the
+    // weights are decoded to bf16 for the bf16 GEMMs
+    bool mx_native = false;
 };
 
 struct Timer {
@@ -108,6 +111,7 @@ struct mlap_prolog {
     mlap_config cfg;
     bool w8a8;
     bool mx;      // MXFP8 projections
+    bool mx_mfma;  // ... on the block-scaled MFMA where the shapes allow
     int N1;       // down-projection width
     int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
     int bn_q, bn_kv;
@@ -121,12 +125,26 @@ struct mlap_prolog {
 
     bool head_norm() const { return (cfg.flags & MLAP_Q_HEAD_NORM) && cfg.q_lora > 0; }
 
+    // MXFP8 runs on the block-scaled MFMA when asked for and every projection fits the LDS-DMA
+    // kernel (whole 128-value K stages), else through the decoded bf16 weights.
     Plan plan(int T) const {
+        if (mx && mx_mfma) {
+            Plan p = plan_for(T, InType::kFp8);
+            if (p.big_down && (cfg.q_lora == 0 || p.big_q) && (cfg.v_dim == 0 || p.big_kv)) {
+                p.mx_native = true;
+                return p;
+            }
+        }
+        return plan_for(T, w8a8 ? InType::kInt8 : InType::kBf16);
+    }
+
+    Plan plan_for(int T, InType it) const {
         Plan p{};
         const bool small = T <= kSmallBatch;
-        const int kb = w8a8 ? 128 : 64;  // elements per 128-byte K-tile
+        const bool i8 = it == InType::kInt8;
+        const int kb = it == InType::kBf16 ? 64 : 128;  // elements per 128-byte K-tile
         const int nk = cfg.hidden / kb;
-        if (!w8a8 && small) {
+        if (!i8 && small) {
             p.down = {256, 64, 3};
             p.down_epi = Epi::kStoreF32;
             p.down_splits = one_round_splits(((T + 255) / 256) * ((N1 + 63) / 64), nk);
@@ -137,7 +155,6 @@ struct mlap_prolog {
         }
         p.up_q = {small ? 128 : 256, bn_q, small ? 3 : 1};
         p.up_kv = {small ? 128 : 256, bn_kv, small ? 3 : 1};
-        const InType it = w8a8 ? InType::kInt8 : InType::kBf16;
         if (!small) {
             // MFMA-bound: the large-batch kernel wherever the shapes suit it
             GemmArgs d{};
@@ -149,7 +166,7 @@ struct mlap_prolog {
                 p.down_epi = Epi::kStoreBf16;
                 p.down_splits = 1;
                 const int c0 = N1 / kBigTile * kBigTile;
-                if (!w8a8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
+                if (!i8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
                     p.tail_c0 = c0;
                     p.tail_splits = one_round_splits((T + 255) / 256 * ((N1 - c0) / 64), nk);
                 }
@@ -172,7 +189,7 @@ struct mlap_prolog {
                 u.rope = 0;
                 p.big_kv = gemm_big_fits(u, it, Epi::kHeads);
             }
-        } else if (!w8a8) {
+        } else if (!i8) {
             // weight streaming: the LDS-DMA kernel with split-K fp32 partials for the down
             // projection and half-head tiles spanning the whole batch for the q up projection
             GemmArgs d{};
@@ -247,7 +264,18 @@ struct mlap_prolog {
                 L.kvs = take(t * 4);
             }
         }
-        if (mx) {  // decoded weights and converted activations for the bf16 GEMMs
+        if (mx && p.mx_native) {  // E4M3 codes and E8M0 block scales of the GEMM inputs
+            L.xq = take(t * cfg.hidden);
+            L.xs = take(t * (cfg.hidden / 32));
+            if (cfg.q_lora > 0) {
+                L.qnq = take(t * cfg.q_lora);
+                L.qns = take(t * (cfg.q_lora / 32));
+            }
+            if (cfg.v_dim > 0) {
+                L.kvq = take(t * cfg.kv_lora);
+                L.kvs = take(t * (cfg.kv_lora / 32));
+            }
+        } else if (mx) {  // decoded weights and converted activations for the bf16 GEMMs
             L.wd_down = take(static_cast<size_t>(N1) * cfg.hidden * 2);
             L.xm = take(t * cfg.hidden * 2);
             if (cfg.q_lora > 0) {
@@ -276,8 +304,9 @@ namespace {
 int validate(const mlap_config* c) {
     const bool w8 = (c->flags & MLAP_W8A8) != 0;
     if (c->flags & ~(MLAP_W8A8 | MLAP_NORM_RSQRT | MLAP_ROPE_INTERLEAVED | MLAP_QUANT_Q_PER_HEAD |
-                     MLAP_Q_HEAD_NORM | MLAP_MXFP8))
+                     MLAP_Q_HEAD_NORM | MLAP_MXFP8 | MLAP_MXFP8_MFMA))
         return MLAP_ERR_INVALID_ARG;
+    if ((c->flags & MLAP_MXFP8_MFMA) && !(c->flags & MLAP_MXFP8)) return MLAP_ERR_INVALID_ARG;
     if ((c->flags & MLAP_W8A8) && (c->flags & MLAP_MXFP8)) return MLAP_ERR_INVALID_ARG;
     const bool head_norm = (c->flags & MLAP_Q_HEAD_NORM) && c->q_lora > 0;
     if (c->t_max < 1 || c->hidden < 1 || c->kv_lora < 1 || c->rope_dim < 1 || c->n_heads < 1 ||
@@ -341,6 +370,7 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
     h->cfg = *cfg;
     h->w8a8 = (cfg->flags & MLAP_W8A8) != 0;
     h->mx = (cfg->flags & MLAP_MXFP8) != 0;
+    h->mx_mfma = (cfg->flags & MLAP_MXFP8_MFMA) != 0;
     h->N1 = cfg->q_lora + cfg->kv_lora + cfg->rope_dim;
     h->QH = cfg->nope_dim + cfg->rope_dim;
     h->KH = cfg->nope_dim + cfg->v_dim;
@@ -419,6 +449,9 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     const bool mx = h->mx;
     if (mx && (!in->ms_kva || (has_q && (!in->ms_qa || !in->ms_qb)) || (has_kvb && !in->ms_kvb)))
         return MLAP_ERR_INVALID_ARG;
+    if (mx && ((reinterpret_cast<uintptr_t>(in->ms_qa) | reinterpret_cast<uintptr_t>(in->ms_qb) |
+                reinterpret_cast<uintptr_t>(in->ms_kva) | reinterpret_cast<uintptr_t>(in->ms_kvb)) & 3))
+        return MLAP_ERR_INVALID_ARG;  // the GEMMs read four block scales per 32-bit load
     if (w8 && (!in->ws_kva || (has_q && (!in->ws_qa || !in->ws_qb)) || (has_kvb && !in->ws_kvb)))
         return MLAP_ERR_INVALID_ARG;
     // outputs that need a branch this configuration lacks
@@ -458,10 +491,19 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         if (e != hipSuccess) return MLAP_ERR_HIP; \
     } while (0)
 
-    // 0. MXFP8: weights decoded to bf16 and x converted block by block, for the bf16 GEMMs
-    uint16_t* wd_down = mx ? reinterpret_cast<uint16_t*>(wsb + L.wd_down) : nullptr;
-    uint16_t* xm = mx ? reinterpret_cast<uint16_t*>(wsb + L.xm) : nullptr;
-    if (mx) {
+    const Plan plan = h->plan(T);
+    // 0. MXFP8: x converted block by block to E4M3 codes and E8M0 scales for the block-scaled
+    // MFMA, or (shapes it does not take) the weights decoded to bf16 and x converted to its
+    // exactly representable bf16 values, for the bf16 GEMMs
+    const bool mxn = plan.mx_native;
+    const bool mxd = mx && !mxn;
+    uint16_t* wd_down = mxd ? reinterpret_cast<uint16_t*>(wsb + L.wd_down) : nullptr;
+    uint16_t* xm = mxd ? reinterpret_cast<uint16_t*>(wsb + L.xm) : nullptr;
+    if (mxn)
+        MLAP_LAUNCH(kKMxConvert, launch_mx_act_codes(static_cast<const uint16_t*>(in->x), T, c.hidden,
+                                                     reinterpret_cast<uint8_t*>(wsb + L.xq),
+                                                     reinterpret_cast<uint8_t*>(wsb + L.xs), s));
+    if (mxd) {
         if (has_q)
             MLAP_LAUNCH(kKMxConvert, launch_mx_dequant(static_cast<const uint8_t*>(in->w_qa), in->ms_qa, Lq,
                                                       c.hidden, wd_down, s));
@@ -483,15 +525,14 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     g.K = c.hidden;
     g.lda = c.hidden;
     g.ldb = c.hidden;
-    g.B0 = mx ? static_cast<const void*>(wd_down) : (has_q ? in->w_qa : in->w_kva);
-    g.B1 = mx ? static_cast<const void*>(wd_down + static_cast<size_t>(Lq) * c.hidden) : in->w_kva;
+    g.B0 = mxd ? static_cast<const void*>(wd_down) : (has_q ? in->w_qa : in->w_kva);
+    g.B1 = mxd ? static_cast<const void*>(wd_down + static_cast<size_t>(Lq) * c.hidden) : in->w_kva;
     g.b_split = Lq;
     if (c.flags & MLAP_ROPE_INTERLEAVED) {  // the k_pe slice of [q_a | c_kv | k_pe]
         g.pe_period = h->N1;
         g.pe_off = Lq + Lkv;
         g.pe_w = R;
     }
-    const Plan plan = h->plan(T);
     g.k_splits = plan.down_splits;
     g.group_m = kGroupM;
     g.out = a1;
@@ -509,30 +550,49 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                                     ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
                                     : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
     } else if (plan.tail_splits) {
-        g.A = mx ? static_cast<const void*>(xm) : in->x;
+        const InType it = mxn ? InType::kFp8 : InType::kBf16;
+        const size_t eb = mxn ? 1 : 2;                                   // bytes per weight
+        const size_t mxrow = static_cast<size_t>(c.hidden / 32);         // E8M0 bytes per row
+        if (mxn) {
+            g.A = wsb + L.xq;
+            g.a_mx = reinterpret_cast<const uint8_t*>(wsb + L.xs);
+            g.b_mx0 = has_q ? in->ms_qa : in->ms_kva;
+            g.b_mx1 = in->ms_kva;
+        } else {
+            g.A = mxd ? static_cast<const void*>(xm) : in->x;
+        }
         GemmArgs r = g;  // columns [tail_c0, N1): split-K fp32 partials
         r.N = h->N1 - plan.tail_c0;
         r.pe_c0 = plan.tail_c0;
         r.k_splits = plan.tail_splits;
         if (plan.tail_c0 >= g.b_split) {
-            r.B0 = r.B1 = static_cast<const char*>(g.B1) +
-                          static_cast<size_t>(plan.tail_c0 - g.b_split) * g.ldb * 2;
+            const size_t rows = static_cast<size_t>(plan.tail_c0 - g.b_split);
+            r.B0 = r.B1 = static_cast<const char*>(g.B1) + rows * g.ldb * eb;
+            if (mxn) r.b_mx0 = r.b_mx1 = g.b_mx1 + rows * mxrow;
             r.b_split = r.N;
         } else {
-            r.B0 = static_cast<const char*>(g.B0) + static_cast<size_t>(plan.tail_c0) * g.ldb * 2;
+            const size_t rows = static_cast<size_t>(plan.tail_c0);
+            r.B0 = static_cast<const char*>(g.B0) + rows * g.ldb * eb;
+            if (mxn) r.b_mx0 = g.b_mx0 + rows * mxrow;
             r.b_split = g.b_split - plan.tail_c0;
         }
         r.out = wsb + L.tail;
         r.ldo = r.N;
         g.N = plan.tail_c0;
-        MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, InType::kBf16, Epi::kStoreBf16, s) != hipSuccess
+        MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, it, Epi::kStoreBf16, s) != hipSuccess
                                     ? hipErrorInvalidValue
-                                    : gemm_big_fits(r, InType::kBf16, Epi::kStoreF32, BigShape::kSplitK)
-                                          ? launch_gemm_big(r, InType::kBf16, Epi::kStoreF32, s, BigShape::kSplitK)
-                                          : launch_gemm(r, InType::kBf16, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
+                                    : gemm_big_fits(r, it, Epi::kStoreF32, BigShape::kSplitK)
+                                          ? launch_gemm_big(r, it, Epi::kStoreF32, s, BigShape::kSplitK)
+                                          : launch_gemm(r, it, GemmTile{256, 64, 3}, Epi::kStoreF32, s));
         g.N = h->N1;
+    } else if (mxn) {
+        g.A = wsb + L.xq;
+        g.a_mx = reinterpret_cast<const uint8_t*>(wsb + L.xs);
+        g.b_mx0 = has_q ? in->ms_qa : in->ms_kva;
+        g.b_mx1 = in->ms_kva;
+        MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, InType::kFp8, plan.down_epi, s, plan.down_shape));
     } else {
-        g.A = mx ? static_cast<const void*>(xm) : in->x;
+        g.A = mxd ? static_cast<const void*>(xm) : in->x;
         MLAP_LAUNCH(kKGemmDown, plan.big_down
                                     ? launch_gemm_big(g, InType::kBf16, plan.down_epi, s, plan.down_shape)
                                     : launch_gemm(g, InType::kBf16, plan.down, plan.down_epi, s));
@@ -599,7 +659,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.K = Lq;
         u.lda = Lq;
         u.ldb = Lq;
-        u.B0 = u.B1 = mx ? static_cast<const void*>(wsb + L.wd_qb) : in->w_qb;
+        u.B0 = u.B1 = mxd ? static_cast<const void*>(wsb + L.wd_qb) : in->w_qb;
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
@@ -624,11 +684,17 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         // per-token q quant: the epilogue's per-tile partial amax (per-head quant reads the rows)
         u.part_amax = quant_q && !per_head && !head_norm ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
         u.n_tiles = plan.nt_q;
-        const InType it = w8 ? InType::kInt8 : InType::kBf16;
+        const InType it = w8 ? InType::kInt8 : mxn ? InType::kFp8 : InType::kBf16;
         if (w8) {
             u.A = na.qn_i8;
             u.a_scale = na.qn_scale;
             u.b_scale0 = u.b_scale1 = in->ws_qb;
+        } else if (mxn) {  // q_norm as E4M3 codes with E8M0 block scales
+            MLAP_LAUNCH(kKMxConvert, launch_mx_act_codes(qn, T, Lq, reinterpret_cast<uint8_t*>(wsb + L.qnq),
+                                                         reinterpret_cast<uint8_t*>(wsb + L.qns), s));
+            u.A = wsb + L.qnq;
+            u.a_mx = reinterpret_cast<const uint8_t*>(wsb + L.qns);
+            u.b_mx0 = u.b_mx1 = in->ms_qb;
         } else if (mx) {  // the MX conversion of q_norm
             uint16_t* qnm = reinterpret_cast<uint16_t*>(wsb + L.qnm);
             MLAP_LAUNCH(kKMxConvert, launch_mx_act(qn, T, Lq, qnm, s));
@@ -715,7 +781,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.K = Lkv;
         u.lda = Lkv;
         u.ldb = Lkv;
-        u.B0 = u.B1 = mx ? static_cast<const void*>(wsb + L.wd_kvb) : in->w_kvb;
+        u.B0 = u.B1 = mxd ? static_cast<const void*>(wsb + L.wd_kvb) : in->w_kvb;
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
@@ -726,11 +792,17 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         u.n_heads = H;
         u.out0 = out->k_nope;
         u.out1 = out->value;
-        const InType it = w8 ? InType::kInt8 : InType::kBf16;
+        const InType it = w8 ? InType::kInt8 : mxn ? InType::kFp8 : InType::kBf16;
         if (w8) {
             u.A = na.kv_i8_b;
             u.a_scale = na.kv_scale_b;
             u.b_scale0 = u.b_scale1 = in->ws_kvb;
+        } else if (mxn) {  // kv_norm as E4M3 codes with E8M0 block scales
+            MLAP_LAUNCH(kKMxConvert, launch_mx_act_codes(kvn, T, Lkv, reinterpret_cast<uint8_t*>(wsb + L.kvq),
+                                                         reinterpret_cast<uint8_t*>(wsb + L.kvs), s));
+            u.A = wsb + L.kvq;
+            u.a_mx = reinterpret_cast<const uint8_t*>(wsb + L.kvs);
+            u.b_mx0 = u.b_mx1 = in->ms_kvb;
         } else if (mx) {  // the MX conversion of kv_norm
             uint16_t* kvnm = reinterpret_cast<uint16_t*>(wsb + L.kvnm);
             MLAP_LAUNCH(kKMxConvert, launch_mx_act(kvn, T, Lkv, kvnm, s));
@@ -806,6 +878,33 @@ MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C,
     g.out = C;
     g.ldo = N;
     return launch_gemm(g, InType::kBf16, GemmTile{128, 128, 1}, Epi::kStoreBf16, as_stream(stream)) == hipSuccess
+               ? MLAP_OK
+               : MLAP_ERR_HIP;
+}
+
+MLAP_API int mlap_gemm_mxfp8_f32(void* stream, const uint8_t* A, const uint8_t* A_scale, const uint8_t* B,
+                                 const uint8_t* B_scale, float* C, int32_t M, int32_t N, int32_t K) {
+    if (M < 0 || N < 0 || K <= 0) return MLAP_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MLAP_OK;
+    if (!A || !A_scale || !B || !B_scale || !C) return MLAP_ERR_INVALID_ARG;
+    if (K % 128 || N % 4) return MLAP_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(A_scale) | reinterpret_cast<uintptr_t>(B_scale)) & 3) return MLAP_ERR_INVALID_ARG;
+    GemmArgs g{};
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.lda = K;
+    g.B0 = g.B1 = B;
+    g.b_split = N;
+    g.ldb = K;
+    g.k_splits = 1;
+    g.group_m = kGroupM;
+    g.out = C;
+    g.ldo = N;
+    g.a_mx = A_scale;
+    g.b_mx0 = g.b_mx1 = B_scale;
+    return launch_gemm_big(g, InType::kFp8, Epi::kStoreF32, as_stream(stream), BigShape::kSplitK) == hipSuccess
                ? MLAP_OK
                : MLAP_ERR_HIP;
 }

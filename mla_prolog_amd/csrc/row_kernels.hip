@@ -1019,6 +1019,65 @@ __global__ __launch_bounds__(256) void mx_act_kernel(const uint16_t* x, size_t n
     }
 }
 
+// E4M3FN byte of a value already on the E4M3 grid (|v| <= 448, as e4m3_round returns).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a < 0x1p-6f) {
+        c = static_cast<uint32_t>(a * 512.0f);  // subnormal: m * 2^-9 (0 for zero)
+    } else {
+        const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;
+        const uint32_t m = (__float_as_uint(a) >> 20) & 7;  // the three mantissa bits
+        c = (static_cast<uint32_t>(e + 7) << 3) | m;
+    }
+    return c | (v < 0.f ? 0x80u : 0u);
+}
+
+// Activations to MXFP8 operands: the conversion of mx_act_kernel, written as E4M3 codes and
+// one E8M0 byte per 32-value block; one block per thread.
+__global__ __launch_bounds__(256) void mx_act_codes_kernel(const uint16_t* x, size_t nblocks, uint8_t* codes,
+                                                           uint8_t* scales) {
+    for (size_t b = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; b < nblocks;
+         b += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+        float f[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) unpack8(src[j], f + 8 * j);
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        int sh = -127;
+        if (amax > 0.f) {
+            const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // floor(log2)
+            sh = min(127, max(-127, e - 8));
+        }
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float y = amax > 0.f ? e4m3_round(ldexpf(f[4 * j + q], -sh)) : 0.f;
+                v |= e4m3_code(y) << (8 * q);
+            }
+            w[j] = v;
+        }
+        uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        scales[b] = static_cast<uint8_t>(sh + 127);
+    }
+}
+
+hipError_t launch_mx_act_codes(const uint16_t* x, int T, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (K % 32) return hipErrorInvalidValue;
+    const size_t nb = static_cast<size_t>(T) * K / 32;
+    const int grid = static_cast<int>(std::min<size_t>((nb + 255) / 256, 8192));
+    hipLaunchKernelGGL(mx_act_codes_kernel, dim3(grid), dim3(256), 0, s, x, nb, codes, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, int N, int K, uint16_t* out,
                              hipStream_t s) {
     if (N <= 0 || K <= 0) return hipSuccess;

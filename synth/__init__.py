@@ -68,6 +68,7 @@ class Config:
     q_quant_per_head: bool = False  # q codes / scales per (token, head)
     q_head_norm: bool = False       # RMSNorm of every q head after q_b (the V4-shape prolog)
     mxfp8: bool = False             # MXFP8 weights (E4M3 codes + E8M0 block scales)
+    mxfp8_mfma: bool = False        # run MXFP8 on the GPU's block-scaled MFMA (same method)
 
     def asdict(self):
         return asdict(self)
@@ -122,7 +123,7 @@ CONFIGS = {
 
 def get_config(name: str, T: int | None = None, **variants) -> Config:
     """A named configuration, optionally with another token count and variant flags
-    (norm_rsqrt, rope_interleaved, q_quant_per_head, q_head_norm, mxfp8)."""
+    (norm_rsqrt, rope_interleaved, q_quant_per_head, q_head_norm, mxfp8, mxfp8_mfma)."""
     cfg = CONFIGS[name]
     if T is not None:
         cfg = replace(cfg, T=int(T))

@@ -43,6 +43,13 @@ import synth
 
 RTOL, ATOL = 1e-2, 1e-3
 SCALE_RTOL = 1e-3
+CODE_EXACT = 0.999
+# MXFP8 on the block-scaled MFMA: the instruction's sum of 64 products is not exact (about 1e-4
+# relative, see test_gemm_mxfp8_core), so ~2% of the normalised bf16 rows land one ulp from the
+# exact result, and a code moves when such an ulp crosses a rounding boundary of z*127/amax
+# (probability |code| 2^-8 <= 1/2, about 0.1 on average): ~0.2% of codes, 99.86-99.94% exact
+# measured at V3 sizes.
+CODE_EXACT_MFMA = 0.997
 
 
 def bits(t):
@@ -103,7 +110,8 @@ def check_self_consistent_quant(name, vals_bf16, codes, scales):
                                   err_msg=name + " scales")
 
 
-def check_quant_vs_oracle(name, g_rows_bits, g_codes, g_scales, o_rows_bits, o_codes, o_scales):
+def check_quant_vs_oracle(name, g_rows_bits, g_codes, g_scales, o_rows_bits, o_codes, o_scales,
+                          min_exact=CODE_EXACT):
     g_rows = np.asarray(g_rows_bits).reshape(len(g_scales), -1)
     o_rows = np.asarray(o_rows_bits).reshape(len(o_scales), -1)
     ga = np.abs(oracle.f32(g_rows)).max(1)
@@ -127,7 +135,7 @@ def check_quant_vs_oracle(name, g_rows_bits, g_codes, g_scales, o_rows_bits, o_c
     if d.size:
         assert d.max() <= 1, "%s: code off by %d" % (name, int(d.max()))
         exact = float((d == 0).mean())
-        assert exact >= 0.999, "%s: only %.5f of codes exact" % (name, exact)
+        assert exact >= min_exact, "%s: only %.5f of codes exact" % (name, exact)
     return excused
 
 
@@ -176,6 +184,7 @@ def check_prolog(cfg, inp, gpu, rows=None):
     G = {k: v.detach().cpu()[sel] for k, v in gpu.items()}
     ref = oracle.prolog(cfg, inp, rows=rows)                 # independent chain
     stats = {}
+    min_exact = CODE_EXACT_MFMA if getattr(cfg, "mxfp8_mfma", False) else CODE_EXACT
 
     R = cfg.rope_dim
     # stage 1: from x
@@ -189,7 +198,7 @@ def check_prolog(cfg, inp, gpu, rows=None):
         check_self_consistent_quant("kv", G["kv_norm"], G["kv_i8"], G["kv_scale"])
         stats["kv_excused"] = check_quant_vs_oracle(
             "kv", bits(G["kv_norm"]), G["kv_i8"].numpy(), G["kv_scale"].numpy(),
-            ref["kv_norm"], ref["kv_i8"], ref["kv_scale"])
+            ref["kv_norm"], ref["kv_i8"], ref["kv_scale"], min_exact)
 
     # stage 2: from the GPU's own normalised rows
     has_q, has_kvb = cfg.q_lora > 0, cfg.v_dim > 0
@@ -215,7 +224,7 @@ def check_prolog(cfg, inp, gpu, rows=None):
             gq, oq, gs, os_ = gq.reshape(-1, QH), oq.reshape(-1, QH), gs.reshape(-1), os_.reshape(-1)
         check_self_consistent_quant("q", gq, gc, gs)
         stats["q_excused"] = check_quant_vs_oracle(
-            "q", bits(gq), gc.numpy(), gs.numpy(), oq, st2["q_i8"], os_)
+            "q", bits(gq), gc.numpy(), gs.numpy(), oq, st2["q_i8"], os_, min_exact)
 
     # end to end against the independent chain, with the measured stage-1 differences
     # propagated linearly through the up projection (and RoPE's pair mixing)

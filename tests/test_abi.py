@@ -75,7 +75,9 @@ def create(**kw):
     (dict(q_lora=16384), mlap.MLAP_ERR_UNSUPPORTED),
     (dict(flags=mlap.MLAP_NORM_RSQRT | mlap.MLAP_ROPE_INTERLEAVED | mlap.MLAP_QUANT_Q_PER_HEAD),
      mlap.MLAP_OK),
-    (dict(flags=0x40), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=0x80), mlap.MLAP_ERR_INVALID_ARG),
+    (dict(flags=mlap.MLAP_MXFP8_MFMA), mlap.MLAP_ERR_INVALID_ARG),  # needs MLAP_MXFP8
+    (dict(flags=mlap.MLAP_MXFP8 | mlap.MLAP_MXFP8_MFMA), mlap.MLAP_OK),
     (dict(flags=mlap.MLAP_MXFP8), mlap.MLAP_OK),
     (dict(flags=mlap.MLAP_MXFP8 | mlap.MLAP_W8A8), mlap.MLAP_ERR_INVALID_ARG),
     (dict(flags=mlap.MLAP_Q_HEAD_NORM, hidden=4096, q_lora=1024, nope_dim=448, n_heads=64), mlap.MLAP_OK),
