@@ -212,10 +212,11 @@ def cpu_baseline(name, seconds=12.0):
     cfg = synth.get_config(name)
     inp = synth.make_inputs(cfg)
     n = 8
-    t0 = time.time()
-    oracle.prolog(cfg, inp, rows=np.arange(n, dtype=np.int32))
-    dt = time.time() - t0
-    n = int(min(cfg.T, max(n, seconds / max(dt / n, 1e-6))))
+    for _ in range(2):  # size the sample from a timed probe (the second one warm and larger)
+        t0 = time.time()
+        oracle.prolog(cfg, inp, rows=np.arange(n, dtype=np.int32))
+        dt = time.time() - t0
+        n = int(min(cfg.T, max(n, seconds / max(dt / n, 1e-6) / (4 if _ == 0 else 1))))
     t0 = time.time()
     oracle.prolog(cfg, inp, rows=np.arange(n, dtype=np.int32))
     dt = time.time() - t0

@@ -26,11 +26,14 @@ def _diff(a, b):
 
 
 # v3_w8a8 at T=2048 runs the q up projection in token blocks whose quant forks onto a
-# second stream and joins back, so the capture must carry that fork/join
-@pytest.mark.parametrize("name,T", [("v3_decode", 64), ("v3_decode", 256), ("v2lite_kv_decode", None),
-                                    ("v3_prefill", 1000), ("v3_w8a8", 2048)])
-def test_graph_replay_matches_eager(name, T):
-    cfg = synth.get_config(name, T=T)
+# second stream and joins back, so the capture must carry that fork/join; the MXFP8 cases
+# add the weight decode / activation conversion launches of both routes
+@pytest.mark.parametrize("name,T,var", [("v3_decode", 64, {}), ("v3_decode", 256, {}),
+                                        ("v2lite_kv_decode", None, {}), ("v3_prefill", 1000, {}),
+                                        ("v3_w8a8", 2048, {}), ("v3_mxfp8", 300, {}),
+                                        ("v3_mxfp8", 1000, {"mxfp8_mfma": True})])
+def test_graph_replay_matches_eager(name, T, var):
+    cfg = synth.get_config(name, T=T, **var)
     say("graph replay", name, "T=%d" % cfg.T)
     inp = {k: v.cuda() for k, v in synth.make_inputs(cfg).items()}
     other = {k: v.cuda() for k, v in synth.make_inputs(cfg, seed=synth.seed_for(cfg) + 7).items()}
