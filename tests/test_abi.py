@@ -181,3 +181,26 @@ def test_export_gemm_argument_errors():
     assert lib.mlap_gemm_bf16(None, 1, 1, 1, 4, 4, 96) == mlap.MLAP_ERR_UNSUPPORTED
     assert lib.mlap_gemm_bf16(None, 1, 1, 1, 4, 12, 64) == mlap.MLAP_ERR_UNSUPPORTED
     assert lib.mlap_gemm_bf16(None, None, None, None, 4, 4, -1) == mlap.MLAP_ERR_INVALID_ARG
+
+
+def test_mxfp8_run_needs_aligned_block_scales():
+    rc, h = create(t_max=64, flags=mlap.MLAP_MXFP8)
+    assert rc == 0
+    fake = 0x10000
+    full = dict(T=8, x=fake, positions=fake, w_qa=fake, w_qb=fake, w_kva=fake, gamma_q=fake,
+                gamma_kv=fake, cos=fake, sin=fake, ms_qa=fake, ms_qb=fake, ms_kva=fake)
+    for k in ("ms_qa", "ms_qb", "ms_kva"):
+        assert _run_raw(h, mlap._Inputs(**dict(full, **{k: None})), mlap._Outputs(), 0x100000,
+                        1 << 30) == mlap.MLAP_ERR_INVALID_ARG, k
+        assert _run_raw(h, mlap._Inputs(**dict(full, **{k: fake + 2})), mlap._Outputs(), 0x100000,
+                        1 << 30) == mlap.MLAP_ERR_INVALID_ARG, k  # 32-bit scale loads
+    lib.mlap_destroy(h)
+
+
+def test_export_mxfp8_gemm_argument_errors():
+    f = lib.mlap_gemm_mxfp8_f32
+    assert f(None, None, None, None, None, None, 4, 4, 128) == mlap.MLAP_ERR_INVALID_ARG
+    assert f(None, 1, 4, 1, 4, 1, 4, 4, 64) == mlap.MLAP_ERR_UNSUPPORTED    # K not whole stages
+    assert f(None, 1, 4, 1, 4, 1, 4, 6, 128) == mlap.MLAP_ERR_UNSUPPORTED   # N % 4
+    assert f(None, 1, 5, 1, 4, 1, 4, 4, 128) == mlap.MLAP_ERR_INVALID_ARG   # misaligned scales
+    assert f(None, None, None, None, None, None, 0, 4, 128) == mlap.MLAP_OK
