@@ -555,6 +555,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // [split * kbs, (split + 1) * kbs) of every row
     const int kbs = g.K * static_cast<int>(sizeof(Tin)) / g.k_splits;
     const int nk = kbs / KB;
+    // K-stages run in a per-tile rotated order, so that the workgroups sharing activation rows
+    // (every tile of a weight-streaming launch) do not all fetch the same lines at once
+    const int krot = (n_tile + m_tile) % (nk > 0 ? nk : 1);
+    auto kphys = [&](int kt) __attribute__((always_inline)) { return kt + krot < nk ? kt + krot : kt + krot - nk; };
     const size_t k0 = static_cast<size_t>(split) * kbs;
 
     // Copy sources: round i moves tile row i*RROWS + tid/LPR, physical chunk tid%LPR.
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     auto issue_part = [&](int kt, int slot, auto r0_c, auto r1_c) __attribute__((always_inline)) {
         constexpr int R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
         char* dst = smem + slot * SH::STAGE + wave * 1024;
-        const int koff = kt * KB;
+        const int koff = kphys(kt) * KB;
         static_for<R1 - R0>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = R0 + decltype(i_c)::value;
             big::copy16_to_lds(src[i] + koff, dst + i * SH::RROWS * KB);
@@ -633,11 +637,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         if constexpr (MX) {
             static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                 constexpr int i = decltype(i_c)::value;
-                sx_n[i] = *reinterpret_cast<const uint32_t*>(a_sp[i] + 4 * kt);
+                sx_n[i] = *reinterpret_cast<const uint32_t*>(a_sp[i] + 4 * kphys(kt));
             });
             static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
                 constexpr int j = decltype(j_c)::value;
-                sw_n[j] = *reinterpret_cast<const uint32_t*>(b_sp[j] + 4 * kt);
+                sw_n[j] = *reinterpret_cast<const uint32_t*>(b_sp[j] + 4 * kphys(kt));
             });
         }
     };
