@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--decode-workload", default="v3_decode")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--extra-workloads", default="v3_w8a8,v2lite_kv_decode,v3_decode+kvcache,v3_decode+variants,v4_decode,"
-                            "v3_mxfp8,v3_mxfp8+mfma",
+                            "v3_mxfp8,v3_mxfp8+mfma,v3_mxfp8_decode,v3_mxfp8_decode+mfma",
                     help="comma-separated workloads reported as extra objects (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",

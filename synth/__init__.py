@@ -110,11 +110,15 @@ CONFIGS = {
     "v4_decode": Config("v4_decode", T=16, hidden=4096, q_lora=1024, kv_lora=512, rope_dim=64,
                         nope_dim=448, v_dim=0, n_heads=64, max_pos=8192, positions="uniform",
                         q_head_norm=True, index=5),
-    # Same shape with int8 W8A8 projections.
-    # Same shape with MXFP8 projections (E4M3 weights, one E8M0 scale per 32 of K).
+    # Same shape with MXFP8 projections (E4M3 weights, one E8M0 scale per 32 of K), a
+    # mid-size batch and the decode batch.
     "v3_mxfp8": Config("v3_mxfp8", T=4096, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
                        nope_dim=128, v_dim=0, n_heads=128, max_pos=8192, positions="arange",
                        mxfp8=True, index=6),
+    "v3_mxfp8_decode": Config("v3_mxfp8_decode", T=256, hidden=7168, q_lora=1536, kv_lora=512,
+                              rope_dim=64, nope_dim=128, v_dim=0, n_heads=128, max_pos=8192,
+                              positions="uniform", mxfp8=True, index=7),
+    # Same shape with int8 W8A8 projections.
     "v3_w8a8": Config("v3_w8a8", T=16384, hidden=7168, q_lora=1536, kv_lora=512, rope_dim=64,
                       nope_dim=128, v_dim=0, n_heads=128, max_pos=16384,
                       positions="arange", w8a8=True, index=4),
