@@ -21,8 +21,9 @@ struct GemmTile {
 // (type, tile, epilogue) combination that has no instantiation.
 hipError_t launch_gemm(const GemmArgs& g, InType t, const GemmTile& tile, Epi epi, hipStream_t s);
 
-// LDS-DMA GEMM (gemm_big.hpp) in four shapes:
-//   kWide        -- 256 x 256 tiles, eight waves (large batches, MFMA-bound); kStoreBf16 and
+// LDS-DMA GEMM (gemm_big.hpp) in four shapes (the bf16 ones also on MXFP8 E4M3 operands):
+//   kWide        -- 256 x 256 tiles, eight waves (large batches, MFMA-bound; four waves of
+//                   128 x 128 with MXFP8); kStoreBf16 and
 //                   kHeads (head width and d0 multiples of 64, a 64-wide rope slice);
 //   kHalfHead    -- 96-column tiles: one per half of a 192-wide q head, the whole batch in
 //                   one tile row (bf16, kHeads);
@@ -94,6 +95,7 @@ struct QuantQArgs {
     int8_t* q_i8;             // [T, H, Dn+R] or null
     float* q_scale;           // [T] or null; [T, H] with per_head
     int per_head;             // one scale per (token, head) instead of per token
+    int parts;                // per-token quant: workgroups per token (set by the launcher)
 };
 // Limits of the per-head q quant (one workgroup holds a token's row).
 constexpr int kMaxQuantHeads = 1024;
