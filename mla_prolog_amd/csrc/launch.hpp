@@ -115,7 +115,8 @@ struct QHeadNormArgs {
     int max_pos;
     uint16_t* q_nope;         // [T, H, Dn], in place
     uint16_t* q_pe;           // [T, H, R], in place
-    float* part_amax;         // [T] or null
+    float* part_amax;         // [T, groups] or null
+    int groups;               // workgroups per token, each a whole-head share (H % groups == 0)
 };
 // Limits of the per-head norm (one workgroup holds a token's q row): H*(Dn+R) <= 32768 and
 // H*R <= 8192 (the rope chunks staged in LDS).

@@ -86,6 +86,7 @@ struct Plan {
     int tail_c0 = 0, tail_splits = 0;
     BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide, kv_shape = BigShape::kWide;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
+    int hn_groups = 1;  // per-head q norm: workgroups per token (each writes one partial amax)
     // MXFP8 on the block-scaled MFMA (E4M3 operands in the GEMMs); else, with MXFP8, the
     // weights are decoded to bf16 for the bf16 GEMMs
     bool mx_native = false;
@@ -233,6 +234,14 @@ struct mlap_prolog {
             const int nq = cfg.n_heads * QH;
             const int bn = p.big_q ? big_tile_n(p.q_shape) : bn_q;
             p.nt_q = (nq + bn - 1) / bn;
+            // small batches split each token's heads over up to 8 workgroups (whole heads, at
+            // most one workgroup per CU in all), one partial amax each
+            if (head_norm())
+                for (int g = 8; g > 1; g >>= 1)
+                    if (cfg.n_heads % g == 0 && g <= p.nt_q && T * g <= kCUs) {
+                        p.hn_groups = g;
+                        break;
+                    }
         }
         return p;
     }
@@ -724,6 +733,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                 hn.q_nope = static_cast<uint16_t*>(out->q_nope);
                 hn.q_pe = static_cast<uint16_t*>(out->q_pe);
                 hn.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+                hn.groups = plan.hn_groups;
                 MLAP_LAUNCH(kKQHeadNorm, launch_q_head_norm(hn, s));
             }
         } else {
@@ -821,7 +831,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         qa.H = H;
         qa.Dn = c.nope_dim;
         qa.R = R;
-        qa.n_tiles = head_norm ? 1 : plan.nt_q;  // the head-norm kernel leaves one partial per token
+        qa.n_tiles = head_norm ? plan.hn_groups : plan.nt_q;  // head norm: one partial per group
         qa.part_amax = reinterpret_cast<const float*>(wsb + L.qpart);
         qa.per_head = per_head;
         qa.q_nope = static_cast<const uint16_t*>(out->q_nope);

@@ -853,10 +853,15 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
     __shared__ float hrstd[kMaxQuantHeads];
     __shared__ uint4 pe_stage[kHeadNormPeChunks];
     __shared__ float red[kRowWaves];
-    const int t = blockIdx.x;
+    // `groups` workgroups per token (small batches), each with a whole-head share of the row:
+    // heads [h0, h0 + hg), chunks [c0, total)
+    const int G = a.groups > 0 ? a.groups : 1;
+    const int t = blockIdx.x / G, grp = blockIdx.x - t * G;
     const int QH = a.Dn + a.R;
     const int cph = QH >> 3, cn = a.Dn >> 3, cr = a.R >> 3;
-    const int total = a.H * cph;
+    const int hg = a.H / G, h0 = grp * hg;
+    const int c0 = h0 * cph;
+    const int total = c0 + hg * cph;
     const float invD = 1.0f / static_cast<float>(QH);
     const float e = a.rsqrt ? 1.0f : invD;  // per-element 1/D (variant B)
     auto chunk_ptr = [&](int c) -> uint16_t* {
@@ -868,10 +873,10 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
     uint4 held[kHeadNormChunks];
 #pragma unroll
     for (int k = 0; k < kHeadNormChunks; ++k)
-        held[k] = *reinterpret_cast<const uint4*>(chunk_ptr(min(static_cast<int>(threadIdx.x) + k * kRowThreads, total - 1)));
+        held[k] = *reinterpret_cast<const uint4*>(chunk_ptr(min(c0 + static_cast<int>(threadIdx.x) + k * kRowThreads, total - 1)));
 #pragma unroll
     for (int k = 0; k < kHeadNormChunks; ++k) {
-        const int c = threadIdx.x + k * kRowThreads;
+        const int c = c0 + threadIdx.x + k * kRowThreads;
         if (c < total) {
             float f[8], s = 0.f;
             unpack8(held[k], f);
@@ -880,36 +885,36 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
                 const float sq = f[q] * f[q];
                 s += sq * e;
             }
-            csq[c] = s;
+            csq[c - c0] = s;
         }
     }
     __syncthreads();
-    for (int h = threadIdx.x; h < a.H; h += kRowThreads) {
+    for (int hl = threadIdx.x; hl < hg; hl += kRowThreads) {
         float s = 0.f;
-        for (int j = 0; j < cph; ++j) s += csq[h * cph + j];
-        hrstd[h] = a.rsqrt ? rsqrtf(s * invD + a.eps) : 1.0f / sqrtf(s + a.eps);
+        for (int j = 0; j < cph; ++j) s += csq[hl * cph + j];
+        hrstd[hl] = a.rsqrt ? rsqrtf(s * invD + a.eps) : 1.0f / sqrtf(s + a.eps);
     }
     __syncthreads();
     // normalise (bf16 cast point); rope chunks go to LDS for their partners
 #pragma unroll
     for (int k = 0; k < kHeadNormChunks; ++k) {
-        const int c = threadIdx.x + k * kRowThreads;
+        const int c = c0 + threadIdx.x + k * kRowThreads;
         if (c < total) {
             const int h = c / cph, j = c - h * cph;
-            const float r = hrstd[h];
+            const float r = hrstd[h - h0];
             float f[8];
             unpack8(held[k], f);
 #pragma unroll
             for (int q = 0; q < 8; ++q) f[q] = f[q] * r;
             held[k] = pack8(f);
-            if (j >= cn) pe_stage[h * cr + (j - cn)] = held[k];
+            if (j >= cn) pe_stage[(h - h0) * cr + (j - cn)] = held[k];
         }
     }
     __syncthreads();
     float mx = 0.f;
 #pragma unroll
     for (int k = 0; k < kHeadNormChunks; ++k) {
-        const int c = threadIdx.x + k * kRowThreads;
+        const int c = c0 + threadIdx.x + k * kRowThreads;
         if (c < total) {
             const int h = c / cph, j = c - h * cph;
             uint4 o = held[k];
@@ -918,7 +923,7 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
                 // at this chunk's own columns; the partner is the other half
                 const int jr = j - cn;
                 const bool low = jr < (cr >> 1);
-                const uint4 pv = pe_stage[h * cr + (low ? jr + (cr >> 1) : jr - (cr >> 1))];
+                const uint4 pv = pe_stage[(h - h0) * cr + (low ? jr + (cr >> 1) : jr - (cr >> 1))];
                 float own[8], oth[8], res[8];
                 unpack8(o, own);
                 unpack8(pv, oth);
@@ -938,7 +943,7 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
     }
     if (a.part_amax) {
         const float amax = block_max(mx, red);
-        if (threadIdx.x == 0) a.part_amax[t] = amax;
+        if (threadIdx.x == 0) a.part_amax[static_cast<size_t>(t) * G + grp] = amax;
     }
 }
 
@@ -947,7 +952,9 @@ hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s) {
     if (a.H > kMaxQuantHeads || a.H * ((a.Dn + a.R) >> 3) > kHeadNormChunks * kRowThreads ||
         a.H * (a.R >> 3) > kHeadNormPeChunks || (a.R >> 3) % 2)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(q_head_norm_kernel, dim3(a.T), dim3(kRowThreads), 0, s, a);
+    const int G = a.groups > 0 ? a.groups : 1;
+    if (a.H % G) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(q_head_norm_kernel, dim3(a.T * G), dim3(kRowThreads), 0, s, a);
     return hipGetLastError();
 }
 
