@@ -234,10 +234,10 @@ struct mlap_prolog {
             const int nq = cfg.n_heads * QH;
             const int bn = p.big_q ? big_tile_n(p.q_shape) : bn_q;
             p.nt_q = (nq + bn - 1) / bn;
-            // small batches split each token's heads over up to 8 workgroups (whole heads, at
+            // small batches split each token's heads over up to 16 workgroups (whole heads, at
             // most one workgroup per CU in all), one partial amax each
             if (head_norm())
-                for (int g = 8; g > 1; g >>= 1)
+                for (int g = 16; g > 1; g >>= 1)
                     if (cfg.n_heads % g == 0 && g <= p.nt_q && T * g <= kCUs) {
                         p.hn_groups = g;
                         break;
