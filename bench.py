@@ -263,7 +263,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    import synth
+
+    def dominant_of(name):  # the up projection that dominates: q_b, or kv_b in KV-Prolog mode
+        return "gemm_up_kv" if synth.get_config(name).q_lora == 0 else DOMINANT
+
     cfg, e_ms, k_ms, e_pct, g_ms, g_pct = bench_workload(a.workload, a.steps, a.warmup, rotate=a.rotate,
+                                                         dominant=dominant_of(a.workload),
                                                          graph=not a.no_graph)
     # headline: the faster of the two launch modes (both run the whole step); both reported
     use_g = g_ms is not None and g_ms < e_ms
@@ -298,7 +304,9 @@ def main():
     }
     if a.decode_workload:
         dcfg, de_ms, dk_ms, de_pct, dg_ms, dg_pct = bench_workload(a.decode_workload, a.decode_steps,
-                                                                   a.warmup, rotate=4, graph=not a.no_graph)
+                                                                   a.warmup, rotate=4,
+                                                                   dominant=dominant_of(a.decode_workload),
+                                                                   graph=not a.no_graph)
         d_use_g = dg_ms is not None and dg_ms < de_ms
         dms, dpct = (dg_ms, dg_pct) if d_use_g else (de_ms, de_pct)
         dpf, dpb = path_work(dcfg, dcfg.T)
