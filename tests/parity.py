@@ -45,11 +45,10 @@ RTOL, ATOL = 1e-2, 1e-3
 SCALE_RTOL = 1e-3
 CODE_EXACT = 0.999
 # MXFP8 on the block-scaled MFMA: the instruction's sum of 64 products is not exact (up to ~5e-5
-# of sum |products| on the prolog's operands, see test_gemm_mxfp8_core), so ~2% of the normalised
-# bf16 values land one ulp from the
-# exact result, and a code moves when such an ulp crosses a rounding boundary of z*127/amax
-# (probability |code| 2^-8 <= 1/2, about 0.1 on average): ~0.2% of codes, 99.86-99.94% exact
-# measured at V3 sizes.
+# of sum |products| on the prolog's operands, see test_gemm_mxfp8_core), so ~2% of the
+# normalised bf16 values land one ulp from the exact result, and a code moves when such an ulp
+# crosses a rounding boundary of z*127/amax (probability |code| 2^-8 <= 1/2, about 0.1 on
+# average): ~0.2% of codes, 99.86-99.94% exact measured at V3 sizes.
 CODE_EXACT_MFMA = 0.997
 
 
