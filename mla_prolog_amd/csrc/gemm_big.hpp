@@ -555,9 +555,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // [split * kbs, (split + 1) * kbs) of every row
     const int kbs = g.K * static_cast<int>(sizeof(Tin)) / g.k_splits;
     const int nk = kbs / KB;
-    // K-stages run in a per-tile rotated order, so that the workgroups sharing activation rows
-    // (every tile of a weight-streaming launch) do not all fetch the same lines at once
-    const int krot = (n_tile + m_tile) % (nk > 0 ? nk : 1);
+    // Weight-streaming shapes (three-stage rings) run their K-stages in a per-tile rotated
+    // order, so that the workgroups sharing activation rows (every tile of the launch) do not
+    // all fetch the same lines at once. The large-batch tiles keep the common order: there,
+    // tiles running side by side share their operand rows through L2 (rotated, the kernel's
+    // HBM traffic grew 12% at T=8192 for no gain in time).
+    const int krot = S > 2 ? (n_tile + m_tile) % (nk > 0 ? nk : 1) : 0;
     auto kphys = [&](int kt) __attribute__((always_inline)) { return kt + krot < nk ? kt + krot : kt + krot - nk; };
     const size_t k0 = static_cast<size_t>(split) * kbs;
 
