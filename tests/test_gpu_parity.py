@@ -142,6 +142,7 @@ CASES = [
     ("tiny_kv", None),
     ("v2lite_kv_decode", None),
     ("v2lite_kv_decode", 1),
+    ("v3_decode", 8),         # the smoke case
     ("v3_decode", 37),
     ("v3_decode", 64),        # last batch size of the 64-row weight-streaming tiles
     ("v3_decode", 65),        # first batch size of the 256-row weight-streaming tiles
