@@ -91,12 +91,11 @@ typedef enum {
 #define MLAP_MXFP8 0x20u
 /* MLAP_MXFP8_MFMA (with MLAP_MXFP8): run the projections on gfx950's block-scaled MFMA
  * (E4M3 operands with their E8M0 scales, 64 values of K per instruction) instead of decoding
- * the weights to bf16. Faster, but the instruction's own sum of 64 products is not exact: the
- * projections then differ from the exact sum by about 1e-4 relative (so bf16 outputs more often
- * land one ulp away: INT8 codes measured 99.86-99.94% exact at V3 sizes, against >= 99.9% on the
- * default route). Without this flag the
- * MXFP8 products and sums are exact up to the fp32 accumulation. Needs hidden, q_lora and (with
- * kv_b) kv_lora multiples of 128; otherwise the decoded path runs. */
+ * the weights to bf16. Faster, but the instruction's own sum of 64 products is not exact (up to
+ * ~5e-5 of the sum of |products| on prolog-like operands), so bf16 outputs more often land one
+ * ulp away: INT8 codes measured 99.86-99.94% exact at V3 sizes, against >= 99.9% on the default
+ * route, where the MXFP8 products and sums are exact up to the fp32 accumulation. Needs hidden,
+ * q_lora and (with kv_b) kv_lora multiples of 128; otherwise the decoded path runs. */
 #define MLAP_MXFP8_MFMA 0x40u
 
 typedef struct {
