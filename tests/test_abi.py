@@ -204,3 +204,19 @@ def test_export_mxfp8_gemm_argument_errors():
     assert f(None, 1, 4, 1, 4, 1, 4, 6, 128) == mlap.MLAP_ERR_UNSUPPORTED   # N % 4
     assert f(None, 1, 5, 1, 4, 1, 4, 4, 128) == mlap.MLAP_ERR_INVALID_ARG   # misaligned scales
     assert f(None, None, None, None, None, None, 0, 4, 128) == mlap.MLAP_OK
+
+
+@pytest.mark.parametrize("name,var", [("v3_decode", {}), ("v2lite_kv_decode", {}), ("v4_decode", {}),
+                                      ("v3_w8a8", {}), ("v3_mxfp8", {}),
+                                      ("v3_mxfp8", {"mxfp8_mfma": True}), ("tiny_kv", {"mxfp8": True,
+                                                                                      "mxfp8_mfma": True})])
+def test_plan_sweep_every_batch_size_has_a_workspace(name, var):
+    """The host plan (tile shapes, split counts, head groups) holds for every batch size up to
+    a few thousand: the workspace query succeeds, is 256-byte aligned and covers at least the
+    down-projection output."""
+    cfg = synth.get_config(name, **var)
+    p = mlap.Prolog.from_config(cfg, t_max=4096)
+    n1 = cfg.q_lora + cfg.kv_lora + cfg.rope_dim
+    for T in list(range(1, 300)) + [511, 512, 513, 1000, 1023, 1024, 2047, 2048, 4095, 4096]:
+        n = p.workspace_size(T)
+        assert n % 256 == 0 and n >= T * n1 * 2, (T, n)
