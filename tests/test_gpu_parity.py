@@ -148,6 +148,8 @@ CASES = [
     ("v3_decode", 65),        # first batch size of the 256-row weight-streaming tiles
     ("v3_decode", 200),       # 128-row head tiles with a ragged second row tile
     ("v3_decode", None),      # T = 256, every row
+    ("v3_decode", 512),       # the largest weight-streaming batch
+    ("v3_prefill", 513),      # the smallest batch on the large-batch tiles, ragged row tile
     ("v2lite_kv_decode", 200),
     ("v2lite_kv_decode", 300),  # two row tiles of the narrow kv_b tiles
     ("v3_w8a8", 37),
