@@ -59,6 +59,17 @@ class _Outputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in _OUT_FIELDS]
 
 
+class _Given(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("a", "qn", "kvn", "qraw", "qpe")]
+
+
+_TAP_FIELDS = ("a_proj", "q_proj", "q_pre")
+
+
+class _Taps(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _TAP_FIELDS]
+
+
 def load():
     global _lib
     with _lock:
@@ -93,9 +104,10 @@ def load():
             lib.orc_prolog.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p, C.c_int32,
                                        C.POINTER(_Outputs)]
             lib.orc_prolog.restype = C.c_int
-            lib.orc_prolog_from.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p,
-                                            C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(_Outputs)]
-            lib.orc_prolog_from.restype = C.c_int
+            lib.orc_prolog_staged.argtypes = [C.POINTER(_Cfg), C.POINTER(_Inputs), C.c_void_p,
+                                              C.c_int32, C.POINTER(_Given), C.POINTER(_Outputs),
+                                              C.POINTER(_Taps)]
+            lib.orc_prolog_staged.restype = C.c_int
             lib.orc_num_threads.restype = C.c_int
             _lib = lib
     return _lib
@@ -258,14 +270,20 @@ def quant_rows(Z):
 
 # ----------------------------------------------------------------- prolog ----
 
-def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
+def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None, a=None, q_raw=None, q_pe_in=None,
+           taps=False):
     """Run the whole MLA Prolog for token ``rows`` (default: all) of ``inputs``.
 
     ``cfg`` is a ``synth.Config`` (or anything with its attributes); ``inputs``
     the dict from ``synth.make_inputs``. Returns a dict of numpy arrays, one row
     per entry of ``rows``: bf16 outputs as uint16 bits, codes int8, scales fp32.
-    ``q_norm`` / ``kv_norm`` (optional, [len(rows), width] bf16): start the q_b / kv_b
-    projections from these rows instead of the oracle's own normalised rows.
+    Staging (each optional, one row per entry of ``rows``, bf16): ``a`` [n, Lq+Lkv+R] replaces
+    the down projection, ``q_norm`` / ``kv_norm`` the inputs of the q_b / kv_b projections,
+    ``q_raw`` [n, H, Dn+R] the q_b projection (before any per-head norm), ``q_pe_in`` [n, H, R]
+    every head's rope slice just before RoPE; everything downstream of a given row is
+    computed from it. With ``taps`` the result also holds the oracle's own ``a_proj``,
+    ``q_proj`` and ``q_pre`` (the same quantities). Rope slices in these rows are in the
+    order the rotate-half takes them (with the QuantRope3D form: already de-interleaved).
     The chain is the V3 MLA Prolog of the AT-10 card, section 五 (q_a -> RMSNorm
     -> *gamma -> bf16 -> q_b; kv_a -> RMSNorm -> *gamma -> bf16), with the kv_b
     stage of the V2-Lite KV Prolog ("DeepSeek-V2-Lite-Chat MLA KV Prolog 迁移指南",
@@ -323,11 +341,24 @@ def prolog(cfg, inputs, rows=None, q_norm=None, kv_norm=None):
              int(mx))
     i = _Inputs(**{f: (_p(arrs[f]) if f in arrs else None) for f, _ in _Inputs._fields_})
     o = _Outputs(**{f: (_p(outs[f]) if f in outs else None) for f in _OUT_FIELDS})
-    qn = None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq)
-    kvn = None if kv_norm is None else _np(kv_norm, np.uint16).reshape(n, Lkv)
-    rc = load().orc_prolog_from(C.byref(c), C.byref(i), _p(rows), n, _p(qn), _p(kvn), C.byref(o))
+    N1 = Lq + Lkv + R
+    giv = {"a": None if a is None else _np(a, np.uint16).reshape(n, N1),
+           "qn": None if q_norm is None else _np(q_norm, np.uint16).reshape(n, Lq),
+           "kvn": None if kv_norm is None else _np(kv_norm, np.uint16).reshape(n, Lkv),
+           "qraw": None if q_raw is None else _np(q_raw, np.uint16).reshape(n, H, Dn + R),
+           "qpe": None if q_pe_in is None else _np(q_pe_in, np.uint16).reshape(n, H, R)}
+    g = _Given(**{k: _p(v) for k, v in giv.items()})
+    tp = {}
+    if taps:
+        tp["a_proj"] = np.empty((n, N1), np.uint16)
+        if Lq > 0:
+            tp.update(q_proj=np.empty((n, H, Dn + R), np.uint16), q_pre=np.empty((n, H, R), np.uint16))
+    t = _Taps(**{f: (_p(tp[f]) if f in tp else None) for f in _TAP_FIELDS})
+    rc = load().orc_prolog_staged(C.byref(c), C.byref(i), _p(rows), n, C.byref(g), C.byref(o),
+                                  C.byref(t))
     if rc != 0:
         raise ValueError("oracle rejected the inputs (rc=%d)" % rc)
+    outs.update(tp)
     return outs
 
 

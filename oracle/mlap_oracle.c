@@ -203,13 +203,18 @@ ORC_API void orc_rope_row(const uint16_t* u, const float* c, const float* s, int
  * values, the two axes are transposed, and rotate-half is applied to the result. With
  * CHUNK = 2 the transpose de-interleaves adjacent pairs (u_0 u_2 u_4 ... | u_1 u_3 ...), so
  * pair (2i, 2i+1) rotates with the cos/sin of columns i and i + R/2; the output keeps the
- * transposed (half-split) order. */
+ * transposed (half-split) order. orc_rope_transpose is the first step on its own: t = the
+ * [R/chunk, chunk] -> [chunk, R/chunk] transpose of u (t must not alias u). */
+static void orc_rope_transpose(const uint16_t* u, int64_t R, int64_t chunk, uint16_t* t) {
+    const int64_t nch = R / chunk;
+    for (int64_t a = 0; a < nch; ++a)
+        for (int64_t b = 0; b < chunk; ++b) t[b * nch + a] = u[a * chunk + b];
+}
+
 ORC_API void orc_rope_row_chunked(const uint16_t* u, const float* c, const float* s, int64_t R,
                                   int64_t chunk, uint16_t* out) {
     uint16_t t[1024];
-    const int64_t nch = R / chunk;
-    for (int64_t a = 0; a < nch; ++a)          /* [nch, chunk] -> [chunk, nch] */
-        for (int64_t b = 0; b < chunk; ++b) t[b * nch + a] = u[a * chunk + b];
+    orc_rope_transpose(u, R, chunk, t);
     orc_rope_row(t, c, s, R, out);
 }
 
@@ -363,12 +368,13 @@ static void orc_norm(const orc_cfg* cfg, const uint16_t* v, const uint16_t* gamm
         orc_rmsnorm_row(v, gamma, D, cfg->eps, out);
 }
 
-static void orc_rope(const orc_cfg* cfg, const uint16_t* u, const float* c, const float* s,
-                     int64_t R, uint16_t* out) {
-    if (cfg->rope_chunk > 0)
-        orc_rope_row_chunked(u, c, s, R, cfg->rope_chunk, out);
-    else
-        orc_rope_row(u, c, s, R, out);
+/* A raw rope slice put in the order the rotate-half takes it, in place: the QuantRope3D
+ * transpose when the configuration uses that form, else nothing. */
+static void orc_rope_order(const orc_cfg* cfg, uint16_t* u, int64_t R) {
+    if (cfg->rope_chunk <= 0) return;
+    uint16_t t[1024];
+    orc_rope_transpose(u, R, cfg->rope_chunk, t);
+    memcpy(u, t, sizeof(uint16_t) * (size_t)R);
 }
 
 /* One projection of one bf16 row v (length K) through W [N,K]: bf16, W8A8 or MXFP8
@@ -408,18 +414,41 @@ static void orc_project(const orc_cfg* cfg, const uint16_t* v, int64_t K, const 
     }
 }
 
-/* Full prolog for the token rows listed in rows[0..nrows). NULL outputs are skipped.
- * qn_given [nrows, q_lora] / kvn_given [nrows, kv_lora] (bf16, optional): when given,
- * the up projections start from these normalised rows instead of the ones this
- * function computes (the rest of the chain is unchanged); this lets a caller check
- * the second stage on exactly the inputs another implementation fed it.
- * Returns 0, or -1 on an argument the oracle does not accept. */
-ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
-                            int32_t nrows, const uint16_t* qn_given, const uint16_t* kvn_given,
-                            const orc_outputs* out) {
+/* Rows that stand in for the oracle's own intermediate results of the same rows, so a caller
+ * can check one step of the chain on exactly the inputs another implementation fed that step
+ * (every array optional, [nrows, ...] bf16 in the order of rows[]). Every rope slice in these
+ * rows (and in the taps below) is in the order the rotate-half takes it: with the QuantRope3D
+ * form, already transposed (orc_rope_transpose). */
+typedef struct {
+    const uint16_t* a;    /* [nrows, Lq + Lkv + R]: the down projection [q_a | c_kv | k_pe raw] */
+    const uint16_t* qn;   /* [nrows, Lq]: q_norm, the input of the q_b projection */
+    const uint16_t* kvn;  /* [nrows, Lkv]: kv_norm, the input of the kv_b projection */
+    const uint16_t* qraw; /* [nrows, H, Dn + R]: the q_b projection per head, before any head norm */
+    const uint16_t* qpe;  /* [nrows, H, R]: each head's rope slice just before RoPE */
+} orc_given;
+
+/* The oracle's own intermediate results (every array optional, [nrows, ...] bf16). */
+typedef struct {
+    uint16_t* a_proj; /* [nrows, Lq + Lkv + R]: the down projection */
+    uint16_t* q_proj; /* [nrows, H, Dn + R]: the q_b projection of the q_b input in use */
+    uint16_t* q_pre;  /* [nrows, H, R]: each head's rope slice just before RoPE (after the head
+                         norm when there is one) */
+} orc_taps;
+
+/* Full prolog for the token rows listed in rows[0..nrows). NULL outputs are skipped. `given`
+ * (optional) replaces intermediate rows as described above: everything downstream of a given
+ * row is computed from it, the rest of the chain is unchanged. `taps` (optional) receives
+ * intermediate rows. Returns 0, or -1 on an argument the oracle does not accept. */
+ORC_API int orc_prolog_staged(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
+                              int32_t nrows, const orc_given* given, const orc_outputs* out,
+                              const orc_taps* taps) {
     const int64_t Hd = cfg->hidden, Lq = cfg->q_lora, Lkv = cfg->kv_lora, R = cfg->rope_dim;
     const int64_t Dn = cfg->nope_dim, Dv = cfg->v_dim, H = cfg->n_heads;
-    const int64_t QH = Dn + R, KH = Dn + Dv;
+    const int64_t QH = Dn + R, KH = Dn + Dv, N1 = Lq + Lkv + R;
+    static const orc_given no_given;
+    static const orc_taps no_taps;
+    if (!given) given = &no_given;
+    if (!taps) taps = &no_taps;
     if (R <= 0 || (R & 1) || Lkv <= 0 || Hd <= 0) return -1;
     if (cfg->rope_chunk < 0 || (cfg->rope_chunk > 0 && (R % cfg->rope_chunk || R > 1024))) return -1;
     for (int32_t i = 0; i < nrows; ++i) {
@@ -437,24 +466,34 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
         int64_t maxK = Hd > Lq ? Hd : Lq;
         if (Lkv > maxK) maxK = Lkv;
         int64_t maxN = H * (QH > KH ? QH : KH);
-        if (Lq > maxN) maxN = Lq;
-        if (Lkv + R > maxN) maxN = Lkv + R;
-        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)maxN);
+        if (N1 > maxN) maxN = N1;
+        uint16_t* A = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N1);
+        uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)maxN);
         uint16_t* qn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(Lq > 0 ? Lq : 1));
         uint16_t* kvn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Lkv);
         uint16_t* qrow = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(H * QH));
         int8_t* codes = (int8_t*)malloc((size_t)(maxK > H * QH ? maxK : H * QH));
-        if (!a || !qn || !kvn || !qrow || !codes) {
+        if (!A || !y || !qn || !kvn || !qrow || !codes) {
             bad = 1;
-            free(a); free(qn); free(kvn); free(qrow); free(codes);
+            free(A); free(y); free(qn); free(kvn); free(qrow); free(codes);
             continue;
         }
 
-        /* kv branch: kv_a projection -> [c_kv | k_pe] */
-        orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, in->ms_kva, Lkv + R, a, codes);
-        orc_norm(cfg, a, in->gamma_kv, Lkv, kvn);
+        /* down projection A = [q_a | c_kv | k_pe raw]: x . W_qa^T and x . W_kva^T */
+        if (given->a) {
+            memcpy(A, given->a + i * N1, sizeof(uint16_t) * (size_t)N1);
+        } else {
+            if (Lq > 0) orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, in->ms_qa, Lq, A, codes);
+            orc_project(cfg, x, Hd, in->w_kva, in->ws_kva, in->ms_kva, Lkv + R, A + Lq, codes);
+            orc_rope_order(cfg, A + Lq + Lkv, R);
+        }
+        if (taps->a_proj) memcpy(taps->a_proj + i * N1, A, sizeof(uint16_t) * (size_t)N1);
+
+        /* kv branch: RMSNorm of c_kv, RoPE of k_pe, quant of kv_norm */
+        const uint16_t* ckv = A + Lq;
+        orc_norm(cfg, ckv, in->gamma_kv, Lkv, kvn);
         if (out->kv_norm) memcpy(out->kv_norm + i * Lkv, kvn, sizeof(uint16_t) * (size_t)Lkv);
-        if (out->k_pe) orc_rope(cfg, a + Lkv, c, s, R, out->k_pe + i * R);
+        if (out->k_pe) orc_rope_row(ckv + Lkv, c, s, R, out->k_pe + i * R);
         if (out->kv_i8 || out->kv_scale) {
             float sc;
             orc_quant_row(kvn, Lkv, codes, &sc);
@@ -462,30 +501,34 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
             if (out->kv_scale) out->kv_scale[i] = sc;
         }
         if (Dv > 0) { /* kv_b projection of the normalised compressed KV */
-            const uint16_t* kv_src = kvn_given ? kvn_given + i * Lkv : kvn;
-            orc_project(cfg, kv_src, Lkv, in->w_kvb, in->ws_kvb, in->ms_kvb, H * KH, a, codes);
+            const uint16_t* kv_src = given->kvn ? given->kvn + i * Lkv : kvn;
+            orc_project(cfg, kv_src, Lkv, in->w_kvb, in->ws_kvb, in->ms_kvb, H * KH, y, codes);
             for (int64_t h = 0; h < H; ++h) {
                 if (out->k_nope)
-                    memcpy(out->k_nope + (i * H + h) * Dn, a + h * KH, sizeof(uint16_t) * (size_t)Dn);
+                    memcpy(out->k_nope + (i * H + h) * Dn, y + h * KH, sizeof(uint16_t) * (size_t)Dn);
                 if (out->value)
-                    memcpy(out->value + (i * H + h) * Dv, a + h * KH + Dn, sizeof(uint16_t) * (size_t)Dv);
+                    memcpy(out->value + (i * H + h) * Dv, y + h * KH + Dn, sizeof(uint16_t) * (size_t)Dv);
             }
         }
 
-        /* q branch: q_a projection -> RMSNorm*gamma -> q_b projection -> split, RoPE */
+        /* q branch: RMSNorm*gamma of q_a -> q_b projection -> split, [head norm], RoPE -> quant */
         if (Lq > 0) {
-            orc_project(cfg, x, Hd, in->w_qa, in->ws_qa, in->ms_qa, Lq, a, codes);
-            orc_norm(cfg, a, in->gamma_q, Lq, qn);
+            orc_norm(cfg, A, in->gamma_q, Lq, qn);
             if (out->q_norm) memcpy(out->q_norm + i * Lq, qn, sizeof(uint16_t) * (size_t)Lq);
-            const uint16_t* q_src = qn_given ? qn_given + i * Lq : qn;
-            orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, in->ms_qb, H * QH, a, codes);
+            const uint16_t* q_src = given->qn ? given->qn + i * Lq : qn;
+            orc_project(cfg, q_src, Lq, in->w_qb, in->ws_qb, in->ms_qb, H * QH, y, codes);
+            for (int64_t h = 0; h < H; ++h) orc_rope_order(cfg, y + h * QH + Dn, R);
+            if (taps->q_proj) memcpy(taps->q_proj + i * H * QH, y, sizeof(uint16_t) * (size_t)(H * QH));
+            if (given->qraw) memcpy(y, given->qraw + i * H * QH, sizeof(uint16_t) * (size_t)(H * QH));
             if (cfg->q_head_norm) /* [AT-10] section 九: q_b -> reshape (heads, head_dim) -> RMSNorm */
-                for (int64_t h = 0; h < H; ++h) orc_norm(cfg, a + h * QH, NULL, QH, a + h * QH);
+                for (int64_t h = 0; h < H; ++h) orc_norm(cfg, y + h * QH, NULL, QH, y + h * QH);
             for (int64_t h = 0; h < H; ++h) {
-                const uint16_t* head = a + h * QH;
+                const uint16_t* head = y + h * QH;
                 uint16_t* qh = qrow + h * QH;
+                const uint16_t* pe = given->qpe ? given->qpe + (i * H + h) * R : head + Dn;
+                if (taps->q_pre) memcpy(taps->q_pre + (i * H + h) * R, head + Dn, sizeof(uint16_t) * (size_t)R);
                 memcpy(qh, head, sizeof(uint16_t) * (size_t)Dn);
-                orc_rope(cfg, head + Dn, c, s, R, qh + Dn);
+                orc_rope_row(pe, c, s, R, qh + Dn);
                 if (out->q_nope) memcpy(out->q_nope + (i * H + h) * Dn, qh, sizeof(uint16_t) * (size_t)Dn);
                 if (out->q_pe) memcpy(out->q_pe + (i * H + h) * R, qh + Dn, sizeof(uint16_t) * (size_t)R);
             }
@@ -503,14 +546,14 @@ ORC_API int orc_prolog_from(const orc_cfg* cfg, const orc_inputs* in, const int3
                 if (out->q_scale) out->q_scale[i] = sc;
             }
         }
-        free(a); free(qn); free(kvn); free(qrow); free(codes);
+        free(A); free(y); free(qn); free(kvn); free(qrow); free(codes);
     }
     return bad ? -1 : 0;
 }
 
 ORC_API int orc_prolog(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows,
                        int32_t nrows, const orc_outputs* out) {
-    return orc_prolog_from(cfg, in, rows, nrows, NULL, NULL, out);
+    return orc_prolog_staged(cfg, in, rows, nrows, NULL, out, NULL);
 }
 
 /* ------------------------------------------------------------ KV cache --- */

@@ -616,3 +616,134 @@ def test_mx_projection_is_the_bf16_gemm_of_dequantised_operands():
     assert np.array_equal(from_bits(wd).astype(np.float64), (w * s).numpy())   # exact in bf16
     ref = oracle.gemm_bf16(xd.reshape(1, -1), wd)[0]
     np.testing.assert_array_equal(out["k_pe"][0], ref[cfg.kv_lora:cfg.kv_lora + cfg.rope_dim])
+
+
+# ------------------------------------------------- W8A8 dequant and wiring ----
+
+def _ulp_within(got_bits, exact_f64, n_ulp=1):
+    """Every bf16 value within n_ulp bf16 steps of the exact value: a wrong factor (a dropped or
+    squared activation scale, another channel's weight scale) moves it by far more."""
+    got = from_bits(got_bits).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact_f64), 2.0 ** -126))) - 7)
+    err = np.abs(got - exact_f64)
+    assert (err <= n_ulp * ulp).all(), "worst %g ulp" % float((err / ulp).max())
+    return err / ulp
+
+
+def test_w8a8_dequant_k_pe_row_at_position_zero():
+    """AT-10 card, section 四: y = dequant(int32 x_q . w_q, x_scale, w_scale). At position 0
+    RoPE is the identity, so the W8A8 k_pe row is the dequantised kv_a projection of the rope
+    channels itself: the exact product (integer brute force) times x_scale times each channel's
+    w_scale, within one bf16 step."""
+    cfg = synth.get_config("v3_w8a8", T=3)
+    inp = synth.make_inputs(cfg)
+    inp["positions"] = torch.zeros(cfg.T, dtype=torch.int32)
+    out = oracle.prolog(cfg, inp)
+    wq = inp["w_kva"].numpy().astype(np.int64)[cfg.kv_lora:]       # the rope channels
+    ws = inp["w_kva_scale"].numpy().astype(np.float64)[cfg.kv_lora:]
+    for t in range(cfg.T):
+        xq, xs = oracle.quant_row(synth.bf16_bits(inp["x"][t]))
+        assert 0.005 < xs < 0.2                                       # far from 1: a dropped scale shows
+        acc = wq @ xq.astype(np.int64)
+        _ulp_within(out["k_pe"][t], acc.astype(np.float64) * xs * ws)
+
+
+def test_w8a8_dequant_q_nope_row_of_the_q_b_stage():
+    """The q_b stage of the W8A8 path on a given q_norm row: per-token quant of that row, exact
+    int32 products, dequant with the row's scale and each output channel's scale."""
+    cfg = synth.get_config("v3_w8a8", T=2)
+    inp = synth.make_inputs(cfg)
+    qn = to_bf16_bits(rng.standard_normal((cfg.T, cfg.q_lora)) * 1.7)
+    out = oracle.prolog(cfg, inp, q_norm=qn)
+    H, Dn, QH = cfg.n_heads, cfg.nope_dim, cfg.q_head
+    wq = inp["w_qb"].numpy().astype(np.int64)
+    ws = inp["w_qb_scale"].numpy().astype(np.float64)
+    nope_rows = (np.arange(H)[:, None] * QH + np.arange(Dn)[None, :]).reshape(-1)
+    for t in range(cfg.T):
+        codes, sc = oracle.quant_row(qn[t])
+        acc = wq[nope_rows] @ codes.astype(np.int64)
+        _ulp_within(out["q_nope"][t].reshape(-1), acc.astype(np.float64) * sc * ws[nope_rows])
+
+
+def test_q_pe_of_the_v3_chain_against_fp64_rotation():
+    """q_pe = RoPE(q_b projection of q_norm) per head at the token's position: the raw rope
+    slice from an exact fp64 GEMM (rounded once to bf16 by torch), rotated as complex numbers
+    by the table's cos/sin, within one bf16 step of the oracle; catches a wrong head offset,
+    slice, pairing, sign or table row."""
+    cfg = synth.get_config("v3_decode", T=3)
+    inp = synth.make_inputs(cfg)
+    assert (inp["positions"] > 0).all()
+    out = oracle.prolog(cfg, inp)
+    H, Dn, R, QH = cfg.n_heads, cfg.nope_dim, cfg.rope_dim, cfg.q_head
+    h = R // 2
+    qn = from_bits(out["q_norm"]).astype(np.float64)
+    W = from_bits(synth.bf16_bits(inp["w_qb"])).astype(np.float64)
+    raw = from_bits(to_bf16_bits((qn @ W.T).astype(np.float32))).reshape(cfg.T, H, QH)[..., Dn:]
+    pos = inp["positions"].numpy()
+    c = inp["cos"].numpy().astype(np.float64)[pos][:, None, :]
+    s = inp["sin"].numpy().astype(np.float64)[pos][:, None, :]
+    lo = raw[..., :h] * c[..., :h] - raw[..., h:] * s[..., :h]
+    hi = raw[..., h:] * c[..., h:] + raw[..., :h] * s[..., h:]
+    d = _ulp_within(out["q_pe"], np.concatenate([lo, hi], axis=-1))
+    assert (d < 0.5 + 1e-9).mean() > 0.99       # nearly all are the correctly rounded value
+    # the rope slice really moved (the positions are not 0): the raw slice differs
+    assert (out["q_pe"] != to_bf16_bits(raw.astype(np.float32))).mean() > 0.9
+
+
+def _selection_config(**kw):
+    return synth.Config("sel", T=2, hidden=1040, q_lora=512, kv_lora=512, rope_dim=16,
+                        nope_dim=16, v_dim=0, n_heads=2, max_pos=4, positions="arange", **kw)
+
+
+def _row_where_variants_differ(g, lo, hi):
+    """A bf16 row whose [lo, hi) segment RMSNorm variants A and B round differently."""
+    for _ in range(5000):
+        x = to_bf16_bits(rng.standard_normal(1040) * rng.uniform(0.05, 20))
+        if (oracle.rmsnorm_row_rsqrt(x[lo:hi], g, 1e-6) != oracle.rmsnorm_row(x[lo:hi], g, 1e-6)).any():
+            return x
+    raise AssertionError("no row found")
+
+
+def test_rmsnorm_variant_routing_on_rows_where_the_variants_differ():
+    """With one-hot weights the down projection returns x's columns exactly (pinned above), so
+    q_norm and kv_norm are RMSNorm of given rows. Token 0's q segment and token 1's kv segment
+    are rows on which variant A (rsqrt) and variant B (sqrt, divide) round differently: the
+    default configuration must give B and the rsqrt flag A, on both branches."""
+    gq = to_bf16_bits(rng.uniform(0.5, 1.5, 512))
+    gkv = to_bf16_bits(rng.uniform(0.5, 1.5, 512))
+    x = np.stack([_row_where_variants_differ(gq, 0, 512), _row_where_variants_differ(gkv, 512, 1024)])
+    eye = torch.zeros(1040, 1040, dtype=torch.bfloat16)
+    eye[torch.arange(1040), torch.arange(1040)] = 1
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    inp = {"x": bf(x), "positions": torch.zeros(2, dtype=torch.int32),
+           "w_qa": eye[:512].contiguous(), "w_kva": eye[512:].contiguous(),
+           "w_qb": (torch.randn(2 * 32, 512) * 0.02).to(torch.bfloat16),
+           "gamma_q": bf(gq), "gamma_kv": bf(gkv)}
+    inp["cos"], inp["sin"] = synth.rope_table(4, 16)
+    for rsqrt, fn in ((False, oracle.rmsnorm_row), (True, oracle.rmsnorm_row_rsqrt)):
+        o = oracle.prolog(_selection_config(norm_rsqrt=rsqrt), inp)
+        for t in range(2):
+            np.testing.assert_array_equal(o["q_norm"][t], fn(x[t, :512], gq, 1e-6))
+            np.testing.assert_array_equal(o["kv_norm"][t], fn(x[t, 512:1024], gkv, 1e-6))
+
+
+def test_staging_hooks_reproduce_the_unstaged_chain():
+    """Feeding the oracle its own intermediate rows (the down projection, q_norm, the raw q_b
+    heads, the pre-RoPE slices) reproduces its unstaged outputs bit for bit, with and without the
+    de-interleaved RoPE and the per-head norm (the hooks change where a row comes from, not the
+    arithmetic)."""
+    for var in ({}, {"rope_interleaved": True}, {"q_head_norm": True, "rope_interleaved": True}):
+        name = "v4_decode" if var.get("q_head_norm") else "v3_decode"
+        cfg = synth.get_config(name, T=2, **var)
+        inp = synth.make_inputs(cfg)
+        ref = oracle.prolog(cfg, inp, taps=True)
+        st = oracle.prolog(cfg, inp, a=ref["a_proj"], q_norm=ref["q_norm"], q_raw=ref["q_proj"],
+                           q_pe_in=ref["q_pre"], taps=True)
+        for k in ref:
+            np.testing.assert_array_equal(st[k], ref[k], err_msg="%s %s" % (var, k))
+    # the tap of the down projection is the bf16 GEMM of x with [W_qa ; W_kva]
+    cfg = synth.get_config("v3_decode", T=2)
+    inp = synth.make_inputs(cfg)
+    ref = oracle.prolog(cfg, inp, taps=True)
+    W = np.concatenate([synth.bf16_bits(inp["w_qa"]), synth.bf16_bits(inp["w_kva"])])
+    np.testing.assert_array_equal(ref["a_proj"], oracle.gemm_bf16(synth.bf16_bits(inp["x"]), W))
