@@ -34,7 +34,8 @@
  *   - bf16 tensors are passed as raw 16-bit patterns (void pointers).
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or keeps them past the call. They must be 16-byte
- *     aligned and must not overlap (inputs may alias other inputs).
+ *     aligned (a misaligned pointer is MLAP_ERR_INVALID_ARG; the MXFP8 scale
+ *     tensors ms_* need 4 bytes) and must not overlap (inputs may alias other inputs).
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     on it; no call synchronises the host except where stated.
  *   - Errors are returned as status codes (mlap_status); nothing aborts and no
@@ -60,7 +61,8 @@ typedef enum {
     MLAP_ERR_INVALID_ARG = 1, /* NULL required pointer, T out of [0, t_max], bad handle */
     MLAP_ERR_UNSUPPORTED = 2, /* dimensions the kernels do not support */
     MLAP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than mlap_workspace_size */
-    MLAP_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+    MLAP_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+    MLAP_ERR_NO_MEMORY = 5    /* a host allocation failed (mlap_create) */
 } mlap_status;
 
 /* Configuration flags. */
@@ -173,12 +175,24 @@ typedef struct {
     int8_t* kv_cache_i8;    /* [cache_slots, Lkv] int8 codes of kv_norm */
     float* kv_cache_scale;  /* [cache_slots] fp32 kv scale */
     void* kr_cache;         /* [cache_slots, R] bf16 k_pe, after RoPE */
+    /* Diagnostic taps (optional), for checking the path one step at a time against a reference
+       that can start from given intermediate rows:
+       a_proj: [T, Lq+Lkv+R] bf16, the down projection [q_a | c_kv | k_pe raw] exactly as the
+         row stage takes it (each value at the projection's bf16 cast point; with
+         MLAP_ROPE_INTERLEAVED the k_pe slice already de-interleaved, the order the rotate-half
+         reads it in);
+       q_proj: [T, H, Dn+R] bf16, the q up projection per head before the per-head norm (rope
+         slice in rotate-half order as above); only with MLAP_Q_HEAD_NORM, where it needs the
+         q_nope and q_pe outputs too. */
+    void* a_proj;
+    void* q_proj;
 } mlap_outputs;
 
 typedef struct mlap_prolog* mlap_handle;
 
 /* Validate `cfg` and create a host-side handle (no device allocation, no sync).
- * Returns MLAP_ERR_UNSUPPORTED for dimensions the kernels do not handle. */
+ * Returns MLAP_ERR_UNSUPPORTED for dimensions the kernels do not handle (among them a
+ * rope_dim above 4096) and MLAP_ERR_NO_MEMORY if the handle cannot be allocated. */
 MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out);
 
 /* Bytes of device workspace a run with T tokens needs (GEMM intermediates, the
@@ -205,9 +219,14 @@ MLAP_API const char* mlap_status_str(int status);
 
 /*
  * Test export of the W8A8 matmul core (AT-10 page, section 四: int8 x int8 ->
- * int32): C[m, n] = sum_k A[m, k] * B[n, k], exact int32, with the same MFMA
- * kernel the W8A8 prolog uses. A [M, K] int8, B [N, K] int8, C [M, N] int32,
- * device pointers; K must be a multiple of 128. Enqueued on `stream`.
+ * int32): C[m, n] = sum_k A[m, k] * B[n, k], exact int32, on the kernel and tiles the
+ * W8A8 prolog runs for a batch of M tokens: for M > 512 the LDS-DMA GEMM with 256 x 256
+ * tiles (a column remainder that is a multiple of 64 on 64 x 64 tiles), as the W8A8 down
+ * and q up projections of large batches; for M <= 512 the register-staged GEMM with the
+ * small-batch projections' tiles (128 x 192 when N is a multiple of 192, as the q up
+ * projection, else 256 x 64, as the down projection). Only the epilogue differs: the
+ * accumulators are stored instead of dequantised. A [M, K] int8, B [N, K] int8, C [M, N]
+ * int32, device pointers (16-byte aligned); K must be a multiple of 128. Enqueued on `stream`.
  */
 MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, int32_t* C, int32_t M,
                      int32_t N, int32_t K);

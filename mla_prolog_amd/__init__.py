@@ -21,7 +21,8 @@ __all__ = ["Prolog", "MlapError", "gemm_i8_i32", "gemm_bf16", "KERNELS", "lib_pa
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libmlap.so")
 
-MLAP_OK, MLAP_ERR_INVALID_ARG, MLAP_ERR_UNSUPPORTED, MLAP_ERR_WORKSPACE, MLAP_ERR_HIP = range(5)
+(MLAP_OK, MLAP_ERR_INVALID_ARG, MLAP_ERR_UNSUPPORTED, MLAP_ERR_WORKSPACE, MLAP_ERR_HIP,
+ MLAP_ERR_NO_MEMORY) = range(6)
 MLAP_W8A8 = 0x1
 MLAP_NORM_RSQRT = 0x2        # RMSNorm variant A
 MLAP_ROPE_INTERLEAVED = 0x4  # rope slices de-interleaved before rotate-half
@@ -59,12 +60,15 @@ OUTPUTS = ("q_nope", "q_pe", "kv_norm", "k_pe", "k_nope", "value", "q_norm", "q_
 # KV cache rows written at inputs["slot_mapping"]: [cache_slots, Lkv] bf16, [cache_slots, Lkv]
 # int8, [cache_slots] fp32, [cache_slots, R] bf16
 CACHES = ("kv_cache", "kv_cache_i8", "kv_cache_scale", "kr_cache")
+# diagnostic taps: the down projection as the row stage reads it [T, Lq+Lkv+R] bf16, and (with the
+# per-head q norm) the raw q up projection [T, H, Dn+R] bf16
+TAPS = ("a_proj", "q_proj")
 _DTYPES = {"q_i8": torch.int8, "kv_i8": torch.int8, "q_scale": torch.float32,
            "kv_scale": torch.float32, "kv_cache_i8": torch.int8, "kv_cache_scale": torch.float32}
 
 
 class _Outputs(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in OUTPUTS + CACHES]
+    _fields_ = [(n, C.c_void_p) for n in OUTPUTS + CACHES + TAPS]
 
 
 def _load():
@@ -196,22 +200,52 @@ class Prolog:
             self._ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
         return self._ws
 
-    def alloc_outputs(self, T, device="cuda", want=None):
-        """Allocate output tensors; ``want`` selects names (default: all this config makes)."""
+    def _shapes(self, T, slots=0):
+        """Shape of every tensor the run may take, by name: the inputs (``w_*_scale`` for W8A8,
+        ``w_*_mxscale`` for MXFP8), the outputs, the caches (``slots`` rows) and the taps."""
         c = self.cfg
-        H, Dn, R, Dv, Lq, Lkv = (c["n_heads"], c["nope_dim"], c["rope_dim"], c["v_dim"],
-                                 c["q_lora"], c["kv_lora"])
-        bf, i8, f = torch.bfloat16, torch.int8, torch.float32
-        shapes = {"kv_norm": ((T, Lkv), bf), "k_pe": ((T, R), bf), "kv_i8": ((T, Lkv), i8),
-                  "kv_scale": ((T,), f)}
+        H, Dn, R, Dv, Lq, Lkv, Hd = (c["n_heads"], c["nope_dim"], c["rope_dim"], c["v_dim"],
+                                     c["q_lora"], c["kv_lora"], c["hidden"])
+        sh = {"x": (T, Hd), "positions": (T,), "slot_mapping": (T,), "gamma_kv": (Lkv,),
+              "cos": (c["max_pos"], R), "sin": (c["max_pos"], R),
+              "kv_norm": (T, Lkv), "k_pe": (T, R), "kv_i8": (T, Lkv), "kv_scale": (T,),
+              "kv_cache": (slots, Lkv), "kv_cache_i8": (slots, Lkv), "kv_cache_scale": (slots,),
+              "kr_cache": (slots, R), "a_proj": (T, Lq + Lkv + R)}
+        weights = {"w_kva": (Lkv + R, Hd)}
         if Lq > 0:
-            shapes.update(q_nope=((T, H, Dn), bf), q_pe=((T, H, R), bf), q_i8=((T, H, Dn + R), i8),
-                          q_scale=((T, H) if c["q_quant_per_head"] else (T,), f), q_norm=((T, Lq), bf))
+            weights.update(w_qa=(Lq, Hd), w_qb=(H * (Dn + R), Lq))
+            sh.update(gamma_q=(Lq,), q_nope=(T, H, Dn), q_pe=(T, H, R), q_i8=(T, H, Dn + R),
+                      q_scale=(T, H) if c["q_quant_per_head"] else (T,), q_norm=(T, Lq),
+                      q_proj=(T, H, Dn + R))
         if Dv > 0:
-            shapes.update(k_nope=((T, H, Dn), bf), value=((T, H, Dv), bf))
+            weights["w_kvb"] = (H * (Dn + Dv), Lkv)
+            sh.update(k_nope=(T, H, Dn), value=(T, H, Dv))
+        for k, (n, kk) in weights.items():
+            sh[k] = (n, kk)
+            sh[k + "_scale"] = (n,)
+            sh[k + "_mxscale"] = (n, kk // 32)
+        return sh
+
+    def alloc_outputs(self, T, device="cuda", want=None):
+        """Allocate output tensors; ``want`` selects names (default: all this config makes; the
+        optional q_norm and the diagnostic taps a_proj / q_proj only when named)."""
+        sh = self._shapes(T)
+        names = ["kv_norm", "k_pe", "kv_i8", "kv_scale"]
+        if self.cfg["q_lora"] > 0:
+            names += ["q_nope", "q_pe", "q_i8", "q_scale"]
+        if self.cfg["v_dim"] > 0:
+            names += ["k_nope", "value"]
         if want is None:
-            want = [k for k in shapes if k != "q_norm"]
-        return {k: torch.empty(shapes[k][0], dtype=shapes[k][1], device=device) for k in want}
+            want = names
+        return {k: torch.empty(sh[k], dtype=_DTYPES.get(k, torch.bfloat16), device=device) for k in want}
+
+    def _check_shapes(self, tensors, T, slots):
+        sh = self._shapes(T, slots)
+        for k, t in tensors.items():
+            if t is None or k not in sh:
+                continue
+            if tuple(t.shape) != tuple(sh[k]):
+                raise ValueError("%s has shape %s, expected %s" % (k, tuple(t.shape), tuple(sh[k])))
 
     def _marshal(self, inputs, outputs, workspace):
         x = inputs["x"]
@@ -241,8 +275,13 @@ class Prolog:
             i.cache_slots = int(caches[0].shape[0])
             if any(int(c.shape[0]) != i.cache_slots for c in caches):
                 raise ValueError("every KV cache must have the same number of rows")
+        unknown = set(outputs) - set(OUTPUTS + CACHES + TAPS)
+        if unknown:
+            raise ValueError("unknown outputs: %s" % sorted(unknown))
+        self._check_shapes(inputs, T, i.cache_slots)
+        self._check_shapes(outputs, T, i.cache_slots)
         o = _Outputs(**{k: _ptr(outputs.get(k), _DTYPES.get(k, torch.bfloat16), k)
-                        for k in OUTPUTS + CACHES})
+                        for k in OUTPUTS + CACHES + TAPS})
         ws = self.workspace(T, device=x.device) if workspace is None else workspace
         return i, o, ws, outputs
 

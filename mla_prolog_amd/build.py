@@ -14,13 +14,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmlap.so")
-SOURCES = ["gemm_kernels.hip", "row_kernels.hip", "mlap_host.hip"]
-HEADERS = ["common.hpp", "gemm.hpp", "launch.hpp"]
+SOURCES = ["gemm_kernels.hip", "gemm_big_bf16.hip", "gemm_big_i8.hip", "gemm_big_fp8.hip", "gemm_nt.hip",
+           "row_kernels.hip", "mlap_host.hip"]
+HEADERS = ["common.hpp", "gemm.hpp", "gemm_big.hpp", "gemm_big_launch.hpp", "gemm_inst.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     # IEEE semantics where the method fixes the arithmetic: no FMA contraction of the
     # RoPE / RMSNorm steps, correctly rounded fp32 divide and sqrt.
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -32,18 +33,38 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
+    return r.returncode, "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (one hipcc per translation unit), then
+    link the shared library; the objects go to a temporary folder."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(prefix="mlap_build_") as tmpd:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpd, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        jobs = min(len(cmds), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, cmds))
+        for (rc, out), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s:\n%s" % (src, out))
+            if verbose and out.strip():
+                print(out)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + out)
     os.replace(tmp, LIB)
     return LIB
 

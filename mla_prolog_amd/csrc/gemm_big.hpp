@@ -189,9 +189,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     // W8A8 dequantisation scales of this lane's rows and columns, fetched in one burst:
     // a_scale of each of its FM tokens, b_scale of its 4-column runs (float4 when the run
     // lies inside one weight segment and inside N).
-    float asc[kIsI8<Tin> ? FM : 1];
-    float4 bsc[kIsI8<Tin> ? FN : 1][4];
-    if constexpr (kIsI8<Tin>) {
+    constexpr bool DEQ = kIsI8<Tin> && EPI != Epi::kStoreI32;  // int32 export: raw accumulators
+    float asc[DEQ ? FM : 1];
+    float4 bsc[DEQ ? FN : 1][4];
+    if constexpr (DEQ) {
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
             asc[i] = g.a_scale[min(mb + 32 * i, g.M - 1)];
@@ -224,7 +225,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             float v[4];
-            if constexpr (kIsI8<Tin>) {
+            if constexpr (DEQ) {
                 const float as = asc[i];
                 const float bs[4] = {bsc[j][gq].x, bsc[j][gq].y, bsc[j][gq].z, bsc[j][gq].w};
 #pragma unroll
@@ -241,6 +242,35 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
         }
     };
 
+    if constexpr (EPI == Epi::kStoreI32) {
+        // the raw int32 accumulators [M, ldo] (the W8A8 core's test export): four consecutive
+        // columns per lane, element by element past the last whole run of N
+        static_assert(kIsI8<Tin>, "int32 output needs int8 operands");
+        int32_t* out = static_cast<int32_t*>(g.out);
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(j_c)::value;
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                const int m = mb + 32 * i;
+                if (m < g.M) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int n = nb + 32 * j + 8 * gq;
+                        int32_t* o = out + static_cast<size_t>(m) * g.ldo + n;
+                        if (n + 3 < g.N && g.ldo % 4 == 0) {
+                            *reinterpret_cast<int4*>(o) = make_int4(acc[j][i][4 * gq], acc[j][i][4 * gq + 1],
+                                                                    acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (n + q < g.N) o[q] = acc[j][i][4 * gq + q];
+                        }
+                    }
+                }
+            });
+        });
+        return;
+    }
     if constexpr (EPI == Epi::kStoreF32) {
         // split-K partial sums, fp32 [k_splits][M][ldo]: four consecutive columns per lane
         float* out = static_cast<float*>(g.out) + static_cast<size_t>(split) * g.M * g.ldo;

@@ -1,0 +1,39 @@
+// gemm_big_fp8.hip -- MXFP8 (E4M3 operands, E8M0 block scales) instantiations of the LDS-DMA
+// GEMM (gemm_big.hpp) on the block-scaled MFMA.
+#include "gemm_big_launch.hpp"
+
+namespace mlap {
+
+hipError_t launch_big_fp8(const GemmArgs& g, Epi epi, BigTile t, hipStream_t s) {
+    using T = fp8e4m3;
+    switch (t) {
+        case BigTile::kWide:
+            if (epi == Epi::kStoreBf16) return launch_big_one<T, 256, 256, 2, 2, 2, Epi::kStoreBf16>(g, s);
+            if (epi == Epi::kHeads) return launch_big_one<T, 256, 256, 2, 2, 2, Epi::kHeads>(g, s);
+            break;
+        case BigTile::kHalfHead:
+            if (epi == Epi::kHeads) return launch_big_one<T, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
+            break;
+        case BigTile::kHalfHead64:
+            if (epi == Epi::kHeads) return launch_big_one<T, 64, 96, 2, 1, 3, Epi::kHeads>(g, s);
+            break;
+        case BigTile::kSplitK:
+            if (epi == Epi::kStoreF32) return launch_big_one<T, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
+            break;
+        case BigTile::kSplitK64:
+            if (epi == Epi::kStoreF32) return launch_big_one<T, 64, 64, 2, 1, 3, Epi::kStoreF32>(g, s);
+            break;
+        case BigTile::kNarrowHeads:
+            if (epi == Epi::kHeads) return launch_big_one<T, 256, 32, 4, 1, 3, Epi::kHeads>(g, s);
+            break;
+        case BigTile::kNarrowHeads64:
+            if (epi == Epi::kHeads) return launch_big_one<T, 64, 32, 2, 1, 3, Epi::kHeads>(g, s);
+            break;
+        case BigTile::kRem64:
+            if (epi == Epi::kStoreBf16) return launch_big_one<T, 64, 64, 2, 1, 3, Epi::kStoreBf16>(g, s);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mlap

@@ -1,71 +1,21 @@
-// gemm_kernels.hip -- instantiations of the gfx950 MFMA GEMM and their launcher.
-//
-// Tile shapes (rows x columns of the output tile, K-tiles of prefetch in flight):
-//   256 x {64..256}, 1 ahead  -- large batches (prefill): 128x128 (or 64x64) per wave,
-//                                enough MFMA work per LDS byte to stay MFMA-bound;
-//   128 x {64..256}, 3 ahead  -- small batches (decode): weight streaming, where the
-//                                bytes in flight per workgroup set the bandwidth;
-//   256 x 64, 3 ahead         -- the split-K down projection of small batches;
-//   128 x 128, 1 ahead        -- the GEMM-core test exports.
-// and the large-batch kernel of gemm_big.hpp: 256 x 256 tiles, eight waves, operands
-// copied HBM -> LDS directly in 128-byte row stages, two stages in LDS.
-#include "gemm.hpp"
-#include "gemm_big.hpp"
-#include "launch.hpp"
+// gemm_kernels.hip -- tile choice of the gfx950 MFMA GEMMs. The kernels are the LDS-DMA
+// GEMM of gemm_big.hpp (256 x 256 tiles, eight waves, operands copied HBM -> LDS directly in
+// 128-byte row stages, for large batches; narrow weight-streaming tiles for small ones) and
+// the register-staged GEMM of gemm.hpp; their instantiations live in gemm_big_*.hip and
+// gemm_nt.hip.
+#include "gemm_inst.hpp"
 
 namespace mlap {
 
 namespace {
 
-template <typename Tin, int BM, int BN, int WM, int WN, int P, Epi EPI>
-hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.k_splits;
-    hipLaunchKernelGGL((gemm_nt_kernel<Tin, BM, BN, WM, WN, P, EPI>), dim3(tiles),
-                       dim3(kWave * WM * WN), 0, s, g);
-    return hipGetLastError();
-}
-
-template <typename Tin>
-hipError_t dispatch(const GemmArgs& g, const GemmTile& t, Epi epi, hipStream_t s) {
-    const int BM = t.bm, BN = t.bn, P = t.prefetch;
-    switch (epi) {
-        case Epi::kStoreBf16:
-            if (BM == 128 && BN == 128 && P == 1) return launch_one<Tin, 128, 128, 2, 2, 1, Epi::kStoreBf16>(g, s);
-            if (BM == 256 && BN == 192 && P == 1) return launch_one<Tin, 256, 192, 2, 2, 1, Epi::kStoreBf16>(g, s);
-            if (BM == 256 && BN == 64 && P == 1) return launch_one<Tin, 256, 64, 4, 1, 1, Epi::kStoreBf16>(g, s);
-            break;
-        case Epi::kStoreF32:
-            if constexpr (sizeof(Tin) == 2)
-                if (BM == 256 && BN == 64 && P == 3) return launch_one<Tin, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
-            break;
-        case Epi::kStoreI32:
-            if constexpr (sizeof(Tin) == 1)
-                if (BM == 128 && BN == 128 && P == 1) return launch_one<Tin, 128, 128, 2, 2, 1, Epi::kStoreI32>(g, s);
-            break;
-        case Epi::kHeads:
-            if (BM == 128 && P == 3) {
-                if (BN == 64) return launch_one<Tin, 128, 64, 2, 2, 3, Epi::kHeads>(g, s);
-                if (BN == 128) return launch_one<Tin, 128, 128, 2, 2, 3, Epi::kHeads>(g, s);
-                if (BN == 192) return launch_one<Tin, 128, 192, 2, 2, 3, Epi::kHeads>(g, s);
-                if (BN == 256) return launch_one<Tin, 128, 256, 2, 2, 3, Epi::kHeads>(g, s);
-            }
-            if (BM == 256 && P == 1) {
-                if (BN == 64) return launch_one<Tin, 256, 64, 4, 1, 1, Epi::kHeads>(g, s);
-                if (BN == 128) return launch_one<Tin, 256, 128, 2, 2, 1, Epi::kHeads>(g, s);
-                if (BN == 192) return launch_one<Tin, 256, 192, 2, 2, 1, Epi::kHeads>(g, s);
-                if (BN == 256) return launch_one<Tin, 256, 256, 2, 2, 1, Epi::kHeads>(g, s);
-            }
-            break;
+hipError_t launch_big_typed(const GemmArgs& g, InType t, Epi epi, BigTile tile, hipStream_t s) {
+    switch (t) {
+        case InType::kBf16: return launch_big_bf16(g, epi, tile, s);
+        case InType::kInt8: return launch_big_i8(g, epi, tile, s);
+        case InType::kFp8: return launch_big_fp8(g, epi, tile, s);
     }
     return hipErrorInvalidValue;
-}
-
-template <typename Tin, int BM, int BN, int WM, int WN, int S, Epi EPI>
-hipError_t launch_big_one(const GemmArgs& g, hipStream_t s) {
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.k_splits;
-    hipLaunchKernelGGL((gemm_big_kernel<Tin, BM, BN, WM, WN, 128, S, EPI>), dim3(tiles),
-                       dim3(64 * WM * WN), 0, s, g);
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -88,6 +38,7 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
     switch (shape) {
         case BigShape::kWide:
             if (epi == Epi::kStoreBf16) return g.N % 8 == 0 && g.ldo % 8 == 0;
+            if (epi == Epi::kStoreI32) return t == InType::kInt8;
             if (epi == Epi::kHeads) {
                 if (g.head_w % 64 || g.d0 % 64) return false;
                 return g.rope ? g.d1 == 64 : g.d1 % 8 == 0;
@@ -110,10 +61,10 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
 
 hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, BigShape shape) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    if (shape == BigShape::kWide && epi == Epi::kStoreBf16 && g.N > kBigTile && g.N % kBigTile &&
-        g.N % 64 == 0) {
+    if (shape == BigShape::kWide && (epi == Epi::kStoreBf16 || epi == Epi::kStoreI32) && g.N > kBigTile &&
+        g.N % kBigTile && g.N % 64 == 0) {
         // A ragged last column tile would cost a whole extra round of 256x256 tiles: run the
-        // full-width columns here and the remainder with 256 x 64 tiles.
+        // full-width columns here and the remainder with 64 x 64 tiles.
         const int nm = g.N / kBigTile * kBigTile;
         GemmArgs a = g;
         a.N = nm;
@@ -135,60 +86,30 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
             r.b_mx0 = g.b_mx0 ? g.b_mx0 + static_cast<size_t>(nm) * mxrow : nullptr;
             r.b_split = g.b_split - nm;
         }
-        r.out = static_cast<uint16_t*>(g.out) + nm;
+        r.out = static_cast<char*>(g.out) + static_cast<size_t>(nm) * (epi == Epi::kStoreI32 ? 4 : 2);
         // 64 x 64 tiles: one per 64 tokens, so the narrow remainder still spreads over the CUs
-        if ((static_cast<size_t>(r.K) * eb) % 128 == 0) {
-            if (t == InType::kFp8) return launch_big_one<fp8e4m3, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s);
-            return t == InType::kInt8 ? launch_big_one<int8_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s)
-                                      : launch_big_one<uint16_t, 64, 64, 2, 1, 3, Epi::kStoreBf16>(r, s);
-        }
+        if ((static_cast<size_t>(r.K) * eb) % 128 == 0) return launch_big_typed(r, t, epi, BigTile::kRem64, s);
+        if (epi == Epi::kStoreI32) return hipErrorInvalidValue;
         return launch_gemm(r, t, GemmTile{256, 64, 1}, Epi::kStoreBf16, s);
     }
     if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
     // Weight-streaming shapes cover the whole batch in one row tile; at most 64 tokens take
     // 64-row tiles (two waves), so no copy bandwidth goes to clamped duplicate rows.
     const bool m64 = g.M <= 64;
-    if (t == InType::kFp8) {  // MXFP8: the same shapes on E4M3 operands
-        switch (shape) {
-            case BigShape::kWide:
-                return epi == Epi::kStoreBf16 ? launch_big_one<fp8e4m3, 256, 256, 2, 2, 2, Epi::kStoreBf16>(g, s)
-                                              : launch_big_one<fp8e4m3, 256, 256, 2, 2, 2, Epi::kHeads>(g, s);
-            case BigShape::kHalfHead:
-                return m64 ? launch_big_one<fp8e4m3, 64, 96, 2, 1, 3, Epi::kHeads>(g, s)
-                           : launch_big_one<fp8e4m3, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
-            case BigShape::kSplitK:
-                return m64 ? launch_big_one<fp8e4m3, 64, 64, 2, 1, 3, Epi::kStoreF32>(g, s)
-                           : launch_big_one<fp8e4m3, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
-            case BigShape::kNarrowHeads:
-                return m64 ? launch_big_one<fp8e4m3, 64, 32, 2, 1, 3, Epi::kHeads>(g, s)
-                           : launch_big_one<fp8e4m3, 256, 32, 4, 1, 3, Epi::kHeads>(g, s);
-        }
-        return hipErrorInvalidValue;
-    }
+    BigTile tile = BigTile::kWide;
     switch (shape) {
-        case BigShape::kWide:
-            if (t == InType::kBf16)
-                return epi == Epi::kStoreBf16 ? launch_big_one<uint16_t, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s)
-                                              : launch_big_one<uint16_t, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
-            return epi == Epi::kStoreBf16 ? launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s)
-                                          : launch_big_one<int8_t, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
-        case BigShape::kHalfHead:
-            return m64 ? launch_big_one<uint16_t, 64, 96, 2, 1, 3, Epi::kHeads>(g, s)
-                       : launch_big_one<uint16_t, 256, 96, 4, 1, 3, Epi::kHeads>(g, s);
-        case BigShape::kSplitK:
-            return m64 ? launch_big_one<uint16_t, 64, 64, 2, 1, 3, Epi::kStoreF32>(g, s)
-                       : launch_big_one<uint16_t, 256, 64, 4, 1, 3, Epi::kStoreF32>(g, s);
-        case BigShape::kNarrowHeads:
-            return m64 ? launch_big_one<uint16_t, 64, 32, 2, 1, 3, Epi::kHeads>(g, s)
-                       : launch_big_one<uint16_t, 256, 32, 4, 1, 3, Epi::kHeads>(g, s);
+        case BigShape::kWide: tile = BigTile::kWide; break;
+        case BigShape::kHalfHead: tile = m64 ? BigTile::kHalfHead64 : BigTile::kHalfHead; break;
+        case BigShape::kSplitK: tile = m64 ? BigTile::kSplitK64 : BigTile::kSplitK; break;
+        case BigShape::kNarrowHeads: tile = m64 ? BigTile::kNarrowHeads64 : BigTile::kNarrowHeads; break;
     }
-    return hipErrorInvalidValue;
+    return launch_big_typed(g, t, epi, tile, s);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, InType type, const GemmTile& t, Epi epi, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (type == InType::kFp8) return hipErrorInvalidValue;  // MXFP8 runs on the LDS-DMA kernel only
-    return type == InType::kBf16 ? dispatch<uint16_t>(g, t, epi, s) : dispatch<int8_t>(g, t, epi, s);
+    return type == InType::kBf16 ? launch_nt_bf16(g, t, epi, s) : launch_nt_i8(g, t, epi, s);
 }
 
 }  // namespace mlap

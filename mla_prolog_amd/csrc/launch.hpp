@@ -78,6 +78,9 @@ struct NormArgs {
     int8_t* kv_cache_i8;    // [n_slots, Lkv]
     float* kv_cache_scale;  // [n_slots]
     uint16_t* kr_cache;     // [n_slots, R]
+    // diagnostic tap: the down-projection row as read, [T, N1] bf16 (rope slice in rotate-half
+    // order), or null
+    uint16_t* a_proj;
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
@@ -117,6 +120,7 @@ struct QHeadNormArgs {
     uint16_t* q_pe;           // [T, H, R], in place
     float* part_amax;         // [T, groups] or null
     int groups;               // workgroups per token, each a whole-head share (H % groups == 0)
+    uint16_t* q_proj;         // diagnostic tap: the raw heads as read, [T, H, Dn+R], or null
 };
 // Limits of the per-head norm (one workgroup holds a token's q row): H*(Dn+R) <= 32768 and
 // H*R <= 8192 (the rope chunks staged in LDS).

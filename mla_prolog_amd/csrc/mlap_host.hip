@@ -327,7 +327,7 @@ int validate(const mlap_config* c) {
     if (c->hidden % kmul) return MLAP_ERR_UNSUPPORTED;
     if (c->q_lora % kmul) return MLAP_ERR_UNSUPPORTED;
     if (c->kv_lora % 8 || (c->v_dim > 0 && c->kv_lora % kmul)) return MLAP_ERR_UNSUPPORTED;
-    if (c->rope_dim % 16) return MLAP_ERR_UNSUPPORTED;
+    if (c->rope_dim % 16 || c->rope_dim > 4096) return MLAP_ERR_UNSUPPORTED;  // row kernels: R/16 <= 256
     if (c->nope_dim % 8 || c->v_dim % 8) return MLAP_ERR_UNSUPPORTED;
     if (c->q_lora > 8192 || c->kv_lora > 8192) return MLAP_ERR_UNSUPPORTED;  // row kernel
     if (c->q_lora > 0 && !head_norm && heads_tile(c->nope_dim + c->rope_dim) == 0) return MLAP_ERR_UNSUPPORTED;
@@ -350,6 +350,10 @@ int validate(const mlap_config* c) {
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// A tensor pointer the kernels cannot use: the 16-byte vector accesses and global->LDS copies
+// need 16-byte alignment (NULL passes: optional tensors are checked separately).
+inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -363,6 +367,7 @@ MLAP_API const char* mlap_status_str(int status) {
         case MLAP_ERR_UNSUPPORTED: return "unsupported dimensions";
         case MLAP_ERR_WORKSPACE: return "workspace missing or too small";
         case MLAP_ERR_HIP: return "HIP runtime error";
+        case MLAP_ERR_NO_MEMORY: return "host allocation failed";
         default: return "unknown status";
     }
 }
@@ -377,7 +382,7 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
     const int v = validate(cfg);
     if (v != MLAP_OK) return v;
     mlap_prolog* h = new (std::nothrow) mlap_prolog();
-    if (!h) return MLAP_ERR_INVALID_ARG;
+    if (!h) return MLAP_ERR_NO_MEMORY;
     h->cfg = *cfg;
     h->w8a8 = (cfg->flags & MLAP_W8A8) != 0;
     h->mx = (cfg->flags & MLAP_MXFP8) != 0;
@@ -478,6 +483,23 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
     const bool head_norm = h->head_norm();
     bool quant_done = false;  // the q quant already ran per token block
     if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
+    // the per-head quant reads every head's values back, and the per-head norm rewrites the
+    // raw heads in place: both need the two q tensors, for any q output
+    const bool need_q = has_q && (out->q_nope || out->q_pe || quant_q || out->q_proj);
+    if ((head_norm && need_q) || (quant_q && per_head))
+        if (!out->q_nope || !out->q_pe) return MLAP_ERR_INVALID_ARG;
+    if (out->q_proj && !head_norm) return MLAP_ERR_INVALID_ARG;  // the tap exists with the head norm only
+    // 16-byte alignment of every tensor the kernels touch (the MXFP8 scales: 4 bytes, above)
+    {
+        const void* ptrs[] = {in->x, in->positions, in->w_qa, in->w_qb, in->w_kva, in->w_kvb,
+                              in->ws_qa, in->ws_qb, in->ws_kva, in->ws_kvb, in->gamma_q, in->gamma_kv,
+                              in->cos, in->sin, in->slot_mapping, out->q_nope, out->q_pe, out->kv_norm,
+                              out->k_pe, out->k_nope, out->value, out->q_norm, out->q_i8, out->q_scale,
+                              out->kv_i8, out->kv_scale, out->kv_cache, out->kv_cache_i8,
+                              out->kv_cache_scale, out->kr_cache, out->a_proj, out->q_proj};
+        for (const void* p : ptrs)
+            if (misaligned16(p)) return MLAP_ERR_INVALID_ARG;
+    }
     const WsLayout L = h->layout(T);
     if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign))
         return MLAP_ERR_WORKSPACE;
@@ -647,9 +669,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         na.kv_cache_scale = out->kv_cache_scale;
         na.kr_cache = static_cast<uint16_t*>(out->kr_cache);
     }
-    const bool need_q = has_q && (out->q_nope || out->q_pe || quant_q);
-    // the per-head norm rewrites the raw heads in place: it needs both q tensors
-    if (head_norm && need_q && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
+    na.a_proj = static_cast<uint16_t*>(out->a_proj);
     const bool need_kvb = has_kvb && (out->k_nope || out->value);
     if (need_kvb && !w8) na.kv_norm = kvn;  // the bf16 kv_b reads it
     if (w8 && need_q) {
@@ -736,6 +756,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
                 hn.q_pe = static_cast<uint16_t*>(out->q_pe);
                 hn.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
                 hn.groups = plan.hn_groups;
+                hn.q_proj = static_cast<uint16_t*>(out->q_proj);
                 MLAP_LAUNCH(kKQHeadNorm, launch_q_head_norm(hn, s));
             }
         } else {
@@ -852,6 +873,7 @@ MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, in
     if (M == 0 || N == 0) return MLAP_OK;
     if (!A || !B || !C) return MLAP_ERR_INVALID_ARG;
     if (K % 128) return MLAP_ERR_UNSUPPORTED;
+    if (misaligned16(A) || misaligned16(B) || misaligned16(C)) return MLAP_ERR_INVALID_ARG;
     GemmArgs g{};
     g.M = M;
     g.N = N;
@@ -865,9 +887,19 @@ MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, in
     g.group_m = kGroupM;
     g.out = C;
     g.ldo = N;
-    return launch_gemm(g, InType::kInt8, GemmTile{128, 128, 1}, Epi::kStoreI32, as_stream(stream)) == hipSuccess
-               ? MLAP_OK
-               : MLAP_ERR_HIP;
+    // The W8A8 prolog's own tiles for a batch of M tokens: past the weight-streaming bucket the
+    // LDS-DMA 256 x 256 tiles (with 64 x 64 tiles for a column remainder that is a multiple of
+    // 64), else the register-staged tiles of the small-batch projections (128 x 192 as for the
+    // q up projection when N is a whole number of 192-wide heads, else the down projection's
+    // 256 x 64).
+    hipError_t e;
+    if (M > kSmallBatch)
+        e = launch_gemm_big(g, InType::kInt8, Epi::kStoreI32, as_stream(stream));
+    else if (N % 192 == 0)
+        e = launch_gemm(g, InType::kInt8, GemmTile{128, 192, 3}, Epi::kStoreI32, as_stream(stream));
+    else
+        e = launch_gemm(g, InType::kInt8, GemmTile{256, 64, 1}, Epi::kStoreI32, as_stream(stream));
+    return e == hipSuccess ? MLAP_OK : MLAP_ERR_HIP;
 }
 
 MLAP_API int mlap_gemm_bf16(void* stream, const void* A, const void* B, void* C, int32_t M, int32_t N,

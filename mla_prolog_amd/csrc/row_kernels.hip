@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
         const int c = tid + i * kRowThreads;
         if (c < nq) {
             load_a8(a, t, c * 8, qv[i]);
+            if (a.a_proj) *reinterpret_cast<uint4*>(a.a_proj + static_cast<size_t>(t) * a.N1 + c * 8) = pack8(qv[i]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = qv[i][e] * qv[i][e];
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
         }
         if (c < nkv) {
             load_a8(a, t, a.Lq + c * 8, kv[i]);
+            if (a.a_proj) *reinterpret_cast<uint4*>(a.a_proj + static_cast<size_t>(t) * a.N1 + a.Lq + c * 8) = pack8(kv[i]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float p = kv[i][e] * kv[i][e];
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
 
     // rotate-half RoPE of the k_pe slice (pairs i, i + R/2), one cos/sin row per token
     const int half = a.R >> 1;
-    if ((a.k_pe || a.kr_cache) && tid < (half >> 3)) {
+    if ((a.k_pe || a.kr_cache || a.a_proj) && tid < (half >> 3)) {
         const int i0 = tid * 8;
         const int p = clamp_pos(a.positions[t], a.max_pos);
         const float* cr = a.cos + static_cast<size_t>(p) * a.R;
@@ -211,6 +213,11 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
         float x1[8], x2[8], lo[8], hi[8];
         load_a8(a, t, a.Lq + a.Lkv + i0, x1);
         load_a8(a, t, a.Lq + a.Lkv + half + i0, x2);
+        if (a.a_proj) {
+            uint16_t* ar = a.a_proj + static_cast<size_t>(t) * a.N1 + a.Lq + a.Lkv;
+            *reinterpret_cast<uint4*>(ar + i0) = pack8(x1);
+            *reinterpret_cast<uint4*>(ar + half + i0) = pack8(x2);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float p1 = x1[e] * cr[i0 + e];
@@ -321,7 +328,7 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
         }
     };
 
-    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr) && half >= 8;
+    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr || a.a_proj != nullptr) && half >= 8;
     const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
     const bool roper = rope && tid < (half >> 3);
     const int i0 = rope ? min(tid, (half >> 3) - 1) * 8 : 0;
@@ -389,6 +396,21 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
     static_for<KC>([&](auto c_c) __attribute__((always_inline)) { finish(kv[decltype(c_c)::value]); });
     finish(x1);
     finish(x2);
+    if (a.a_proj) {  // the down-projection row as read (the GEMM's bf16 cast point)
+        uint16_t* ar = a.a_proj + static_cast<size_t>(t) * a.N1;
+        static_for<QC>([&](auto c_c) __attribute__((always_inline)) {
+            const int ch = tid + kRowThreads * decltype(c_c)::value;
+            if (ch < nq) *reinterpret_cast<uint4*>(ar + ch * 8) = pack8(qv[decltype(c_c)::value]);
+        });
+        static_for<KC>([&](auto c_c) __attribute__((always_inline)) {
+            const int ch = tid + kRowThreads * decltype(c_c)::value;
+            if (ch < nkv) *reinterpret_cast<uint4*>(ar + a.Lq + ch * 8) = pack8(kv[decltype(c_c)::value]);
+        });
+        if (roper) {
+            *reinterpret_cast<uint4*>(ar + a.Lq + a.Lkv + i0) = pack8(x1);
+            *reinterpret_cast<uint4*>(ar + a.Lq + a.Lkv + half + i0) = pack8(x2);
+        }
+    }
 
     // RMS statistics: per thread in element order, then the fixed-order block sum
     float sq = 0.f, skv = 0.f;
@@ -531,7 +553,7 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
     const int nq = a.Lq >> 3, nkv = a.Lkv >> 3;
     const int half = a.R >> 1;
     const int rc = half >> 3;  // rope chunks per half
-    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr) && rc > 0;
+    const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr || a.a_proj != nullptr) && rc > 0;
     const uint16_t* arow = a.a_bf16 + static_cast<size_t>(t) * a.N1;
     const int c_rope = a.Lq + a.Lkv;  // first column of the rope slice
     // rope slice from the tail partials, one (chunk, split) pair per lane
@@ -580,6 +602,16 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
         sl[1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
         shh[0] = *reinterpret_cast<const float4*>(sr + half + i0);
         shh[1] = *reinterpret_cast<const float4*>(sr + half + i0 + 4);
+    }
+
+    if (a.a_proj) {  // the down-projection row as read (q and kv segments; rope slice below)
+        uint16_t* ar = a.a_proj + static_cast<size_t>(t) * a.N1;
+#pragma unroll
+        for (int i = 0; i < QC; ++i)
+            if (lane + 64 * i < nq) *reinterpret_cast<uint4*>(ar + (lane + 64 * i) * 8) = rq[i];
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+            if (lane + 64 * i < nkv) *reinterpret_cast<uint4*>(ar + a.Lq + (lane + 64 * i) * 8) = rkv[i];
     }
 
     // ---- RMSNorm of both segments
@@ -667,6 +699,11 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
             x1[e] = bf2f(f2bf(__shfl(sum[e], il * S)));
             x2[e] = bf2f(f2bf(__shfl(sum[e], (il + rc) * S)));
         }
+    }
+    if (rope && lane < rc && a.a_proj) {
+        uint16_t* ar = a.a_proj + static_cast<size_t>(t) * a.N1 + c_rope;
+        *reinterpret_cast<uint4*>(ar + i0) = pack8(x1);
+        *reinterpret_cast<uint4*>(ar + half + i0) = pack8(x2);
     }
     if (rope && lane < rc) {
         const float cv[8] = {cl[0].x, cl[0].y, cl[0].z, cl[0].w, cl[1].x, cl[1].y, cl[1].z, cl[1].w};
@@ -878,6 +915,7 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
     for (int k = 0; k < kHeadNormChunks; ++k) {
         const int c = c0 + threadIdx.x + k * kRowThreads;
         if (c < total) {
+            if (a.q_proj) *reinterpret_cast<uint4*>(a.q_proj + static_cast<size_t>(t) * a.H * QH + c * 8) = held[k];
             float f[8], s = 0.f;
             unpack8(held[k], f);
 #pragma unroll

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_kernel_names():
-    for s in range(5):
+    assert lib.mlap_status_str(mlap.MLAP_ERR_NO_MEMORY) == b"host allocation failed"
+    for s in range(6):
         assert lib.mlap_status_str(s)
     assert lib.mlap_status_str(99) == b"unknown status"
     assert mlap.KERNELS == ("act_quant", "gemm_down", "norm_rope", "gemm_up_q", "gemm_up_kv",
@@ -86,6 +87,7 @@ def create(**kw):
     (dict(nope_dim=448, n_heads=64), mlap.MLAP_ERR_UNSUPPORTED),  # head 512 without the head norm
     (dict(flags=mlap.MLAP_QUANT_Q_PER_HEAD, n_heads=2048), mlap.MLAP_ERR_UNSUPPORTED),
     (dict(flags=mlap.MLAP_QUANT_Q_PER_HEAD, n_heads=256), mlap.MLAP_ERR_UNSUPPORTED),  # 49152 values
+    (dict(rope_dim=8192, nope_dim=64), mlap.MLAP_ERR_UNSUPPORTED),  # the row kernels cover R <= 4096
 ])
 def test_create_validation(kw, status):
     rc, h = create(**kw)
@@ -220,3 +222,75 @@ def test_plan_sweep_every_batch_size_has_a_workspace(name, var):
     for T in list(range(1, 300)) + [511, 512, 513, 1000, 1023, 1024, 2047, 2048, 4095, 4096]:
         n = p.workspace_size(T)
         assert n % 256 == 0 and n >= T * n1 * 2, (T, n)
+
+
+# Every call below must fail validation: with a workspace of None, a check that did not fire
+# would return MLAP_ERR_WORKSPACE (not launch), so the fake pointers are never dereferenced.
+_IN_PTRS = ("x", "positions", "w_qa", "w_qb", "w_kva", "gamma_q", "gamma_kv", "cos", "sin")
+
+
+def test_run_rejects_misaligned_tensors():
+    rc, h = create(t_max=64)
+    assert rc == 0
+    fake = 0x10000
+    full = dict(T=8, **{k: fake for k in _IN_PTRS})
+    outs = dict(q_nope=fake, q_pe=fake, kv_norm=fake, k_pe=fake, q_i8=fake, q_scale=fake,
+                kv_i8=fake, kv_scale=fake, q_norm=fake, a_proj=fake)
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(**outs), None, 0) == mlap.MLAP_ERR_WORKSPACE
+    for k in _IN_PTRS:
+        assert _run_raw(h, mlap._Inputs(**dict(full, **{k: fake + 8})), mlap._Outputs(**outs), None,
+                        0) == mlap.MLAP_ERR_INVALID_ARG, k
+    for k in outs:
+        assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(**dict(outs, **{k: fake + 4})), None,
+                        0) == mlap.MLAP_ERR_INVALID_ARG, k
+    lib.mlap_destroy(h)
+    # the int32 export too
+    assert lib.mlap_gemm_i8_i32(None, fake + 4, fake, fake, 4, 4, 128) == mlap.MLAP_ERR_INVALID_ARG
+    assert lib.mlap_gemm_i8_i32(None, fake, fake, fake + 8, 4, 4, 128) == mlap.MLAP_ERR_INVALID_ARG
+
+
+def test_q_outputs_that_read_the_q_tensors_back_need_them():
+    """The per-head q quant reads every head's values back, so even a scale-only run needs both
+    q tensors; the per-head norm rewrites the raw heads in place, so any q output needs both;
+    the raw-head tap exists with the per-head norm only. All rejected before any launch."""
+    fake = 0x10000
+    full = dict(T=8, **{k: fake for k in _IN_PTRS})
+    rc, h = create(t_max=64, flags=mlap.MLAP_QUANT_Q_PER_HEAD)
+    assert rc == 0
+    for outs in (dict(q_scale=fake), dict(q_scale=fake, q_pe=fake), dict(q_scale=fake, q_nope=fake)):
+        assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(**outs), None, 0) == \
+            mlap.MLAP_ERR_INVALID_ARG, outs
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(q_scale=fake, q_nope=fake, q_pe=fake),
+                    None, 0) == mlap.MLAP_ERR_WORKSPACE
+    lib.mlap_destroy(h)
+    rc, h = create(t_max=64, flags=mlap.MLAP_Q_HEAD_NORM, hidden=4096, q_lora=1024, nope_dim=448,
+                   n_heads=64)
+    assert rc == 0
+    for outs in (dict(q_nope=fake), dict(q_pe=fake), dict(q_scale=fake), dict(q_proj=fake)):
+        assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(**outs), None, 0) == \
+            mlap.MLAP_ERR_INVALID_ARG, outs
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(q_nope=fake, q_pe=fake, q_proj=fake),
+                    None, 0) == mlap.MLAP_ERR_WORKSPACE
+    lib.mlap_destroy(h)
+    rc, h = create(t_max=64)
+    assert _run_raw(h, mlap._Inputs(**full), mlap._Outputs(q_nope=fake, q_pe=fake, q_proj=fake),
+                    None, 0) == mlap.MLAP_ERR_INVALID_ARG  # no per-head norm: no raw-head tap
+    lib.mlap_destroy(h)
+
+
+def test_binding_checks_shapes_against_the_configuration():
+    """The binding compares every tensor's shape with the configuration before a pointer
+    reaches the library (shape logic only; no tensor is created on a device)."""
+    p = mlap.Prolog.from_config(synth.get_config("v3_decode", T=8))
+    sh = p._shapes(8, slots=16)
+    assert sh["x"] == (8, 7168) and sh["w_qb"] == (128 * 192, 1536) and sh["q_i8"] == (8, 128, 192)
+    assert sh["a_proj"] == (8, 2112) and sh["kv_cache"] == (16, 512) and sh["w_qa_mxscale"] == (1536, 224)
+    import torch
+    ok = {"x": torch.empty(8, 7168), "q_nope": torch.empty(8, 128, 128)}
+    p._check_shapes(ok, 8, 0)
+    for bad in ({"x": torch.empty(8, 7169)}, {"q_nope": torch.empty(8, 128, 64)},
+                {"kv_scale": torch.empty(9)}, {"cos": torch.empty(8192, 32)}):
+        with pytest.raises(ValueError):
+            p._check_shapes(bad, 8, 0)
+    ph = mlap.Prolog.from_config(synth.get_config("v3_decode", T=8, q_quant_per_head=True))
+    assert ph._shapes(8)["q_scale"] == (8, 128)

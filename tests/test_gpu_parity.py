@@ -16,7 +16,7 @@ import torch
 import mla_prolog_amd as mlap
 import oracle
 import synth
-from parity import check_bf16, check_prolog
+from parity import check_bf16, check_prolog, run_staged, staged_names
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -31,19 +31,24 @@ def to_dev(inp):
     return {k: v.to(DEV) for k, v in inp.items()}
 
 
-def all_outputs(p, T):
-    want = list(p.alloc_outputs(0).keys())
-    if p.cfg["q_lora"] > 0:
-        want.append("q_norm")
-    return p.alloc_outputs(T, want=want)
-
-
 def run_gpu(cfg, inp, t_max=None, outputs=None):
+    """One run with every output the staged check reads (q_norm and the taps included)."""
     p = mlap.Prolog.from_config(cfg, t_max=t_max)
     T = int(inp["x"].shape[0])
-    out = p.run(to_dev(inp), outputs=outputs if outputs is not None else all_outputs(p, T))
+    out = p.run(to_dev(inp), outputs=outputs if outputs is not None else p.alloc_outputs(T, want=staged_names(cfg)))
     torch.cuda.synchronize()
     return out
+
+
+def run_checked(cfg, inp, t_max=None, rows=None):
+    """The run and its position-0 twin, then the staged parity check (tests/parity.py)."""
+    p = mlap.Prolog.from_config(cfg, t_max=t_max)
+    out, out0 = run_staged(p, cfg, to_dev(inp))
+    return out, check_prolog(cfg, inp, out, out0, rows=rows)
+
+
+def fmt(stats):
+    return {k: (tuple(round(x, 4) for x in v) if isinstance(v, tuple) else round(v, 4)) for k, v in stats.items()}
 
 
 # ------------------------------------------------------------- GEMM cores ----
@@ -61,7 +66,13 @@ def test_gemm_bf16_core(M, N, K):
     assert exact > 0.99, exact
 
 
-@pytest.mark.parametrize("M,N,K", [(37, 200, 256), (130, 136, 7168), (1, 1, 128)])
+# The int32 export runs the W8A8 prolog's own tiles for an M-token batch: M > 512 the LDS-DMA
+# 256 x 256 tiles (N = 2112: 8 of them plus the 64 x 64 remainder tiles; N = 24576: the q up
+# projection's 96 column tiles), M <= 512 the small-batch register-staged tiles (N = 2112:
+# 256 x 64; N = 24576: 128 x 192), at the V3 W8A8 projection shapes, ragged batches included.
+@pytest.mark.parametrize("M,N,K", [(37, 200, 256), (130, 136, 7168), (1, 1, 128),
+                                   (1000, 2112, 7168), (1000, 24576, 1536), (513, 2112, 7168),
+                                   (130, 2112, 7168), (130, 24576, 1536), (600, 520, 256)])
 def test_gemm_i8_core_bit_exact(M, N, K):
     say("gemm_i8", M, N, K)
     g = torch.Generator().manual_seed(M + N + K)
@@ -162,9 +173,8 @@ def test_prolog_parity(name, T):
     cfg = synth.get_config(name, T=T)
     say("prolog parity", name, "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
-    out = run_gpu(cfg, inp)
-    stats = check_prolog(cfg, inp, out)
-    say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
+    out, stats = run_checked(cfg, inp)
+    say("  bit-exact fractions / excused rows / e2e (inside, worst):", fmt(stats))
 
 
 # Numeric variants (configuration flags): RMSNorm variant A, the QuantRope3D de-interleaved
@@ -202,9 +212,8 @@ def test_prolog_variants_parity(name, T, var):
     cfg = synth.get_config(name, T=T, **var)
     say("prolog parity", name, "T=%d" % cfg.T, var)
     inp = synth.make_inputs(cfg)
-    out = run_gpu(cfg, inp)
-    stats = check_prolog(cfg, inp, out)
-    say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
+    out, stats = run_checked(cfg, inp)
+    say("  bit-exact fractions / excused rows / e2e (inside, worst):", fmt(stats))
 
 
 def sample_rows(T, n_random=40, seed=0):
@@ -223,11 +232,10 @@ def test_prolog_parity_full_size_sampled_rows(name, T):
     cfg = synth.get_config(name, T=T)
     say("prolog full-size", name, "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
-    out = run_gpu(cfg, inp)
     rows = sample_rows(cfg.T)
     rows = np.union1d(rows, [r for r in (255, 256, 511, 512, 767, 768) if r < cfg.T]).astype(np.int32)
-    stats = check_prolog(cfg, inp, out, rows=rows)
-    say("  rows", len(rows), {k: round(v, 4) for k, v in stats.items()})
+    out, stats = run_checked(cfg, inp, rows=rows)
+    say("  rows", len(rows), fmt(stats))
     # every row with a nonzero amax reaches |code| = 127
     if "q_i8" in out:
         assert (out["q_i8"].abs().reshape(cfg.T, -1).amax(1) == 127).all()
@@ -287,20 +295,18 @@ def test_zero_tokens_give_zero_outputs_and_zero_scales():
     x[3] = 0
     x[7] = 0
     inp["x"] = x
-    out = run_gpu(cfg, inp)
+    out, _ = run_checked(cfg, inp)
     for k in ("q_nope", "q_pe", "kv_norm", "k_pe", "q_i8", "kv_i8"):
         assert not out[k][[3, 7]].float().abs().sum().item(), k
     assert out["q_scale"][[3, 7]].abs().sum().item() == 0
     assert out["kv_scale"][[3, 7]].abs().sum().item() == 0
-    check_prolog(cfg, inp, out)
 
 
 def test_last_table_position_and_t_max():
     cfg = synth.get_config("v2lite_kv_decode", T=5)
     inp = synth.make_inputs(cfg)
     inp["positions"] = torch.full((5,), cfg.max_pos - 1, dtype=torch.int32)
-    out = run_gpu(cfg, inp, t_max=5)
-    check_prolog(cfg, inp, out)
+    run_checked(cfg, inp, t_max=5)
 
 
 def test_subset_of_outputs_and_repeatability():
@@ -324,10 +330,10 @@ def test_q_norm_output_matches_oracle():
     cfg = synth.get_config("v3_decode", T=20)
     inp = synth.make_inputs(cfg)
     p = mlap.Prolog.from_config(cfg)
-    outs = p.alloc_outputs(cfg.T, want=["q_norm", "q_nope", "q_pe", "q_i8", "q_scale"])
-    p.run(to_dev(inp), outputs=outs)
-    torch.cuda.synchronize()
-    check_prolog(cfg, inp, outs)
+    outs, outs0 = run_staged(p, cfg, to_dev(inp),
+                             outputs=p.alloc_outputs(cfg.T, want=["q_norm", "q_nope", "q_pe", "q_i8",
+                                                                  "q_scale", "a_proj"]))
+    check_prolog(cfg, inp, outs, outs0)
 
 
 def test_empty_batch_is_a_noop():
@@ -358,7 +364,6 @@ def test_prolog_variants_large_batch_sampled_rows(name, T, var):
     cfg = synth.get_config(name, T=T, **var)
     say("variants, sampled rows", name, "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
-    out = run_gpu(cfg, inp)
-    stats = check_prolog(cfg, inp, out, rows=sample_rows(cfg.T, n_random=24))
-    say("  bit-exact fractions / excused rows:", {k: round(v, 4) for k, v in stats.items()})
+    out, stats = run_checked(cfg, inp, rows=sample_rows(cfg.T, n_random=24))
+    say("  bit-exact fractions / excused rows / e2e (inside, worst):", fmt(stats))
 
