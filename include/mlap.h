@@ -211,6 +211,22 @@ MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes);
 MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
              void* ws, size_t ws_bytes);
 
+/*
+ * mlap_run for callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, with the library's own device scratch in
+ * place of the caller's workspace. That scratch is one array of MLAP_STATIC_SCRATCH_BYTES
+ * (64 MiB) per GPU, part of the library's code object: it is loaded with the library on each GPU
+ * the library runs on and held until the process ends. A run whose mlap_workspace_size exceeds
+ * it returns MLAP_ERR_WORKSPACE (V3 bf16: up to T = 8192 fits). Nothing here allocates: no
+ * device or host buffer, stream or event (large W8A8 batches therefore run their q quant on
+ * `stream` after the projection instead of on the second stream mlap_run uses). Every call on
+ * one GPU shares that GPU's array, from any handle: calls that overlap in time on one GPU race
+ * and give wrong results; order them on one stream or serialise them. No run needs the array
+ * cleared (each run writes every workspace byte it reads).
+ */
+#define MLAP_STATIC_SCRATCH_BYTES (64u << 20)
+MLAP_API int mlap_run_static(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out);
+
 /* Free the handle (host memory, timing events and its second stream). NULL is allowed. */
 MLAP_API void mlap_destroy(mlap_handle h);
 

@@ -30,8 +30,9 @@ MLAP_QUANT_Q_PER_HEAD = 0x8  # q codes / scales per (token, head)
 MLAP_Q_HEAD_NORM = 0x10      # RMSNorm of every q head after q_b (the V4-shape prolog)
 MLAP_MXFP8 = 0x20            # E4M3 weights with E8M0 scales per 32 of K; MX-converted activations
 MLAP_MXFP8_MFMA = 0x40       # ... on the block-scaled MFMA (hardware sums, not exact)
+MLAP_STATIC_SCRATCH_BYTES = 64 << 20  # device scratch per GPU behind mlap_run_static
 
-EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_destroy", "mlap_status_str",
+EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_run_static", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_gemm_mxfp8_f32", "mlap_timing_begin", "mlap_timing_end",
            "mlap_kernel_name", "mlap_version")
 
@@ -82,6 +83,7 @@ def _load():
     lib.mlap_workspace_size.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]
     lib.mlap_run.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(_Inputs), C.POINTER(_Outputs),
                              C.c_void_p, C.c_size_t]
+    lib.mlap_run_static.argtypes = [C.c_void_p, C.c_void_p, C.POINTER(_Inputs), C.POINTER(_Outputs)]
     lib.mlap_destroy.argtypes = [C.c_void_p]
     lib.mlap_destroy.restype = None
     lib.mlap_status_str.argtypes = [C.c_int]
@@ -282,7 +284,8 @@ class Prolog:
         self._check_shapes(outputs, T, i.cache_slots)
         o = _Outputs(**{k: _ptr(outputs.get(k), _DTYPES.get(k, torch.bfloat16), k)
                         for k in OUTPUTS + CACHES + TAPS})
-        ws = self.workspace(T, device=x.device) if workspace is None else workspace
+        # workspace False: none (mlap_run_static); None: the cached one, grown on demand
+        ws = None if workspace is False else self.workspace(T, device=x.device) if workspace is None else workspace
         return i, o, ws, outputs
 
     def run(self, inputs, outputs=None, workspace=None, stream=None):
@@ -296,6 +299,14 @@ class Prolog:
         _check(_lib.mlap_run(self._h, _stream(stream), C.byref(i), C.byref(o),
                              C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel() * ws.element_size())),
                "mlap_run")
+        return outputs
+
+    def run_static(self, inputs, outputs=None, stream=None):
+        """The same run through mlap_run_static: no workspace and no allocation in the library
+        (its device scratch of MLAP_STATIC_SCRATCH_BYTES per GPU is shared by every call on that
+        GPU, so overlapping calls race). Returns the outputs dict."""
+        i, o, _, outputs = self._marshal(inputs, outputs, workspace=False)
+        _check(_lib.mlap_run_static(self._h, _stream(stream), C.byref(i), C.byref(o)), "mlap_run_static")
         return outputs
 
     def bind(self, inputs, outputs=None, workspace=None, stream=None):

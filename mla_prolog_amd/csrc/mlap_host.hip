@@ -15,12 +15,16 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mlap.h"
 #include "launch.hpp"
 
 using namespace mlap;
+
+// Workspace of mlap_run_static (see static_scratch below).
+static __device__ __align__(256) char scratch[size_t(MLAP_STATIC_SCRATCH_BYTES)];
 
 namespace {
 
@@ -350,6 +354,36 @@ int validate(const mlap_config* c) {
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out, void* ws,
+             size_t ws_bytes, bool may_fork);
+
+// The allocation-free entry point's workspace: a device array of kStaticScratchBytes in every
+// GPU's copy of this code object. Host code must never pass `scratch` itself to a kernel or a
+// copy (it names a host-side stand-in); it uses the per-device address from static_scratch().
+// Nothing in the prolog needs its workspace cleared: every byte a run reads, the same run wrote
+// first (the down-projection output and its split-K partials, q_norm / kv_norm, the per-tile
+// partial amax, the int8 and MX activations), so the contents a previous call left are inert.
+constexpr size_t kStaticScratchBytes = size_t(MLAP_STATIC_SCRATCH_BYTES);
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device.
+int static_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MLAP_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MLAP_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLAP_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *ptr = g_scratch_addr[dev];
+    return MLAP_OK;
+}
+
 // A tensor pointer the kernels cannot use: the 16-byte vector accesses and global->LDS copies
 // need 16-byte alignment (NULL passes: optional tensors are checked separately).
 inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
@@ -451,6 +485,30 @@ MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n) 
 
 MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
              void* ws, size_t ws_bytes) {
+    return run_impl(h, stream, in, out, ws, ws_bytes, true);
+}
+
+// The allocation-free run: the workspace is the file-scope device array `scratch` (one per GPU,
+// loaded with the library and held until the process ends), reached through its device address,
+// which hipGetSymbolAddress gives once per device (in host code the array's name is a host-side
+// stand-in, not a device address). No call here allocates: no buffer, stream or event.
+MLAP_API int mlap_run_static(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out) {
+    if (!h || !in || !out) return MLAP_ERR_INVALID_ARG;
+    if (in->T < 0 || in->T > h->cfg.t_max) return MLAP_ERR_INVALID_ARG;
+    if (in->T == 0) return MLAP_OK;
+    if (h->layout(in->T).total > kStaticScratchBytes) return MLAP_ERR_WORKSPACE;  // beyond the array
+    void* ptr = nullptr;
+    const int rc = static_scratch(&ptr);
+    if (rc != MLAP_OK) return rc;
+    return run_impl(h, stream, in, out, ptr, kStaticScratchBytes, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out, void* ws,
+             size_t ws_bytes, bool may_fork) {
     if (!h || !in || !out) return MLAP_ERR_INVALID_ARG;
     const mlap_config& c = h->cfg;
     const int T = in->T;
@@ -736,7 +794,8 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
         // Only the int8 projection gains from the overlap: it is twice as fast per FLOP, so
         // its quant is a larger share of the step; the bf16 projection slows under the
         // concurrent quant by about what the overlap saves (measured at T=8192).
-        const bool blocks = quant_q && w8 && plan.big_q && plan.q_shape == BigShape::kWide && T >= kQBlockMinT;
+        const bool blocks = may_fork && quant_q && w8 && plan.big_q && plan.q_shape == BigShape::kWide &&
+                            T >= kQBlockMinT;
         if (!blocks) {
             MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
                                               : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
@@ -866,6 +925,10 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
 #undef MLAP_LAUNCH
     return MLAP_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 MLAP_API int mlap_gemm_i8_i32(void* stream, const int8_t* A, const int8_t* B, int32_t* C, int32_t M,
                      int32_t N, int32_t K) {

@@ -294,3 +294,22 @@ def test_binding_checks_shapes_against_the_configuration():
             p._check_shapes(bad, 8, 0)
     ph = mlap.Prolog.from_config(synth.get_config("v3_decode", T=8, q_quant_per_head=True))
     assert ph._shapes(8)["q_scale"] == (8, 128)
+
+
+def test_run_static_checks_before_touching_the_device():
+    """mlap_run_static rejects a missing handle, a batch past t_max and a batch whose workspace
+    exceeds its fixed scratch before any device call (fake pointers, never dereferenced)."""
+    rc, h = create(t_max=16384)
+    assert rc == 0
+    fake = 0x10000
+    full = dict(T=16384, **{k: fake for k in _IN_PTRS})
+    need = C.c_size_t()
+    assert lib.mlap_workspace_size(h, 16384, C.byref(need)) == 0
+    assert need.value > mlap.MLAP_STATIC_SCRATCH_BYTES
+    run = lambda i: lib.mlap_run_static(h, None, C.byref(mlap._Inputs(**i)), C.byref(mlap._Outputs(kv_norm=fake)))
+    assert run(full) == mlap.MLAP_ERR_WORKSPACE
+    assert run(dict(full, T=16385)) == mlap.MLAP_ERR_INVALID_ARG
+    assert run(dict(full, T=0)) == mlap.MLAP_OK
+    assert lib.mlap_run_static(None, None, C.byref(mlap._Inputs(**full)),
+                               C.byref(mlap._Outputs(kv_norm=fake))) == mlap.MLAP_ERR_INVALID_ARG
+    lib.mlap_destroy(h)
