@@ -277,6 +277,14 @@ MLAP_API int mlap_gemm_mxfp8_f32(void* stream, const uint8_t* A, const uint8_t* 
 MLAP_API int mlap_timing_begin(mlap_handle h, int32_t kernel_id, int32_t max_launches);
 MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n);
 
+/* Shader clock of the timed kernel (measurement support): while timing is armed, every
+ * launch of the armed kernel that runs on the LDS-DMA GEMM (gemm_down, gemm_up_q, gemm_up_kv
+ * past the weight-streaming batches or on its tiles) adds, per workgroup, the shader-clock
+ * cycles and the constant 100 MHz clock ticks it ran for into counters[0] and counters[1]
+ * (device memory, two uint64, caller-owned, zeroed by the caller; 8-byte aligned). Their ratio
+ * times 100 MHz is the average shader clock while that kernel ran. NULL disarms. */
+MLAP_API int mlap_timing_clock(mlap_handle h, unsigned long long* counters);
+
 /* Name of kernel `kernel_id` ("gemm_down", "norm_rope", "gemm_up_q", ...), or NULL
  * past the last one. */
 MLAP_API const char* mlap_kernel_name(int32_t kernel_id);

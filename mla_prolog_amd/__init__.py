@@ -34,6 +34,7 @@ MLAP_STATIC_SCRATCH_BYTES = 64 << 20  # device scratch per GPU behind mlap_run_s
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_run_static", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_gemm_mxfp8_f32", "mlap_timing_begin", "mlap_timing_end",
+           "mlap_timing_clock",
            "mlap_kernel_name", "mlap_version")
 
 
@@ -94,6 +95,7 @@ def _load():
     lib.mlap_timing_begin.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
     lib.mlap_timing_end.argtypes = [C.c_void_p, C.POINTER(C.c_float), C.c_int32,
                                     C.POINTER(C.c_int32)]
+    lib.mlap_timing_clock.argtypes = [C.c_void_p, C.c_void_p]
     lib.mlap_kernel_name.argtypes = [C.c_int32]
     lib.mlap_kernel_name.restype = C.c_char_p
     lib.mlap_version.restype = C.c_char_p
@@ -319,6 +321,12 @@ class Prolog:
     def timing_begin(self, kernel, max_launches):
         kid = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
         _check(_lib.mlap_timing_begin(self._h, kid, int(max_launches)), "mlap_timing_begin")
+
+    def timing_clock(self, counters):
+        """Arm (a CUDA int64 tensor of 2, zeroed) or disarm (None) the shader-clock counters of
+        the timed kernel; after the run, counters[0] / counters[1] * 100 is its clock in MHz."""
+        ptr = None if counters is None else _ptr(counters, torch.int64, "counters")
+        _check(_lib.mlap_timing_clock(self._h, ptr), "mlap_timing_clock")
 
     def timing_end(self, cap=100000):
         buf = (C.c_float * cap)()

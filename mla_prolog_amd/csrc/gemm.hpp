@@ -73,6 +73,9 @@ struct GemmArgs {
     const uint8_t* a_mx;
     const uint8_t* b_mx0;
     const uint8_t* b_mx1;
+    // Measurement (LDS-DMA kernel): when set, every workgroup adds the shader-clock cycles
+    // and the 100 MHz constant-clock ticks it ran for to clk[0] and clk[1].
+    unsigned long long* clk;
 };
 
 // Weight row (and per-channel scale) feeding output column n of this launch, relative to

@@ -539,6 +539,11 @@ template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     using SH = big::Shape<BM, BN, WM, WN, KB, S>;
     using Op = MfmaOp<Tin>;
+    unsigned long long clk0 = 0, wall0 = 0;  // measurement only (g.clk)
+    if (g.clk) {
+        clk0 = clock64();
+        wall0 = wall_clock64();
+    }
     // MXFP8: a k-step is one 64-deep block-scaled MFMA, 64 bytes of every row, read as two
     // 16-byte chunks per lane
     constexpr bool MX = kIsMx<Tin>;
@@ -843,6 +848,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     if (EARLY && nk == 0) rope_ops.gather(g, lh);
 
     tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, m0, n0, n_tile, split, rope_ops);
+    if (g.clk && threadIdx.x == 0) {
+        atomicAdd(g.clk, clock64() - clk0);
+        atomicAdd(g.clk + 1, wall_clock64() - wall0);
+    }
 }
 
 }  // namespace mlap

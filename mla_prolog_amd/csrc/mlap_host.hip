@@ -101,6 +101,7 @@ struct Timer {
     int32_t cap = 0;
     int32_t used = 0;
     std::vector<hipEvent_t> ev;  // 2 per launch
+    unsigned long long* clk = nullptr;  // shader-clock counters of the timed kernel, or null
 };
 
 // Workspace carve-up for T tokens.
@@ -306,6 +307,11 @@ struct mlap_prolog {
         return L;
     }
 
+    // the clock counters for a launch of kernel k (while it is the timed one)
+    unsigned long long* clock_for(int32_t k) const {
+        return (timer.kernel == k && timer.used < timer.cap) ? timer.clk : nullptr;
+    }
+
     void tick(int32_t k, hipStream_t s, bool begin) {
         Timer& tm = timer;
         if (tm.kernel != k || tm.used >= tm.cap) return;
@@ -457,6 +463,12 @@ MLAP_API int mlap_timing_begin(mlap_handle h, int32_t kernel_id, int32_t max_lau
     tm.kernel = kernel_id;
     tm.cap = max_launches;
     tm.used = 0;
+    return MLAP_OK;
+}
+
+MLAP_API int mlap_timing_clock(mlap_handle h, unsigned long long* counters) {
+    if (!h || (reinterpret_cast<uintptr_t>(counters) & 7)) return MLAP_ERR_INVALID_ARG;
+    h->timer.clk = counters;
     return MLAP_OK;
 }
 
@@ -626,6 +638,7 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
     }
     g.k_splits = plan.down_splits;
     g.group_m = kGroupM;
+    g.clk = h->clock_for(kKGemmDown);
     g.out = a1;
     g.ldo = h->N1;
     if (w8) {
@@ -754,6 +767,7 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
         u.group_m = kGroupM;
         u.n_major = 1;   // B (75 MB at V3) dwarfs A: give each XCD a 1/8 share of B
         u.group_m = kGroupNq;
+        u.clk = h->clock_for(kKGemmUpQ);
         u.head_w = h->QH;
         u.d0 = c.nope_dim;
         u.d1 = R;
@@ -877,6 +891,7 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
         u.b_split = u.N;
         u.k_splits = 1;
         u.group_m = kGroupM;
+        u.clk = h->clock_for(kKGemmUpKv);
         u.head_w = h->KH;
         u.d0 = c.nope_dim;
         u.d1 = c.v_dim;

@@ -109,6 +109,8 @@ def load():
                                               C.POINTER(_Taps)]
             lib.orc_prolog_staged.restype = C.c_int
             lib.orc_num_threads.restype = C.c_int
+            lib.orc_set_num_threads.argtypes = [C.c_int]
+            lib.orc_set_num_threads.restype = None
             _lib = lib
     return _lib
 
@@ -135,6 +137,11 @@ def _np(t, dtype=None):
 
 def num_threads() -> int:
     return int(load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on."""
+    load().orc_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------- pieces ----

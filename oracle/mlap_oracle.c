@@ -577,6 +577,17 @@ ORC_API int orc_cache_scatter(const int32_t* slots, int32_t T, int32_t n_slots, 
     return 0;
 }
 
+/* Threads the OpenMP loops use from now on (the CPU-baseline timing runs the oracle on all
+ * host cores and on one). */
+ORC_API void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 ORC_API int orc_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);
