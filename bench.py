@@ -212,14 +212,20 @@ def roofline_for(cfg, T, k, workload):
     ach = rate(k_ms)
     out = {"bound": "mfma" if mfma else "hbm", "achieved": round(ach, 2 if mfma else 1), "peak": peak,
            "unit": ("TOP/s" if cfg.w8a8 else "TFLOP/s") if mfma else "GB/s", "frac": round(ach / peak, 4),
-           "traffic": prof.get("hbm_bytes_per_launch") if prof else None, "kernel": kernel,
+           "traffic": None, "kernel": kernel,
            "kernel_ms": round(k_ms, 5), "kernel_ms_trace": None, "frac_trace": None, "sclk_mhz": sclk,
            "algorithmic_flops": flops, "algorithmic_bytes": byts}
     if prof and prof.get("trace_us_avg"):
-        t_ms = prof["trace_us_avg"] / 1e3
-        out["kernel_ms_trace"] = {"avg": round(t_ms, 5), "median": round(prof["trace_us_median"] / 1e3, 5),
-                                  "summary": prof.get("summary")}
+        # FLOPs, bytes and times are per step; a kernel launched once per token block
+        # (launches_per_step > 1) adds its launches up
+        n = prof.get("launches_per_step", 1)
+        t_ms = n * prof["trace_us_avg"] / 1e3
+        out["launches_per_step"] = n
+        out["kernel_ms_trace"] = {"avg": round(t_ms, 5), "median": round(n * prof["trace_us_median"] / 1e3, 5),
+                                  "sclk_mhz_traced": prof.get("sclk_mhz_traced"), "summary": prof.get("summary")}
         out["frac_trace"] = round(rate(t_ms) / peak, 4)
+        if prof.get("hbm_bytes_per_launch"):
+            out["traffic"] = n * prof["hbm_bytes_per_launch"]
     return out
 
 
@@ -280,31 +286,33 @@ def short_kernel(name):
     """Readable kernel name: drop the namespace, the argument list and spell bf16."""
     n = name.replace("void ", "").replace("mlap::", "").replace("unsigned short", "bf16")
     n = n.replace("signed char", "int8").replace("(Epi)", "Epi")
-    return n.split("(GemmArgs")[0].split("(NormArgs")[0].split("(QuantQArgs")[0].strip()
+    for arg in ("(GemmArgs", "(NormArgs", "(QuantQArgs", "(QHeadNormArgs", "(bf16 const*"):
+        n = n.split(arg)[0]
+    return n.strip()
 
 
 def summarize(a):
-    """rocprofv3 CSVs -> a markdown summary (trace statistics and per-dispatch counters, HBM
-    bytes scaled by the calibration copy/fill of the same run) and the workload's entry in
-    profiles/roofline_inputs.json (for the dominant kernel, matched by ``--dominant``)."""
+    """rocprofv3 CSVs -> a markdown summary and the workload's entry in
+    profiles/roofline_inputs.json (for the dominant kernel, matched by ``--dominant``).
+
+    The summary gives, per kernel: the trace statistics; HBM bytes per dispatch from
+    FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter read for the largest
+    calibration dispatch of its run (a device copy of --calibrate-mib MiB for FETCH_SIZE, a
+    fill of as many bytes for WRITE_SIZE); the MFMA pipe's busy share, SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over the 1024 SIMDs) over the trace median at the shader clock measured in the
+    traced run (--sclk-mhz); the L2 hit rate; LDS bank-conflict cycles per LDS instruction;
+    and the raw per-dispatch averages of every counter."""
     import csv
     import statistics
     from collections import defaultdict
 
     lines = ["# %s" % a.title, "", "Commands (from the repository root on the MI355X box):", ""]
     lines += ["    " + c for c in a.command]
-    # kernel trace
     dur = defaultdict(list)
     with open(a.trace) as fh:
         for r in csv.DictReader(fh):
             dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in dur.values())
-    lines += ["", "Kernel trace (durations in us; averages include the first, cold launches):", "",
-              "| kernel | calls | avg | median | min | max | % of GPU time |", "|---|---|---|---|---|---|---|"]
-    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
-        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
-            short_kernel(k), len(v), sum(v) / len(v), statistics.median(v), min(v), max(v), 100 * sum(v) / total))
-    # counters: per kernel and counter, the average per dispatch
     cnt = defaultdict(lambda: defaultdict(list))
     for path in a.pmc:
         with open(path) as fh:
@@ -312,58 +320,75 @@ def summarize(a):
                 cnt[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
     avg = {k: {c: sum(x) / len(x) for c, x in d.items()} for k, d in cnt.items()}
     calib = a.calibrate_mib * 1024.0  # KiB the calibration copy reads and the fill writes
-    fscale = wscale = None
-    for k, d in avg.items():
-        if "copyBuffer" in k and "FETCH_SIZE" in d and d["FETCH_SIZE"] > 0:
-            fscale = calib / max(x for x in cnt[k]["FETCH_SIZE"])
-        if "FillFunctor" in k and "WRITE_SIZE" in d and d["WRITE_SIZE"] > 0:
-            wscale = calib / max(x for x in cnt[k]["WRITE_SIZE"])
+
+    def largest(tag, counter):
+        vals = [x for k in cnt if tag in k for x in cnt[k].get(counter, [])]
+        return max(vals) if vals else 0.0
+
+    f_ref, w_ref = largest("copyBuffer", "FETCH_SIZE"), largest("FillFunctor", "WRITE_SIZE")
+    fscale = calib / f_ref if f_ref > 0 else None
+    wscale = calib / w_ref if w_ref > 0 else None
+    ours = [k for k in dur if "mlap::" in k]
+    steps = min(len(dur[k]) for k in ours) if ours else 1
+
+    def hbm(d):
+        if fscale and wscale and "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+            return (d["FETCH_SIZE"] * fscale + d["WRITE_SIZE"] * wscale) * 1024
+        return None
+
+    lines += ["", "Per kernel. Durations in us from the kernel trace (averages include the first, cold "
+              "launches). HBM bytes per dispatch are FETCH_SIZE and WRITE_SIZE scaled by the calibration "
+              "below; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the trace median at %s; L2 hit "
+              "is TCC_HIT / (TCC_HIT + TCC_MISS); LDS conflict is SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS."
+              % ("%d MHz" % a.sclk_mhz if a.sclk_mhz else "(no clock given)"), "",
+              "| kernel | calls | avg | median | % of GPU time | HBM MB / dispatch | MFMA busy | L2 hit | LDS conflict |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        d = avg.get(k, {})
+        med = statistics.median(v)
+        b = hbm(d)
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        mf = "%.1f%%" % (100 * busy / 1024.0 / (med * a.sclk_mhz)) if busy and a.sclk_mhz else ""
+        hit = ("%.1f%%" % (100 * d["TCC_HIT_sum"] / max(1.0, d["TCC_HIT_sum"] + d["TCC_MISS_sum"]))
+               if "TCC_HIT_sum" in d and "TCC_MISS_sum" in d else "")
+        lds = "%.3f" % (d.get("SQ_LDS_BANK_CONFLICT", 0) / d["SQ_INSTS_LDS"]) if d.get("SQ_INSTS_LDS") else ""
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %s | %s | %s | %s |" % (
+            short_kernel(k), len(v), sum(v) / len(v), med, 100 * sum(v) / total,
+            "%.1f" % (b / 1e6) if b is not None else "", mf, hit, lds))
     names = sorted({c for d in avg.values() for c in d})
-    lines += ["", "Counters, average per dispatch (one rocprofv3 --pmc pass per group of counters):", "",
+    lines += ["", "Raw counters, average per dispatch (one rocprofv3 --pmc pass per group of counters; "
+              "FETCH_SIZE and WRITE_SIZE in KiB):", "",
               "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
     for k in sorted(avg, key=lambda k: -sum(dur.get(k, [0]))):
-        if "copyBuffer" in k or "Functor" in k:
-            continue
         lines.append("| `%s` | " % short_kernel(k) + " | ".join(
             ("%.4g" % avg[k][c]) if c in avg[k] else "" for c in names) + " |")
-    derived = ["", "Derived:", ""]
+    lines += ["", "Calibration and derived figures:", ""]
     if fscale:
-        derived.append("- FETCH_SIZE scale %.3f (the %d MiB calibration copy read %.0f KiB), WRITE_SIZE "
-                       "scale %s." % (fscale, a.calibrate_mib, calib / fscale,
-                                      "%.3f" % wscale if wscale else "n/a"))
+        lines.append("- FETCH_SIZE read %.0f KiB for the %d MiB device copy (scale %.3f); WRITE_SIZE read %s "
+                     "KiB for the %d MiB fill (scale %s)." % (
+                         f_ref, a.calibrate_mib, fscale, "%.0f" % w_ref if w_ref else "n/a",
+                         a.calibrate_mib, "%.3f" % wscale if wscale else "n/a"))
     entry = None
-    for k in avg:
-        if a.dominant and a.dominant in k:
-            d = avg[k]
-            v = dur.get(k, [])
-            entry = {"kernel_source_hash": kernel_source_hash(), "kernel_name": short_kernel(k),
-                     "trace_us_avg": round(sum(v) / len(v), 3) if v else None,
-                     "trace_us_median": round(statistics.median(v), 3) if v else None,
-                     "summary": os.path.relpath(a.out, ROOT)}
-            if fscale and wscale and "FETCH_SIZE" in d and "WRITE_SIZE" in d:
-                entry["hbm_bytes_per_launch"] = int((d["FETCH_SIZE"] * fscale + d["WRITE_SIZE"] * wscale) * 1024)
-                derived.append("- %s: HBM %.1f MB per launch (FETCH %.1f MB + WRITE %.1f MB, scaled)." % (
-                    entry["kernel_name"], entry["hbm_bytes_per_launch"] / 1e6, d["FETCH_SIZE"] * fscale * 1.024e-3,
-                    d["WRITE_SIZE"] * wscale * 1.024e-3))
-    for k in avg:
-        d = avg[k]
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and k in dur and "copyBuffer" not in k:
-            us = statistics.median(dur[k])
-            busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0
-            line = "- `%s`: MFMA busy %.0f cycles per SIMD per dispatch" % (short_kernel(k), busy)
-            if a.sclk_mhz:
-                line += ", %.1f%% of the %.1f us trace median at %d MHz" % (
-                    100 * busy / (us * a.sclk_mhz), us, a.sclk_mhz)
-            if d.get("SQ_INSTS_LDS"):
-                line += "; LDS bank-conflict cycles per LDS instruction %.3f" % (
-                    d.get("SQ_LDS_BANK_CONFLICT", 0) / d["SQ_INSTS_LDS"])
-            if d.get("TCC_HIT_sum") is not None and d.get("TCC_MISS_sum") is not None:
-                line += "; L2 hit rate %.1f%%" % (100 * d["TCC_HIT_sum"] / max(1.0, d["TCC_HIT_sum"] + d["TCC_MISS_sum"]))
-            derived.append(line + ".")
+    dom = [k for k in dur if a.dominant and a.dominant in k]
+    if dom:
+        k = dom[0]
+        v = dur[k]
+        per_step = len(v) / steps
+        entry = {"kernel_source_hash": kernel_source_hash(), "kernel_name": short_kernel(k),
+                 "launches_per_step": round(per_step),
+                 "trace_us_avg": round(sum(v) / len(v), 3), "trace_us_median": round(statistics.median(v), 3),
+                 "summary": os.path.relpath(a.out, ROOT), "sclk_mhz_traced": a.sclk_mhz}
+        b = hbm(avg.get(k, {}))
+        if b is not None:
+            entry["hbm_bytes_per_launch"] = int(b)
+            lines.append("- Dominant kernel `%s`: %d launch(es) per step, trace average %.2f us, median %.2f us; "
+                         "HBM %.1f MB per launch (FETCH %.1f MB + WRITE %.1f MB, scaled)." % (
+                             entry["kernel_name"], entry["launches_per_step"], entry["trace_us_avg"],
+                             entry["trace_us_median"], b / 1e6, avg[k]["FETCH_SIZE"] * fscale * 1.024e-3,
+                             avg[k]["WRITE_SIZE"] * wscale * 1.024e-3))
     if a.sclk_mhz:
-        derived.append("- Shader clock %d MHz: measured inside the dominant kernel by bench.py (sclk_mhz) "
-                       "in the run these profiles accompany." % a.sclk_mhz)
-    lines += derived
+        lines.append("- Shader clock %d MHz: measured inside the dominant kernel (clock64 over "
+                     "wall_clock64, summed over its workgroups) by bench.py in the traced run." % a.sclk_mhz)
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     if entry:
@@ -372,9 +397,6 @@ def summarize(a):
                 rec = json.load(fh)
         except (OSError, ValueError):
             rec = {}
-        prev = rec.get(a.workload, {})
-        if "hbm_bytes_per_launch" not in entry and prev.get("kernel_source_hash") == entry["kernel_source_hash"]:
-            entry["hbm_bytes_per_launch"] = prev.get("hbm_bytes_per_launch")
         rec[a.workload] = entry
         with open(PROFILE_INPUTS, "w") as fh:
             json.dump(rec, fh, indent=1, sort_keys=True)
