@@ -19,7 +19,8 @@ import torch  # noqa: F401  -- must precede the library: libmlap binds to torch'
 __all__ = ["Prolog", "MlapError", "gemm_i8_i32", "gemm_bf16", "KERNELS", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_HERE, "libmlap.so")
+# MLAP_LIBRARY names another build of the same library (the sanitizer build of the tests)
+_LIB = os.environ.get("MLAP_LIBRARY") or os.path.join(_HERE, "libmlap.so")
 
 (MLAP_OK, MLAP_ERR_INVALID_ARG, MLAP_ERR_UNSUPPORTED, MLAP_ERR_WORKSPACE, MLAP_ERR_HIP,
  MLAP_ERR_NO_MEMORY) = range(6)

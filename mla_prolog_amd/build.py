@@ -38,9 +38,15 @@ def _run(cmd):
     return r.returncode, "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
 
 
-def build(verbose: bool = False) -> str:
+# AddressSanitizer on the host half only (argument checks, planning, the C ABI); the
+# device code is built as usual. The library then needs the ASan runtime preloaded.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
     """Compile every source to an object in parallel (one hipcc per translation unit), then
-    link the shared library; the objects go to a temporary folder."""
+    link the shared library `out`; the objects go to a temporary folder. With `asan`, the
+    host code is instrumented with AddressSanitizer (ASAN_HOST)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -49,24 +55,25 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmpd, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([HIPCC, *FLAGS, *(ASAN_HOST if asan else []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
         jobs = min(len(cmds), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with ThreadPoolExecutor(jobs) as ex:
             results = list(ex.map(_run, cmds))
-        for (rc, out), src in zip(results, SOURCES):
+        for (rc, log), src in zip(results, SOURCES):
             if rc != 0:
-                raise RuntimeError("hipcc failed on %s:\n%s" % (src, out))
-            if verbose and out.strip():
-                print(out)
-        tmp = LIB + ".tmp%d" % os.getpid()
-        rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+                raise RuntimeError("hipcc failed on %s:\n%s" % (src, log))
+            if verbose and log.strip():
+                print(log)
+        tmp = out + ".tmp%d" % os.getpid()
+        rc, log = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                        *(ASAN_HOST[:2] + ["-shared-libsan"] if asan else []), *objs, "-o", tmp])
         if rc != 0:
-            raise RuntimeError("link failed:\n" + out)
-    os.replace(tmp, LIB)
-    return LIB
+            raise RuntimeError("link failed:\n" + log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

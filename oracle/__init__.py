@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mlap_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MLAP_ORACLE_LIBRARY names another build of the oracle (the sanitizer build of the tests)
+_LIB_PATH = os.environ.get("MLAP_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -27,13 +28,19 @@ CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast
           "-std=c11", "-Wall", "-Wno-unknown-pragmas"]
 
 
-def build(force: bool = True) -> str:
-    """Compile ``liboracle.so`` with gcc (plain C, OpenMP over token rows)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+# UndefinedBehaviorSanitizer, every finding fatal
+UBSAN = ["-fsanitize=undefined", "-fno-sanitize-recover=all", "-g"]
+
+
+def build(force: bool = True, out: str = None, ubsan: bool = False) -> str:
+    """Compile ``liboracle.so`` (or `out`) with gcc (plain C, OpenMP over token rows); with
+    `ubsan`, under UndefinedBehaviorSanitizer."""
+    out = out or _LIB_PATH
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, *(UBSAN if ubsan else []), _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _Cfg(C.Structure):
