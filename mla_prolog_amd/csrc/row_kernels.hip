@@ -832,7 +832,18 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
         const int c = c0 + threadIdx.x + k * kRowThreads;
         if (c < total) store(c, held[k]);
     }
-    for (int c = c0 + threadIdx.x + kHeld * kRowThreads; c < total; c += kRowThreads) store(c, *chunk_at(c));
+    // the rest of the row in batches of four chunks per thread: four loads in flight before
+    // the first store (measured: the quant 4-5% faster at T=8192 and in the W8A8 blocks)
+    int c = c0 + threadIdx.x + kHeld * kRowThreads;
+    for (; c + 3 * kRowThreads < total; c += 4 * kRowThreads) {
+        const uint4 v0 = *chunk_at(c), v1 = *chunk_at(c + kRowThreads), v2 = *chunk_at(c + 2 * kRowThreads),
+                    v3 = *chunk_at(c + 3 * kRowThreads);
+        store(c, v0);
+        store(c + kRowThreads, v1);
+        store(c + 2 * kRowThreads, v2);
+        store(c + 3 * kRowThreads, v3);
+    }
+    for (; c < total; c += kRowThreads) store(c, *chunk_at(c));
 }
 
 // Per-(token, head) INT8 quant of q: each head's [q_nope | q_pe] row on its own (the row
