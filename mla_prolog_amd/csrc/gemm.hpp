@@ -29,7 +29,10 @@
 
 namespace mlap {
 
-enum class Epi : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreI32 = 2, kHeads = 3 };
+// kStoreBf16X: kStoreBf16 for the BN tile columns plus eight extra columns per column
+// tile, g.N + 8 n_tile + [0, 8), from the weight rows of the same index (the 256 x 256 bf16
+// tile only): a narrow column slice that rides on the operand rows already staged.
+enum class Epi : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreI32 = 2, kHeads = 3, kStoreBf16X = 4 };
 
 struct GemmArgs {
     int M, N, K;

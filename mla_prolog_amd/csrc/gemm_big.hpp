@@ -50,7 +50,8 @@ __device__ __forceinline__ int swz(int r) {
 constexpr int epi_pitch(int bn) { return bn * 2 + 16; }
 constexpr int epi_lds(int bm, int bn, int wn) { return bm * epi_pitch(bn) + wn * bm * 4; }
 
-template <int BM, int BN, int WM, int WN, int KB, int S>
+// XR extra weight rows per stage follow the BM + BN tile rows (kStoreBf16X).
+template <int BM, int BN, int WM, int WN, int KB, int S, int XR = 0>
 struct Shape {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;  // per-wave block
@@ -60,7 +61,7 @@ struct Shape {
     static constexpr int ROWS = BM + BN;
     static constexpr int RROWS = NT / LPR;            // rows one workgroup-wide copy round fills
     static constexpr int ROUNDS = ROWS / RROWS;
-    static constexpr int STAGE = ROWS * KB;
+    static constexpr int STAGE = (ROWS + XR) * KB;
     static constexpr int MAIN = S * STAGE;
     static constexpr int EPI = epi_lds(BM, BN, WN);           // staged tile + row amaxes
     static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
@@ -94,6 +95,15 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// v_mfma_f32_16x16x32_bf16: lane l holds row l % 16 of the 16 x 32 first operand and column
+// l % 16 of the 32 x 16 second one, K values 8 (l / 16) + [0, 8) of both; the result's lane
+// l holds rows 4 (l / 16) + [0, 4) of column l % 16 (layout checked on gfx950 with exact
+// small-integer operands).
+__device__ __forceinline__ f32x4 mma16x16x32(const i32x4& a, const i32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
 
 // One 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4); `lds` must be
 // wave-uniform: lane l writes lds + 16 l. A device function rather than a lambda body:
@@ -305,7 +315,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             *reinterpret_cast<uint2*>(smem + row * PITCH + (col + 8 * gq) * 2) = make_uint2(w[2 * gq], w[2 * gq + 1]);
     };
     big::lds_barrier();  // every wave is done reading the last stage
-    if constexpr (EPI == Epi::kStoreBf16) {
+    if constexpr (EPI == Epi::kStoreBf16 || EPI == Epi::kStoreBf16X) {
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
             constexpr int j = decltype(j_c)::value;
             static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
@@ -537,7 +547,13 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
 
 template <typename Tin, int BM, int BN, int WM, int WN, int KB, int S, Epi EPI>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
-    using SH = big::Shape<BM, BN, WM, WN, KB, S>;
+    // kStoreBf16X: XR = 8 extra weight rows per stage (rows BM + BN .. + 7 of the stage), the
+    // eight extra output columns of this column tile; see xcols below
+    constexpr int XR = EPI == Epi::kStoreBf16X ? 8 : 0;
+    static_assert(XR == 0 || (std::is_same<Tin, uint16_t>::value && BM == 256 && WM == 4 && WN == 2 &&
+                              S == 2 && KB == 128),
+                  "extra columns: the 256 x 256 bf16 tile with a two-slot ring only");
+    using SH = big::Shape<BM, BN, WM, WN, KB, S, XR>;
     using Op = MfmaOp<Tin>;
     unsigned long long clk0 = 0, wall0 = 0;  // measurement only (g.clk)
     if (g.clk) {
@@ -622,6 +638,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             }
         });
     }
+    // kStoreBf16X: the extra columns g.N + XR n_tile + [0, XR) come from weight rows of the
+    // same index (through b_row), staged after the tile rows of every stage. The XR rows of
+    // 128 bytes are one wave-wide copy: wave 0 moves them, lane l physical chunk l % 8 of
+    // extra row l / 8.
+    const char* xsrc = nullptr;
+    if constexpr (XR > 0) {
+        const int r = lane >> 3;
+        const int c = (lane & 7) ^ big::swz<KB>(BM + BN + r);
+        const int n = b_row(g, g.N + XR * n_tile + r);
+        const ptrdiff_t ldb_b = static_cast<ptrdiff_t>(g.ldb) * static_cast<ptrdiff_t>(sizeof(Tin));
+        const char* row = n < g.b_split ? static_cast<const char*>(g.B0) + static_cast<ptrdiff_t>(n) * ldb_b
+                                        : static_cast<const char*>(g.B1) + static_cast<ptrdiff_t>(n - g.b_split) * ldb_b;
+        xsrc = row + k0 + c * 16;
+    }
+    auto issue_x = [&](int kt, int slot) __attribute__((always_inline)) {
+        if constexpr (XR > 0) {
+            if (wave == 0) big::copy16_to_lds(xsrc + kphys(kt) * KB, smem + slot * SH::STAGE + (BM + BN) * KB);
+        }
+    };
     // Copy rounds [R0, R1) of stage kt into `slot`.
     auto issue_part = [&](int kt, int slot, auto r0_c, auto r1_c) __attribute__((always_inline)) {
         constexpr int R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
@@ -694,6 +729,41 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 sw[j] = sw_n[j] >> (8 * lh);
             });
         }
+    };
+
+    // kStoreBf16X operands, 16x16x32 MFMA layout (mma16x16x32): the XR extra weight rows as
+    // the first operand (lanes with l % 16 >= 8 repeat rows 0..7; those result rows are
+    // dropped) and this wave's 32 tokens wm TM + 32 wn + [0, 32) as two 16-token groups, for
+    // the two 32-deep halves of a stage; 16-byte chunk 4 h + l / 16 of each row.
+    int xw_rd[2] = {0, 0}, xx_rd[2][2] = {{0, 0}, {0, 0}};
+    f32x4 acc_x[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    i32x4 xw[2], xx[2][2];
+    if constexpr (XR > 0) {
+        const int xq = lane & 15, xk = lane >> 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int wr = BM + BN + (xq & 7);
+            xw_rd[h] = wr * KB + ((4 * h + xk) ^ big::swz<KB>(wr)) * 16;
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const int xr = wm * TM + 32 * wn + 16 * gi + xq;
+                xx_rd[gi][h] = xr * KB + ((4 * h + xk) ^ big::swz<KB>(xr)) * 16;
+            }
+        }
+    }
+    auto xread = [&](const char* base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            xw[h] = *reinterpret_cast<const i32x4*>(base + xw_rd[h]);
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) xx[gi][h] = *reinterpret_cast<const i32x4*>(base + xx_rd[gi][h]);
+        }
+    };
+    auto xmultiply = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) acc_x[gi] = big::mma16x16x32(xw[h], xx[gi][h], acc_x[gi]);
     };
 
     typename Op::acc_t acc[FN][FM];
@@ -784,7 +854,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     if (nk > 0) load_scales(0);
     static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
-        if (s < nk) issue(s, s);
+        if (s < nk) {
+            issue(s, s);
+            issue_x(s, s);
+        }
     });
     constexpr int SPREAD = S == 2 ? 1 : KS;
     constexpr int NR = FN + FM, NM = FN * FM;
@@ -801,6 +874,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         const int cslot = slot == 0 ? S - 1 : slot - 1;
         const int nslot = slot + 1 == S ? 0 : slot + 1;
         const char* base = smem + slot * SH::STAGE;
+        if constexpr (copy) issue_x(kt + S - 1, cslot);  // extra rows (the stage-end wait covers them)
         // the next stage's scales, ahead of this stage's copies (the stage-end wait covers them)
         if (kt + 1 < nk) load_scales(kt + 1);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
@@ -813,6 +887,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             using IF = std::integral_constant<int, FN>;
             big::wait_lgkmcnt0();
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (XR > 0 && ks == 1) {
+                xread(base);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (XR > 0 && ks == 2) {
+                xmultiply();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             pin(f[ks & 1]);
             if constexpr (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
             if constexpr (ks + 1 < KS) {
@@ -848,6 +930,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     if (EARLY && nk == 0) rope_ops.gather(g, lh);
 
     tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, m0, n0, n_tile, split, rope_ops);
+    if constexpr (XR > 0) {
+        // lane l < 32 holds extra columns 4 (l / 16) + [0, 4) of token l % 16 of each group
+        if (lane < 32) {
+            uint16_t* out = static_cast<uint16_t*>(g.out);
+            const int col = g.N + XR * n_tile + 4 * (lane >> 4);
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const int m = m0 + wm * TM + 32 * wn + 16 * gi + (lane & 15);
+                if (m < g.M)
+                    *reinterpret_cast<uint2*>(out + static_cast<size_t>(m) * g.ldo + col) =
+                        make_uint2(big::pack_bf16x2(acc_x[gi][0], acc_x[gi][1]),
+                                   big::pack_bf16x2(acc_x[gi][2], acc_x[gi][3]));
+            }
+        }
+    }
     if (g.clk && threadIdx.x == 0) {
         atomicAdd(g.clk, clock64() - clk0);
         atomicAdd(g.clk + 1, wall_clock64() - wall0);
