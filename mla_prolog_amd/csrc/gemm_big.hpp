@@ -97,12 +97,17 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // v_mfma_f32_16x16x32_bf16: lane l holds row l % 16 of the 16 x 32 first operand and column
-// l % 16 of the 32 x 16 second one, K values 8 (l / 16) + [0, 8) of both; the result's lane
-// l holds rows 4 (l / 16) + [0, 4) of column l % 16 (layout checked on gfx950 with exact
-// small-integer operands).
-__device__ __forceinline__ f32x4 mma16x16x32(const i32x4& a, const i32x4& b, const f32x4& c) {
+// l % 16 of the 32 x 16 second one, K values 8 (l / 16) + [0, 8) of both (one 16-byte chunk);
+// the result's lane l holds rows 4 (l / 16) + [0, 4) of column l % 16 (layout checked on
+// gfx950 with exact small-integer operands).
+__device__ __forceinline__ f32x4 mma16x16(const i32x4& a, const i32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
+}
+// v_mfma_i32_16x16x64_i8: the same lanes, 16 int8 K values 16 (l / 16) + [0, 16) per lane
+// (checked the same way).
+__device__ __forceinline__ i32x4 mma16x16(const i32x4& a, const i32x4& b, const i32x4& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
 // One 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4); `lds` must be
@@ -550,9 +555,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // kStoreBf16X: XR = 8 extra weight rows per stage (rows BM + BN .. + 7 of the stage), the
     // eight extra output columns of this column tile; see xcols below
     constexpr int XR = EPI == Epi::kStoreBf16X ? 8 : 0;
-    static_assert(XR == 0 || (std::is_same<Tin, uint16_t>::value && BM == 256 && WM == 4 && WN == 2 &&
-                              S == 2 && KB == 128),
-                  "extra columns: the 256 x 256 bf16 tile with a two-slot ring only");
+    static_assert(XR == 0 || ((std::is_same<Tin, uint16_t>::value || kIsI8<Tin>) && BM == 256 && WM == 4 &&
+                              WN == 2 && S == 2 && KB == 128),
+                  "extra columns: the 256 x 256 bf16 / int8 tile with a two-slot ring only");
     using SH = big::Shape<BM, BN, WM, WN, KB, S, XR>;
     using Op = MfmaOp<Tin>;
     unsigned long long clk0 = 0, wall0 = 0;  // measurement only (g.clk)
@@ -731,12 +736,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         }
     };
 
-    // kStoreBf16X operands, 16x16x32 MFMA layout (mma16x16x32): the XR extra weight rows as
+    // kStoreBf16X operands, 16 x 16 MFMA layout (mma16x16): the XR extra weight rows as
     // the first operand (lanes with l % 16 >= 8 repeat rows 0..7; those result rows are
     // dropped) and this wave's 32 tokens wm TM + 32 wn + [0, 32) as two 16-token groups, for
     // the two 32-deep halves of a stage; 16-byte chunk 4 h + l / 16 of each row.
     int xw_rd[2] = {0, 0}, xx_rd[2][2] = {{0, 0}, {0, 0}};
-    f32x4 acc_x[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    using XAcc = typename std::conditional<kIsI8<Tin>, i32x4, f32x4>::type;
+    XAcc acc_x[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     i32x4 xw[2], xx[2][2];
     if constexpr (XR > 0) {
         const int xq = lane & 15, xk = lane >> 4;
@@ -763,7 +769,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int gi = 0; gi < 2; ++gi) acc_x[gi] = big::mma16x16x32(xw[h], xx[gi][h], acc_x[gi]);
+            for (int gi = 0; gi < 2; ++gi) acc_x[gi] = big::mma16x16(xw[h], xx[gi][h], acc_x[gi]);
     };
 
     typename Op::acc_t acc[FN][FM];
@@ -931,17 +937,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
 
     tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, m0, n0, n_tile, split, rope_ops);
     if constexpr (XR > 0) {
-        // lane l < 32 holds extra columns 4 (l / 16) + [0, 4) of token l % 16 of each group
+        // lane l < 32 holds extra columns 4 (l / 16) + [0, 4) of token l % 16 of each group;
+        // W8A8 dequantises them like the tile, f32(acc) * (a_scale[m] * b_scale[n])
         if (lane < 32) {
             uint16_t* out = static_cast<uint16_t*>(g.out);
             const int col = g.N + XR * n_tile + 4 * (lane >> 4);
+            float bs[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (kIsI8<Tin>) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nn = b_row(g, col + q);
+                    bs[q] = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
+                }
+            }
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 const int m = m0 + wm * TM + 32 * wn + 16 * gi + (lane & 15);
-                if (m < g.M)
+                if (m < g.M) {
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (kIsI8<Tin>) {
+                            const float sc = g.a_scale[m] * bs[q];
+                            v[q] = static_cast<float>(acc_x[gi][q]) * sc;
+                        } else {
+                            v[q] = acc_x[gi][q];
+                        }
+                    }
                     *reinterpret_cast<uint2*>(out + static_cast<size_t>(m) * g.ldo + col) =
-                        make_uint2(big::pack_bf16x2(acc_x[gi][0], acc_x[gi][1]),
-                                   big::pack_bf16x2(acc_x[gi][2], acc_x[gi][3]));
+                        make_uint2(big::pack_bf16x2(v[0], v[1]), big::pack_bf16x2(v[2], v[3]));
+                }
             }
         }
     }

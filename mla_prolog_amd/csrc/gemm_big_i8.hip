@@ -9,6 +9,7 @@ hipError_t launch_big_i8(const GemmArgs& g, Epi epi, BigTile t, hipStream_t s) {
     switch (t) {
         case BigTile::kWide:
             if (epi == Epi::kStoreBf16) return launch_big_one<T, 256, 256, 4, 2, 2, Epi::kStoreBf16>(g, s);
+            if (epi == Epi::kStoreBf16X) return launch_big_one<T, 256, 256, 4, 2, 2, Epi::kStoreBf16X>(g, s);
             if (epi == Epi::kHeads) return launch_big_one<T, 256, 256, 4, 2, 2, Epi::kHeads>(g, s);
             if (epi == Epi::kStoreI32) return launch_big_one<T, 256, 256, 4, 2, 2, Epi::kStoreI32>(g, s);
             break;

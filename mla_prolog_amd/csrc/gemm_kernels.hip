@@ -39,7 +39,7 @@ bool gemm_big_fits(const GemmArgs& g, InType t, Epi epi, BigShape shape) {
         case BigShape::kWide:
             if (epi == Epi::kStoreBf16) return g.N % 8 == 0 && g.ldo % 8 == 0;
             if (epi == Epi::kStoreBf16X)  // whole column tiles; the output rows hold the extras
-                return t == InType::kBf16 && g.k_splits <= 1 && g.N % kBigTile == 0 &&
+                return t != InType::kFp8 && g.k_splits <= 1 && g.N % kBigTile == 0 &&
                        g.ldo >= g.N + 8 * (g.N / kBigTile) && g.ldo % 4 == 0;
             if (epi == Epi::kStoreI32) return t == InType::kInt8;
             if (epi == Epi::kHeads) {

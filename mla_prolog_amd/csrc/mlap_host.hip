@@ -88,9 +88,9 @@ struct Plan {
     // (the k_pe slice at V3 and V2-Lite widths) run as a split-K GEMM with fp32 partials
     // that the row kernel sums, instead of a second, mostly idle round of tiles.
     int tail_c0 = 0, tail_splits = 0;
-    // ... or, in bf16 when the slice is eight columns per 256-wide tile (the k_pe slice at V3
-    // width: 64 columns over 8 tiles), as eight extra columns of every tile (kStoreBf16X),
-    // from the activation rows already staged: x is read once
+    // ... or, in bf16 and int8 when the slice is eight columns per 256-wide tile (the k_pe
+    // slice at V3 width: 64 columns over 8 tiles), as eight extra columns of every tile
+    // (kStoreBf16X), from the activation rows already staged: x is read once
     bool x_fuse = false;
     BigShape down_shape = BigShape::kWide, q_shape = BigShape::kWide, kv_shape = BigShape::kWide;
     int nt_q = 0;  // per-token partial amax entries of q (N tiles of the q up projection)
@@ -178,12 +178,12 @@ struct mlap_prolog {
                 p.down_epi = Epi::kStoreBf16;
                 p.down_splits = 1;
                 const int c0 = N1 / kBigTile * kBigTile;
-                if (!i8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
+                if (it != InType::kFp8 && c0 > 0 && N1 - c0 == 8 * (c0 / kBigTile)) {
                     p.tail_c0 = c0;
-                    if (it == InType::kBf16 && N1 - c0 == 8 * (c0 / kBigTile))
-                        p.x_fuse = true;
-                    else
-                        p.tail_splits = one_round_splits((T + 255) / 256 * ((N1 - c0) / 64), nk);
+                    p.x_fuse = true;
+                } else if (!i8 && c0 > 0 && c0 < N1 && (N1 - c0) % 64 == 0) {
+                    p.tail_c0 = c0;
+                    p.tail_splits = one_round_splits((T + 255) / 256 * ((N1 - c0) / 64), nk);
                 }
             }
             if (cfg.q_lora > 0) {
@@ -657,9 +657,15 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
         g.a_scale = xs;
         g.b_scale0 = has_q ? in->ws_qa : in->ws_kva;
         g.b_scale1 = in->ws_kva;
-        MLAP_LAUNCH(kKGemmDown, plan.big_down
-                                    ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
-                                    : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
+        if (plan.x_fuse) {  // the k_pe columns as eight extra columns of every 256 x 256 tile
+            g.N = plan.tail_c0;
+            MLAP_LAUNCH(kKGemmDown, launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16X, s));
+            g.N = h->N1;
+        } else {
+            MLAP_LAUNCH(kKGemmDown, plan.big_down
+                                        ? launch_gemm_big(g, InType::kInt8, Epi::kStoreBf16, s)
+                                        : launch_gemm(g, InType::kInt8, plan.down, plan.down_epi, s));
+        }
     } else if (plan.x_fuse) {
         // columns [0, tail_c0) as 256 x 256 tiles, each with eight of [tail_c0, N1) as extras
         g.A = mxd ? static_cast<const void*>(xm) : in->x;
