@@ -352,7 +352,8 @@ def test_empty_batch_is_a_noop():
 
 
 # the variants on the large-batch kernels: the 256 x 256 heads epilogue (late cos/sin in LDS),
-# the split-K tail of the down projection (its column range starts at the k_pe slice), the
+# the k_pe columns of the large-batch down projection (eight extra columns per 256 x 256 tile
+# at V3 width; a split-K tail launch on the block-scaled MXFP8 route and at other widths), the
 # wave-per-token row kernel and the W8A8 token blocks with their forked quant
 @pytest.mark.parametrize("name,T,var", [("v3_prefill", 1000, ALL3), ("v3_prefill", 2048, ALL3),
                                         ("v3_w8a8", 2048, ALL3), ("v4_decode", 1000, {}),
