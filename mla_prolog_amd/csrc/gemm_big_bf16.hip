@@ -32,6 +32,12 @@ hipError_t launch_big_bf16(const GemmArgs& g, Epi epi, BigTile t, hipStream_t s)
         case BigTile::kRem64:
             if (epi == Epi::kStoreBf16) return launch_big_one<T, 64, 64, 2, 1, 3, Epi::kStoreBf16>(g, s);
             break;
+        case BigTile::kSplitK32:
+            if (epi == Epi::kStoreF32) return launch_big_one<T, 32, 64, 1, 1, 3, Epi::kStoreF32>(g, s);
+            break;
+        case BigTile::kNarrowHeads32:
+            if (epi == Epi::kHeads) return launch_big_one<T, 32, 32, 1, 1, 3, Epi::kHeads>(g, s);
+            break;
     }
     return hipErrorInvalidValue;
 }

@@ -10,7 +10,8 @@
 namespace mlap {
 
 // Tiles of the LDS-DMA kernel (gemm_big.hpp): the BigShape families, their 64-row forms for
-// batches of at most 64 tokens, and the 64 x 64 tiles of a ragged column remainder.
+// batches of at most 64 tokens (32-row forms of two of them for at most 32), and the 64 x 64
+// tiles of a ragged column remainder.
 enum class BigTile : int {
     kWide = 0,       // 256 x 256 (bf16, int8: 4 x 2 waves; E4M3: 2 x 2 waves)
     kHalfHead,       // 256 x 96, 4 x 1 waves, 3 stages
@@ -19,7 +20,9 @@ enum class BigTile : int {
     kSplitK64,       // 64 x 64, 2 x 1 waves
     kNarrowHeads,    // 256 x 32, 4 x 1 waves, 3 stages
     kNarrowHeads64,  // 64 x 32, 2 x 1 waves
-    kRem64           // 64 x 64, 2 x 1 waves, 3 stages (column remainder of a kWide launch)
+    kRem64,          // 64 x 64, 2 x 1 waves, 3 stages (column remainder of a kWide launch)
+    kSplitK32,       // 32 x 64, one wave, 3 stages (batches of at most 32 tokens)
+    kNarrowHeads32   // 32 x 32, one wave, 3 stages
 };
 
 // Launch tile `t` with epilogue `epi` on a 1-D grid of tiles x k_splits workgroups; returns

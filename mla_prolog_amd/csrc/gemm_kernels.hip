@@ -98,13 +98,18 @@ hipError_t launch_gemm_big(const GemmArgs& g, InType t, Epi epi, hipStream_t s, 
     if (!gemm_big_fits(g, t, epi, shape)) return hipErrorInvalidValue;
     // Weight-streaming shapes cover the whole batch in one row tile; at most 64 tokens take
     // 64-row tiles (two waves), so no copy bandwidth goes to clamped duplicate rows.
-    const bool m64 = g.M <= 64;
+    // At most 32 tokens take the 32-row (one-wave) forms where they exist (bf16).
+    const bool m64 = g.M <= 64, m32 = g.M <= 32 && t == InType::kBf16;
     BigTile tile = BigTile::kWide;
     switch (shape) {
         case BigShape::kWide: tile = BigTile::kWide; break;
         case BigShape::kHalfHead: tile = m64 ? BigTile::kHalfHead64 : BigTile::kHalfHead; break;
-        case BigShape::kSplitK: tile = m64 ? BigTile::kSplitK64 : BigTile::kSplitK; break;
-        case BigShape::kNarrowHeads: tile = m64 ? BigTile::kNarrowHeads64 : BigTile::kNarrowHeads; break;
+        case BigShape::kSplitK:
+            tile = m32 ? BigTile::kSplitK32 : m64 ? BigTile::kSplitK64 : BigTile::kSplitK;
+            break;
+        case BigShape::kNarrowHeads:
+            tile = m32 ? BigTile::kNarrowHeads32 : m64 ? BigTile::kNarrowHeads64 : BigTile::kNarrowHeads;
+            break;
     }
     return launch_big_typed(g, t, epi, tile, s);
 }
