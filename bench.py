@@ -289,9 +289,7 @@ def short_kernel(name):
     """Readable kernel name: drop the namespace, the argument list and spell bf16."""
     n = name.replace("void ", "").replace("mlap::", "").replace("unsigned short", "bf16")
     n = n.replace("signed char", "int8").replace("(Epi)", "Epi")
-    for arg in ("(GemmArgs", "(NormArgs", "(QuantQArgs", "(QHeadNormArgs", "(bf16 const*"):
-        n = n.split(arg)[0]
-    return n.strip()
+    return n.split("(")[0].strip()  # the argument list goes
 
 
 def summarize(a):
