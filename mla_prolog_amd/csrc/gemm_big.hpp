@@ -96,6 +96,12 @@ __device__ __forceinline__ void lds_barrier() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// One 4-byte-per-lane copy global -> LDS (global_load_lds_dword): lane l writes lds + 4 l
+// (`lds` wave-uniform); lanes outside the exec mask write nothing.
+__device__ __forceinline__ void copy4_to_lds(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(lds), 4, 0, 0);
+}
+
 // v_mfma_f32_16x16x32_bf16: lane l holds row l % 16 of the 16 x 32 first operand and column
 // l % 16 of the 32 x 16 second one, K values 8 (l / 16) + [0, 8) of both (one 16-byte chunk);
 // the result's lane l holds rows 4 (l / 16) + [0, 4) of column l % 16 (layout checked on
@@ -184,10 +190,12 @@ struct RopeOps<0> {
 // 32 j + 8 g + 4 (l / 32) + q of its columns). `smem` must hold
 // big::epi_lds(BM, BN, WN) bytes and be free: every wave is done with the operand stages.
 // EARLY: the cos/sin operands were gathered under the last K-stage (else the epilogue
-// copies the tile's cos/sin rows into LDS while it packs the accumulators).
+// copies the tile's cos/sin rows into LDS while it packs the accumulators). W8A8: `scl`
+// holds the tile's dequantisation scales in LDS, a_scale of rows m0 + [0, BM) then b_scale
+// of columns n0 + [0, BN) (through b_row; rows and columns past the matrix edge clamped).
 template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, bool EARLY, typename AccT, int FN, int FM, int RF>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN][FM], char* smem,
-                                              int m0, int n0, int n_tile, int split,
+                                              const float* scl, int m0, int n0, int n_tile, int split,
                                               RopeOps<RF>& rope_ops) {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -201,35 +209,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     const int mb = m0 + wm * TM + lr;
     const int nb = n0 + wn * TN + 4 * lh;
 
-    // W8A8 dequantisation scales of this lane's rows and columns, fetched in one burst:
-    // a_scale of each of its FM tokens, b_scale of its 4-column runs (float4 when the run
-    // lies inside one weight segment and inside N).
+    // W8A8 dequantisation scales of this lane's rows and columns, from the tile's copy in
+    // LDS: a_scale of each of its FM tokens, b_scale of its 4-column runs.
     constexpr bool DEQ = kIsI8<Tin> && EPI != Epi::kStoreI32;  // int32 export: raw accumulators
     float asc[DEQ ? FM : 1];
     float4 bsc[DEQ ? FN : 1][4];
     if constexpr (DEQ) {
         static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
-            asc[i] = g.a_scale[min(mb + 32 * i, g.M - 1)];
+            asc[i] = scl[min(mb + 32 * i, g.M - 1) - m0];
         });
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
             constexpr int j = decltype(j_c)::value;
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int n = nb + 32 * j + 8 * gq;
-                if (g.pe_w == 0 && n + 3 < g.N && (n + 3 < g.b_split || n >= g.b_split)) {
-                    const float* src = n < g.b_split ? g.b_scale0 + n : g.b_scale1 + (n - g.b_split);
-                    bsc[j][gq] = *reinterpret_cast<const float4*>(src);
-                } else {
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int nn = b_row(g, min(n + q, g.N - 1));
-                        v[q] = nn < g.b_split ? g.b_scale0[nn] : g.b_scale1[nn - g.b_split];
-                    }
-                    bsc[j][gq] = make_float4(v[0], v[1], v[2], v[3]);
-                }
-            }
+            for (int gq = 0; gq < 4; ++gq)
+                bsc[j][gq] = *reinterpret_cast<const float4*>(scl + BM + (nb - n0) + 32 * j + 8 * gq);
         });
     }
 
@@ -571,7 +565,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     constexpr int RPK = MX ? 2 : 1;  // LDS reads per fragment per k-step
     constexpr int TM = SH::TM, TN = SH::TN, FM = SH::FM, FN = SH::FN, KS = MX ? KB / 64 : SH::KS;
     constexpr int ROUNDS = SH::ROUNDS, LPR = SH::LPR;
-    __shared__ __attribute__((aligned(1024))) char smem[SH::LDS];
+    // W8A8: the tile's dequantisation scales (BM + BN floats) follow the stage / epilogue LDS
+    constexpr bool DEQ = kIsI8<Tin> && EPI != Epi::kStoreI32;
+    constexpr int SCL = DEQ ? (BM + BN) * 4 : 0;
+    static_assert(SH::LDS % 16 == 0 && SH::LDS + SCL <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[SH::LDS + SCL];
+    float* const scl = reinterpret_cast<float*>(smem + SH::LDS);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -586,6 +585,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         tile_of(blockIdx.x, tiles_m, tiles_n, g.k_splits, g.group_m, m_tile, n_tile, split);
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
+    // W8A8: the tile's scales go to LDS now, one dword per lane and 64 per wave; the main
+    // loop's first stage wait and barrier cover them (they are the oldest loads)
+    if constexpr (DEQ) {
+        static_assert(BM % 64 == 0 && BN % 64 == 0, "whole waves of scales");
+        for (int c = wave; c < (BM + BN) / 64; c += WM * WN) {
+            const int idx = 64 * c + lane;
+            if (idx < BM) {  // wave-uniform
+                if (m0 + idx < g.M) big::copy4_to_lds(g.a_scale + m0 + idx, scl + 64 * c);
+            } else {
+                const int nn = b_row(g, min(n0 + idx - BM, g.N - 1));
+                big::copy4_to_lds(nn < g.b_split ? g.b_scale0 + nn : g.b_scale1 + (nn - g.b_split), scl + 64 * c);
+            }
+        }
+    }
     // In-register rope operands of the heads epilogue: whether the columns hold a 64-wide
     // rope slice, and if so the tokens' positions now. With one wave per SIMD (a
     // 512-register budget) each wave with a slice gathers its cos/sin values under the last
@@ -935,7 +948,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     }
     if (EARLY && nk == 0) rope_ops.gather(g, lh);
 
-    tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, m0, n0, n_tile, split, rope_ops);
+    tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, scl, m0, n0, n_tile, split, rope_ops);
     if constexpr (XR > 0) {
         // lane l < 32 holds extra columns 4 (l / 16) + [0, 4) of token l % 16 of each group;
         // W8A8 dequantises them like the tile, f32(acc) * (a_scale[m] * b_scale[n])
