@@ -285,6 +285,17 @@ MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n);
  * times 100 MHz is the average shader clock while that kernel ran. NULL disarms. */
 MLAP_API int mlap_timing_clock(mlap_handle h, unsigned long long* counters);
 
+/* Bounds checks of the debug build (the library compiled with MLAP_DEBUG; a test and
+ * development aid, not part of the path): the kernels check their operand rows, K ranges,
+ * output indexes and input positions as they go and set a bit for every check that failed
+ * on the current device, without stopping (the accesses are clamped or guarded anyway).
+ * This call synchronizes the device, stores the bits collected since the last reset in
+ * *flags (0: every check held) and clears them when `reset` is nonzero. Bits: 1 GEMM
+ * activation row, 2 GEMM weight row, 4 GEMM K range, 8 output index, 16 row-kernel index,
+ * 32 q-quant index, 64 an input position outside [0, max_pos) (a precondition of mlap_run
+ * that the kernels clamp). Release builds store 0 and return MLAP_ERR_UNSUPPORTED. */
+MLAP_API int mlap_debug_flags(unsigned int* flags, int32_t reset);
+
 /* Name of kernel `kernel_id` ("gemm_down", "norm_rope", "gemm_up_q", ...), or NULL
  * past the last one. */
 MLAP_API const char* mlap_kernel_name(int32_t kernel_id);

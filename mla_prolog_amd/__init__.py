@@ -16,7 +16,7 @@ import os
 
 import torch  # noqa: F401  -- must precede the library: libmlap binds to torch's HIP runtime
 
-__all__ = ["Prolog", "MlapError", "gemm_i8_i32", "gemm_bf16", "KERNELS", "lib_path", "version"]
+__all__ = ["Prolog", "MlapError", "gemm_i8_i32", "gemm_bf16", "KERNELS", "lib_path", "version", "debug_flags"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # MLAP_LIBRARY names another build of the same library (the sanitizer build of the tests)
@@ -35,7 +35,7 @@ MLAP_STATIC_SCRATCH_BYTES = 64 << 20  # device scratch per GPU behind mlap_run_s
 
 EXPORTS = ("mlap_create", "mlap_workspace_size", "mlap_run", "mlap_run_static", "mlap_destroy", "mlap_status_str",
            "mlap_gemm_i8_i32", "mlap_gemm_bf16", "mlap_gemm_mxfp8_f32", "mlap_timing_begin", "mlap_timing_end",
-           "mlap_timing_clock",
+           "mlap_timing_clock", "mlap_debug_flags",
            "mlap_kernel_name", "mlap_version")
 
 
@@ -97,6 +97,7 @@ def _load():
     lib.mlap_timing_end.argtypes = [C.c_void_p, C.POINTER(C.c_float), C.c_int32,
                                     C.POINTER(C.c_int32)]
     lib.mlap_timing_clock.argtypes = [C.c_void_p, C.c_void_p]
+    lib.mlap_debug_flags.argtypes = [C.POINTER(C.c_uint32), C.c_int32]
     lib.mlap_kernel_name.argtypes = [C.c_int32]
     lib.mlap_kernel_name.restype = C.c_char_p
     lib.mlap_version.restype = C.c_char_p
@@ -112,6 +113,18 @@ def lib_path() -> str:
 
 def version() -> str:
     return _lib.mlap_version().decode()
+
+
+def debug_flags(reset: bool = True):
+    """Bits of the debug build's failed bounds checks on the current device since the last
+    reset (0: none; see mlap_debug_flags in include/mlap.h), or None for a release build."""
+    f = C.c_uint32(0)
+    st = _lib.mlap_debug_flags(C.byref(f), 1 if reset else 0)
+    if st == MLAP_ERR_UNSUPPORTED:
+        return None
+    if st != MLAP_OK:
+        raise MlapError(st, "mlap_debug_flags")
+    return f.value
 
 
 def _kernels():

@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmlap.so")
+# The debug build: the same library with the kernels' bounds checks compiled in (MLAP_DEBUG;
+# mlap_debug_flags reads them). The parity tests run it at ragged batch sizes.
+DEBUG_LIB = os.path.join(HERE, "libmlap_debug.so")
 SOURCES = ["gemm_kernels.hip", "gemm_big_bf16.hip", "gemm_big_i8.hip", "gemm_big_fp8.hip", "gemm_nt.hip",
            "row_kernels.hip", "mlap_host.hip"]
 HEADERS = ["common.hpp", "gemm.hpp", "gemm_big.hpp", "gemm_big_launch.hpp", "gemm_inst.hpp", "launch.hpp"]
@@ -43,10 +46,11 @@ def _run(cmd):
 ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 
 
-def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, asan: bool = False, debug: bool = False) -> str:
     """Compile every source to an object in parallel (one hipcc per translation unit), then
     link the shared library `out`; the objects go to a temporary folder. With `asan`, the
-    host code is instrumented with AddressSanitizer (ASAN_HOST)."""
+    host code is instrumented with AddressSanitizer (ASAN_HOST); with `debug`, the kernels'
+    bounds checks are compiled in (-DMLAP_DEBUG)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -55,7 +59,8 @@ def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmpd, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([HIPCC, *FLAGS, *(ASAN_HOST if asan else []), "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([HIPCC, *FLAGS, *(ASAN_HOST if asan else []), *(["-DMLAP_DEBUG"] if debug else []),
+                         "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
@@ -77,5 +82,5 @@ def build(verbose: bool = False, out: str = LIB, asan: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, out=DEBUG_LIB, debug=True))

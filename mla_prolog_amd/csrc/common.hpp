@@ -119,4 +119,28 @@ __device__ __forceinline__ int clamp_pos(int p, int max_pos) {
     return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
 }
 
+// Bounds checks of the debug build (compiled with MLAP_DEBUG): a failed check sets its bit
+// in *dbg with a vector atomic and the kernel carries on (the access it describes is
+// clamped or guarded anyway); release builds compile the checks away. mlap_debug_flags
+// reads and clears the word.
+enum : unsigned {
+    kDbgARow = 1u,     // GEMM operand row past the activation rows
+    kDbgBRow = 2u,     // GEMM weight row outside the rows the launch may read
+    kDbgK = 4u,        // GEMM K range past the row length
+    kDbgStore = 8u,    // output index past its row or tensor
+    kDbgRow = 16u,     // row-kernel token or column index out of range
+    kDbgQuant = 32u,   // q quant chunk or store index out of range
+    kDbgPos = 64u,     // an input position outside [0, max_pos) (clamped: a precondition)
+};
+#ifdef MLAP_DEBUG
+#define MLAP_CHECK(dbg, cond, bit)                        \
+    do {                                                  \
+        if (!(cond) && (dbg) != nullptr) atomicOr((dbg), (bit)); \
+    } while (0)
+#else
+#define MLAP_CHECK(dbg, cond, bit) \
+    do {                           \
+    } while (0)
+#endif
+
 }  // namespace mlap

@@ -79,6 +79,7 @@ struct GemmArgs {
     // Measurement (LDS-DMA kernel): when set, every workgroup adds the shader-clock cycles
     // and the 100 MHz constant-clock ticks it ran for to clk[0] and clk[1].
     unsigned long long* clk;
+    unsigned int* dbg;  // debug build: bounds-check flags (see MLAP_CHECK), else null
 };
 
 // Weight row (and per-channel scale) feeding output column n of this launch, relative to

@@ -160,7 +160,10 @@ struct RopeOps {
     float4 c[FM][2][4], s[FM][2][4];  // [token fragment][half][column group g]
     __device__ __forceinline__ void fetch_positions(const GemmArgs& g, int mb) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) pos[i] = g.positions[min(mb + 32 * i, g.M - 1)];
+        for (int i = 0; i < FM; ++i) {
+            pos[i] = g.positions[min(mb + 32 * i, g.M - 1)];
+            MLAP_CHECK(g.dbg, pos[i] >= 0 && pos[i] < g.max_pos, kDbgPos);
+        }
     }
     // every token fragment's cos/sin (shapes with registers to hold them)
     __device__ __forceinline__ void gather(const GemmArgs& g, int lh) {
@@ -292,6 +295,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
                         const int n = nb + 32 * j + 8 * gq;
+                        MLAP_CHECK(g.dbg, n >= g.N || (n + 4 <= g.ldo && split < g.k_splits), kDbgStore);
                         if (n < g.N)  // N is a multiple of 4
                             *reinterpret_cast<float4*>(out + static_cast<size_t>(m) * g.ldo + n) =
                                 make_float4(acc[j][i][4 * gq], acc[j][i][4 * gq + 1],
@@ -328,9 +332,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
         for (int idx = tid; idx < BM * CPR; idx += NT) {
             const int row = idx / CPR, c = idx - row * CPR;
             const int m = m0 + row, n = n0 + 8 * c;
-            if (m < g.M && n < g.N)  // N is a multiple of 8
+            if (m < g.M && n < g.N) {  // N is a multiple of 8
+                MLAP_CHECK(g.dbg, n + 8 <= g.ldo, kDbgStore);
                 big::store_nt(out + static_cast<size_t>(m) * g.ldo + n,
                               *reinterpret_cast<const uint4*>(smem + row * PITCH + c * 16));
+            }
         }
     } else if constexpr (EPI == Epi::kHeads) {
         // The heads work is done in registers before the tile is staged. A rope slice is 64
@@ -536,9 +542,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
                 constexpr int p = decltype(p_c)::value;
                 const int row = p * RPP + r_in;
                 const int m = m0 + row;
-                if (row < BM && m < g.M)
+                if (row < BM && m < g.M) {
+                    MLAP_CHECK(g.dbg, h < g.n_heads && dd + 8 <= dw, kDbgStore);
                     big::store_nt(dst + (static_cast<size_t>(m) * g.n_heads + h) * dw + dd,
                                   *reinterpret_cast<const uint4*>(smem + row * PITCH + c * 16));
+                }
             });
         }
     }
@@ -595,6 +603,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 if (m0 + idx < g.M) big::copy4_to_lds(g.a_scale + m0 + idx, scl + 64 * c);
             } else {
                 const int nn = b_row(g, min(n0 + idx - BM, g.N - 1));
+                MLAP_CHECK(g.dbg, nn >= 0 && nn < g.N + XR * tiles_n, kDbgBRow);
                 big::copy4_to_lds(nn < g.b_split ? g.b_scale0 + nn : g.b_scale1 + (nn - g.b_split), scl + 64 * c);
             }
         }
@@ -632,6 +641,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     const int krot = S > 2 ? (n_tile + m_tile) % (nk > 0 ? nk : 1) : 0;
     auto kphys = [&](int kt) __attribute__((always_inline)) { return kt + krot < nk ? kt + krot : kt + krot - nk; };
     const size_t k0 = static_cast<size_t>(split) * kbs;
+    MLAP_CHECK(g.dbg, kbs % KB == 0 && split < g.k_splits && k0 + kbs <= static_cast<size_t>(g.K) * sizeof(Tin), kDbgK);
 
     // Copy sources: round i moves tile row i*RROWS + tid/LPR, physical chunk tid%LPR.
     // Rows past the matrix edge re-read its last row; their results are never stored.
@@ -645,9 +655,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             const int c = (tid % LPR) ^ big::swz<KB>(r);
             if constexpr (i * SH::RROWS < BM) {
                 const int m = min(m0 + r, g.M - 1);
+                MLAP_CHECK(g.dbg, m >= 0 && m < g.M, kDbgARow);
                 src[i] = static_cast<const char*>(g.A) + static_cast<size_t>(m) * lda_b + k0 + c * 16;
             } else {
                 const int n = b_row(g, min(n0 + r - BM, g.N - 1));
+                MLAP_CHECK(g.dbg, n >= 0 && n < g.N + XR * tiles_n, kDbgBRow);
                 const char* row = n < g.b_split
                                       ? static_cast<const char*>(g.B0) + static_cast<ptrdiff_t>(n) * static_cast<ptrdiff_t>(ldb_b)
                                       : static_cast<const char*>(g.B1) +
@@ -665,6 +677,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         const int r = lane >> 3;
         const int c = (lane & 7) ^ big::swz<KB>(BM + BN + r);
         const int n = b_row(g, g.N + XR * n_tile + r);
+        MLAP_CHECK(g.dbg, n >= 0 && n < g.N + XR * tiles_n, kDbgBRow);
         const ptrdiff_t ldb_b = static_cast<ptrdiff_t>(g.ldb) * static_cast<ptrdiff_t>(sizeof(Tin));
         const char* row = n < g.b_split ? static_cast<const char*>(g.B0) + static_cast<ptrdiff_t>(n) * ldb_b
                                         : static_cast<const char*>(g.B1) + static_cast<ptrdiff_t>(n - g.b_split) * ldb_b;
@@ -955,6 +968,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         if (lane < 32) {
             uint16_t* out = static_cast<uint16_t*>(g.out);
             const int col = g.N + XR * n_tile + 4 * (lane >> 4);
+            MLAP_CHECK(g.dbg, col + 4 <= g.ldo, kDbgStore);
             float bs[4] = {1.f, 1.f, 1.f, 1.f};
             if constexpr (kIsI8<Tin>) {
 #pragma unroll

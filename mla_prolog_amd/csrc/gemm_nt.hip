@@ -17,8 +17,10 @@ namespace {
 template <typename Tin, int BM, int BN, int WM, int WN, int P, Epi EPI>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.k_splits;
+    GemmArgs a = g;
+    a.dbg = debug_word();
     hipLaunchKernelGGL((gemm_nt_kernel<Tin, BM, BN, WM, WN, P, EPI>), dim3(tiles),
-                       dim3(kWave * WM * WN), 0, s, g);
+                       dim3(kWave * WM * WN), 0, s, a);
     return hipGetLastError();
 }
 

@@ -8,6 +8,11 @@
 
 namespace mlap {
 
+// The debug build's bounds-check word on the current device (null in release builds); every
+// launcher passes it to its kernels.
+unsigned int* debug_word();
+
+
 enum class InType : int { kBf16 = 0, kInt8 = 1, kFp8 = 2 };  // kFp8: MXFP8 (E4M3 + E8M0 block scales)
 
 // Output tile rows x columns and K-tiles of register prefetch.
@@ -81,6 +86,7 @@ struct NormArgs {
     // diagnostic tap: the down-projection row as read, [T, N1] bf16 (rope slice in rotate-half
     // order), or null
     uint16_t* a_proj;
+    unsigned int* dbg;  // debug build: bounds-check flags (set by the launcher)
 };
 hipError_t launch_norm(const NormArgs& a, hipStream_t s);
 
@@ -99,6 +105,7 @@ struct QuantQArgs {
     float* q_scale;           // [T] or null; [T, H] with per_head
     int per_head;             // one scale per (token, head) instead of per token
     int parts;                // per-token quant: workgroups per token (set by the launcher)
+    unsigned int* dbg;        // debug build: bounds-check flags (set by the launcher)
 };
 // Limits of the per-head q quant (one workgroup holds a token's row).
 constexpr int kMaxQuantHeads = 1024;
@@ -121,6 +128,7 @@ struct QHeadNormArgs {
     float* part_amax;         // [T, groups] or null
     int groups;               // workgroups per token, each a whole-head share (H % groups == 0)
     uint16_t* q_proj;         // diagnostic tap: the raw heads as read, [T, H, Dn+R], or null
+    unsigned int* dbg;        // debug build: bounds-check flags (set by the launcher)
 };
 // Limits of the per-head norm (one workgroup holds a token's q row): H*(Dn+R) <= 32768 and
 // H*R <= 8192 (the rope chunks staged in LDS).

@@ -26,6 +26,12 @@ using namespace mlap;
 // Workspace of mlap_run_static (see static_scratch below).
 static __device__ __align__(256) char scratch[size_t(MLAP_STATIC_SCRATCH_BYTES)];
 
+#ifdef MLAP_DEBUG
+// The debug build's bounds-check word (MLAP_CHECK): each GPU's copy collects the bits of the
+// checks that failed there until mlap_debug_flags reads and clears it.
+static __device__ unsigned int dbg_flags_word;
+#endif
+
 namespace {
 
 enum KernelId : int32_t {
@@ -397,6 +403,33 @@ int static_scratch(void** ptr) {
     return MLAP_OK;
 }
 
+#ifdef MLAP_DEBUG
+std::mutex g_dbg_mu;
+unsigned int* g_dbg_addr[kMaxDevices] = {};
+#endif
+
+}  // namespace
+
+// The bounds-check word of the current device (debug build), looked up once per device; null in
+// release builds or when the lookup fails (the checks are then skipped).
+unsigned int* mlap::debug_word() {
+#ifdef MLAP_DEBUG
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_dbg_mu);
+    if (!g_dbg_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_flags_word)) != hipSuccess) return nullptr;
+        g_dbg_addr[dev] = static_cast<unsigned int*>(p);
+    }
+    return g_dbg_addr[dev];
+#else
+    return nullptr;
+#endif
+}
+
+namespace {
+
 // A tensor pointer the kernels cannot use: the 16-byte vector accesses and global->LDS copies
 // need 16-byte alignment (NULL passes: optional tensors are checked separately).
 inline bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
@@ -471,6 +504,25 @@ MLAP_API int mlap_timing_begin(mlap_handle h, int32_t kernel_id, int32_t max_lau
     tm.cap = max_launches;
     tm.used = 0;
     return MLAP_OK;
+}
+
+MLAP_API int mlap_debug_flags(unsigned int* flags, int32_t reset) {
+    if (!flags) return MLAP_ERR_INVALID_ARG;
+#ifdef MLAP_DEBUG
+    unsigned int* w = mlap::debug_word();
+    if (!w) return MLAP_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return MLAP_ERR_HIP;
+    if (hipMemcpy(flags, w, sizeof(unsigned int), hipMemcpyDeviceToHost) != hipSuccess) return MLAP_ERR_HIP;
+    if (reset) {
+        const unsigned int zero = 0;
+        if (hipMemcpy(w, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return MLAP_ERR_HIP;
+    }
+    return MLAP_OK;
+#else
+    (void)reset;
+    *flags = 0;
+    return MLAP_ERR_UNSUPPORTED;
+#endif
 }
 
 MLAP_API int mlap_timing_clock(mlap_handle h, unsigned long long* counters) {

@@ -208,6 +208,8 @@ __global__ __launch_bounds__(kRowThreads) void norm_rope_kernel(NormArgs a) {
     if ((a.k_pe || a.kr_cache || a.a_proj) && tid < (half >> 3)) {
         const int i0 = tid * 8;
         const int p = clamp_pos(a.positions[t], a.max_pos);
+        MLAP_CHECK(a.dbg, a.positions[t] >= 0 && a.positions[t] < a.max_pos, kDbgPos);
+        MLAP_CHECK(a.dbg, t < a.T && a.Lq + a.Lkv + a.R <= a.N1, kDbgRow);
         const float* cr = a.cos + static_cast<size_t>(p) * a.R;
         const float* sr = a.sin + static_cast<size_t>(p) * a.R;
         float x1[8], x2[8], lo[8], hi[8];
@@ -330,6 +332,8 @@ __device__ __forceinline__ void norm_rope_block_body(const NormArgs& a, float* r
 
     const bool rope = (a.k_pe != nullptr || a.kr_cache != nullptr || a.a_proj != nullptr) && half >= 8;
     const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
+    MLAP_CHECK(a.dbg, !rope || (a.positions[t] >= 0 && a.positions[t] < a.max_pos), kDbgPos);
+    MLAP_CHECK(a.dbg, t < a.T && a.Lq + a.Lkv + a.R <= a.N1 && (cache_r < 0 || cache_r < a.n_slots), kDbgRow);
     const bool roper = rope && tid < (half >> 3);
     const int i0 = rope ? min(tid, (half >> 3) - 1) * 8 : 0;
     float qv[QC > 0 ? QC : 1][8], kv[KC][8], x1[8], x2[8];
@@ -562,6 +566,8 @@ __global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
 
     // ---- one burst of loads: rows, gamma, position, rope inputs
     const int pos = rope ? clamp_pos(a.positions[t], a.max_pos) : 0;
+    MLAP_CHECK(a.dbg, !rope || (a.positions[t] >= 0 && a.positions[t] < a.max_pos), kDbgPos);
+    MLAP_CHECK(a.dbg, a.Lq + a.Lkv + a.R <= a.N1 && (cache_r < 0 || cache_r < a.n_slots), kDbgRow);
     uint4 rq[QC > 0 ? QC : 1], rkv[KC], gq[QC > 0 ? QC : 1], gkv[KC];
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
@@ -825,6 +831,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_q_kernel(QuantQArgs a) {
     auto store = [&](int c, const uint4& v) {
         const int h = c / cph, j = c - h * cph;
         const size_t th = static_cast<size_t>(t) * a.H + h;
+        MLAP_CHECK(a.dbg, t < a.T && h < a.H && (th * QH + j * 8 + 8) <= static_cast<size_t>(a.T) * a.H * QH, kDbgQuant);
         store_nt8(a.q_i8 + th * QH + j * 8, quant8(v, mult));
     };
 #pragma unroll
@@ -918,6 +925,7 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
         return (j < cn) ? a.q_nope + th * a.Dn + j * 8 : a.q_pe + th * a.R + (j - cn) * 8;
     };
     const int p = clamp_pos(a.positions[t], a.max_pos);
+    MLAP_CHECK(a.dbg, a.positions[t] >= 0 && a.positions[t] < a.max_pos, kDbgPos);
     uint4 held[kHeadNormChunks];
 #pragma unroll
     for (int k = 0; k < kHeadNormChunks; ++k)
@@ -996,7 +1004,9 @@ __global__ __launch_bounds__(kRowThreads) void q_head_norm_kernel(QHeadNormArgs 
     }
 }
 
-hipError_t launch_q_head_norm(const QHeadNormArgs& a, hipStream_t s) {
+hipError_t launch_q_head_norm(const QHeadNormArgs& a_in, hipStream_t s) {
+    QHeadNormArgs a = a_in;
+    a.dbg = debug_word();
     if (a.T <= 0) return hipSuccess;
     if (a.H > kMaxQuantHeads || a.H * ((a.Dn + a.R) >> 3) > kHeadNormChunks * kRowThreads ||
         a.H * (a.R >> 3) > kHeadNormPeChunks || (a.R >> 3) % 2)
@@ -1160,7 +1170,9 @@ hipError_t launch_mx_act(const uint16_t* x, int T, int K, uint16_t* out, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_norm(const NormArgs& a, hipStream_t s) {
+hipError_t launch_norm(const NormArgs& a_in, hipStream_t s) {
+    NormArgs a = a_in;
+    a.dbg = debug_word();
     if (a.T <= 0) return hipSuccess;
     const int qc = (a.Lq / 8 + 63) / 64, kc = (a.Lkv / 8 + 63) / 64;
     const dim3 grid((a.T + 3) / 4), block(kRowThreads);
@@ -1202,7 +1214,9 @@ hipError_t launch_act_quant(const uint16_t* x, int T, int K, int8_t* codes, floa
     return hipGetLastError();
 }
 
-hipError_t launch_quant_q(const QuantQArgs& a, hipStream_t s) {
+hipError_t launch_quant_q(const QuantQArgs& a_in, hipStream_t s) {
+    QuantQArgs a = a_in;
+    a.dbg = debug_word();
     if (a.T <= 0) return hipSuccess;
     if (a.per_head) {
         if (a.H > kMaxQuantHeads || a.H * ((a.Dn + a.R) >> 3) > kQuantHeadChunks * kRowThreads)

@@ -313,3 +313,15 @@ def test_run_static_checks_before_touching_the_device():
     assert lib.mlap_run_static(None, None, C.byref(mlap._Inputs(**full)),
                                C.byref(mlap._Outputs(kv_norm=fake))) == mlap.MLAP_ERR_INVALID_ARG
     lib.mlap_destroy(h)
+
+
+def test_debug_flags_in_release_and_debug_builds():
+    """mlap_debug_flags is exported by both builds; the release build reports it unsupported."""
+    if mlap.lib_path().endswith("libmlap_debug.so"):
+        pytest.skip("running against the debug build")
+    assert mlap.debug_flags() is None
+    dbg = os.path.join(os.path.dirname(mlap.lib_path()), "libmlap_debug.so")
+    if os.path.exists(dbg):
+        lib = C.CDLL(dbg)
+        for name in mlap.EXPORTS:
+            getattr(lib, name)
