@@ -340,10 +340,11 @@ def summarize(a):
     lines += ["", "Per kernel. Durations in us from the kernel trace (averages include the first, cold "
               "launches). HBM bytes per dispatch are FETCH_SIZE and WRITE_SIZE scaled by the calibration "
               "below; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the trace median at %s; L2 hit "
-              "is TCC_HIT / (TCC_HIT + TCC_MISS); LDS conflict is SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS."
+              "is TCC_HIT / (TCC_HIT + TCC_MISS); LDS conflict is SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; L2 read "
+              "latency is TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ in cycles (where that pass ran)."
               % ("%d MHz" % a.sclk_mhz if a.sclk_mhz else "(no clock given)"), "",
-              "| kernel | calls | avg | median | % of GPU time | HBM MB / dispatch | MFMA busy | L2 hit | LDS conflict |",
-              "|---|---|---|---|---|---|---|---|---|"]
+              "| kernel | calls | avg | median | % of GPU time | HBM MB / dispatch | MFMA busy | L2 hit | LDS conflict | L2 read latency |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
     for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
         d = avg.get(k, {})
         med = statistics.median(v)
@@ -353,9 +354,11 @@ def summarize(a):
         hit = ("%.1f%%" % (100 * d["TCC_HIT_sum"] / max(1.0, d["TCC_HIT_sum"] + d["TCC_MISS_sum"]))
                if "TCC_HIT_sum" in d and "TCC_MISS_sum" in d else "")
         lds = "%.3f" % (d.get("SQ_LDS_BANK_CONFLICT", 0) / d["SQ_INSTS_LDS"]) if d.get("SQ_INSTS_LDS") else ""
-        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %s | %s | %s | %s |" % (
+        lat = ("%.0f" % (d["TCP_TCC_READ_REQ_LATENCY_sum"] / d["TCP_TCC_READ_REQ_sum"])
+               if d.get("TCP_TCC_READ_REQ_sum") and "TCP_TCC_READ_REQ_LATENCY_sum" in d else "")
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %s | %s | %s | %s | %s |" % (
             short_kernel(k), len(v), sum(v) / len(v), med, 100 * sum(v) / total,
-            "%.1f" % (b / 1e6) if b is not None else "", mf, hit, lds))
+            "%.1f" % (b / 1e6) if b is not None else "", mf, hit, lds, lat))
     names = sorted({c for d in avg.values() for c in d})
     lines += ["", "Raw counters, average per dispatch (one rocprofv3 --pmc pass per group of counters; "
               "FETCH_SIZE and WRITE_SIZE in KiB):", "",
@@ -429,7 +432,7 @@ def main():
                     help="no GPU: turn rocprofv3 CSVs (--trace, --pmc) into --out and the workload's "
                          "entry of profiles/roofline_inputs.json")
     ap.add_argument("--trace", help="rocprofv3 kernel_trace.csv (with --summarize)")
-    ap.add_argument("--pmc", nargs="*", default=[], help="rocprofv3 counter_collection.csv files")
+    ap.add_argument("--pmc", nargs="*", action="extend", default=[], help="rocprofv3 counter_collection.csv files")
     ap.add_argument("--out", help="summary to write (with --summarize)")
     ap.add_argument("--title", default="rocprofv3 summary")
     ap.add_argument("--command", action="append", default=[], help="a command that produced the CSVs")
