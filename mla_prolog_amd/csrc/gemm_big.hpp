@@ -842,46 +842,68 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             big::pin_vgpr(f.x[decltype(i_c)::value]);
         });
     };
-    // MFMAs of weight fragments [J0, J1) against every activation fragment (k-step ks).
-    auto multiply = [&](Frags& f, auto ks_c, auto j0_c, auto j1_c) __attribute__((always_inline)) {
-        constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
-        static_for<J1 - J0>([&](auto j_c) __attribute__((always_inline)) {
-            constexpr int j = J0 + decltype(j_c)::value;
-            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
-                constexpr int i = decltype(i_c)::value;
-                if constexpr (MX)
-                    Op::template mma<2 * decltype(ks_c)::value>(acc[j][i], f.w[j], f.x[i],
-                                                                static_cast<int>(sw[j]), static_cast<int>(sx[i]));
-                else
-                    Op::mma(acc[j][i], f.w[j], f.x[i]);
-            });
-        });
+    // One MFMA (weight fragment idx / FM against activation fragment idx % FM) and one
+    // fragment read (idx < FN: weight fragment idx, else activation fragment idx - FN).
+    auto mma_one = [&](Frags& f, auto ks_c, auto idx_c) __attribute__((always_inline)) {
+        constexpr int idx = decltype(idx_c)::value, j = idx / FM, i = idx % FM;
+        if constexpr (MX)
+            Op::template mma<2 * decltype(ks_c)::value>(acc[j][i], f.w[j], f.x[i], static_cast<int>(sw[j]),
+                                                        static_cast<int>(sx[i]));
+        else
+            Op::mma(acc[j][i], f.w[j], f.x[i]);
     };
-    // Scheduling template for the region just emitted: N MFMAs, after the i-th of which
-    // go the LDS reads of one fragment while i < NR, else one global->LDS copy while
-    // i - NR < NC.
-    auto interleave = [&](auto n_c, auto nr_c, auto nc_c) __attribute__((always_inline)) {
-        constexpr int N = decltype(n_c)::value, NR = decltype(nr_c)::value, NC = decltype(nc_c)::value;
-        static_for<N>([&](auto i_c) __attribute__((always_inline)) {
-            constexpr int i = decltype(i_c)::value;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if constexpr (i < NR)
-                __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);  // DS read(s)
-            else if constexpr (i - NR < NC)
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
-        });
-        __builtin_amdgcn_sched_barrier(0);
+    auto read_one = [&](const char* base, auto ks_c, auto idx_c, Frags& f) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ks_c)::value, idx = decltype(idx_c)::value;
+        if constexpr (idx < FN)
+            f.w[idx] = frag_at(base + idx * 32 * KB, b_rd[ks]);
+        else
+            f.x[idx - FN] = frag_at(base + (idx - FN) * 32 * KB, a_rd[ks]);
     };
 
-    // Stage j goes to slot j % S and is copied S - 1 stages ahead. Every k-step first waits
-    // for its own fragments (read during the previous k-step), then issues the next
-    // k-step's reads and its share of the copy of stage kt + S - 1 between its MFMAs. The
-    // stage barrier sits inside the last k-step, after its first half of MFMAs: it
-    // certifies that stage kt + 1 has landed for every wave (each wave first waits for its
-    // own copies) and that every wave is done reading slot kt % S, which the copy issued
-    // in the next stage reuses; the next stage's first reads then run under the second
-    // half. With two slots the whole copy goes out at the head of the stage, so it has
-    // the most time to land; with more it is spread over the k-steps.
+    // Stage j goes to slot j % S and is copied S - 1 stages ahead. The k-steps are written
+    // as explicit slots: MFMA m, then the fragment reads and copy rounds that fall on slot
+    // m, then a scheduling fence, so the order is the one written here. Every k-step first
+    // waits for its own fragments (read during the previous k-step) and spreads the next
+    // k-step's reads over its slots. The copies of stage kt + S - 1 go out one per slot over
+    // the first CSPAN slots of stage kt: each 1 KB global_load_lds occupies the CU's
+    // address unit for ~16 cycles, so a burst of them at the head of a stage stalls the
+    // issuing wave (in-order issue) and with it the MFMA pipe; one per MFMA keeps the
+    // copies early (two slots leave a stage to land) without that stall. The stage barrier
+    // sits inside the last k-step after half of its MFMAs: it certifies that stage kt + 1
+    // has landed for every wave (each wave first waits for its own copies) and that every
+    // wave is done reading slot kt % S, which the copy issued in the next stage reuses; the
+    // next stage's first reads then run under the second half.
+    constexpr int NR = FN + FM, NM = FN * FM;
+    constexpr int PRE = (KS - 1) * NM + NM / 2;  // MFMA slots of a stage before its barrier
+    constexpr int CSPAN = PRE < 8 ? PRE : 8;  // (small tiles put several copies on a slot)
+    // MFMAs [M0, M0 + N) of k-step ks on fragments fc, stage slots G0 + [0, N); with RD the
+    // NR reads of k-step rks's fragments from rbase into fn, spread over these slots; with
+    // CP the copy rounds of stage ckt into ring slot cslot whose stage slot falls here.
+    auto slots = [&](Frags& fc, auto ks_c, auto m0_c, auto n_c, auto g0_c, auto rd_c, const char* rbase, auto rks_c,
+                     Frags& fn, auto cp_c, int ckt, int cslot) __attribute__((always_inline)) {
+        constexpr int M0 = decltype(m0_c)::value, N = decltype(n_c)::value, G0 = decltype(g0_c)::value;
+        constexpr bool RD = decltype(rd_c)::value, CP = decltype(cp_c)::value;
+        const int koff = kphys(ckt) * KB;
+        char* dst = smem + cslot * SH::STAGE + wave * 1024;
+        static_for<N>([&](auto m_c) __attribute__((always_inline)) {
+            constexpr int m = decltype(m_c)::value;
+            mma_one(fc, ks_c, std::integral_constant<int, M0 + m>{});
+            if constexpr (RD) {
+                static_for<NR>([&](auto r_c) __attribute__((always_inline)) {
+                    constexpr int r = decltype(r_c)::value;
+                    if constexpr ((r * N) / NR == m) read_one(rbase, rks_c, r_c, fn);
+                });
+            }
+            if constexpr (CP) {
+                static_for<ROUNDS>([&](auto c_c) __attribute__((always_inline)) {
+                    constexpr int c = decltype(c_c)::value;
+                    if constexpr ((c * CSPAN) / ROUNDS == G0 + m)
+                        big::copy16_to_lds(src[c] + koff, dst + c * SH::RROWS * KB);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
     // (the first stage's scales go out ahead of the copies, so the waits below cover them)
     if (nk > 0) load_scales(0);
     static_for<S - 1>([&](auto s_c) __attribute__((always_inline)) {
@@ -891,8 +913,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
             issue_x(s, s);
         }
     });
-    constexpr int SPREAD = S == 2 ? 1 : KS;
-    constexpr int NR = FN + FM, NM = FN * FM;
     Frags f[2];
     if (nk > 0) {
         if (nk >= S - 1) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
@@ -900,23 +920,73 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         take_scales();
         read(smem, std::integral_constant<int, 0>{}, f[0]);
     }
+    // MXFP8 k-step (the block-scaled tile: its 32-byte fragments in VGPRs beside 256 AGPRs
+    // of accumulators leave no registers for the slot order, which spills there): the copy
+    // share of this k-step at its head (with two ring slots the whole copy on k-step 0),
+    // then the MFMAs, with scheduling groups that put one fragment read, then one copy,
+    // after each MFMA.
+    auto mma_range = [&](Frags& fc, auto ks_c, auto m0_c, auto n_c) __attribute__((always_inline)) {
+        static_for<decltype(n_c)::value>([&](auto m_c) __attribute__((always_inline)) {
+            mma_one(fc, ks_c, std::integral_constant<int, decltype(m0_c)::value + decltype(m_c)::value>{});
+        });
+    };
+    auto groups = [&](auto n_c, auto nr_c, auto nc_c) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value, NRG = decltype(nr_c)::value, NCG = decltype(nc_c)::value;
+        static_for<N>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if constexpr (i < NRG)
+                __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);  // DS read(s)
+            else if constexpr (i - NRG < NCG)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mx_kstep = [&](int kt, auto ks_c, const char* base, int cslot, int nslot, auto cp_c) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ks_c)::value;
+        constexpr int SPREAD = S == 2 ? 1 : KS;
+        constexpr int r0 = ks < SPREAD ? ROUNDS * ks / SPREAD : ROUNDS;
+        constexpr int r1 = ks < SPREAD ? ROUNDS * (ks + 1) / SPREAD : ROUNDS;
+        constexpr int NC = decltype(cp_c)::value ? r1 - r0 : 0;
+        using I0 = std::integral_constant<int, 0>;
+        if constexpr (NC > 0)
+            issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
+        if constexpr (ks + 1 < KS) {
+            read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
+            mma_range(f[ks & 1], ks_c, I0{}, std::integral_constant<int, NM>{});
+            groups(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{}, std::integral_constant<int, NC>{});
+        } else {
+            mma_range(f[ks & 1], ks_c, I0{}, std::integral_constant<int, NM / 2>{});
+            groups(std::integral_constant<int, NM / 2>{}, I0{}, std::integral_constant<int, NC>{});
+            const bool more = kt + 1 < nk;
+            if (more) {
+                if (decltype(cp_c)::value) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
+                big::lds_barrier();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read(smem + nslot * SH::STAGE, I0{}, f[(ks + 1) & 1]);
+            mma_range(f[ks & 1], ks_c, std::integral_constant<int, NM / 2>{}, std::integral_constant<int, NM - NM / 2>{});
+            groups(std::integral_constant<int, NM - NM / 2>{}, std::integral_constant<int, NR>{}, I0{});
+        }
+    };
     int slot = 0;  // kt % S
     auto stage = [&](int kt, auto copy_c) __attribute__((always_inline)) {
-        constexpr bool copy = decltype(copy_c)::value;
+        using CP = std::integral_constant<bool, decltype(copy_c)::value>;
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        using I0 = std::integral_constant<int, 0>;
+        using IH = std::integral_constant<int, NM / 2>;
+        using IR = std::integral_constant<int, NM - NM / 2>;
+        using INONE = std::integral_constant<int, PRE>;  // stage slots past every copy
         const int cslot = slot == 0 ? S - 1 : slot - 1;
         const int nslot = slot + 1 == S ? 0 : slot + 1;
         const char* base = smem + slot * SH::STAGE;
-        if constexpr (copy) issue_x(kt + S - 1, cslot);  // extra rows (the stage-end wait covers them)
+        if constexpr (CP::value) issue_x(kt + S - 1, cslot);  // extra rows (the stage-end wait covers them)
         // the next stage's scales, ahead of this stage's copies (the stage-end wait covers them)
         if (kt + 1 < nk) load_scales(kt + 1);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
-            constexpr int r0 = ks < SPREAD ? ROUNDS * ks / SPREAD : ROUNDS;
-            constexpr int r1 = ks < SPREAD ? ROUNDS * (ks + 1) / SPREAD : ROUNDS;
-            constexpr int NC = copy ? r1 - r0 : 0;
-            using I0 = std::integral_constant<int, 0>;
-            using IH = std::integral_constant<int, FN / 2>;
-            using IF = std::integral_constant<int, FN>;
+            using G0 = std::integral_constant<int, ks * NM>;
             big::wait_lgkmcnt0();
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (XR > 0 && ks == 1) {
@@ -928,26 +998,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             pin(f[ks & 1]);
-            if constexpr (copy) issue_part(kt + S - 1, cslot, std::integral_constant<int, r0>{}, std::integral_constant<int, r1>{});
-            if constexpr (ks + 1 < KS) {
-                read(base, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
-                multiply(f[ks & 1], ks_c, I0{}, IF{});
-                interleave(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{},
-                           std::integral_constant<int, NC>{});
+            if constexpr (MX) {
+                mx_kstep(kt, ks_c, base, cslot, nslot, CP{});
+            } else if constexpr (ks + 1 < KS) {
+                slots(f[ks & 1], ks_c, I0{}, std::integral_constant<int, NM>{}, G0{}, T_{}, base,
+                      std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1], CP{}, kt + S - 1, cslot);
             } else {
-                multiply(f[ks & 1], ks_c, I0{}, IH{});
-                interleave(std::integral_constant<int, FN / 2 * FM>{},
-                           std::integral_constant<int, 0>{}, std::integral_constant<int, NC>{});
+                slots(f[ks & 1], ks_c, I0{}, IH{}, G0{}, F_{}, base, I0{}, f[(ks + 1) & 1], CP{}, kt + S - 1, cslot);
                 const bool more = kt + 1 < nk;
                 if (more) {
-                    if (copy) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
+                    if (CP::value) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
                     big::lds_barrier();
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (more) read(smem + nslot * SH::STAGE, I0{}, f[(ks + 1) & 1]);
-                multiply(f[ks & 1], ks_c, IH{}, IF{});
-                interleave(std::integral_constant<int, (FN - FN / 2) * FM>{}, std::integral_constant<int, NR>{},
-                           std::integral_constant<int, 0>{});
+                if (more)
+                    slots(f[ks & 1], ks_c, IH{}, IR{}, INONE{}, T_{}, smem + nslot * SH::STAGE, I0{}, f[(ks + 1) & 1],
+                          F_{}, kt, cslot);
+                else
+                    slots(f[ks & 1], ks_c, IH{}, IR{}, INONE{}, F_{}, base, I0{}, f[(ks + 1) & 1], F_{}, kt, cslot);
             }
         });
         take_scales();  // the next stage's (its loads were covered by the stage-end wait)
