@@ -547,9 +547,10 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 
 // workgroup barrier, and 2048 workgroups of four short waves fill the chip. Every input
 // of the token is requested before any is used; when the rope slice lies in the split-K
 // tail, its chunk x split partials are spread one per lane and summed across lanes in
-// split order.
+// split order. Rows of four or more chunks per lane (V3: three q and one kv) hold too many
+// values for four workgroups per CU (128 registers: they spilled to scratch) and run three.
 template <int QC, int KC>
-__global__ __launch_bounds__(256, 4) void norm_rope_wave_kernel(NormArgs a) {
+__global__ __launch_bounds__(256, QC + KC >= 4 ? 3 : 4) void norm_rope_wave_kernel(NormArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T) return;  // the whole wave leaves; nothing below synchronises the workgroup
@@ -770,15 +771,31 @@ __global__ __launch_bounds__(kRowThreads) void act_quant_kernel(const uint16_t* 
     __shared__ float red[kRowWaves];
     const int t = blockIdx.x;
     const uint16_t* row = x + static_cast<size_t>(t) * K;
+    int8_t* crow = codes + static_cast<size_t>(t) * K;
     const int nc = K >> 3;
+    // The row stays in registers between its amax and its codes (x is read once; a second
+    // pass missed L2 often enough to cost 18% of the kernel): up to kHold 16-byte chunks per
+    // thread, rows of up to 8192 values; longer rows read the rest again.
+    constexpr int kHold = 4;
+    uint4 v[kHold];
     float m = 0.f;
-    for (int c = threadIdx.x; c < nc; c += kRowThreads)
+#pragma unroll
+    for (int k = 0; k < kHold; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        v[k] = *reinterpret_cast<const uint4*>(row + min(c, nc - 1) * 8);
+        if (c < nc) m = fmaxf(m, absmax8(v[k]));
+    }
+    for (int c = threadIdx.x + kHold * kRowThreads; c < nc; c += kRowThreads)
         m = fmaxf(m, absmax8(*reinterpret_cast<const uint4*>(row + c * 8)));
     const float amax = block_max(m, red);
     const float mult = amax > 0.f ? 127.0f / amax : 0.f;
-    for (int c = threadIdx.x; c < nc; c += kRowThreads)
-        *reinterpret_cast<uint2*>(codes + static_cast<size_t>(t) * K + c * 8) =
-            quant8(*reinterpret_cast<const uint4*>(row + c * 8), mult);
+#pragma unroll
+    for (int k = 0; k < kHold; ++k) {
+        const int c = threadIdx.x + k * kRowThreads;
+        if (c < nc) *reinterpret_cast<uint2*>(crow + c * 8) = quant8(v[k], mult);
+    }
+    for (int c = threadIdx.x + kHold * kRowThreads; c < nc; c += kRowThreads)
+        *reinterpret_cast<uint2*>(crow + c * 8) = quant8(*reinterpret_cast<const uint4*>(row + c * 8), mult);
     if (threadIdx.x == 0) scale[t] = amax / 127.0f;
 }
 
