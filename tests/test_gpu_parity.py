@@ -7,6 +7,7 @@ benchmark times and the oracle computes a sample of token rows (first, last,
 tile edges and random rows), which is exact because every output row depends
 only on its own token.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -211,6 +212,18 @@ VARIANTS = [("v3_decode", 64, ALL3),
 def test_prolog_variants_parity(name, T, var):
     cfg = synth.get_config(name, T=T, **var)
     say("prolog parity", name, "T=%d" % cfg.T, var)
+    inp = synth.make_inputs(cfg)
+    out, stats = run_checked(cfg, inp)
+    say("  bit-exact fractions / excused rows / e2e (inside, worst):", fmt(stats))
+
+
+# W8A8 with rows longer than 8192 values: the activation quant holds 8192 values of a row in
+# registers between its amax and its codes and reads the rest again (hidden 8320 = 65 K-tiles
+# of 128 int8), on the weight-streaming and the large-batch tiles.
+@pytest.mark.parametrize("T", [37, 520])
+def test_prolog_w8a8_long_rows_parity(T):
+    cfg = dataclasses.replace(synth.get_config("v3_w8a8", T=T), hidden=8320)
+    say("prolog parity", "v3_w8a8 hidden=8320", "T=%d" % cfg.T)
     inp = synth.make_inputs(cfg)
     out, stats = run_checked(cfg, inp)
     say("  bit-exact fractions / excused rows / e2e (inside, worst):", fmt(stats))
