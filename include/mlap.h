@@ -279,10 +279,10 @@ MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n);
 
 /* Shader clock of the timed kernel (measurement support): while timing is armed, every
  * launch of the armed kernel that runs on the LDS-DMA GEMM (gemm_down, gemm_up_q, gemm_up_kv
- * past the weight-streaming batches or on its tiles) adds, per workgroup, the shader-clock
- * cycles and the constant 100 MHz clock ticks it ran for into counters[0] and counters[1]
- * (device memory, two uint64, caller-owned, zeroed by the caller; 8-byte aligned). Their ratio
- * times 100 MHz is the average shader clock while that kernel ran. NULL disarms. */
+ * past the weight-streaming batches or on its tiles) adds, for every 16th workgroup, the
+ * shader-clock cycles and the constant 100 MHz clock ticks it ran for into counters[0] and
+ * counters[1] (device memory, two uint64, caller-owned, zeroed by the caller; 8-byte aligned).
+ * Their ratio times 100 MHz is the average shader clock while that kernel ran. NULL disarms. */
 MLAP_API int mlap_timing_clock(mlap_handle h, unsigned long long* counters);
 
 /* Bounds checks of the debug build (the library compiled with MLAP_DEBUG; a test and
