@@ -203,11 +203,8 @@ MLAP_API int mlap_workspace_size(mlap_handle h, int32_t T, size_t* bytes);
 /* Enqueue the whole prolog for in->T tokens on `stream`. `ws` must hold at least
  * mlap_workspace_size(h, in->T) bytes, 256-byte aligned. T == 0 is a no-op.
  * Runs on one handle must not overlap in time unless they use distinct workspaces, and a
- * handle is not for concurrent calls from several host threads.
- * Large int8 (W8A8) batches also use a second stream, created by the handle on its first
- * such run on the current device: the run forks onto it and joins back to `stream` through
- * events, so all work stays ordered on `stream` and the run can be captured into a HIP
- * graph on `stream`. */
+ * handle is not for concurrent calls from several host threads. All work is enqueued on
+ * `stream` (no host synchronisation), so a run can be captured into a HIP graph. */
 MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
              void* ws, size_t ws_bytes);
 
@@ -218,8 +215,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
  * (64 MiB) per GPU, part of the library's code object: it is loaded with the library on each GPU
  * the library runs on and held until the process ends. A run whose mlap_workspace_size exceeds
  * it returns MLAP_ERR_WORKSPACE (V3 bf16: up to T = 8192 fits). Nothing here allocates: no
- * device or host buffer, stream or event (large W8A8 batches therefore run their q quant on
- * `stream` after the projection instead of on the second stream mlap_run uses). Every call on
+ * device or host buffer, stream or event. Every call on
  * one GPU shares that GPU's array, from any handle: calls that overlap in time on one GPU race
  * and give wrong results; order them on one stream or serialise them. No run needs the array
  * cleared (each run writes every workspace byte it reads).
@@ -227,7 +223,7 @@ MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const 
 #define MLAP_STATIC_SCRATCH_BYTES (64u << 20)
 MLAP_API int mlap_run_static(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out);
 
-/* Free the handle (host memory, timing events and its second stream). NULL is allowed. */
+/* Free the handle (host memory and timing events). NULL is allowed. */
 MLAP_API void mlap_destroy(mlap_handle h);
 
 /* Static description of a status code. */

@@ -1,7 +1,6 @@
 // mlap_host.hip -- the C ABI of libmlap.so: validation, per-run plan and launches.
 //
-// The run is a fixed chain of kernels on the caller's stream (no host sync; at large int8
-// batches the q quant of each token block forks onto a second stream and joins back):
+// The run is a fixed chain of kernels on the caller's stream (no host sync):
 //   [W8A8: act_quant(x)] -> gemm_down (x . [W_qa; W_kva]^T, bf16 out)
 //   -> norm_rope (RMSNorm*gamma -> bf16 for q_a and c_kv, RoPE of k_pe, kv quant)
 //   -> gemm_up_q (q_norm . W_qb^T; per head: q_nope, RoPE'd q_pe, partial amax)
@@ -52,10 +51,7 @@ constexpr size_t kAlign = 256;
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kSmallBatch = 512;  // token counts up to this use the weight-streaming tiles
 constexpr int kGroupM = 4;        // M-tiles per group in the XCD-aware tile order
-constexpr int kGroupNq = 8;
-// token blocks of the q up projection whose quant overlaps the next block (large batches)
-constexpr int kQBlocks = 4;
-constexpr int kQBlockMinT = 2048;       // N-tiles per group for the q up projection (N-major split)
+constexpr int kGroupNq = 8;       // N-tiles per group for the q up projection (N-major split)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -132,12 +128,6 @@ struct mlap_prolog {
     int QH, KH;   // q head width (nope + rope), kv_b head width (nope + v)
     int bn_q, bn_kv;
     Timer timer;
-    // Large int8 batches quantise finished token blocks of q on a second stream while the q up
-    // projection continues with the next block (fork/join through events on the caller's
-    // stream, so the run stays ordered on it and can be captured into a graph). Created on
-    // the first run that uses them, on that run's device.
-    hipStream_t aux = nullptr;
-    hipEvent_t fork[kQBlocks + 1] = {};
 
     bool head_norm() const { return (cfg.flags & MLAP_Q_HEAD_NORM) && cfg.q_lora > 0; }
 
@@ -374,7 +364,7 @@ int validate(const mlap_config* c) {
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out, void* ws,
-             size_t ws_bytes, bool may_fork);
+             size_t ws_bytes);
 
 // The allocation-free entry point's workspace: a device array of kStaticScratchBytes in every
 // GPU's copy of this code object. Host code must never pass `scratch` itself to a kernel or a
@@ -479,9 +469,6 @@ MLAP_API int mlap_create(const mlap_config* cfg, mlap_handle* out) {
 MLAP_API void mlap_destroy(mlap_handle h) {
     if (!h) return;
     for (hipEvent_t e : h->timer.ev) (void)hipEventDestroy(e);
-    for (hipEvent_t e : h->fork)
-        if (e) (void)hipEventDestroy(e);
-    if (h->aux) (void)hipStreamDestroy(h->aux);
     delete h;
 }
 
@@ -556,7 +543,7 @@ MLAP_API int mlap_timing_end(mlap_handle h, float* ms, int32_t cap, int32_t* n) 
 
 MLAP_API int mlap_run(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out,
              void* ws, size_t ws_bytes) {
-    return run_impl(h, stream, in, out, ws, ws_bytes, true);
+    return run_impl(h, stream, in, out, ws, ws_bytes);
 }
 
 // The allocation-free run: the workspace is the file-scope device array `scratch` (one per GPU,
@@ -571,7 +558,7 @@ MLAP_API int mlap_run_static(mlap_handle h, void* stream, const mlap_inputs* in,
     void* ptr = nullptr;
     const int rc = static_scratch(&ptr);
     if (rc != MLAP_OK) return rc;
-    return run_impl(h, stream, in, out, ptr, kStaticScratchBytes, false);
+    return run_impl(h, stream, in, out, ptr, kStaticScratchBytes);
 }
 
 }  // extern "C"
@@ -579,7 +566,7 @@ MLAP_API int mlap_run_static(mlap_handle h, void* stream, const mlap_inputs* in,
 namespace {
 
 int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outputs* out, void* ws,
-             size_t ws_bytes, bool may_fork) {
+             size_t ws_bytes) {
     if (!h || !in || !out) return MLAP_ERR_INVALID_ARG;
     const mlap_config& c = h->cfg;
     const int T = in->T;
@@ -610,7 +597,6 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
     const bool quant_q = out->q_i8 || out->q_scale;
     const int per_head = (c.flags & MLAP_QUANT_Q_PER_HEAD) ? 1 : 0;
     const bool head_norm = h->head_norm();
-    bool quant_done = false;  // the q quant already ran per token block
     if (quant_q && out->q_i8 && (!out->q_nope || !out->q_pe)) return MLAP_ERR_INVALID_ARG;
     // the per-head quant reads every head's values back, and the per-head norm rewrites the
     // raw heads in place: both need the two q tensors, for any q output
@@ -876,77 +862,26 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
         } else {
             u.A = qn;
         }
-        // Only the int8 projection gains from the overlap: it is twice as fast per FLOP, so
-        // its quant is a larger share of the step; the bf16 projection slows under the
-        // concurrent quant by about what the overlap saves (measured at T=8192).
-        const bool blocks = may_fork && quant_q && w8 && plan.big_q && plan.q_shape == BigShape::kWide &&
-                            T >= kQBlockMinT;
-        if (!blocks) {
-            MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
-                                              : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
-            if (head_norm) {
-                QHeadNormArgs hn{};
-                hn.T = T;
-                hn.H = H;
-                hn.Dn = c.nope_dim;
-                hn.R = R;
-                hn.eps = c.eps;
-                hn.rsqrt = (c.flags & MLAP_NORM_RSQRT) ? 1 : 0;
-                hn.positions = in->positions;
-                hn.cos = in->cos;
-                hn.sin = in->sin;
-                hn.max_pos = c.max_pos;
-                hn.q_nope = static_cast<uint16_t*>(out->q_nope);
-                hn.q_pe = static_cast<uint16_t*>(out->q_pe);
-                hn.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
-                hn.groups = plan.hn_groups;
-                hn.q_proj = static_cast<uint16_t*>(out->q_proj);
-                MLAP_LAUNCH(kKQHeadNorm, launch_q_head_norm(hn, s));
-            }
-        } else {
-            // q in kQBlocks token blocks (whole 256-row tiles); block b's quant runs on the
-            // second stream as soon as its projection is done, under block b + 1's GEMM
-            if (!h->aux) {
-                if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess) return MLAP_ERR_HIP;
-                for (hipEvent_t& ev : h->fork)
-                    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return MLAP_ERR_HIP;
-            }
-            const int rows = (T / kQBlocks + kBigTile - 1) / kBigTile * kBigTile;
-            const size_t ea = w8 ? 1 : 2;
-            for (int b = 0; b * rows < T; ++b) {
-                const int r0 = b * rows, nr = std::min(rows, T - r0);
-                GemmArgs ub = u;
-                ub.M = nr;
-                ub.A = static_cast<const char*>(u.A) + static_cast<size_t>(r0) * Lq * ea;
-                if (w8) ub.a_scale = u.a_scale + r0;
-                ub.out0 = out->q_nope ? static_cast<uint16_t*>(out->q_nope) + static_cast<size_t>(r0) * H * c.nope_dim : nullptr;
-                ub.out1 = out->q_pe ? static_cast<uint16_t*>(out->q_pe) + static_cast<size_t>(r0) * H * R : nullptr;
-                ub.positions = in->positions + r0;
-                ub.part_amax = u.part_amax ? u.part_amax + static_cast<size_t>(r0) * plan.nt_q : nullptr;
-                MLAP_LAUNCH(kKGemmUpQ, launch_gemm_big(ub, it, Epi::kHeads, s, plan.q_shape));
-                if (hipEventRecord(h->fork[b], s) != hipSuccess || hipStreamWaitEvent(h->aux, h->fork[b], 0) != hipSuccess)
-                    return MLAP_ERR_HIP;
-                QuantQArgs qa{};
-                qa.T = nr;
-                qa.H = H;
-                qa.Dn = c.nope_dim;
-                qa.R = R;
-                qa.n_tiles = plan.nt_q;
-                qa.part_amax = ub.part_amax;
-                qa.per_head = per_head;
-                qa.q_nope = static_cast<const uint16_t*>(ub.out0);
-                qa.q_pe = static_cast<const uint16_t*>(ub.out1);
-                qa.q_i8 = out->q_i8 ? out->q_i8 + static_cast<size_t>(r0) * H * (c.nope_dim + R) : nullptr;
-                qa.q_scale = out->q_scale ? out->q_scale + static_cast<size_t>(r0) * (per_head ? H : 1) : nullptr;
-                hipStream_t s_main = s;
-                s = h->aux;  // MLAP_LAUNCH records the quant's timing on the stream it runs on
-                MLAP_LAUNCH(kKQuantQ, launch_quant_q(qa, s));
-                s = s_main;
-            }
-            if (hipEventRecord(h->fork[kQBlocks], h->aux) != hipSuccess ||
-                hipStreamWaitEvent(s, h->fork[kQBlocks], 0) != hipSuccess)
-                return MLAP_ERR_HIP;
-            quant_done = true;
+        MLAP_LAUNCH(kKGemmUpQ, plan.big_q ? launch_gemm_big(u, it, Epi::kHeads, s, plan.q_shape)
+                                          : launch_gemm(u, it, plan.up_q, Epi::kHeads, s));
+        if (head_norm) {
+            QHeadNormArgs hn{};
+            hn.T = T;
+            hn.H = H;
+            hn.Dn = c.nope_dim;
+            hn.R = R;
+            hn.eps = c.eps;
+            hn.rsqrt = (c.flags & MLAP_NORM_RSQRT) ? 1 : 0;
+            hn.positions = in->positions;
+            hn.cos = in->cos;
+            hn.sin = in->sin;
+            hn.max_pos = c.max_pos;
+            hn.q_nope = static_cast<uint16_t*>(out->q_nope);
+            hn.q_pe = static_cast<uint16_t*>(out->q_pe);
+            hn.part_amax = quant_q && !per_head ? reinterpret_cast<float*>(wsb + L.qpart) : nullptr;
+            hn.groups = plan.hn_groups;
+            hn.q_proj = static_cast<uint16_t*>(out->q_proj);
+            MLAP_LAUNCH(kKQHeadNorm, launch_q_head_norm(hn, s));
         }
     }
 
@@ -993,7 +928,7 @@ int run_impl(mlap_handle h, void* stream, const mlap_inputs* in, const mlap_outp
     }
 
     // 5. per-token INT8 quant of q (after RoPE), one scale over all heads
-    if (has_q && quant_q && !quant_done) {
+    if (has_q && quant_q) {
         QuantQArgs qa{};
         qa.T = T;
         qa.H = H;

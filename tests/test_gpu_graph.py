@@ -25,9 +25,8 @@ def _diff(a, b):
     return {"count": int(ne.shape[0]), "rows": rows[:12], "n_rows": len(rows), "first": first}
 
 
-# v3_w8a8 at T=2048 runs the q up projection in token blocks whose quant forks onto a
-# second stream and joins back, so the capture must carry that fork/join; the MXFP8 cases
-# add the weight decode / activation conversion launches of both routes
+# v3_w8a8 at T=2048 adds the activation quant and the int8 tiles with their dequantisation;
+# the MXFP8 cases add the weight decode / activation conversion launches of both routes
 @pytest.mark.parametrize("name,T,var", [("v3_decode", 64, {}), ("v3_decode", 256, {}),
                                         ("v2lite_kv_decode", None, {}), ("v3_prefill", 1000, {}),
                                         ("v3_w8a8", 2048, {}), ("v3_mxfp8", 300, {}),

@@ -6,8 +6,7 @@ outputs must equal mlap_run's bit for bit (the same kernels on the same inputs; 
 is held to the oracle by the parity tests), over two calls in a row on one handle, the second
 with fewer tokens (so it runs over the larger first call's leftovers in the shared scratch),
 and across configurations and batch-size buckets: the decode tiles, the large-batch tiles, the
-KV-Prolog mode and W8A8 at a size where mlap_run forks the q quant onto a second stream while
-the static entry point keeps it on the caller's stream.
+KV-Prolog mode and W8A8 on its large-batch int8 tiles.
 """
 import sys
 
