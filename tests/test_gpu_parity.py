@@ -255,6 +255,28 @@ def test_prolog_parity_full_size_sampled_rows(name, T):
     assert (out["kv_i8"].abs().amax(1) == 127).all()
 
 
+# Batch sizes drawn from a seeded generator, one in the weight-streaming bucket and one past
+# it per configuration, so that parity does not rest on hand-picked edges alone; rows are
+# sampled past 512 tokens (the full rows below that).
+def _sweep():
+    rng = np.random.default_rng(20261202)
+    cases = []
+    for name in ("v3_decode", "v3_w8a8", "v2lite_kv_decode", "v4_decode"):
+        cases.append((name, int(rng.integers(1, 513))))
+        cases.append((name, int(rng.integers(513, 1201))))
+    return cases
+
+
+@pytest.mark.parametrize("name,T", _sweep())
+def test_prolog_parity_seeded_batch_sizes(name, T):
+    cfg = synth.get_config(name, T=T)
+    say("prolog parity (seeded size)", name, "T=%d" % cfg.T)
+    inp = synth.make_inputs(cfg)
+    rows = sample_rows(cfg.T, n_random=24) if cfg.T > 512 else None
+    out, stats = run_checked(cfg, inp, rows=rows)
+    say("  rows", cfg.T if rows is None else len(rows), fmt(stats))
+
+
 # ------------------------------------------------------------- invariants ----
 
 def test_rope_keeps_pair_norms_against_position_zero():
