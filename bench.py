@@ -33,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -81,17 +82,25 @@ def path_work(cfg, T):
     return flops, weights + T * per_tok
 
 
+def code_only(text):
+    """C++ source without its comments and blank lines (the code a profile measured)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def kernel_source_hash():
-    """Hash of the sources that define and launch the dominant kernel (the GEMM kernels,
-    their tile choice and the host code that plans and launches them; sorted by name). The
-    row kernels (row_kernels.hip) are left out: the up projections read nothing from them
-    but their outputs."""
+    """Hash of the code that defines and launches the dominant kernel (the GEMM kernels,
+    their tile choice and the host code that plans and launches them; sorted by name),
+    comments left out so that a documentation edit does not void the profiles. The row
+    kernels (row_kernels.hip) are left out: the up projections read nothing from them but
+    their outputs."""
     d = os.path.join(ROOT, "mla_prolog_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp")) and f != "row_kernels.hip":
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(os.path.join(d, f), encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

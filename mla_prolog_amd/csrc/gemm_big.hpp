@@ -21,10 +21,11 @@
 // register 4g + q holds token (l % 32) and output column 8g + 4(l / 32) + q. Every lane
 // therefore owns runs of four consecutive output columns of its tokens.
 //
-// The k-step schedule is explicit (waits placed by hand, sched_group_barrier templates):
-// one MFMA, then one LDS read of the next k-step's fragments or one copy instruction,
-// and so on, so LDS latency and copy issue hide under the matrix pipe; one workgroup
-// barrier per stage, placed inside the last k-step.
+// The k-step schedule is explicit (waits placed by hand, fenced slots): one MFMA, then
+// the LDS reads of the next k-step's fragments and the copy instructions that fall on that
+// slot, so LDS latency and copy issue hide under the matrix pipe and the copies never
+// queue up behind the address unit; one workgroup barrier per stage, placed inside the
+// last k-step. (The block-scaled MXFP8 tile keeps sched_group_barrier templates.)
 #pragma once
 
 #include "gemm.hpp"
