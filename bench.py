@@ -233,12 +233,16 @@ def power_sample(name, seconds, rotate=1):
     for i in range(10):
         runs[i % rotate]()
     torch.cuda.synchronize()
-    samples, stop = [], []
+    samples, stop, errors = [], [], []
 
     def sampler():
         while not stop:
-            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True,
-                               text=True, timeout=30)
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=30)
+            except (OSError, subprocess.SubprocessError) as e:  # no amd-smi, or it hung
+                errors.append(repr(e))
+                return
             try:
                 g = json.loads(r.stdout)
                 g = g["gpu_data"][0] if isinstance(g, dict) and "gpu_data" in g else g[0]
@@ -271,7 +275,8 @@ def power_sample(name, seconds, rotate=1):
     return {"workload": name, "T": cfg.T, "seconds": round(dt, 2), "steps": n, "ms_per_step": round(dt / n * 1e3, 5),
             "samples": len(mid), "socket_power_w": stats([s[1] for s in mid]),
             "gfx_clock_mhz": stats([s[2] for s in mid]),
-            "source": "amd-smi metric -g 0 -p -c --json, sampled every ~0.25 s"}
+            "source": "amd-smi metric -g 0 -p -c --json, sampled every ~0.25 s",
+            "error": errors[0] if errors else (None if mid else "no readable amd-smi samples")}
 
 
 def roofline_for(cfg, T, k, workload):
