@@ -255,22 +255,27 @@ def test_prolog_parity_full_size_sampled_rows(name, T):
     assert (out["kv_i8"].abs().amax(1) == 127).all()
 
 
-# Batch sizes drawn from a seeded generator, one in the weight-streaming bucket and one past
-# it per configuration, so that parity does not rest on hand-picked edges alone; rows are
-# sampled past 512 tokens (the full rows below that).
+# Batch sizes drawn from a seeded generator, per configuration one up to 64 tokens (the 32- and
+# 64-row tiles), one in the 256-row weight-streaming bucket and one past it, each with a seeded
+# choice of the numeric variants, so that parity does not rest on hand-picked edges alone; rows
+# are sampled past 512 tokens (the full rows below that).
 def _sweep():
     rng = np.random.default_rng(20261202)
+    flag_sets = [{}, dict(norm_rsqrt=True), dict(rope_interleaved=True), dict(q_quant_per_head=True), ALL3]
     cases = []
-    for name in ("v3_decode", "v3_w8a8", "v2lite_kv_decode", "v4_decode"):
-        cases.append((name, int(rng.integers(1, 513))))
-        cases.append((name, int(rng.integers(513, 1201))))
+    for name in ("v3_decode", "v3_w8a8", "v2lite_kv_decode", "v4_decode", "v3_mxfp8", "tiny_kv"):
+        for lo, hi in ((1, 65), (65, 513), (513, 1201)):
+            var = dict(flag_sets[int(rng.integers(0, len(flag_sets)))])
+            if name in ("v2lite_kv_decode", "tiny_kv"):
+                var.pop("q_quant_per_head", None)  # no q path in KV-Prolog mode
+            cases.append((name, int(rng.integers(lo, hi)), var))
     return cases
 
 
-@pytest.mark.parametrize("name,T", _sweep())
-def test_prolog_parity_seeded_batch_sizes(name, T):
-    cfg = synth.get_config(name, T=T)
-    say("prolog parity (seeded size)", name, "T=%d" % cfg.T)
+@pytest.mark.parametrize("name,T,var", _sweep())
+def test_prolog_parity_seeded_batch_sizes(name, T, var):
+    cfg = synth.get_config(name, T=T, **var)
+    say("prolog parity (seeded size)", name, "T=%d" % cfg.T, var)
     inp = synth.make_inputs(cfg)
     rows = sample_rows(cfg.T, n_random=24) if cfg.T > 512 else None
     out, stats = run_checked(cfg, inp, rows=rows)
