@@ -524,6 +524,9 @@ def main():
     ap.add_argument("--dominant", help="substring of the dominant kernel's name (with --summarize)")
     ap.add_argument("--calibrate-mib", type=int, default=512)
     ap.add_argument("--sclk-mhz", type=int, default=None)
+    ap.add_argument("--board-seconds", type=float, default=3.0, metavar="SECONDS",
+                    help="after timing the headline workload, run it back to back this long and "
+                         "record the board power and clocks in the line (0: skip)")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="instead of the benchmark: run --workload back to back for SECONDS and print "
                          "the board power and shader clocks sampled meanwhile (amd-smi)")
@@ -589,6 +592,12 @@ def main():
         "path": {"tflops": round(pf / (ms * 1e-3) / 1e12, 2),
                  "frac_bf16_peak": round(pf / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
+    if a.board_seconds > 0:
+        # the board's socket power and shader clocks under sustained load of the headline
+        # workload (the prefill step runs at the power limit, which sets its clock)
+        b = power_sample(a.workload, a.board_seconds, rotate=a.rotate)
+        line["board"] = {k: b[k] for k in ("seconds", "ms_per_step", "samples", "socket_power_w",
+                                           "gfx_clock_mhz", "source", "error")}
     if a.decode_workload:
         dcfg, de_ms, dk_ms, de_pct, dg_ms, dg_pct = bench_workload(a.decode_workload, a.decode_steps,
                                                                    a.warmup, rotate=4,
