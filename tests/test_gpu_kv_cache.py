@@ -63,7 +63,9 @@ CASES = [("v2lite_kv_decode", None, 200),
          ("v3_decode", None, 1024),
          ("v3_prefill", 1000, 4096),
          ("v3_prefill", 2048, 4096),
-         ("v3_w8a8", 130, 512)]
+         ("v3_w8a8", 130, 512),
+         ("v4_decode", None, 64),        # the V4 shape (per-head q norm after q_b)
+         ("v3_mxfp8", 300, 1024)]        # MXFP8 projections
 
 
 @pytest.mark.parametrize("name,T,n_slots", CASES)
