@@ -26,11 +26,13 @@ def _diff(a, b):
 
 
 # v3_w8a8 at T=2048 adds the activation quant and the int8 tiles with their dequantisation;
-# the MXFP8 cases add the weight decode / activation conversion launches of both routes
+# the MXFP8 cases add the weight decode / activation conversion launches of both routes; the
+# V4 shape its head norm spread over several workgroups per token
 @pytest.mark.parametrize("name,T,var", [("v3_decode", 64, {}), ("v3_decode", 256, {}),
                                         ("v2lite_kv_decode", None, {}), ("v3_prefill", 1000, {}),
                                         ("v3_w8a8", 2048, {}), ("v3_mxfp8", 300, {}),
-                                        ("v3_mxfp8", 1000, {"mxfp8_mfma": True})])
+                                        ("v3_mxfp8", 1000, {"mxfp8_mfma": True}),
+                                        ("v4_decode", None, {}), ("v4_decode", 64, {"q_quant_per_head": True})])
 def test_graph_replay_matches_eager(name, T, var):
     cfg = synth.get_config(name, T=T, **var)
     say("graph replay", name, "T=%d" % cfg.T)
