@@ -19,7 +19,10 @@
 // v_mfma_i32_32x32x32_i8). The weight fragment is the MFMA's first operand and the
 // activation fragment its second, so the accumulator is the transposed tile: lane l,
 // register 4g + q holds token (l % 32) and output column 8g + 4(l / 32) + q. Every lane
-// therefore owns runs of four consecutive output columns of its tokens.
+// therefore owns runs of four consecutive output columns of its tokens. The bf16 256 x 256
+// heads tile (the large-batch q up projection, which runs at the board's power limit) uses
+// v_mfma_f32_16x16x32_bf16 instead, 2 x 2 blocks of 16 x 16 per 32 x 32 fragment: less
+// energy per FLOP, so a higher clock under the limit (see the kernel's M16 path).
 //
 // The k-step schedule is explicit (waits placed by hand, fenced slots): one MFMA, then
 // the LDS reads of the next k-step's fragments and the copy instructions that fall on that
@@ -197,7 +200,10 @@ struct RopeOps<0> {
 // copies the tile's cos/sin rows into LDS while it packs the accumulators). W8A8: `scl`
 // holds the tile's dequantisation scales in LDS, a_scale of rows m0 + [0, BM) then b_scale
 // of columns n0 + [0, BN) (through b_row; rows and columns past the matrix edge clamped).
-template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, bool EARLY, typename AccT, int FN, int FM, int RF>
+// M16 (the 16 x 16 x 32 heads tile): register 4 gq + q of fragment (j, i) holds token
+// 32 i + 16 (gq / 2) + l % 16 and column 32 j + 16 (gq % 2) + 4 (l / 16) + q instead.
+template <typename Tin, int BM, int BN, int WM, int WN, Epi EPI, bool EARLY, bool M16, typename AccT, int FN,
+          int FM, int RF>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN][FM], char* smem,
                                               const float* scl, int m0, int n0, int n_tile, int split,
                                               RopeOps<RF>& rope_ops) {
@@ -208,6 +214,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int lr = lane & 31, lh = lane >> 5;
+    const int l16 = lane & 15, lq = lane >> 4;  // M16 lane view
+    static_assert(!M16 || (EPI == Epi::kHeads && RF > 0 && !EARLY), "the 16 x 16 form is the large heads tile");
     // Lane view of the transposed accumulator: token m = mb + 32 i + lr, columns
     // nb + 32 j + 8 g + 4 lh + q for register 4 g + q.
     const int mb = m0 + wm * TM + lr;
@@ -367,8 +375,20 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             }
             return mx;
         };
+        // |max| of the four packed words w[w0 .. w0 + 4) (M16: one token's eight columns)
+        auto absmax_words = [&](const uint32_t* w, int w0) __attribute__((always_inline)) {
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t a = w[w0 + e] & 0x7fff7fffu;
+                mx = fmaxf(mx, fmaxf(big::lo_bf(a), big::hi_bf(a)));
+            }
+            return mx;
+        };
+        float amx16[M16 ? FM : 1][2] = {};
         // lo = x1*cos - x2*sin (first half), hi = x2*cos + x1*sin (second half), cos/sin at
         // each value's own column: cc/ss[half][g] hold columns 32 half + 8 g + 4 (l / 32) + q
+        // (M16: columns 32 half + 16 (g % 2) + 4 (l / 16) + q of token 16 (g / 2) + l % 16)
         auto rotate = [&](uint32_t(&lo)[8], uint32_t(&hi)[8], const float4(&cc)[2][4],
                           const float4(&ss)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -433,18 +453,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
             if (sj >= 0) {
                 static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
-                    const int t = 32 * i + lr;
-                    const char* crow = cs_lds + (wm * CS_ROWS + t) * 256;
-                    const char* srow = crow + TM * 256;
                     float4 cc[2][4], ss[2][4];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int gq = 0; gq < 4; ++gq) {
+                        // the token and the 4-column chunk of group gq (16 B chunks of the row)
+                        const int t = M16 ? 32 * i + 16 * (gq >> 1) + l16 : 32 * i + lr;
+                        const int ch = M16 ? 4 * (gq & 1) + lq : 2 * gq + lh;
+                        const char* crow = cs_lds + (wm * CS_ROWS + t) * 256;
+                        const char* srow = crow + TM * 256;
 #pragma unroll
-                        for (int gq = 0; gq < 4; ++gq) {
-                            const int off = ((8 * h + 2 * gq + lh) ^ (t & 15)) * 16;
+                        for (int h = 0; h < 2; ++h) {
+                            const int off = ((8 * h + ch) ^ (t & 15)) * 16;
                             cc[h][gq] = *reinterpret_cast<const float4*>(crow + off);
                             ss[h][gq] = *reinterpret_cast<const float4*>(srow + off);
                         }
+                    }
                     static_for<FN - 1>([&](auto j_c) __attribute__((always_inline)) {
                         constexpr int j = decltype(j_c)::value;
                         if (j == sj) rotate(w[j][i], w[j + 1][i], cc, ss);
@@ -456,8 +479,21 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
                 constexpr int j = decltype(j_c)::value;
                 static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
-                    stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w[j][i]);
-                    amx[i] = fmaxf(amx[i], absmax_frag(w[j][i]));
+                    if constexpr (M16) {
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int row = wm * TM + 32 * i + 16 * (gq >> 1) + l16;
+                            const int col = wn * TN + 32 * j + 16 * (gq & 1) + 4 * lq;
+                            *reinterpret_cast<uint2*>(smem + row * PITCH + col * 2) =
+                                make_uint2(w[j][i][2 * gq], w[j][i][2 * gq + 1]);
+                        }
+                        // token halves: words 0..3 (first 16 tokens), 4..7 (second 16)
+                        amx16[i][0] = fmaxf(amx16[i][0], absmax_words(w[j][i], 0));
+                        amx16[i][1] = fmaxf(amx16[i][1], absmax_words(w[j][i], 4));
+                    } else {
+                        stage_frag(wm * TM + 32 * i + lr, wn * TN + 32 * j + 4 * lh, w[j][i]);
+                        amx[i] = fmaxf(amx[i], absmax_frag(w[j][i]));
+                    }
                 });
             });
         } else {
@@ -498,7 +534,19 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, AccT (&acc)[FN]
                 }
             }
         }
-        if (g.part_amax) {
+        if (M16 && g.part_amax) {
+            // a token's maxima are spread over the four lanes l % 16 + 16 k
+            static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+#pragma unroll
+                for (int si = 0; si < 2; ++si) {
+                    float mx = amx16[M16 ? i : 0][si];
+                    mx = fmaxf(mx, __shfl_xor(mx, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    if (lq == 0) wave_amax[wn * BM + wm * TM + 32 * i + 16 * si + l16] = mx;
+                }
+            });
+        } else if (g.part_amax) {
             static_for<FM>([&](auto i_c) __attribute__((always_inline)) {
                 constexpr int i = decltype(i_c)::value;
                 const float mx = fmaxf(amx[i], __shfl_xor(amx[i], 32));
@@ -617,6 +665,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // them.
     constexpr int RF = EPI == Epi::kHeads && FN > 1 ? FM : 0;
     constexpr bool EARLY = WM * WN <= 4 && SH::FM <= 2;
+    // The bf16 256 x 256 heads tile (the large-batch q up projection) runs on
+    // v_mfma_f32_16x16x32_bf16 instead of the 32 x 32 x 16 form: the same operand bytes and
+    // FLOPs per cycle, but about 20% less energy per FLOP (the accumulator traffic of a
+    // 16 x 16 block is half that of a 32 x 32 one per FLOP), which the power-limited prefill
+    // step turns into clock.
+    constexpr bool M16 = std::is_same<Tin, uint16_t>::value && EPI == Epi::kHeads && BM == 256 && BN == 256 &&
+                         WM == 4 && WN == 2 && KB == 128 && S == 2 && XR == 0;
     RopeOps<RF> rope_ops;
     if constexpr (RF > 0) {
         rope_ops.on = false;
@@ -915,7 +970,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         }
     });
     Frags f[2];
-    if (nk > 0) {
+    if (!M16 && nk > 0) {
         if (nk >= S - 1) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
         big::lds_barrier();
         take_scales();
@@ -1022,15 +1077,137 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
         take_scales();  // the next stage's (its loads were covered by the stage-end wait)
         slot = nslot;
     };
-    int kt = 0;
-    for (; kt + S - 1 < nk; ++kt) stage(kt, std::true_type{});
-    for (; kt < nk; ++kt) {
-        if (EARLY && kt + 1 == nk) rope_ops.gather(g, lh);  // lands under the last stage's MFMAs
-        stage(kt, std::false_type{});
+    if constexpr (M16) {
+        // 16 x 16 x 32 MFMAs (mma16x16). A k-step is 32 of K (64 bytes of every row); a
+        // 32-row fragment unit is two 16-row sub-fragments, lane l reading row 16 s + l % 16,
+        // logical chunk 4 ks + l / 16 (the swizzle of row l % 16 holds for every unit and
+        // half). Block (sj, si) of unit (j, i), weight half sj times token half si, lives in
+        // registers 4 (2 si + sj) + [0, 4) of acc[j][i]: lane l holds token
+        // 32 i + 16 si + l % 16 and columns 32 j + 16 sj + 4 (l / 16) + [0, 4).
+        // A k-step's 32 MFMAs go weight sub-fragment by weight sub-fragment, each against
+        // the four token sub-fragments; the weight sub-fragments stream through a ring of
+        // LEAD + 1 registers, each read LEAD sub-fragments (4 LEAD MFMAs) ahead of its
+        // first use, into the registers of the one whose last use just passed, so a k-step
+        // holds four of its eight at a time; the token sub-fragments of the next k-step are
+        // read during this one (two sets). Slots as in the 32 x 32 form: MFMA m, the reads
+        // and copy rounds that fall on it, a scheduling fence. The stage barrier follows the
+        // slot that reads the stage's last weight sub-fragment; the next stage's first reads
+        // come after it.
+        constexpr int XS = 2 * FM;         // token sub-fragments per k-step
+        constexpr int WS = 2 * FN;         // weight sub-fragments per k-step
+        constexpr int KS2 = KB / 64;       // k-steps per stage
+        constexpr int MK = WS * XS;        // MFMAs per k-step
+        constexpr int MS = KS2 * MK;       // MFMAs per stage
+        constexpr int NWS = KS2 * WS;      // weight sub-fragments per stage
+        constexpr int LEAD = 3;
+        constexpr int RING = LEAD + 1;
+        constexpr int PRE16 = (NWS - 1 - LEAD) * XS + 1;  // slots up to the last read of the stage
+        static_assert(XS == 4 && KS2 == 2 && NWS % RING == 0 && ROUNDS <= PRE16 && PRE16 + XS <= MS && S == 2,
+                      "schedule written for the 4 x 2 wave tile and a two-slot ring");
+        const int lq = lane >> 4, l16 = lane & 15;
+        int wo[KS2][2], xo[KS2][2];
+#pragma unroll
+        for (int k2 = 0; k2 < KS2; ++k2)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int chunk = ((4 * k2 + lq) ^ big::swz<KB>(l16)) * 16;
+                wo[k2][h] = (BM + wn * TN + 16 * h + l16) * KB + chunk;
+                xo[k2][h] = (wm * TM + 16 * h + l16) * KB + chunk;
+            }
+        i32x4 xa[2][XS];  // [k-step parity][2 i + si]
+        i32x4 wr[RING];   // weight sub-fragment n of a stage (n = WS k-step + 2 j + sj) in wr[n % RING]
+        auto read_w = [&](const char* base, auto n_c) __attribute__((always_inline)) {
+            constexpr int n = decltype(n_c)::value, k2 = n / WS, ws = n % WS;
+            wr[n % RING] = *reinterpret_cast<const i32x4*>(base + (ws >> 1) * 32 * KB + wo[k2][ws & 1]);
+        };
+        auto read_x = [&](const char* base, auto k2_c, auto q_c) __attribute__((always_inline)) {
+            constexpr int k2 = decltype(k2_c)::value, q = decltype(q_c)::value;
+            xa[k2 & 1][q] = *reinterpret_cast<const i32x4*>(base + (q >> 1) * 32 * KB + xo[k2][q & 1]);
+        };
+        auto mma16 = [&](auto m_c) __attribute__((always_inline)) {
+            constexpr int m = decltype(m_c)::value, k2 = m / MK, ws = (m % MK) / XS, q = m % XS;
+            constexpr int j = ws >> 1, i = q >> 1, b = 2 * (q & 1) + (ws & 1);
+            f32x4 t = {acc[j][i][4 * b], acc[j][i][4 * b + 1], acc[j][i][4 * b + 2], acc[j][i][4 * b + 3]};
+            t = big::mma16x16(wr[(k2 * WS + ws) % RING], xa[k2 & 1][q], t);
+            acc[j][i][4 * b] = t[0];
+            acc[j][i][4 * b + 1] = t[1];
+            acc[j][i][4 * b + 2] = t[2];
+            acc[j][i][4 * b + 3] = t[3];
+        };
+        // slots [LO, HI) of a stage; NX: the next stage's first reads (from nbase) after the
+        // barrier; CP: the copy rounds of stage ckt into ring slot cslot, one per slot
+        auto slots16 = [&](auto lo_c, auto hi_c, auto nx_c, auto cp_c, const char* base, const char* nbase, int ckt,
+                           int cslot) __attribute__((always_inline)) {
+            constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+            constexpr bool NX = decltype(nx_c)::value, CP = decltype(cp_c)::value;
+            const int koff = kphys(ckt) * KB;
+            char* dst = smem + cslot * SH::STAGE + wave * 1024;
+            static_for<HI - LO>([&](auto k_c) __attribute__((always_inline)) {
+                constexpr int m = LO + decltype(k_c)::value;
+                mma16(std::integral_constant<int, m>{});
+                __builtin_amdgcn_sched_barrier(0);  // the slot's reads after its MFMA
+                if constexpr (m % XS == 0 && m < PRE16 && m / XS + LEAD < NWS)
+                    read_w(base, std::integral_constant<int, m / XS + LEAD>{});
+                if constexpr (m < MK && m % XS == 2 && m / XS < XS)  // the second k-step's tokens
+                    read_x(base, std::integral_constant<int, 1>{}, std::integral_constant<int, m / XS>{});
+                if constexpr (NX && m >= PRE16) {
+                    if constexpr (m - PRE16 < XS)
+                        read_x(nbase, std::integral_constant<int, 0>{}, std::integral_constant<int, m - PRE16>{});
+                    if constexpr (m % XS == 0 && m / XS + LEAD >= NWS)
+                        read_w(nbase, std::integral_constant<int, m / XS + LEAD - NWS>{});
+                }
+                if constexpr (CP) {
+                    static_for<ROUNDS>([&](auto c_c) __attribute__((always_inline)) {
+                        constexpr int c = decltype(c_c)::value;
+                        if constexpr (c == m) big::copy16_to_lds(src[c] + koff, dst + c * SH::RROWS * KB);
+                    });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        using I0 = std::integral_constant<int, 0>;
+        using IP = std::integral_constant<int, PRE16>;
+        using IE = std::integral_constant<int, MS>;
+        auto stage16 = [&](int kt, auto cp_c) __attribute__((always_inline)) {
+            using CP = std::integral_constant<bool, decltype(cp_c)::value>;
+            const int cslot = slot == 0 ? S - 1 : slot - 1;
+            const int nslot = slot + 1 == S ? 0 : slot + 1;
+            const char* base = smem + slot * SH::STAGE;
+            const char* nbase = smem + nslot * SH::STAGE;
+            // with a two-slot ring the stages that copy ahead are exactly those another stage
+            // follows: the loops below pass that as a constant, so the steady-state stage has
+            // no branch and the compiler's LDS wait counts stay exact across iterations
+            slots16(I0{}, IP{}, F_{}, CP{}, base, nbase, kt + S - 1, cslot);
+            if constexpr (CP::value) {
+                big::wait_vmcnt<0>();
+                big::lds_barrier();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            slots16(IP{}, IE{}, CP{}, F_{}, base, nbase, kt, cslot);
+            slot = nslot;
+        };
+        if (nk > 0) {
+            if (nk >= S - 1) big::wait_vmcnt<(S - 2) * ROUNDS>(); else big::wait_vmcnt<0>();
+            big::lds_barrier();
+            static_for<XS>([&](auto q_c) __attribute__((always_inline)) { read_x(smem, I0{}, q_c); });
+            static_for<LEAD>([&](auto n_c) __attribute__((always_inline)) { read_w(smem, n_c); });
+        }
+        int kt = 0;
+        for (; kt + S - 1 < nk; ++kt) stage16(kt, std::true_type{});
+        for (; kt < nk; ++kt) stage16(kt, std::false_type{});
+    } else {
+        int kt = 0;
+        for (; kt + S - 1 < nk; ++kt) stage(kt, std::true_type{});
+        for (; kt < nk; ++kt) {
+            if (EARLY && kt + 1 == nk) rope_ops.gather(g, lh);  // lands under the last stage's MFMAs
+            stage(kt, std::false_type{});
+        }
+        if (EARLY && nk == 0) rope_ops.gather(g, lh);
     }
-    if (EARLY && nk == 0) rope_ops.gather(g, lh);
 
-    tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY>(g, acc, smem, scl, m0, n0, n_tile, split, rope_ops);
+    tile_epilogue<Tin, BM, BN, WM, WN, EPI, EARLY, M16>(g, acc, smem, scl, m0, n0, n_tile, split, rope_ops);
     if constexpr (XR > 0) {
         // lane l < 32 holds extra columns 4 (l / 16) + [0, 4) of token l % 16 of each group;
         // W8A8 dequantises them like the tile, f32(acc) * (a_scale[m] * b_scale[n])
