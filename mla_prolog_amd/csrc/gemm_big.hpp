@@ -20,9 +20,9 @@
 // activation fragment its second, so the accumulator is the transposed tile: lane l,
 // register 4g + q holds token (l % 32) and output column 8g + 4(l / 32) + q. Every lane
 // therefore owns runs of four consecutive output columns of its tokens. The bf16 256 x 256
-// heads tile (the large-batch q up projection, which runs at the board's power limit) uses
-// v_mfma_f32_16x16x32_bf16 instead, 2 x 2 blocks of 16 x 16 per 32 x 32 fragment: less
-// energy per FLOP, so a higher clock under the limit (see the kernel's M16 path).
+// heads tile (the large-batch q and kv_b up projections; the q projection runs at the board's
+// power limit) uses v_mfma_f32_16x16x32_bf16 instead, 2 x 2 blocks of 16 x 16 per 32 x 32
+// fragment: less energy per FLOP, so a higher clock under the limit (the kernel's M16 path).
 //
 // The k-step schedule is explicit (waits placed by hand, fenced slots): one MFMA, then
 // the LDS reads of the next k-step's fragments and the copy instructions that fall on that
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_big_kernel(GemmArgs g) {
     // them.
     constexpr int RF = EPI == Epi::kHeads && FN > 1 ? FM : 0;
     constexpr bool EARLY = WM * WN <= 4 && SH::FM <= 2;
-    // The bf16 256 x 256 heads tile (the large-batch q up projection) runs on
+    // The bf16 256 x 256 heads tile (the large-batch q and kv_b up projections) runs on
     // v_mfma_f32_16x16x32_bf16 instead of the 32 x 32 x 16 form: the same operand bytes and
     // FLOPs per cycle, but about 20% less energy per FLOP (the accumulator traffic of a
     // 16 x 16 block is half that of a 32 x 32 one per FLOP), which the power-limited prefill
