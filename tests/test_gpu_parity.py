@@ -189,6 +189,11 @@ VARIANTS = [("v3_decode", 64, ALL3),
             ("v2lite_kv_decode", None, dict(norm_rsqrt=True, rope_interleaved=True)),
             ("tiny_kv", None, dict(rope_interleaved=True)),
             ("v3_w8a8", 130, ALL3),
+            # the large-batch 256 x 256 heads tile (16 x 16 x 32 MFMAs in bf16): q with every
+            # variant, kv_b in KV-Prolog mode, the V4 q projection before its per-head norm
+            ("v3_decode", 600, ALL3),
+            ("v2lite_kv_decode", 700, dict(norm_rsqrt=True, rope_interleaved=True)),
+            ("v4_decode", 700, dict(norm_rsqrt=True)),
             # the V4-shape prolog (per-head q RMSNorm after q_b), alone and with the variants
             ("v4_decode", None, {}),
             ("v4_decode", 100, dict(norm_rsqrt=True, rope_interleaved=True)),
